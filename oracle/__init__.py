@@ -1,0 +1,205 @@
+"""ctypes wrapper of the C oracle (test infrastructure only).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark use this package.  It marshals numpy arrays into the C functions of
+leapq_oracle.c and holds no arithmetic of its own beyond widening bf16 inputs
+to fp32, which is exact.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+D = 128
+_LIB = None
+
+
+def lib(path=None):
+    """Load (building if absent) the oracle shared object."""
+    global _LIB
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _LIB = _bind(ctypes.CDLL(_build.LIB))
+    return _LIB
+
+
+def _bind(L):
+    f32p = ctypes.POINTER(ctypes.c_float)
+    i8p = ctypes.POINTER(ctypes.c_int8)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    ci, cf, cd = ctypes.c_int, ctypes.c_float, ctypes.c_double
+    sig = {
+        "lqo_t128_sum": (cf, [f32p]),
+        "lqo_t128_dot": (cf, [f32p, f32p]),
+        "lqo_residual": (None, [i8p, f32p, f32p, f32p]),
+        "lqo_boundary": (None, [i8p, f32p, f32p, ci, i32p, f32p, f32p]),
+        "lqo_current": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, f32p]),
+        "lqo_quantize": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_init": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_fold": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
+        "lqo_append": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p,
+                              f32p, f32p, f32p, cf, cf, f32p]),
+        "lqo_gdn_step_f32": (None, [f32p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
+        "lqo_gdn_step_f64": (None, [f64p, f64p, f64p, f64p, cd, cd, f64p, f64p]),
+        "lqo_gdn_step_bf16": (None, [u16p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
+        "lqo_f32_to_bf16": (ctypes.c_uint16, [cf]),
+        "lqo_dim": (ci, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+def _p(a, ct):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def bf16_bits_to_f32(bits):
+    """Exact widening of bf16 bit patterns (uint16) to fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def t128_sum(f, L=None):
+    L = L or lib()
+    return float(L.lqo_t128_sum(_p(f32(f), ctypes.c_float)))
+
+
+def t128_dot(a, b, L=None):
+    L = L or lib()
+    return float(L.lqo_t128_dot(_p(f32(a), ctypes.c_float), _p(f32(b), ctypes.c_float)))
+
+
+class Head:
+    """One head's LeapQuant state held in numpy arrays, driven by the oracle.
+
+    Q is int8 [128][128] in logical (key row, value column) order; rho and
+    sigma are fp32 [128]; idx int32 [C]; vec fp32 [C][128]; records gam [W],
+    rk [W][128], ru [W][128]; n is the number of records in the window.
+    """
+
+    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None):
+        self.L = L or lib()
+        self.C, self.W, self.smoothing, self.floor = int(C), int(W), int(smoothing), float(sigma_floor)
+        self.Q = np.zeros((D, D), np.int8)
+        self.rho = np.zeros(D, np.float32)
+        self.sigma = np.ones(D, np.float32)
+        self.idx = np.full(max(self.C, 1), -1, np.int32)
+        self.vec = np.zeros((max(self.C, 1), D), np.float32)
+        self.gam = np.zeros(max(self.W, 1), np.float32)
+        self.rk = np.zeros((max(self.W, 1), D), np.float32)
+        self.ru = np.zeros((max(self.W, 1), D), np.float32)
+        self.n = 0
+
+    def _st(self):
+        fp, ip = ctypes.c_float, ctypes.c_int8
+        return (_p(self.Q, ip), _p(self.rho, fp), _p(self.sigma, fp), self.C,
+                _p(self.idx, ctypes.c_int32), _p(self.vec, fp))
+
+    def _rec(self):
+        fp = ctypes.c_float
+        return (self.n, _p(self.gam, fp), _p(self.rk, fp), _p(self.ru, fp))
+
+    def init(self, S0):
+        S0 = f32(S0).reshape(D, D)
+        fp = ctypes.c_float
+        self.L.lqo_init(_p(S0, fp), self.C, self.smoothing, self.floor, _p(self.Q, ctypes.c_int8),
+                        _p(self.rho, fp), _p(self.sigma, fp), _p(self.idx, ctypes.c_int32),
+                        _p(self.vec, fp))
+        self.n = 0
+        return self
+
+    def append(self, q, k, v, alpha, beta):
+        """One token; returns (o, u) as fp32 arrays."""
+        if self.n >= self.W:
+            raise RuntimeError("window full: fold before the next append")
+        q, k, v = f32(q), f32(k), f32(v)
+        o = np.zeros(D, np.float32)
+        fp = ctypes.c_float
+        self.L.lqo_append(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp),
+                          float(np.float32(alpha)), float(np.float32(beta)), _p(o, fp))
+        self.n += 1
+        return o, self.ru[self.n - 1].copy()
+
+    def fold(self):
+        self.L.lqo_fold(*self._st(), *self._rec(), self.smoothing, self.floor)
+        self.n = 0
+        return self
+
+    def dequant(self, what):
+        out = np.zeros((D, D), np.float32)
+        fp = ctypes.c_float
+        if what == 0:
+            self.L.lqo_residual(_p(self.Q, ctypes.c_int8), _p(self.rho, fp), _p(self.sigma, fp),
+                                _p(out, fp))
+        elif what == 1:
+            self.L.lqo_boundary(*self._st(), _p(out, fp))
+        elif what == 2:
+            self.L.lqo_current(*self._st(), *self._rec(), _p(out, fp))
+        else:
+            raise ValueError("what must be 0, 1 or 2")
+        return out
+
+    def copy(self):
+        h = Head(self.C, self.W, self.smoothing, self.floor, self.L)
+        for name in ("Q", "rho", "sigma", "idx", "vec", "gam", "rk", "ru"):
+            setattr(h, name, getattr(self, name).copy())
+        h.n = self.n
+        return h
+
+
+def quantize(R, C=4, smoothing=True, sigma_floor=1e-6, L=None):
+    """Quantize a full fp32 matrix; returns a fresh Head at n = 0."""
+    return Head(C, 16, smoothing, sigma_floor, L).init(R)
+
+
+def gdn_step_f32(S, q, k, v, alpha, beta, L=None):
+    """Dense fp32 GDN token step, in place on S [128][128]; returns (u, o)."""
+    L = L or lib()
+    assert S.dtype == np.float32 and S.flags["C_CONTIGUOUS"]
+    u = np.zeros(D, np.float32)
+    o = np.zeros(D, np.float32)
+    fp = ctypes.c_float
+    L.lqo_gdn_step_f32(_p(S, fp), _p(f32(q), fp), _p(f32(k), fp), _p(f32(v), fp),
+                       float(np.float32(alpha)), float(np.float32(beta)), _p(u, fp), _p(o, fp))
+    return u, o
+
+
+def gdn_step_f64(S, q, k, v, alpha, beta, L=None):
+    """Dense fp64 GDN token step, in place on S; returns (u, o)."""
+    L = L or lib()
+    assert S.dtype == np.float64 and S.flags["C_CONTIGUOUS"]
+    dp = ctypes.c_double
+    u = np.zeros(D, np.float64)
+    o = np.zeros(D, np.float64)
+    c = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+    L.lqo_gdn_step_f64(_p(S, dp), _p(c(q), dp), _p(c(k), dp), _p(c(v), dp), float(alpha),
+                       float(beta), _p(u, dp), _p(o, dp))
+    return u, o
+
+
+def gdn_step_bf16(Sb, q, k, v, alpha, beta, L=None):
+    """Dense bf16-state GDN token step, in place on Sb (uint16 bits); returns (u, o)."""
+    L = L or lib()
+    assert Sb.dtype == np.uint16 and Sb.flags["C_CONTIGUOUS"]
+    u = np.zeros(D, np.float32)
+    o = np.zeros(D, np.float32)
+    fp = ctypes.c_float
+    L.lqo_gdn_step_bf16(_p(Sb, ctypes.c_uint16), _p(f32(q), fp), _p(f32(k), fp), _p(f32(v), fp),
+                        float(np.float32(alpha)), float(np.float32(beta)), _p(u, fp), _p(o, fp))
+    return u, o
+

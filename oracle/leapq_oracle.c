@@ -1,0 +1,416 @@
+/*
+ * LeapQuant per-window int8 recurrent state for Gated DeltaNet heads:
+ * the ORACLE.  A plain, slow, single-threaded CPU statement of what the
+ * decode path computes, one head at a time.
+ *
+ * This file is test infrastructure.  Only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark may load it.  The GPU library
+ * shares no code, header, table or helper with it, and neither includes the
+ * other.
+ *
+ * Sources (the method pages):
+ *   [RN4]  "Recurrent-state quantization for linear attention: a first GPU
+ *          kernel" (fastpathlabs.ai research note 4): Background (the order
+ *          of one GDN token update), Why rounding the state is difficult
+ *          (window of 16, records, fold, compensators, smoothing),
+ *          What we built (append / fold split), Results.
+ *   [LQ]   "LeapQuant: Efficient Linear Attention with Accurate Recurrent
+ *          State Quantization" (paperlayer.ai summary of arXiv 2609.38166v1):
+ *          abstract; 3.1 Preliminaries; 3.2 Per-window quantization;
+ *          3.3 Compensator tokens; 3.4 Residual smoothing; App. A
+ *          (general update, one rank-one record per GDN token); B.1
+ *          (error only at window boundaries); B.2 (window unrolling and
+ *          readout); B.3 (readout with a smoothed quantized residual);
+ *          4.3 (1.19 bytes per element); 4.4 (window 16, four compensators).
+ *
+ * Arithmetic contract.  The pages fix the storage precisions (an 8-bit
+ * residual, higher-precision records and compensators; fp32 for both here)
+ * but not the arithmetic.  Because the int8 codes and the compensator choice
+ * are integer decisions taken from fp32 values, the oracle computes in IEEE
+ * binary32, round to nearest even, no flush of subnormals, no contraction
+ * (a fused multiply-add appears only where fmaf() is written), correctly
+ * rounded '/' and sqrtf, and a fixed summation order: the canonical
+ * 128-term halving tree below.  Build with -ffp-contract=off and without
+ * -ffast-math.
+ *
+ * State of one head (D = 128; rows are key coordinates, columns are value
+ * coordinates, [LQ] 3.1):
+ *   Q[r][c]   int8 residual codes (logical row-major order)
+ *   rho[r]    fp32 per-row scale            sigma[c]  fp32 per-column smoothing
+ *   idx[j]    compensator line, j < C: -1 unused, 0..127 row r, 128+c column c
+ *   vec[j][]  fp32 copy of that line (128 values)
+ *   n         records in the current window; gam[i], rk[i][], ru[i][] for
+ *             i < n: cumulative decay since the window start, key, correction.
+ *
+ * Pins: every function here is pinned by the CPU tests (brute-force
+ * recurrence in fp32 and fp64, closed-form special cases, exact scaling,
+ * tree-automorphism equivariance, planted outliers, brute-force argmax,
+ * textbook absmax int8, round-half-even fixtures, page figures).  The
+ * compensator selection rule, the smoothing floor and the rounding mode are
+ * readings of pages that leave them open; the tests fix them but no page
+ * prints a worked fold to compare against.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define D 128
+
+/* ------------------------------------------------------------------ */
+/* Canonical sums                                                      */
+/* ------------------------------------------------------------------ */
+
+/* Sum of 128 terms by the canonical halving tree: level 0 adds term i and
+ * term i+64 (i < 64); each further level adds partial i and partial i+h for
+ * h = 32, 16, ..., 1.  The result is partial 0. */
+float lqo_t128_sum(const float f[D])
+{
+    float s[64];
+    for (int i = 0; i < 64; ++i) s[i] = f[i] + f[i + 64];
+    for (int h = 32; h >= 1; h >>= 1)
+        for (int i = 0; i < h; ++i) s[i] = s[i] + s[i + h];
+    return s[0];
+}
+
+/* Dot product of two 128-vectors by the same tree; at level 0 the pair
+ * (i, i+64) is formed with one fused multiply-add onto the rounded product
+ * of the upper term. */
+float lqo_t128_dot(const float a[D], const float b[D])
+{
+    float s[64];
+    for (int i = 0; i < 64; ++i) s[i] = fmaf(a[i], b[i], a[i + 64] * b[i + 64]);
+    for (int h = 32; h >= 1; h >>= 1)
+        for (int i = 0; i < h; ++i) s[i] = s[i] + s[i + h];
+    return s[0];
+}
+
+static float gamma_of(int n, const float *gam) { return n > 0 ? gam[n - 1] : 1.0f; }
+
+/* ------------------------------------------------------------------ */
+/* Dequantization ([LQ] B.3: scales apply to the residual only; the     */
+/* compensator lines are added in full precision).                      */
+/* ------------------------------------------------------------------ */
+
+/* Residual in original coordinates: (code * rho_r) * sigma_c. */
+void lqo_residual(const int8_t *Q, const float *rho, const float *sigma, float *out)
+{
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c)
+            out[r * D + c] = ((float)Q[r * D + c] * rho[r]) * sigma[c];
+}
+
+/* Adds scale * (compensator lines) to M, in compensator order.  A row token
+ * r contributes its line to row r, a column token c to column c.  Extracted
+ * lines were zero in the residual, so each entry receives at most one
+ * nonzero term and these adds are exact. */
+static void add_lines(float *M, int C, const int32_t *idx, const float *vec, float scale)
+{
+    for (int j = 0; j < C; ++j) {
+        const float *v = vec + (size_t)j * D;
+        if (idx[j] < 0) continue;
+        if (idx[j] < D) {
+            int r = idx[j];
+            for (int c = 0; c < D; ++c) M[r * D + c] = M[r * D + c] + scale * v[c];
+        } else {
+            int c = idx[j] - D;
+            for (int r = 0; r < D; ++r) M[r * D + c] = M[r * D + c] + scale * v[r];
+        }
+    }
+}
+
+/* Boundary state B = residual + compensator lines. */
+void lqo_boundary(const int8_t *Q, const float *rho, const float *sigma, int C,
+                  const int32_t *idx, const float *vec, float *out)
+{
+    lqo_residual(Q, rho, sigma, out);
+    add_lines(out, C, idx, vec, 1.0f);
+}
+
+/* Current state after n records of the window ([LQ] B.2 unrolling; [RN4]
+ * Why rounding: the fold applies the records):
+ *   S = gamma_n * B + sum_i (gamma_n / gamma_i) k_i u_i^T.
+ * Residual entries are formed as (code * (gamma_n * rho_r)) * sigma_c, the
+ * compensator lines as gamma_n * line, then each record i = 0..n-1 in order
+ * is applied to every entry with one fused multiply-add of
+ * w_i[r] = (gamma_n / gamma_i) * k_i[r] and u_i[c]. */
+void lqo_current(const int8_t *Q, const float *rho, const float *sigma, int C,
+                 const int32_t *idx, const float *vec, int n, const float *gam,
+                 const float *rk, const float *ru, float *out)
+{
+    float gn = gamma_of(n, gam);
+    for (int r = 0; r < D; ++r) {
+        float a = gn * rho[r];
+        for (int c = 0; c < D; ++c) out[r * D + c] = ((float)Q[r * D + c] * a) * sigma[c];
+    }
+    add_lines(out, C, idx, vec, gn);
+    for (int i = 0; i < n; ++i) {
+        float ci = gn / gam[i];
+        float w[D];
+        for (int r = 0; r < D; ++r) w[r] = ci * rk[(size_t)i * D + r];
+        for (int r = 0; r < D; ++r)
+            for (int c = 0; c < D; ++c)
+                out[r * D + c] = fmaf(w[r], ru[(size_t)i * D + c], out[r * D + c]);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantization of a full fp32 matrix: compensator extraction, residual */
+/* smoothing, per-row int8.  Used at init and at every fold.            */
+/* ------------------------------------------------------------------ */
+
+/* Largest row magnitude below which a row is stored as zeros: 127/M must
+ * stay finite. */
+#define LQO_TINY 0x1p-120f
+
+/* R is consumed (extracted lines are zeroed in place). */
+void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
+                  int8_t *Q, float *rho, float *sigma, int32_t *idx, float *vec)
+{
+    /* Compensator tokens ([LQ] 3.3; [RN4] Why rounding): greedy extraction
+     * of whole rows or columns, largest energy first.  Energy of a line is
+     * its canonical sum of squares.  Candidates are scanned rows 0..127 then
+     * columns 0..127 and the first strict maximum wins; a line already taken
+     * is not a candidate.  With no positive score left the slot is unused. */
+    int taken[2 * D];
+    memset(taken, 0, sizeof taken);
+    for (int j = 0; j < C; ++j) {
+        float score[2 * D];
+        for (int r = 0; r < D; ++r) score[r] = lqo_t128_dot(R + r * D, R + r * D);
+        for (int c = 0; c < D; ++c) {
+            float col[D];
+            for (int r = 0; r < D; ++r) col[r] = R[r * D + c];
+            score[D + c] = lqo_t128_dot(col, col);
+        }
+        float best = 0.0f;
+        int pick = -1;
+        for (int cand = 0; cand < 2 * D; ++cand)
+            if (!taken[cand] && score[cand] > best) { best = score[cand]; pick = cand; }
+        float *v = vec + (size_t)j * D;
+        idx[j] = pick;
+        if (pick < 0) {
+            for (int e = 0; e < D; ++e) v[e] = 0.0f;
+            continue;
+        }
+        taken[pick] = 1;
+        if (pick < D) {
+            for (int c = 0; c < D; ++c) { v[c] = R[pick * D + c]; R[pick * D + c] = 0.0f; }
+        } else {
+            int c = pick - D;
+            for (int r = 0; r < D; ++r) { v[r] = R[r * D + c]; R[r * D + c] = 0.0f; }
+        }
+    }
+
+    /* Residual smoothing ([LQ] 3.4): per value column, the square root of
+     * the mean absolute value over the key rows, with a positive floor. */
+    float inv_sigma[D];
+    for (int c = 0; c < D; ++c) {
+        float s = 1.0f;
+        if (smoothing) {
+            float col[D];
+            for (int r = 0; r < D; ++r) col[r] = fabsf(R[r * D + c]);
+            float m = lqo_t128_sum(col) * 0.0078125f;
+            s = sqrtf(m);
+            if (s < sigma_floor) s = sigma_floor;
+        }
+        sigma[c] = s;
+        inv_sigma[c] = 1.0f / s;
+    }
+
+    /* Symmetric per-row int8 with round half to even ([LQ] abstract: 8-bit
+     * state; [RN4] Why rounding: rounded once per window). */
+    for (int r = 0; r < D; ++r) {
+        float x[D];
+        float M = 0.0f;
+        for (int c = 0; c < D; ++c) {
+            x[c] = R[r * D + c] * inv_sigma[c];
+            if (fabsf(x[c]) > M) M = fabsf(x[c]);
+        }
+        if (!(M >= LQO_TINY)) {
+            rho[r] = 0.0f;
+            for (int c = 0; c < D; ++c) Q[r * D + c] = 0;
+            continue;
+        }
+        rho[r] = M / 127.0f;
+        float g = 127.0f / M;
+        for (int c = 0; c < D; ++c) {
+            float y = rintf(x[c] * g);
+            if (y > 127.0f) y = 127.0f;
+            if (y < -127.0f) y = -127.0f;
+            Q[r * D + c] = (int8_t)y;
+        }
+    }
+}
+
+/* Initial quantization of a caller's fp32 state: the fold without records. */
+void lqo_init(const float *S0, int C, int smoothing, float sigma_floor,
+              int8_t *Q, float *rho, float *sigma, int32_t *idx, float *vec)
+{
+    float R[D * D];
+    memcpy(R, S0, sizeof R);
+    lqo_quantize(R, C, smoothing, sigma_floor, Q, rho, sigma, idx, vec);
+}
+
+/* Fold ([RN4] What we built: rebuild, select compensators, rescale, round,
+ * empty the buffer; [LQ] B.3: rebuild in original coordinates before new
+ * factors and scales).  Overwrites the boundary state; the caller sets n=0. */
+void lqo_fold(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *vec,
+              int n, const float *gam, const float *rk, const float *ru,
+              int smoothing, float sigma_floor)
+{
+    float R[D * D];
+    lqo_current(Q, rho, sigma, C, idx, vec, n, gam, rk, ru, R);
+    lqo_quantize(R, C, smoothing, sigma_floor, Q, rho, sigma, idx, vec);
+}
+
+/* ------------------------------------------------------------------ */
+/* Append: one decode token against the fixed boundary plus the records */
+/* ------------------------------------------------------------------ */
+
+/* Read of the boundary with key x ([LQ] B.3): the residual scales act on
+ * the residual's read only, sigma_c * sum_r (x_r * rho_r) * code[r][c];
+ * each compensator then adds its read as a token: a row token r adds
+ * x_r * line, a column token c adds (line . x) to column c. */
+static void boundary_read(const int8_t *Q, const float *rho, const float *sigma, int C,
+                          const int32_t *idx, const float *vec, const float *x, float *out)
+{
+    float w[D];
+    for (int r = 0; r < D; ++r) w[r] = x[r] * rho[r];
+    for (int c = 0; c < D; ++c) {
+        float col[D];
+        for (int r = 0; r < D; ++r) col[r] = (float)Q[r * D + c];
+        out[c] = sigma[c] * lqo_t128_dot(w, col);
+    }
+    for (int j = 0; j < C; ++j) {
+        const float *v = vec + (size_t)j * D;
+        if (idx[j] < 0) continue;
+        if (idx[j] < D) {
+            float xr = x[idx[j]];
+            for (int c = 0; c < D; ++c) out[c] = fmaf(xr, v[c], out[c]);
+        } else {
+            int c = idx[j] - D;
+            out[c] = out[c] + lqo_t128_dot(v, x);
+        }
+    }
+}
+
+/* One token ([RN4] Background: decay, read with the key, correction,
+ * rank-one write, read the output; [LQ] App. A: one record per GDN token;
+ * [LQ] B.2: reads never form the dense state).  With n records present
+ * (n < W), token t = n+1:
+ *   gamma_t = gamma_n * alpha,   c_i = gamma_t / gamma_i
+ *   r   = gamma_t * B^T k + sum_i (c_i * (k_i . k)) u_i     (read of alpha*S_{t-1})
+ *   u_t = beta * (v - r)
+ *   o   = gamma_t * B^T q + sum_i (c_i * (k_i . q)) u_i + (k . q) u_t  (read of S_t)
+ * and the record (gamma_t, k, u_t) is stored at slot n. */
+void lqo_append(const int8_t *Q, const float *rho, const float *sigma, int C,
+                const int32_t *idx, const float *vec, int n, float *gam, float *rk,
+                float *ru, const float *q, const float *k, const float *v, float alpha,
+                float beta, float *o)
+{
+    float gt = gamma_of(n, gam) * alpha;
+    float bk[D], bq[D], u[D];
+    boundary_read(Q, rho, sigma, C, idx, vec, k, bk);
+    boundary_read(Q, rho, sigma, C, idx, vec, q, bq);
+
+    float r[D];
+    for (int c = 0; c < D; ++c) { r[c] = gt * bk[c]; o[c] = gt * bq[c]; }
+    for (int i = 0; i < n; ++i) {
+        float ci = gt / gam[i];
+        const float *ki = rk + (size_t)i * D, *ui = ru + (size_t)i * D;
+        float ak = ci * lqo_t128_dot(ki, k);
+        float aq = ci * lqo_t128_dot(ki, q);
+        for (int c = 0; c < D; ++c) {
+            r[c] = fmaf(ak, ui[c], r[c]);
+            o[c] = fmaf(aq, ui[c], o[c]);
+        }
+    }
+    for (int c = 0; c < D; ++c) u[c] = beta * (v[c] - r[c]);
+    float kq = lqo_t128_dot(k, q);
+    for (int c = 0; c < D; ++c) o[c] = fmaf(kq, u[c], o[c]);
+
+    gam[n] = gt;
+    memcpy(rk + (size_t)n * D, k, D * sizeof(float));
+    memcpy(ru + (size_t)n * D, u, D * sizeof(float));
+}
+
+/* ------------------------------------------------------------------ */
+/* Dense per-token GDN recurrences: the brute-force checker of the       */
+/* windowed path and the unquantized quality references.                */
+/* ------------------------------------------------------------------ */
+
+/* One GDN token on a dense fp32 state ([RN4] Background order; [LQ] App. A
+ * with D_t = alpha I and b_t = beta): S = alpha S; r = S^T k;
+ * u = beta (v - r); S += k u^T; o = S^T q.  Plain sequential sums. */
+void lqo_gdn_step_f32(float *S, const float *q, const float *k, const float *v,
+                      float alpha, float beta, float *u_out, float *o)
+{
+    for (int e = 0; e < D * D; ++e) S[e] = alpha * S[e];
+    float u[D];
+    for (int c = 0; c < D; ++c) {
+        float rc = 0.0f;
+        for (int r = 0; r < D; ++r) rc = fmaf(S[r * D + c], k[r], rc);
+        u[c] = beta * (v[c] - rc);
+    }
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c) S[r * D + c] = fmaf(k[r], u[c], S[r * D + c]);
+    for (int c = 0; c < D; ++c) {
+        float oc = 0.0f;
+        for (int r = 0; r < D; ++r) oc = fmaf(S[r * D + c], q[r], oc);
+        o[c] = oc;
+    }
+    if (u_out) memcpy(u_out, u, sizeof u);
+}
+
+/* The same step in fp64, to attribute a disagreement to conditioning. */
+void lqo_gdn_step_f64(double *S, const double *q, const double *k, const double *v,
+                      double alpha, double beta, double *u_out, double *o)
+{
+    for (int e = 0; e < D * D; ++e) S[e] = alpha * S[e];
+    double u[D];
+    for (int c = 0; c < D; ++c) {
+        double rc = 0.0;
+        for (int r = 0; r < D; ++r) rc += S[r * D + c] * k[r];
+        u[c] = beta * (v[c] - rc);
+    }
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c) S[r * D + c] += k[r] * u[c];
+    for (int c = 0; c < D; ++c) {
+        double oc = 0.0;
+        for (int r = 0; r < D; ++r) oc += S[r * D + c] * q[r];
+        o[c] = oc;
+    }
+    if (u_out) memcpy(u_out, u, sizeof u);
+}
+
+/* bf16 helpers: widening is exact; narrowing rounds to nearest even. */
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+uint16_t lqo_f32_to_bf16(float f)
+{
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    if ((b & 0x7f800000u) == 0x7f800000u && (b & 0x007fffffu)) return (uint16_t)((b >> 16) | 0x40);
+    uint32_t lsb = (b >> 16) & 1u;
+    b += 0x7fffu + lsb;
+    return (uint16_t)(b >> 16);
+}
+
+/* Per-token bf16 state ([RN4] Why rounding: a bf16 state rounded at every
+ * token; [LQ] 4.2/4.4 per-step baselines): widen, take the fp32 step, keep
+ * the output of the fp32 state, store the state rounded to bf16. */
+void lqo_gdn_step_bf16(uint16_t *Sb, const float *q, const float *k, const float *v,
+                       float alpha, float beta, float *u_out, float *o)
+{
+    float S[D * D];
+    for (int e = 0; e < D * D; ++e) S[e] = bf16_to_f32(Sb[e]);
+    lqo_gdn_step_f32(S, q, k, v, alpha, beta, u_out, o);
+    for (int e = 0; e < D * D; ++e) Sb[e] = lqo_f32_to_bf16(S[e]);
+}
+
+int lqo_dim(void) { return D; }

@@ -1,0 +1,190 @@
+"""Seeded synthetic decode workloads for GDN heads (inputs only).
+
+This module draws the inputs that both the GPU library and the CPU oracle
+consume: initial fp32 states and per-token q, k, v, alpha, beta.  It holds
+none of the decode path's arithmetic (no recurrence, no quantization); every
+tensor it returns is an input.  The shapes follow a Qwen3.5-9B-like hybrid
+model: 24 GDN layers of 32 heads with a 128 x 128 state each ("Recurrent-state
+quantization for linear attention: a first GPU kernel", Background).  The
+recorded traces that page replays are not available, so these seeded
+distributions stand in for them:
+
+  q, k   ~ N(0, 1)^128, each L2-normalized per head and token
+  v      ~ N(0, 1)^128
+  beta   = sigmoid(z),         z ~ N(0, 1)
+  alpha  = exp(-softplus(z)),  z ~ N(-3, 1)     (median 0.953)
+
+Initial states:
+  "gauss":   N(0, 0.02^2) entries with 2 random rows and 2 random columns
+             scaled x50 (outlier rows and columns, LeapQuant 1 Introduction).
+  "writes":  a stand-in for a prefilled state: the sum of 64 rank-one writes
+             k_m v_m^T (k_m unit-norm Gaussian, v_m Gaussian) with geometric
+             weights 0.95^(63-m), then 1..4 distinct lines per head, each a
+             row or a column with probability 1/2, scaled by U[20, 100].
+             (The rank-one writes use no delta-rule correction: the generator
+             carries none of the path's arithmetic.)
+  "hard":    "writes" for heads < 24; heads 24..31 draw alpha from
+             z ~ N(-6.9, 0.25) (alpha ~ 0.999) and, in place of the lines
+             above, scale 2 rows and 2 columns x200 (a hard, slowly decaying
+             late layer).
+
+Every draw comes from a torch generator seeded by a 64-bit mix of
+(seed, stream, layer, token), so any (layer, token) slice can be regenerated
+on demand, on the CPU or on the GPU.  The CPU and GPU generators produce
+different numbers for the same seed; a comparison always hands both sides the
+same tensor.
+"""
+from dataclasses import dataclass, field
+
+import torch
+
+D = 128
+MASK64 = (1 << 64) - 1
+
+
+def _mix(*parts):
+    """splitmix64 over the parts; a 63-bit torch seed."""
+    x = 0x9E3779B97F4A7C15
+    for p in parts:
+        x = (x + (int(p) & MASK64) + 0x9E3779B97F4A7C15) & MASK64
+        z = x
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+        x = z ^ (z >> 31)
+    return x & ((1 << 63) - 1)
+
+
+def _gen(device, *parts):
+    g = torch.Generator(device=device)
+    g.manual_seed(_mix(*parts))
+    return g
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    layers: int
+    heads: int
+    tokens: int
+    window: int = 16
+    n_comp: int = 4
+    in_dtype: str = "f32"          # "f32" or "bf16" for q, k, v
+    init: str = "writes"           # "gauss", "writes" or "hard"
+    seed: int = 0
+    smoothing: bool = True
+    sigma_floor: float = 1e-6
+    notes: str = field(default="", compare=False)
+
+    @property
+    def heads_per_layer(self):
+        return self.batch * self.heads
+
+    def torch_dtype(self):
+        return torch.bfloat16 if self.in_dtype == "bf16" else torch.float32
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 4, 64, init="gauss", seed=0,
+                     notes="1 request, 1 layer, 4 heads, 64 tokens (4 folds)"),
+    "b32": Workload("b32", 32, 1, 32, 256, seed=1,
+                    notes="single layer, batch 32, 256 tokens (16 folds)"),
+    "b128": Workload("b128", 128, 24, 32, 512, seed=2,
+                     notes="24 layers x 32 heads, batch 128, 512 tokens"),
+    "b512": Workload("b512", 512, 24, 32, 1024, in_dtype="bf16", seed=3,
+                     notes="24 layers x 32 heads, batch 512, 1024 tokens, bf16 q/k/v"),
+    "long": Workload("long", 8, 3, 32, 4095, init="hard", seed=4,
+                     notes="batch 8, 3 layers x 32 heads, 4095 tokens (255 folds)"),
+}
+
+# stream ids
+_S_INIT, _S_TOK, _S_HARD = 1, 2, 3
+
+
+def _normal(shape, g, device, mean=0.0, std=1.0):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std + mean
+
+
+def _distinct(B, H, m, g, device):
+    """m distinct indices in [0, 128) per head: [B, H, m] int64."""
+    return torch.rand((B, H, D), generator=g, device=device).argsort(dim=-1)[..., :m].contiguous()
+
+
+def initial_state(wl, layer, device="cpu", return_lines=False):
+    """fp32 initial states of one layer: [batch, heads, 128, 128].
+
+    With return_lines, also returns the planted outlier lines: for "gauss"
+    (rows [B,H,2], cols [B,H,2]); otherwise (line [B,H,4], is_row [B,H,4],
+    active [B,H,4]) for the regular heads' lines.
+    """
+    B, H = wl.batch, wl.heads
+    g = _gen(device, wl.seed, _S_INIT, layer)
+    if wl.init == "gauss":
+        S = _normal((B, H, D, D), g, device, std=0.02)
+        rows = _distinct(B, H, 2, g, device)
+        cols = _distinct(B, H, 2, g, device)
+        mult_r = torch.ones((B, H, D), device=device).scatter_(2, rows, 50.0)
+        mult_c = torch.ones((B, H, D), device=device).scatter_(2, cols, 50.0)
+        S = (S * mult_r.unsqueeze(-1) * mult_c.unsqueeze(-2)).contiguous()
+        return (S, (rows, cols)) if return_lines else S
+    M = 64
+    kk = _normal((B, H, D, M), g, device)
+    kk = kk / kk.norm(dim=2, keepdim=True)
+    vv = _normal((B, H, M, D), g, device)
+    w = 0.95 ** torch.arange(M - 1, -1, -1, device=device, dtype=torch.float32)
+    S = torch.matmul(kk * w, vv.contiguous())
+    # per-head outlier lines: count U{1..4}, axis with p = 1/2, scale U[20, 100]
+    count = torch.randint(1, 5, (B, H), generator=g, device=device)
+    axis = torch.randint(0, 2, (B, H, 4), generator=g, device=device)
+    line = _distinct(B, H, 4, g, device)
+    scale = torch.rand((B, H, 4), generator=g, device=device) * 80.0 + 20.0
+    # distinct lines: a row and a column may share an index, two rows may not
+    mult_r = torch.ones((B, H, D), device=device)
+    mult_c = torch.ones((B, H, D), device=device)
+    j = torch.arange(4, device=device).view(1, 1, 4)
+    active = j < count.unsqueeze(-1)
+    sr = torch.where(active & (axis == 0), scale, torch.ones_like(scale))
+    sc = torch.where(active & (axis == 1), scale, torch.ones_like(scale))
+    mult_r.scatter_(2, line, sr)
+    mult_c.scatter_(2, line, sc)
+    if wl.init == "hard":
+        # heads 24..31: exactly 2 rows and 2 columns x200 replace the lines above
+        gh = _gen(device, wl.seed, _S_HARD, layer)
+        hl = _distinct(B, H, 4, gh, device)
+        hr = torch.ones((B, H, D), device=device).scatter_(2, hl[..., :2], 200.0)
+        hc = torch.ones((B, H, D), device=device).scatter_(2, hl[..., 2:], 200.0)
+        mult_r[:, 24:] = hr[:, 24:]
+        mult_c[:, 24:] = hc[:, 24:]
+    S = (S * mult_r.unsqueeze(-1) * mult_c.unsqueeze(-2)).contiguous()
+    return (S, (line, axis == 0, active)) if return_lines else S
+
+
+def token_inputs(wl, layer, token, device="cpu"):
+    """Inputs of one decode token for one layer.
+
+    Returns q, k, v as [batch, heads, 128] in the workload's input dtype and
+    alpha, beta as fp32 [batch, heads].
+    """
+    B, H = wl.batch, wl.heads
+    g = _gen(device, wl.seed, _S_TOK, layer, token)
+    q = _normal((B, H, D), g, device)
+    k = _normal((B, H, D), g, device)
+    v = _normal((B, H, D), g, device)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    zb = _normal((B, H), g, device)
+    za = _normal((B, H), g, device, mean=-3.0)
+    if wl.init == "hard":
+        zh = _normal((B, H), g, device, mean=-6.9, std=0.25)
+        za = za.clone()
+        za[:, 24:] = zh[:, 24:]
+    beta = torch.sigmoid(zb)
+    alpha = torch.exp(-torch.nn.functional.softplus(za))
+    dt = wl.torch_dtype()
+    return (q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous(),
+            alpha.contiguous(), beta.contiguous())
+
+
+def widen(x):
+    """Input tensor as fp32 (exact for bf16)."""
+    return x.to(torch.float32)

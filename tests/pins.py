@@ -1,0 +1,437 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each pin takes a loaded oracle library handle `L` and raises AssertionError
+when the oracle disagrees with:
+  * hand-derived arithmetic fixtures (tests/golden/arith_fixtures.json),
+  * the dense GDN recurrence written here in float64 numpy, which the windowed
+    path must reproduce to rounding (LeapQuant B.2 window unrolling; B.1 no
+    error inside a window),
+  * closed-form special cases of the delta rule (LeapQuant App. A),
+  * exact scaling and tree-automorphism equivariance of the quantizer,
+  * planted outliers, a float64 brute-force argmax, textbook absmax int8.
+The same pins run against deliberately broken copies of the oracle in
+test_oracle_mutants.py, where each copy must fail at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from quantized_recurrent_state_amd import workloads
+
+D = 128
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(float(np.max(np.abs(b))), 1e-30))
+
+
+def sparse_vec(d):
+    v = np.zeros(D, np.float32)
+    for i, x in d.items():
+        v[int(i)] = np.float32(x)
+    return v
+
+
+# ---------------------------------------------------------------- inputs
+
+def tiny_inputs(seed=0, tokens=16, heads=1, init="gauss", C=4, head=0):
+    """Seeded tiny case: (S0 [heads,128,128], per-token (q, k, v, alpha, beta)
+    of head `head`)."""
+    wl = workloads.Workload("pin", 1, 1, heads, tokens, init=init, seed=seed, n_comp=C)
+    S0 = workloads.initial_state(wl, 0).numpy()[0]
+    toks = []
+    for t in range(tokens):
+        q, k, v, a, b = workloads.token_inputs(wl, 0, t)
+        toks.append((q.numpy()[0, head], k.numpy()[0, head], v.numpy()[0, head],
+                     np.float32(a.numpy()[0, head]), np.float32(b.numpy()[0, head])))
+    return S0, toks
+
+
+def np_gdn_f64(S, q, k, v, alpha, beta):
+    """The dense GDN token step in float64 (decay, read with k, correction,
+    rank-one write, read with q); S is [key row, value column]."""
+    S *= alpha
+    r = S.T @ k
+    u = beta * (v - r)
+    S += np.outer(k, u)
+    return u, S.T @ q
+
+
+# ---------------------------------------------------------------- pins
+
+def pin_t128_fixtures(L):
+    g = golden("arith_fixtures.json")
+    for key in ("t128_sum_level0_pairs_i_with_i_plus_64", "t128_sum_levels_halve_from_32"):
+        case = g[key]
+        got = oracle.t128_sum(sparse_vec(case["nonzero"]), L)
+        assert got == case["expected"], (key, got)
+    for key in ("t128_dot_fma_on_lower_term", "t128_dot_upper_term_rounded"):
+        case = g[key]
+        got = oracle.t128_dot(sparse_vec(case["a"]), sparse_vec(case["b"]), L)
+        assert got == case["expected"], (key, got)
+
+
+def pin_t128_exact_integers(L):
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        a = rng.integers(-1000, 1000, D).astype(np.float32)
+        b = rng.integers(-1000, 1000, D).astype(np.float32)
+        assert oracle.t128_sum(a, L) == float(a.astype(np.int64).sum())
+        assert oracle.t128_dot(a, b, L) == float((a.astype(np.int64) * b.astype(np.int64)).sum())
+        # a single nonzero term anywhere is returned unchanged
+        j = int(rng.integers(0, D))
+        e = np.zeros(D, np.float32)
+        e[j] = a[j] + 0.5
+        assert oracle.t128_sum(e, L) == float(e[j])
+
+
+def pin_round_half_even(L):
+    case = golden("arith_fixtures.json")["round_half_even"]
+    R = np.zeros((D, D), np.float32)
+    R[17] = sparse_vec(case["row"])
+    h = oracle.Head(C=0, smoothing=False, L=L).init(R)
+    want = np.zeros(D, np.int8)
+    for i, c in case["expected_codes"].items():
+        want[int(i)] = c
+    assert np.array_equal(h.Q[17], want), h.Q[17][:12]
+    assert h.rho[17] == np.float32(case["expected_rho"])
+    others = np.delete(np.arange(D), 17)
+    assert not h.Q[others].any() and not h.rho[others].any()
+
+
+def pin_pick_ties(L):
+    g = golden("arith_fixtures.json")
+    R = np.zeros((D, D), np.float32)
+    R[3, :] = 1.0
+    R[:, 7] = 1.0
+    h = oracle.Head(C=2, smoothing=False, L=L).init(R)
+    assert list(h.idx) == g["pick_ties"]["expected_idx"], list(h.idx)
+    R = np.zeros((D, D), np.float32)
+    line = (np.arange(1, D + 1) / 64.0).astype(np.float32)
+    R[9] = line
+    R[5] = line
+    h = oracle.Head(C=1, smoothing=False, L=L).init(R)
+    assert list(h.idx) == g["pick_equal_rows"]["expected_idx"], list(h.idx)
+
+
+def pin_textbook_int8(L):
+    """C=0 without smoothing is per-row symmetric absmax int8: scale = max|x|/127,
+    code = round-half-even(x*127/max).  Computed here in float64; a code may
+    differ only where the float64 value is within 1e-5 of a .5 boundary."""
+    rng = np.random.default_rng(3)
+    for trial in range(4):
+        R = (rng.standard_normal((D, D)) * (10.0 ** rng.integers(-3, 3, (D, 1)))).astype(np.float32)
+        h = oracle.Head(C=0, smoothing=False, L=L).init(R)
+        M = np.abs(R.astype(np.float64)).max(axis=1)
+        assert np.allclose(h.rho, M / 127.0, rtol=2e-7, atol=0)
+        assert np.all(h.sigma == 1.0) and np.all(h.idx[:0] == -1)
+        y = R.astype(np.float64) * (127.0 / M)[:, None]
+        want = np.rint(y)
+        diff = h.Q.astype(np.float64) != want
+        near = np.abs(np.abs(y - np.trunc(y)) - 0.5) < 1e-5
+        assert not np.any(diff & ~near), np.argwhere(diff & ~near)[:5]
+        assert int(diff.sum()) <= 2
+
+
+def pin_smoothing_closed_form(L):
+    """Column c holds +-s_c (alternating signs) with s_c a power of 4, so the mean
+    absolute value over the key rows is s_c and sigma_c = sqrt(s_c) exactly;
+    a zero column takes the floor.  Rows then quantize x = R / sigma."""
+    e = (np.arange(D) % 9) - 4
+    s = np.power(4.0, e).astype(np.float32)
+    sign = np.where(np.arange(D) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    R = (sign[:, None] * s[None, :]).astype(np.float32)
+    R[:, 100] = 0.0
+    h = oracle.Head(C=0, smoothing=True, sigma_floor=1e-6, L=L).init(R)
+    want = np.sqrt(s.astype(np.float64)).astype(np.float32)
+    want[100] = np.float32(1e-6)
+    assert np.array_equal(h.sigma, want), np.flatnonzero(h.sigma != want)[:5]
+    # every smoothed entry is +-sqrt(s_c); the row max is 16 (s=256), so codes
+    # are round(127 * sqrt(s_c) / 16) with the row's sign (all products exact)
+    mag = np.rint(127.0 * np.sqrt(s.astype(np.float64)) / 16.0)
+    mag[100] = 0
+    assert np.array_equal(np.abs(h.Q[0].astype(np.int64)), mag.astype(np.int64))
+    assert np.all(np.sign(h.Q[1][mag > 0]) == -1)
+
+
+def pin_scaling_exact(L):
+    """Scaling the state by 4 leaves codes and picks unchanged and scales
+    rho and sigma by 2 and the compensator lines by 4, exactly (with
+    smoothing on; without smoothing any power of two scales rho by itself)."""
+    S0, _ = tiny_inputs(seed=11, tokens=1)
+    S = S0[0]
+    a = oracle.Head(C=4, smoothing=True, L=L).init(S)
+    b = oracle.Head(C=4, smoothing=True, L=L).init(S * np.float32(4.0))
+    assert np.array_equal(a.Q, b.Q) and np.array_equal(a.idx, b.idx)
+    assert np.array_equal(b.rho, a.rho * 2) and np.array_equal(b.vec, a.vec * 4)
+    # extracted (zeroed) columns sit at the floor in both; the rest scale by 2
+    floor = a.sigma == np.float32(1e-6)
+    assert sorted(np.flatnonzero(floor) + D) == sorted(int(i) for i in a.idx if i >= D)
+    assert np.array_equal(b.sigma[~floor], a.sigma[~floor] * 2)
+    assert np.all(b.sigma[floor] == np.float32(1e-6))
+    for p in (0.125, 8.0):
+        a = oracle.Head(C=4, smoothing=False, L=L).init(S)
+        b = oracle.Head(C=4, smoothing=False, L=L).init(S * np.float32(p))
+        assert np.array_equal(a.Q, b.Q) and np.array_equal(a.idx, b.idx)
+        assert np.array_equal(b.rho, a.rho * np.float32(p))
+        assert np.array_equal(b.vec, a.vec * np.float32(p))
+
+
+def pin_planted_outliers(L):
+    """The tiny case plants 2 rows and 2 columns x50; with C=4 the four
+    compensators are exactly those lines at init, and they stay the picks
+    after a window of pure decay (beta = 0), where S = gamma B."""
+    wl = workloads.Workload("pin", 1, 1, 4, 16, init="gauss", seed=0)
+    S0, lines = workloads.initial_state(wl, 0, return_lines=True)
+    for h_ in range(4):
+        rows, cols = lines
+        want = set(int(r) for r in rows[0, h_]) | set(D + int(c) for c in cols[0, h_])
+        head = oracle.Head(C=4, L=L).init(S0.numpy()[0, h_])
+        assert set(int(i) for i in head.idx) == want, (h_, head.idx, want)
+        for t in range(16):
+            q, k, v, a, b = workloads.token_inputs(wl, 0, t)
+            head.append(q.numpy()[0, h_], k.numpy()[0, h_], v.numpy()[0, h_], a[0, h_], 0.0)
+        head.fold()
+        assert set(int(i) for i in head.idx) == want, (h_, head.idx, want)
+
+
+def pin_greedy_bruteforce(L):
+    """Every greedy pick is the float64 argmax of the line energies of the
+    matrix left after the earlier picks, unless the top two are within 1e-6."""
+    rng = np.random.default_rng(5)
+    for trial in range(6):
+        R = rng.standard_normal((D, D)).astype(np.float32)
+        R[rng.integers(0, D, 3)] *= np.float32(3 + trial)
+        R[:, rng.integers(0, D, 3)] *= np.float32(2 + trial)
+        h = oracle.Head(C=4, smoothing=bool(trial % 2), L=L).init(R)
+        Rw = R.astype(np.float64)
+        taken = set()
+        for j in range(4):
+            e = np.concatenate([(Rw ** 2).sum(axis=1), (Rw ** 2).sum(axis=0)])
+            for t in taken:
+                e[t] = -1.0
+            order = np.argsort(-e, kind="stable")
+            top, second = e[order[0]], e[order[1]]
+            if (top - second) / top > 1e-6:
+                assert h.idx[j] == order[0], (trial, j, h.idx[j], order[:3])
+            else:
+                assert h.idx[j] in (order[0], order[1])
+            pick = int(h.idx[j])
+            line = Rw[pick] if pick < D else Rw[:, pick - D]
+            assert np.array_equal(h.vec[j], line.astype(np.float32))
+            taken.add(pick)
+            if pick < D:
+                Rw[pick] = 0
+            else:
+                Rw[:, pick - D] = 0
+
+
+def pin_reconstruction_bound(L):
+    """After quantization every entry is within half a step rho_r*sigma_c of
+    the input (plus a few fp32 roundings), and extracted lines come back
+    exactly.  Error budget: |code*rho*sigma - R| <= rho*sigma*(0.5 + 1200*2^-24)."""
+    S0, _ = tiny_inputs(seed=2, tokens=1, heads=2)
+    for sm in (True, False):
+        for h_ in range(2):
+            R = S0[h_]
+            h = oracle.Head(C=4, smoothing=sm, L=L).init(R)
+            res = h.dequant(0).astype(np.float64)
+            B = h.dequant(1)
+            step = h.rho.astype(np.float64)[:, None] * h.sigma.astype(np.float64)[None, :]
+            lines = np.zeros((D, D), bool)
+            for j, i in enumerate(h.idx):
+                if i < 0:
+                    continue
+                if i < D:
+                    lines[i, :] = True
+                else:
+                    lines[:, i - D] = True
+            assert np.array_equal(B[lines], R[lines])
+            err = np.abs(res - R.astype(np.float64))
+            bound = step * (0.5 + 1200 * 2.0 ** -24)
+            assert np.all(err[~lines] <= bound[~lines]), float(np.max(err[~lines] / bound[~lines]))
+            assert not np.any(h.Q[lines])
+
+
+def _window(L, S0, toks, C=4, smoothing=True, W=16):
+    """Run one window through the oracle beside the float64 dense recurrence
+    from the oracle's own dequantized boundary.  Returns the worst relative
+    errors of o, u (per token) and of the state rebuilt at the window end."""
+    h = oracle.Head(C=C, W=W, smoothing=smoothing, L=L).init(S0)
+    S = h.dequant(1).astype(np.float64)
+    eo = eu = 0.0
+    for (q, k, v, a, b) in toks[:W]:
+        o, u = h.append(q, k, v, a, b)
+        u64, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                              float(a), float(b))
+        eo, eu = max(eo, rel(o, o64)), max(eu, rel(u, u64))
+    es = rel(h.dequant(2), S)
+    return h, eo, eu, es
+
+
+def pin_window_vs_dense_f64(L):
+    """Within a window the windowed path equals the dense recurrence started
+    from the dequantized boundary (exact in real arithmetic): o, u and the
+    rebuilt state agree to 1e-5 relative."""
+    for seed, init in ((0, "gauss"), (1, "writes"), (4, "hard")):
+        S0, toks = tiny_inputs(seed=seed, tokens=16, heads=1, init=init)
+        for C, sm in ((4, True), (0, False), (2, True)):
+            _, eo, eu, es = _window(L, S0[0], toks, C=C, smoothing=sm)
+            assert eo < 1e-5 and eu < 1e-5 and es < 1e-5, (seed, C, sm, eo, eu, es)
+
+
+def pin_beta_zero(L):
+    """beta = 0 writes nothing: u = 0, o_t = gamma_t B^T q and the state at
+    the window end is gamma_16 B (to rounding)."""
+    S0, toks = tiny_inputs(seed=3, tokens=16)
+    h = oracle.Head(C=4, L=L).init(S0[0])
+    B = h.dequant(1).astype(np.float64)
+    g = 1.0
+    for (q, k, v, a, _) in toks:
+        o, u = h.append(q, k, v, a, 0.0)
+        g = float(np.float32(g * np.float64(a)))
+        assert not u.any()
+        assert rel(o, g * (B.T @ q.astype(np.float64))) < 1e-6
+    assert rel(h.dequant(2), g * B) < 1e-6
+
+
+def pin_overwrite_identity(L):
+    """beta = 1 and q = k with |k| = 1 read back exactly what was written:
+    o = (alpha S)^T k + (k.k)(v - (alpha S)^T k) = v."""
+    S0, toks = tiny_inputs(seed=6, tokens=16, init="writes")
+    h = oracle.Head(C=4, L=L).init(S0[0])
+    for (_, k, v, a, _) in toks:
+        k64 = k.astype(np.float64)
+        kn = (k64 / np.sqrt(k64 @ k64)).astype(np.float32)
+        o, _ = h.append(kn, kn, v, a, 1.0)
+        assert rel(o, v) < 2e-5, rel(o, v)
+
+
+def pin_fold_invariants(L):
+    """After a fold the buffer is empty and the current state equals the
+    boundary; the fold's new boundary is within the quantization bound of the
+    state rebuilt before it."""
+    S0, toks = tiny_inputs(seed=8, tokens=16, init="writes")
+    h = oracle.Head(C=4, L=L).init(S0[0])
+    for (q, k, v, a, b) in toks:
+        h.append(q, k, v, a, b)
+    S = h.dequant(2)
+    h.fold()
+    assert h.n == 0
+    assert np.array_equal(h.dequant(2), h.dequant(1))
+    step = h.rho.astype(np.float64)[:, None] * h.sigma.astype(np.float64)[None, :]
+    err = np.abs(h.dequant(1).astype(np.float64) - S)
+    assert np.all(err <= step * (0.5 + 1200 * 2.0 ** -24) + 1e-30)
+
+
+def pin_xor_equivariance(L):
+    """Relabelling key rows (with k and q) or value columns (with v) by
+    i -> i XOR m, 0 < m < 64, is an automorphism of the canonical trees, so
+    every output and every state field is permuted exactly."""
+    S0, toks = tiny_inputs(seed=9, tokens=16, init="writes")
+    S = S0[0]
+    for m in (1, 22, 63):
+        p = np.arange(D) ^ m
+        a = oracle.Head(C=4, L=L).init(S)
+        b = oracle.Head(C=4, L=L).init(S[p])
+        c = oracle.Head(C=4, L=L).init(S[:, p])
+        for (q, k, v, al, be) in toks:
+            oa, ua = a.append(q, k, v, al, be)
+            ob, ub = b.append(q[p], k[p], v, al, be)
+            oc, uc = c.append(q, k, v[p], al, be)
+            assert np.array_equal(oa, ob) and np.array_equal(ua, ub)
+            assert np.array_equal(oa[p], oc) and np.array_equal(ua[p], uc)
+        for h in (a, b, c):
+            h.fold()
+        assert np.array_equal(a.Q[p], b.Q) and np.array_equal(a.rho[p], b.rho)
+        assert np.array_equal(a.sigma, b.sigma)
+        assert np.array_equal(a.Q[:, p], c.Q) and np.array_equal(a.sigma[p], c.sigma)
+        assert np.array_equal(a.rho, c.rho)
+        ia, ib, ic = list(a.idx), list(b.idx), list(c.idx)
+        assert ib == [(int(p[i]) if i < D else i) for i in ia]
+        assert ic == [(i if i < D else D + int(p[i - D])) for i in ia]
+
+
+def pin_zero_state(L):
+    """An all-zero state has no compensators, zero scales, floor smoothing,
+    and the first token reads u = beta v and o = (k.q) u."""
+    h = oracle.Head(C=4, sigma_floor=1e-6, L=L).init(np.zeros((D, D), np.float32))
+    assert list(h.idx) == [-1] * 4 and not h.vec.any()
+    assert not h.rho.any() and not h.Q.any() and np.all(h.sigma == np.float32(1e-6))
+    _, toks = tiny_inputs(seed=10, tokens=1)
+    q, k, v, a, b = toks[0]
+    o, u = h.append(q, k, v, a, b)
+    assert rel(u, np.float64(b) * v) < 1e-7
+    kq = float(k.astype(np.float64) @ q.astype(np.float64))
+    assert rel(o, kq * u.astype(np.float64)) < 1e-6
+
+
+def pin_tiny_rows(L):
+    """A row whose largest magnitude is below 2^-120 is stored as zeros."""
+    R = np.zeros((D, D), np.float32)
+    R[4, :] = np.float32(2.0 ** -121)
+    R[5, :3] = np.float32(1.0)
+    h = oracle.Head(C=0, smoothing=False, L=L).init(R)
+    assert h.rho[4] == 0 and not h.Q[4].any()
+    assert h.rho[5] == np.float32(1.0 / 127.0) and list(h.Q[5, :4]) == [127, 127, 127, 0]
+
+
+def pin_dense_steps(L):
+    """The fp32 and fp64 dense steps match the float64 numpy recurrence, and
+    the bf16 step equals the fp32 step on the widened state followed by
+    torch's round-to-nearest-even bf16 conversion."""
+    S0, toks = tiny_inputs(seed=12, tokens=8, init="writes")
+    S32 = S0[0].copy()
+    S64 = S0[0].astype(np.float64)
+    Sn = S0[0].astype(np.float64)
+    for (q, k, v, a, b) in toks:
+        u32, o32 = oracle.gdn_step_f32(S32, q, k, v, a, b, L)
+        u64, o64 = oracle.gdn_step_f64(S64, q, k, v, a, b, L)
+        un, on = np_gdn_f64(Sn, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            float(np.float32(a)), float(np.float32(b)))
+        assert rel(o32, on) < 1e-5 and rel(u32, un) < 1e-5
+        assert rel(o64, on) < 1e-12 and rel(u64, un) < 1e-12
+    Sb = torch.from_numpy(S0[0]).to(torch.bfloat16)
+    bits = Sb.view(torch.int16).numpy().view(np.uint16).copy()
+    Sw = Sb.to(torch.float32).numpy().copy()
+    q, k, v, a, b = toks[0]
+    ub, ob = oracle.gdn_step_bf16(bits, q, k, v, a, b, L)
+    uw, ow = oracle.gdn_step_f32(Sw, q, k, v, a, b, L)
+    assert np.array_equal(ob, ow) and np.array_equal(ub, uw)
+    want = torch.from_numpy(Sw).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, want)
+
+
+def pin_window_one(L):
+    """W=1 quantizes after every token: each fold's input state equals the
+    dense step from the previous boundary."""
+    S0, toks = tiny_inputs(seed=13, tokens=4, init="writes")
+    h = oracle.Head(C=4, W=1, L=L).init(S0[0])
+    for (q, k, v, a, b) in toks:
+        S = h.dequant(1).astype(np.float64)
+        o, u = h.append(q, k, v, a, b)
+        _, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            float(a), float(b))
+        assert rel(o, o64) < 1e-5
+        assert rel(h.dequant(2), S) < 1e-5
+        h.fold()
+
+
+ALL = [
+    pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
+    pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
+    pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
+    pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
+    pin_tiny_rows, pin_dense_steps, pin_window_one,
+]

@@ -1,0 +1,70 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each mutant below is a copy of oracle/leapq_oracle.c with one plausible slip
+(a dropped term, a wrong sign, index or axis, a transposed operand, another
+rounding or tie rule).  It is compiled on the CPU into a temporary library,
+and at least one pin of tests/pins.py must fail against it.  The mistakes are
+planted in the oracle only; nothing here touches the GPU library.
+"""
+import os
+
+import pytest
+
+from oracle import build as obuild
+from tests import pins
+
+MUTANTS = [
+    ("sum_pairs_i_i63", "s[i] = f[i] + f[i + 64];", "s[i] = f[i] + f[i + 63];"),
+    ("sum_adjacent_tree", "for (int i = 0; i < h; ++i) s[i] = s[i] + s[i + h];\n    return s[0];\n}\n\n/* Dot",
+     "for (int i = 0; i < h; ++i) s[i] = s[2 * i] + s[2 * i + 1];\n    return s[0];\n}\n\n/* Dot"),
+    ("dot_fuse_upper", "fmaf(a[i], b[i], a[i + 64] * b[i + 64])", "fmaf(a[i + 64], b[i + 64], a[i] * b[i])"),
+    ("residual_scale_axes", "((float)Q[r * D + c] * rho[r]) * sigma[c];\n}",
+     "((float)Q[r * D + c] * rho[c]) * sigma[r];\n}"),
+    ("read_transposed_codes", "col[r] = (float)Q[r * D + c];", "col[r] = (float)Q[c * D + r];"),
+    ("read_no_sigma", "out[c] = sigma[c] * lqo_t128_dot(w, col);", "out[c] = lqo_t128_dot(w, col);"),
+    ("read_row_token_wrong_coord", "out[c] = fmaf(xr, v[c], out[c]);", "out[c] = fmaf(x[c], v[c], out[c]);"),
+    ("read_drop_column_token", "out[c] = out[c] + lqo_t128_dot(v, x);", "out[c] = out[c];"),
+    ("append_sign", "u[c] = beta * (v[c] - r[c]);", "u[c] = beta * (v[c] + r[c]);"),
+    ("append_coef_inverted", "float ci = gt / gam[i];", "float ci = gam[i] / gt;"),
+    ("append_drop_current_token", "o[c] = fmaf(kq, u[c], o[c]);", "o[c] = o[c];"),
+    ("append_read_undecayed", "r[c] = gt * bk[c];", "r[c] = gamma_of(n, gam) * bk[c];"),
+    ("append_record_not_stored", "gam[n] = gt;", "gam[n] = 1.0f;"),
+    ("current_lines_unscaled", "add_lines(out, C, idx, vec, gn);", "add_lines(out, C, idx, vec, 1.0f);"),
+    ("current_coef_inverted", "float ci = gn / gam[i];", "float ci = gam[i] / gn;"),
+    ("current_drop_gamma", "float a = gn * rho[r];", "float a = rho[r];"),
+    ("pick_last_max", "score[cand] > best", "score[cand] >= best"),
+    ("pick_row_not_zeroed", "v[c] = R[pick * D + c]; R[pick * D + c] = 0.0f;", "v[c] = R[pick * D + c];"),
+    ("pick_col_energy_of_row", "score[D + c] = lqo_t128_dot(col, col);", "score[D + c] = lqo_t128_dot(R + c * D, R + c * D);"),
+    ("smooth_axis", "col[r] = fabsf(R[r * D + c]);", "col[r] = fabsf(R[c * D + r]);"),
+    ("smooth_mean_64", "* 0.0078125f", "* 0.015625f"),
+    ("smooth_no_floor", "if (s < sigma_floor) s = sigma_floor;", ";"),
+    ("smooth_no_sqrt", "s = sqrtf(m);", "s = m;"),
+    ("quant_128", "rho[r] = M / 127.0f;", "rho[r] = M / 128.0f;"),
+    ("quant_round_away", "rintf(x[c] * g)", "roundf(x[c] * g)"),
+    ("quant_truncate", "rintf(x[c] * g)", "truncf(x[c] * g)"),
+    ("quant_no_tiny_guard", "if (!(M >= LQO_TINY)) {", "if (!(M > 0.0f)) {"),
+    ("step_no_decay", "    for (int e = 0; e < D * D; ++e) S[e] = alpha * S[e];\n    float u[D];",
+     "    float u[D];"),
+    ("step_read_output_with_k", "oc = fmaf(S[r * D + c], q[r], oc);", "oc = fmaf(S[r * D + c], k[r], oc);"),
+    ("bf16_truncate", "b += 0x7fffu + lsb;", "b += 0u * lsb;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    import oracle
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique ({src.count(old)})"
+    mpath = os.path.join(tmp_path, f"{name}.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    so = obuild.build(mpath, os.path.join(tmp_path, f"lib{name}.so"))
+    L = oracle.lib(so)
+    failed = []
+    for pin in pins.ALL:
+        try:
+            pin(L)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            failed.append((pin.__name__, type(e).__name__))
+            break
+    assert failed, f"mutant {name} passes every pin"
