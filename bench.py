@@ -1,0 +1,290 @@
+"""Decode benchmark of the LeapQuant append + fold path on one MI355X.
+
+One step = one window of the whole hot path: for each of the window's 16
+tokens, the append of all 24 layers; after the 16th token each layer's fold.
+Workload (default "b512"): 24 GDN layers x 32 heads x 128x128 state, batch
+512, W=16, C=4, bf16 q/k/v, fp32 records; seeded synthetic inputs (a pool of
+16 tokens per layer, cycled every window), resident in HBM before timing.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps 64] [--warmup 2] [--workload b512]
+                  [--no-baselines] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s and HBM GB/s (% of peak), append+fold, 24Lx32H, batch 512"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "quantized_recurrent_state_amd", "csrc", "leapq_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_b512_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64, help="timed windows (16 tokens each)")
+    p.add_argument("--warmup", type=int, default=2, help="untimed windows")
+    p.add_argument("--workload", default="b512")
+    p.add_argument("--no-baselines", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--baseline-tokens", type=int, default=16)
+    p.add_argument("--cpu-threads", type=int, default=16)
+    return p.parse_args()
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only: every head is independent and the path has no "
+              f"collective, so a multi-GPU run would only repeat this measurement per GPU "
+              f"(requested --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_recurrent_state_amd import leapq as lq
+    from quantized_recurrent_state_amd import metrics, workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Lyr, Hh, W, C = wl.batch, wl.layers, wl.heads, wl.window, wl.n_comp
+    H = B * Hh
+    D = 128
+    in_bytes = 2 if wl.in_dtype == "bf16" else 4
+    stream = torch.cuda.current_stream(dev)
+    log(f"[bench] {wl.name}: {wl.notes}; {Lyr} layers x {H} heads; device {torch.cuda.get_device_name(0)}")
+
+    # ---- state and inputs, resident before timing
+    cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype)
+    layers = []
+    for l in range(Lyr):
+        L = lq.Layer(cfg, dev)
+        S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
+        lq.leapq_init_state(L, S0)
+        del S0
+        layers.append(L)
+    pool = []
+    for l in range(Lyr):
+        toks = []
+        for pos in range(W):
+            q, k, v, a, b = workloads.token_inputs(wl, l, pos, device=dev)
+            toks.append((q.reshape(H, D), k.reshape(H, D), v.reshape(H, D), a.reshape(H), b.reshape(H)))
+        pool.append(toks)
+    outs = [torch.empty(H, D, dtype=torch.float32, device=dev) for _ in range(Lyr)]
+    torch.cuda.synchronize(dev)
+    log(f"[bench] states and input pool resident: "
+        f"{torch.cuda.memory_allocated(dev) / 2**30:.1f} GiB allocated")
+
+    def window(events=None):
+        for pos in range(W):
+            for l in range(Lyr):
+                q, k, v, a, b = pool[l][pos]
+                if events is not None:
+                    events.append(("append", pos, torch.cuda.Event(enable_timing=True)))
+                    events[-1][2].record(stream)
+                lq.leapq_append(layers[l], q, k, v, a, b, outs[l], stream)
+                if events is not None:
+                    events.append(("end", pos, torch.cuda.Event(enable_timing=True)))
+                    events[-1][2].record(stream)
+                if layers[l].n_records == W:
+                    if events is not None:
+                        events.append(("fold", pos, torch.cuda.Event(enable_timing=True)))
+                        events[-1][2].record(stream)
+                    lq.leapq_fold(layers[l], stream)
+                    if events is not None:
+                        events.append(("end", pos, torch.cuda.Event(enable_timing=True)))
+                        events[-1][2].record(stream)
+
+    for _ in range(args.warmup):
+        window()
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup {args.warmup} windows done")
+
+    # ---- timed region: K windows, bracketed by synchronize
+    torch.cuda.synchronize(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(args.steps):
+        window()
+        if (s + 1) % 16 == 0:
+            log(f"[bench] timed windows enqueued: {s + 1}/{args.steps}")
+    t1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = B * W / (ms_per_step / 1e3)
+    log(f"[bench] {args.steps} windows: {total_ms:.1f} ms on the GPU clock ({wall:.2f} s wall); "
+        f"{ms_per_step:.3f} ms per window, {tokens_per_s:,.0f} tokens/s")
+
+    # ---- per-launch durations (HIP events on the launch stream), 2 windows
+    ev_app = {pos: [] for pos in range(W)}
+    ev_fold = []
+    for _ in range(2):
+        events = []
+        window(events)
+        torch.cuda.synchronize(dev)
+        for (kind, pos, e0), (_, _, e1) in zip(events[0::2], events[1::2]):
+            (ev_app[pos] if kind == "append" else ev_fold).append(e0.elapsed_time(e1))
+    app_us = {pos: 1e3 * float(np.mean(v)) for pos, v in ev_app.items()}
+    append_us = float(np.mean(list(app_us.values())))
+    fold_us = 1e3 * float(np.mean(ev_fold))
+    app_bytes_avg = float(np.mean([metrics.append_bytes(n, C, in_bytes) for n in range(W)])) * H
+    fold_bytes = metrics.fold_bytes(W, C) * H
+    append_gbps = app_bytes_avg / (append_us * 1e-6) / 1e9
+    fold_gbps = fold_bytes / (fold_us * 1e-6) / 1e9
+    share = metrics.fold_share(W * append_us, fold_us)
+    window_bytes = metrics.window_bytes(W, C, in_bytes) * H * Lyr
+    path_gbps = window_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] append {append_us:.1f} us ({append_gbps:.0f} GB/s algorithmic), fold {fold_us:.1f} us "
+        f"({fold_gbps:.0f} GB/s), fold share {100 * share:.1f}%, whole path {path_gbps:.0f} GB/s")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha") == kernel_sha() and tr.get("workload") == wl.name:
+            traffic = tr.get("bytes_per_launch")
+
+    # ---- baselines at the same shape: dense fp32-state and bf16-state decode
+    baselines = None
+    if not args.no_baselines:
+        baselines = {}
+        for name, sdt, sbytes in (("fp32_state", torch.float32, 4), ("bf16_state", torch.bfloat16, 2)):
+            states = []
+            for l in range(Lyr):
+                S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
+                states.append(S0.to(sdt).contiguous())
+                del S0
+            for pos in range(2):  # warmup
+                for l in range(Lyr):
+                    q, k, v, a, b = pool[l][pos]
+                    lq.leapq_gdn_decode(cfg, states[l], q, k, v, a, b, outs[l], stream)
+            torch.cuda.synchronize(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            T = args.baseline_tokens
+            e0.record(stream)
+            for t in range(T):
+                for l in range(Lyr):
+                    q, k, v, a, b = pool[l][t % W]
+                    lq.leapq_gdn_decode(cfg, states[l], q, k, v, a, b, outs[l], stream)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            ms_tok = e0.elapsed_time(e1) / T
+            gb = metrics.gdn_step_bytes(sbytes, in_bytes) * H * Lyr / (ms_tok * 1e-3) / 1e9
+            baselines[name] = {"tokens_per_s": B / (ms_tok * 1e-3), "ms_per_token": ms_tok,
+                               "hbm_gbps_algorithmic": gb}
+            log(f"[bench] baseline {name}: {ms_tok:.3f} ms/token, {B / (ms_tok * 1e-3):,.0f} tokens/s, "
+                f"{gb:.0f} GB/s")
+            del states
+            torch.cuda.empty_cache()
+
+    # ---- CPU baseline: the oracle on one layer's heads for one window
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, pool, args.cpu_threads)
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; 16-token input pool per layer, cycled every window)",
+        "config": {"workload": f"{wl.name}: {wl.notes}", "batch": B, "layers": Lyr, "heads": Hh,
+                   "dk": D, "dv": D, "window": W, "n_comp": C, "in_dtype": wl.in_dtype,
+                   "state": "int8 residual + fp32 compensators + fp32 records",
+                   "tokens_per_step": W},
+        "append_us": append_us,
+        "append_us_by_position": [round(app_us[p], 2) for p in range(W)],
+        "fold_us": fold_us,
+        "fold_share": share,
+        "hbm_gbps_path_algorithmic": path_gbps,
+        "roofline": {"bound": "hbm", "kernel": "leapq append", "achieved": append_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": append_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "bytes_per_launch_algorithmic": app_bytes_avg},
+        "fold_roofline": {"bound": "alu", "achieved_gbps_algorithmic": fold_gbps},
+        "baselines": baselines,
+        "cpu_baseline": cpu,
+        "kernel_sha": kernel_sha(),
+    }
+    if baselines:
+        result["speedup_vs_fp32_state"] = tokens_per_s / baselines["fp32_state"]["tokens_per_s"]
+        result["speedup_vs_bf16_state"] = tokens_per_s / baselines["bf16_state"]["tokens_per_s"]
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, pool, threads):
+    """The oracle (unmodified, single-threaded per head; heads spread over a
+    thread pool) on layer 0's heads for one whole window, scaled to the
+    workload's tokens/s."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from quantized_recurrent_state_amd import workloads
+
+    D = 128
+    H = wl.batch * wl.heads
+    S0 = workloads.initial_state(wl, 0, device="cuda").reshape(H, D, D).cpu().numpy()
+    toks = [tuple(x.float().cpu().numpy() for x in pool[0][pos]) for pos in range(wl.window)]
+    heads = list(range(H))
+
+    def one(h):
+        st = oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor).init(S0[h])
+        for (q, k, v, a, b) in toks:
+            st.append(q[h], k[h], v[h], a[h], b[h])
+        st.fold()
+        return 1
+
+    oracle.lib()
+    log(f"[bench] cpu baseline: oracle on {H} heads x 1 window, {threads} threads")
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        done = 0
+        for i, _ in enumerate(ex.map(one, heads)):
+            done += 1
+            if done % 4096 == 0:
+                log(f"[bench] cpu baseline heads done: {done}/{H}")
+    dt = time.perf_counter() - t0
+    scale = wl.layers  # one layer of the workload's layers
+    tok_s = wl.batch * wl.window / (dt * scale)
+    log(f"[bench] cpu baseline: {dt:.2f} s for one layer-window -> {tok_s:.1f} tokens/s")
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 only ({H} heads), one window (16 appends + fold per head), "
+                      f"{dt:.2f} s wall; scaled by {scale} layers",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

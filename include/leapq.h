@@ -1,0 +1,168 @@
+/*
+ * leapq.h - C ABI of the LeapQuant per-window int8 recurrent-state decode
+ * path for Gated DeltaNet heads, on AMD Instinct MI355X (gfx950).
+ *
+ * The method ("LeapQuant: Efficient Linear Attention with Accurate Recurrent
+ * State Quantization", sections 3.2-3.4 and appendix B; "Recurrent-state
+ * quantization for linear attention: a first GPU kernel", Background and
+ * What we built): each head's 128 x 128 state (rows = key coordinates,
+ * columns = value coordinates) is held as an int8 residual with per-row
+ * scales rho and per-column smoothing scales sigma, plus C fp32 compensator
+ * lines.  Each decode token runs an APPEND: the output is read from that
+ * fixed boundary state plus the fp32 records of the current window, and a new
+ * record (cumulative decay, correction u_t, key k_t) is added.  After W
+ * tokens a FOLD rebuilds the state, extracts the largest rows or columns as
+ * compensators, smooths the residual per column, rounds it to int8 per row
+ * and empties the record buffer.
+ *
+ * Arithmetic: IEEE binary32 with a fixed order of operations (canonical
+ * 128-term halving trees, explicit fused multiply-adds), so results are
+ * reproducible bit for bit; see the kernel sources for the exact sequences.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device addresses owned by the caller.  The
+ *     library never allocates, frees or synchronizes; every call is enqueued
+ *     on `stream` (a hipStream_t passed as void*, NULL = default stream) and
+ *     returns without waiting.
+ *   - Return value: LEAPQ_OK (0) or a negative status.  Every status except
+ *     LEAPQ_ERR_HIP is decided on the host before any HIP call; on an error
+ *     nothing is enqueued and no state (including n_records) changes.
+ *     LEAPQ_ERR_HIP reports hipGetLastError() right after a launch.  Faults
+ *     inside a kernel surface on the stream, not here.
+ *   - Tensors are dense, row-major, contiguous; "heads" below means
+ *     batch * heads, and head h's data starts at h * (per-head size).
+ *   - A leapq_layer must not be used from two streams at once.
+ */
+#ifndef LEAPQ_H
+#define LEAPQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define LEAPQ_OK 0
+#define LEAPQ_ERR_NULL (-1)        /* a required pointer is NULL */
+#define LEAPQ_ERR_SHAPE (-2)       /* dk or dv is not 128 */
+#define LEAPQ_ERR_RANGE (-3)       /* batch/heads < 1, window not in [1,64], n_comp not in [0,8],
+                                      smoothing not 0/1, sigma_floor not > 0, what not in {0,1,2},
+                                      heads*batch too large, n_records out of [0, window] */
+#define LEAPQ_ERR_ALIGN (-4)       /* state not 256-byte aligned, or a tensor not 16-byte aligned */
+#define LEAPQ_ERR_WINDOW_FULL (-5) /* append with n_records == window: fold first */
+#define LEAPQ_ERR_DTYPE (-6)       /* in_dtype / state_dtype not LEAPQ_F32 or LEAPQ_BF16 */
+#define LEAPQ_ERR_HIP (-7)         /* the HIP launch failed */
+
+/* element types of q, k, v (in_dtype) and of the dense baseline state */
+#define LEAPQ_F32 0
+#define LEAPQ_BF16 1
+
+/* what leapq_dequant writes */
+#define LEAPQ_DEQ_RESIDUAL 0 /* (code * rho_r) * sigma_c, compensator lines left at zero */
+#define LEAPQ_DEQ_BOUNDARY 1 /* residual + compensator lines: the window's fixed state B */
+#define LEAPQ_DEQ_CURRENT 2  /* gamma_n * B + sum_i (gamma_n / gamma_i) k_i u_i^T: state after n records */
+
+typedef struct leapq_config {
+    int32_t batch;       /* requests (>= 1) */
+    int32_t heads;       /* GDN heads per request (>= 1) */
+    int32_t dk, dv;      /* state shape; must be 128, 128 */
+    int32_t window;      /* W: tokens per window, [1, 64]; 16 in the pages' setting */
+    int32_t n_comp;      /* C: compensator lines, [0, 8]; 4 in the pages' setting */
+    int32_t smoothing;   /* 1: per-column residual smoothing; 0: sigma = 1 */
+    float sigma_floor;   /* positive floor of the smoothing scale (1e-6) */
+    int32_t in_dtype;    /* LEAPQ_F32 or LEAPQ_BF16 for q, k, v */
+    int32_t reserved[3]; /* must be zero */
+} leapq_config;
+
+/* Byte layout of one layer's state buffer.  Sections are "structure of
+ * arrays" over heads; each section starts on a 256-byte boundary and head h's
+ * slice starts at off_X + h * (per-head size of X).
+ *   codes     int8  [heads][128][128]  per head 16384 B.  Row r occupies bytes
+ *                                      128r..128r+127; within a row, byte
+ *                                      16*j + m (j < 8, m < 16) holds value
+ *                                      column j + 8*m (column-interleaved).
+ *   row_scale fp32  [heads][128]       rho_r
+ *   col_scale fp32  [heads][128]       sigma_c
+ *   comp_idx  int32 [heads][C]         -1 unused, 0..127 row r, 128+c column c
+ *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
+ *                                      over r for a column)
+ *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
+ *   rec_k     fp32  [heads][W][128]    record keys
+ *   rec_u     fp32  [heads][W][128]    record corrections
+ * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
+ * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 512 + 512). */
+typedef struct leapq_layout {
+    uint64_t total_bytes;
+    uint64_t off_codes, off_row_scale, off_col_scale, off_comp_idx, off_comp_vec;
+    uint64_t off_rec_gamma, off_rec_k, off_rec_u;
+    uint64_t boundary_bytes_per_head;
+    uint64_t record_bytes_per_head;
+} leapq_layout;
+
+/* One layer: its configuration, its state buffer (device, caller-owned,
+ * total_bytes long, 256-byte aligned) and the host-side count of records in
+ * the current window.  All heads of a layer share the window phase. */
+typedef struct leapq_layer {
+    leapq_config cfg;
+    void *state;
+    int32_t n_records;
+    int32_t reserved;
+} leapq_layer;
+
+/* Fills *out with the layout for cfg.  Host only; touches no device. */
+int32_t leapq_query_layout(const leapq_config *cfg, leapq_layout *out);
+
+/* Quantizes the caller's fp32 states S0 [heads][128][128] (device) into the
+ * layer's boundary state: compensator extraction, smoothing and per-row int8
+ * exactly as a fold does ("LeapQuant" 3.3-3.4), then empties the window
+ * (n_records := 0).  S0 is read only. */
+int32_t leapq_init_state(leapq_layer *layer, const float *S0, void *stream);
+
+/* One decode token for every head of the layer ("Recurrent-state
+ * quantization for linear attention: a first GPU kernel", Background: decay,
+ * read with the key, correction, rank-one write, read the output; "LeapQuant"
+ * B.2-B.3: read from the fixed boundary plus the records).
+ *   q, k [heads][128], v [heads][128] in cfg.in_dtype (device);
+ *   alpha, beta [heads] fp32 (device): decay and step size of this token;
+ *   o [heads][128] fp32 (device, written): the output S_t^T q_t.
+ * Writes record n_records (gamma_t = gamma_{t-1} * alpha, k_t, u_t =
+ * beta (v_t - (alpha S_{t-1})^T k_t)) and increments n_records.  Requires
+ * n_records < window (else LEAPQ_ERR_WINDOW_FULL). */
+int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const void *v,
+                     const float *alpha, const float *beta, float *o, void *stream);
+
+/* Closes the window ("Recurrent-state quantization for linear attention: a
+ * first GPU kernel", What we built: rebuild, select compensators, rescale,
+ * round, empty the buffer; "LeapQuant" B.3): rebuilds the current state from
+ * the boundary and the n_records records, re-extracts the compensators,
+ * recomputes smoothing and row scales, rounds to int8 in place, and sets
+ * n_records := 0.  Valid for any n_records in [0, window]. */
+int32_t leapq_fold(leapq_layer *layer, void *stream);
+
+/* Writes an fp32 [heads][128][128] view of the layer's state to S_out
+ * (device): what = LEAPQ_DEQ_RESIDUAL, LEAPQ_DEQ_BOUNDARY or LEAPQ_DEQ_CURRENT
+ * (see above).  Reads the state only. */
+int32_t leapq_dequant(const leapq_layer *layer, int32_t what, float *S_out, void *stream);
+
+/* Unquantized per-token GDN decode on a dense state, in place (the fp32-state
+ * and bf16-state baselines).  S [heads][128][128] in state_dtype (device,
+ * natural row-major layout); q, k, v in cfg->in_dtype; alpha, beta fp32;
+ * o fp32.  Per token: S = alpha S; u = beta (v - S^T k); S += k u^T;
+ * o = S^T q; a bf16 state is widened, updated in fp32 and rounded to nearest
+ * even on store.  Uses batch, heads, dk, dv and in_dtype of cfg only. */
+int32_t leapq_gdn_decode(const leapq_config *cfg, int32_t state_dtype, void *S, const void *q,
+                         const void *k, const void *v, const float *alpha, const float *beta,
+                         float *o, void *stream);
+
+/* Static description of a status code. */
+const char *leapq_status_str(int32_t status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t leapq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEAPQ_H */

@@ -1,0 +1,46 @@
+"""Build libleapq.so (gfx950) in-tree with hipcc.
+
+Flags that matter for the numbers:
+  -ffp-contract=off   no fused multiply-add except the explicit ones
+  packed-fp32-ops off the kernels are written for unpacked fp32 VALU
+  (no fast-math, no denormal flush; '/' and sqrtf stay correctly rounded,
+   which is hipcc's default for HIP)
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libleapq.so")
+SOURCES = [os.path.join(CSRC, "leapq_kernels.hip"), os.path.join(CSRC, "leapq_abi.cpp")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def build(out=LIB, extra=(), verbose=False):
+    """Compile every HIP source into `out`; returns the path."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libleapq")
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

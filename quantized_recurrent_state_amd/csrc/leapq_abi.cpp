@@ -1,0 +1,197 @@
+// C ABI of libleapq: argument validation, state layout, kernel launches.
+// Every check happens on the host before any HIP call; the library never
+// allocates, frees or synchronizes.
+#include "leapq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "leapq_internal.h"
+
+namespace {
+
+constexpr int kD = 128;
+constexpr uint64_t kAlign = 256;
+constexpr int64_t kMaxHeads = (int64_t)1 << 31;
+
+uint64_t round_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int32_t check_config(const leapq_config *c)
+{
+    if (!c) return LEAPQ_ERR_NULL;
+    if (c->dk != kD || c->dv != kD) return LEAPQ_ERR_SHAPE;
+    if (c->batch < 1 || c->heads < 1) return LEAPQ_ERR_RANGE;
+    if ((int64_t)c->batch * c->heads >= kMaxHeads) return LEAPQ_ERR_RANGE;
+    if (c->in_dtype != LEAPQ_F32 && c->in_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
+    return LEAPQ_OK;
+}
+
+int32_t check_method_config(const leapq_config *c)
+{
+    int32_t st = check_config(c);
+    if (st != LEAPQ_OK) return st;
+    if (c->window < 1 || c->window > 64) return LEAPQ_ERR_RANGE;
+    if (c->n_comp < 0 || c->n_comp > 8) return LEAPQ_ERR_RANGE;
+    if (c->smoothing != 0 && c->smoothing != 1) return LEAPQ_ERR_RANGE;
+    if (!(c->sigma_floor > 0.0f) || c->sigma_floor > 3.0e38f) return LEAPQ_ERR_RANGE;
+    if (c->reserved[0] || c->reserved[1] || c->reserved[2]) return LEAPQ_ERR_RANGE;
+    return LEAPQ_OK;
+}
+
+void compute_layout(const leapq_config *c, leapq_layout *L)
+{
+    const uint64_t H = (uint64_t)c->batch * (uint64_t)c->heads;
+    const uint64_t C = (uint64_t)c->n_comp, W = (uint64_t)c->window;
+    uint64_t off = 0;
+    L->off_codes = off;
+    off = round_up(off + H * kD * kD);
+    L->off_row_scale = off;
+    off = round_up(off + H * kD * 4);
+    L->off_col_scale = off;
+    off = round_up(off + H * kD * 4);
+    L->off_comp_idx = off;
+    off = round_up(off + H * C * 4);
+    L->off_comp_vec = off;
+    off = round_up(off + H * C * kD * 4);
+    L->off_rec_gamma = off;
+    off = round_up(off + H * W * 4);
+    L->off_rec_k = off;
+    off = round_up(off + H * W * kD * 4);
+    L->off_rec_u = off;
+    off = round_up(off + H * W * kD * 4);
+    L->total_bytes = off;
+    L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * kD * 4;
+    L->record_bytes_per_head = W * (4 + 2 * kD * 4);
+}
+
+int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
+{
+    if (!layer) return LEAPQ_ERR_NULL;
+    int32_t st = check_method_config(&layer->cfg);
+    if (st != LEAPQ_OK) return st;
+    if (!layer->state) return LEAPQ_ERR_NULL;
+    if (!aligned(layer->state, kAlign)) return LEAPQ_ERR_ALIGN;
+    if (layer->n_records < 0 || layer->n_records > layer->cfg.window) return LEAPQ_ERR_RANGE;
+    leapq_layout L;
+    compute_layout(&layer->cfg, &L);
+    char *b = (char *)layer->state;
+    sv->codes = (int8_t *)(b + L.off_codes);
+    sv->rho = (float *)(b + L.off_row_scale);
+    sv->sigma = (float *)(b + L.off_col_scale);
+    sv->cidx = (int32_t *)(b + L.off_comp_idx);
+    sv->cvec = (float *)(b + L.off_comp_vec);
+    sv->rgam = (float *)(b + L.off_rec_gamma);
+    sv->rk = (float *)(b + L.off_rec_k);
+    sv->ru = (float *)(b + L.off_rec_u);
+    sv->C = layer->cfg.n_comp;
+    sv->W = layer->cfg.window;
+    return LEAPQ_OK;
+}
+
+int heads_of(const leapq_config *c) { return c->batch * c->heads; }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? LEAPQ_OK : LEAPQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t leapq_query_layout(const leapq_config *cfg, leapq_layout *out)
+{
+    if (!out) return LEAPQ_ERR_NULL;
+    int32_t st = check_method_config(cfg);
+    if (st != LEAPQ_OK) return st;
+    compute_layout(cfg, out);
+    return LEAPQ_OK;
+}
+
+int32_t leapq_init_state(leapq_layer *layer, const float *S0, void *stream)
+{
+    leapq::StateView sv;
+    int32_t st = view_of(layer, &sv);
+    if (st != LEAPQ_OK) return st;
+    if (!S0) return LEAPQ_ERR_NULL;
+    if (!aligned(S0, 16)) return LEAPQ_ERR_ALIGN;
+    st = hip_status(leapq::launch_init(sv, heads_of(&layer->cfg), S0, layer->cfg.smoothing,
+                                       layer->cfg.sigma_floor, (hipStream_t)stream));
+    if (st == LEAPQ_OK) layer->n_records = 0;
+    return st;
+}
+
+int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const void *v, const float *alpha,
+                     const float *beta, float *o, void *stream)
+{
+    leapq::StateView sv;
+    int32_t st = view_of(layer, &sv);
+    if (st != LEAPQ_OK) return st;
+    if (!q || !k || !v || !alpha || !beta || !o) return LEAPQ_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 4) ||
+        !aligned(beta, 4))
+        return LEAPQ_ERR_ALIGN;
+    if (layer->n_records >= layer->cfg.window) return LEAPQ_ERR_WINDOW_FULL;
+    st = hip_status(leapq::launch_append(sv, heads_of(&layer->cfg), layer->n_records,
+                                         layer->cfg.in_dtype == LEAPQ_BF16, q, k, v, alpha, beta, o,
+                                         (hipStream_t)stream));
+    if (st == LEAPQ_OK) layer->n_records += 1;
+    return st;
+}
+
+int32_t leapq_fold(leapq_layer *layer, void *stream)
+{
+    leapq::StateView sv;
+    int32_t st = view_of(layer, &sv);
+    if (st != LEAPQ_OK) return st;
+    st = hip_status(leapq::launch_fold(sv, heads_of(&layer->cfg), layer->n_records, layer->cfg.smoothing,
+                                       layer->cfg.sigma_floor, (hipStream_t)stream));
+    if (st == LEAPQ_OK) layer->n_records = 0;
+    return st;
+}
+
+int32_t leapq_dequant(const leapq_layer *layer, int32_t what, float *S_out, void *stream)
+{
+    leapq::StateView sv;
+    int32_t st = view_of(layer, &sv);
+    if (st != LEAPQ_OK) return st;
+    if (what < LEAPQ_DEQ_RESIDUAL || what > LEAPQ_DEQ_CURRENT) return LEAPQ_ERR_RANGE;
+    if (!S_out) return LEAPQ_ERR_NULL;
+    if (!aligned(S_out, 16)) return LEAPQ_ERR_ALIGN;
+    return hip_status(leapq::launch_dequant(sv, heads_of(&layer->cfg), layer->n_records, what, S_out,
+                                            (hipStream_t)stream));
+}
+
+int32_t leapq_gdn_decode(const leapq_config *cfg, int32_t state_dtype, void *S, const void *q, const void *k,
+                         const void *v, const float *alpha, const float *beta, float *o, void *stream)
+{
+    int32_t st = check_config(cfg);
+    if (st != LEAPQ_OK) return st;
+    if (state_dtype != LEAPQ_F32 && state_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
+    if (!S || !q || !k || !v || !alpha || !beta || !o) return LEAPQ_ERR_NULL;
+    if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(alpha, 4) || !aligned(beta, 4))
+        return LEAPQ_ERR_ALIGN;
+    return hip_status(leapq::launch_gdn_decode(heads_of(cfg), state_dtype == LEAPQ_BF16,
+                                               cfg->in_dtype == LEAPQ_BF16, S, q, k, v, alpha, beta, o,
+                                               (hipStream_t)stream));
+}
+
+const char *leapq_status_str(int32_t status)
+{
+    switch (status) {
+    case LEAPQ_OK: return "ok";
+    case LEAPQ_ERR_NULL: return "a required pointer is NULL";
+    case LEAPQ_ERR_SHAPE: return "dk and dv must be 128";
+    case LEAPQ_ERR_RANGE: return "an argument is out of range";
+    case LEAPQ_ERR_ALIGN: return "misaligned pointer (state: 256 bytes, tensors: 16 bytes)";
+    case LEAPQ_ERR_WINDOW_FULL: return "window full: fold before the next append";
+    case LEAPQ_ERR_DTYPE: return "unsupported element type";
+    case LEAPQ_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int32_t leapq_version(void) { return 100; }
+
+}  // extern "C"

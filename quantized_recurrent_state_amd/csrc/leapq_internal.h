@@ -1,0 +1,33 @@
+// Private to libleapq: the per-layer view of a state buffer passed to the
+// kernels, and the launchers the C ABI calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace leapq {
+
+// Section base pointers of one layer's state buffer (see leapq_layout).
+struct StateView {
+    int8_t *codes;
+    float *rho;
+    float *sigma;
+    int32_t *cidx;
+    float *cvec;
+    float *rgam;
+    float *rk;
+    float *ru;
+    int C;  // compensator lines per head
+    int W;  // record slots per head
+};
+
+hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
+                       hipStream_t s);
+hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s);
+hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s);
+hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
+                         const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
+hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, void *S, const void *q, const void *k,
+                             const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
+
+}  // namespace leapq

@@ -1,0 +1,250 @@
+"""ctypes binding of libleapq (include/leapq.h), under the C names.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libleapq.so.  Tensors are torch tensors (device memory); streams
+are torch streams.  If the shared library is missing this module raises on
+first use; there is no fallback implementation.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+D = 128
+
+LEAPQ_OK = 0
+LEAPQ_ERR_NULL = -1
+LEAPQ_ERR_SHAPE = -2
+LEAPQ_ERR_RANGE = -3
+LEAPQ_ERR_ALIGN = -4
+LEAPQ_ERR_WINDOW_FULL = -5
+LEAPQ_ERR_DTYPE = -6
+LEAPQ_ERR_HIP = -7
+
+LEAPQ_F32 = 0
+LEAPQ_BF16 = 1
+
+LEAPQ_DEQ_RESIDUAL = 0
+LEAPQ_DEQ_BOUNDARY = 1
+LEAPQ_DEQ_CURRENT = 2
+
+SYMBOLS = ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_fold", "leapq_dequant",
+           "leapq_gdn_decode", "leapq_status_str", "leapq_version")
+
+
+class leapq_config(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
+                ("smoothing", ctypes.c_int32), ("sigma_floor", ctypes.c_float),
+                ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+class leapq_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "total_bytes", "off_codes", "off_row_scale", "off_col_scale", "off_comp_idx", "off_comp_vec",
+        "off_rec_gamma", "off_rec_k", "off_rec_u", "boundary_bytes_per_head", "record_bytes_per_head")]
+
+
+class leapq_layer(ctypes.Structure):
+    _fields_ = [("cfg", leapq_config), ("state", ctypes.c_void_p), ("n_records", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class LeapqError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libleapq.so.  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(f"libleapq.so not found at {_build.LIB}; run __graft_entry__.build() "
+                               "or python -m quantized_recurrent_state_amd.build")
+        L = ctypes.CDLL(_build.LIB)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.leapq_query_layout.argtypes = [ctypes.POINTER(leapq_config), ctypes.POINTER(leapq_layout)]
+        L.leapq_init_state.argtypes = [ctypes.POINTER(leapq_layer), vp, vp]
+        L.leapq_append.argtypes = [ctypes.POINTER(leapq_layer), vp, vp, vp, vp, vp, vp, vp]
+        L.leapq_fold.argtypes = [ctypes.POINTER(leapq_layer), vp]
+        L.leapq_dequant.argtypes = [ctypes.POINTER(leapq_layer), i32, vp, vp]
+        L.leapq_gdn_decode.argtypes = [ctypes.POINTER(leapq_config), i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        for f in ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_fold", "leapq_dequant",
+                  "leapq_gdn_decode", "leapq_version"):
+            getattr(L, f).restype = i32
+        L.leapq_status_str.argtypes = [i32]
+        L.leapq_status_str.restype = ctypes.c_char_p
+        L.leapq_version.argtypes = []
+        _LIB = L
+    return _LIB
+
+
+def status_str(status):
+    return lib().leapq_status_str(int(status)).decode()
+
+
+def _check(status, what):
+    if status != LEAPQ_OK:
+        raise LeapqError(status, what)
+
+
+def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32"):
+    c = leapq_config()
+    c.batch, c.heads, c.dk, c.dv = int(batch), int(heads), D, D
+    c.window, c.n_comp, c.smoothing = int(window), int(n_comp), int(bool(smoothing))
+    c.sigma_floor = float(sigma_floor)
+    c.in_dtype = LEAPQ_BF16 if in_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
+    return c
+
+
+def leapq_query_layout(cfg):
+    out = leapq_layout()
+    _check(lib().leapq_query_layout(ctypes.byref(cfg), ctypes.byref(out)), "leapq_query_layout")
+    return out
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dev_tensor(t, name, dtype, shape, device):
+    if t.device != device or t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device} (contiguous={t.is_contiguous()})")
+
+
+class Layer:
+    """One layer: config + its state buffer (torch uint8 tensor) + window count."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.layout = leapq_query_layout(cfg)
+        n = int(self.layout.total_bytes)
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=self.device)
+        off = (-buf.data_ptr()) % 256
+        self._buf = buf
+        self.state = buf[off:off + n]
+        self.c = leapq_layer()
+        self.c.cfg = cfg
+        self.c.state = self.state.data_ptr()
+        self.c.n_records = 0
+
+    @property
+    def heads(self):
+        return self.cfg.batch * self.cfg.heads
+
+    @property
+    def n_records(self):
+        return self.c.n_records
+
+    @property
+    def in_dtype(self):
+        return torch.bfloat16 if self.cfg.in_dtype == LEAPQ_BF16 else torch.float32
+
+    # ---- read-only views of the state sections (layout of include/leapq.h)
+    def _sec(self, off, count, dtype, shape):
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return self.state[off:off + nbytes].view(dtype).view(*shape)
+
+    def codes_physical(self):
+        H = self.heads
+        return self._sec(self.layout.off_codes, H * D * D, torch.int8, (H, D, D))
+
+    def codes(self):
+        """int8 [heads, 128(row), 128(column)] in logical column order."""
+        phys = self.codes_physical()
+        col = torch.arange(D, device=self.device)
+        pos = (col % 8) * 16 + col // 8  # byte position of column c in a row
+        return phys[:, :, pos]
+
+    def rho(self):
+        return self._sec(self.layout.off_row_scale, self.heads * D, torch.float32, (self.heads, D))
+
+    def sigma(self):
+        return self._sec(self.layout.off_col_scale, self.heads * D, torch.float32, (self.heads, D))
+
+    def comp_idx(self):
+        C = max(self.cfg.n_comp, 0)
+        return self._sec(self.layout.off_comp_idx, self.heads * C, torch.int32, (self.heads, C))
+
+    def comp_vec(self):
+        C = max(self.cfg.n_comp, 0)
+        return self._sec(self.layout.off_comp_vec, self.heads * C * D, torch.float32, (self.heads, C, D))
+
+    def rec_gamma(self):
+        W = self.cfg.window
+        return self._sec(self.layout.off_rec_gamma, self.heads * W, torch.float32, (self.heads, W))
+
+    def rec_k(self):
+        W = self.cfg.window
+        return self._sec(self.layout.off_rec_k, self.heads * W * D, torch.float32, (self.heads, W, D))
+
+    def rec_u(self):
+        W = self.cfg.window
+        return self._sec(self.layout.off_rec_u, self.heads * W * D, torch.float32, (self.heads, W, D))
+
+
+def leapq_init_state(layer, S0, stream=None):
+    _dev_tensor(S0, "S0", torch.float32, (layer.heads, D, D), layer.device)
+    _check(lib().leapq_init_state(ctypes.byref(layer.c), _ptr(S0), _stream(stream, layer.device)),
+           "leapq_init_state")
+
+
+def leapq_append(layer, q, k, v, alpha, beta, o, stream=None):
+    H, dt, dev = layer.heads, layer.in_dtype, layer.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, dt, (H, D), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, (H,), dev)
+    _dev_tensor(beta, "beta", torch.float32, (H,), dev)
+    _dev_tensor(o, "o", torch.float32, (H, D), dev)
+    _check(lib().leapq_append(ctypes.byref(layer.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                              _ptr(o), _stream(stream, dev)), "leapq_append")
+
+
+def leapq_fold(layer, stream=None):
+    _check(lib().leapq_fold(ctypes.byref(layer.c), _stream(stream, layer.device)), "leapq_fold")
+
+
+def leapq_dequant(layer, what, out, stream=None):
+    _dev_tensor(out, "S_out", torch.float32, (layer.heads, D, D), layer.device)
+    _check(lib().leapq_dequant(ctypes.byref(layer.c), int(what), _ptr(out), _stream(stream, layer.device)),
+           "leapq_dequant")
+
+
+def leapq_gdn_decode(cfg, S, q, k, v, alpha, beta, o, stream=None):
+    """Dense baseline step in place on S (fp32 or bf16 [heads, 128, 128])."""
+    H = cfg.batch * cfg.heads
+    dev = S.device
+    if S.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("S must be float32 or bfloat16")
+    _dev_tensor(S, "S", S.dtype, (H, D, D), dev)
+    dt = torch.bfloat16 if cfg.in_dtype == LEAPQ_BF16 else torch.float32
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, dt, (H, D), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, (H,), dev)
+    _dev_tensor(beta, "beta", torch.float32, (H,), dev)
+    _dev_tensor(o, "o", torch.float32, (H, D), dev)
+    sd = LEAPQ_BF16 if S.dtype == torch.bfloat16 else LEAPQ_F32
+    _check(lib().leapq_gdn_decode(ctypes.byref(cfg), sd, _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                  _ptr(beta), _ptr(o), _stream(stream, dev)), "leapq_gdn_decode")
+
+
+def leapq_version():
+    return int(lib().leapq_version())

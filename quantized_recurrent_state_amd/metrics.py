@@ -1,0 +1,71 @@
+"""Algorithmic byte counts and step definitions of the decode path.
+
+Algorithmic bytes are what each kernel must move between HBM and the chip
+for one head (no re-reads, no dense fp32 state):
+
+  append, with n records already in the window (token n+1):
+      read   codes 128*128 + rho, sigma 2*512 + compensators C*(4+512)
+             + q, k, v 3*128*e_in + alpha, beta 8 + records n*(4+512+512)
+      write  record 4+512+512 + output 512
+  fold of n records:
+      read   boundary (codes, scales, compensators) + n records
+      write  boundary
+  dense GDN step (baselines): read + write the state, plus q, k, v, alpha,
+      beta and the output.
+
+"Recurrent-state quantization for linear attention: a first GPU kernel"
+(Where the time goes) defines the per-token step of the windowed path as a
+window's appends plus its fold, divided by the window length; the fold's
+share of window time is fold / (appends + fold).
+"""
+D = 128
+
+
+def boundary_bytes(C=4):
+    """Bytes of one head's boundary state: int8 codes, rho, sigma, C lines."""
+    return D * D + 2 * D * 4 + C * (4 + D * 4)
+
+
+def record_bytes():
+    """Bytes of one record: gamma, k, u in fp32."""
+    return 4 + 2 * D * 4
+
+
+def append_bytes(n, C=4, in_bytes=2):
+    """Algorithmic bytes of one head's append with n records present."""
+    read = boundary_bytes(C) + 3 * D * in_bytes + 8 + n * record_bytes()
+    write = record_bytes() + D * 4
+    return read + write
+
+
+def fold_bytes(n, C=4):
+    return 2 * boundary_bytes(C) + n * record_bytes()
+
+
+def init_bytes(C=4):
+    return D * D * 4 + boundary_bytes(C)
+
+
+def window_bytes(W=16, C=4, in_bytes=2):
+    """Bytes of one head over a whole window: W appends and one fold."""
+    return sum(append_bytes(n, C, in_bytes) for n in range(W)) + fold_bytes(W, C)
+
+
+def gdn_step_bytes(state_bytes=4, in_bytes=2):
+    """Dense per-token GDN step: state read + write, inputs, output."""
+    return 2 * D * D * state_bytes + 3 * D * in_bytes + 8 + D * 4
+
+
+def step_ms(append_ms, fold_extra_ms, W=16):
+    """Mean per-token step: W appends plus the fold's extra time, over W."""
+    return (W * append_ms + fold_extra_ms) / W
+
+
+def fold_budget_ms(append_ms, target_step_ms, W=16):
+    """Largest fold time (beyond an append) that keeps the step at target."""
+    return W * (target_step_ms - append_ms)
+
+
+def fold_share(append_total, fold_total):
+    """Fold time over window time (appends + fold)."""
+    return fold_total / (append_total + fold_total)

@@ -1,0 +1,177 @@
+"""Side-by-side runs of libleapq (GPU, through the C ABI) and the CPU oracle.
+
+Both sides consume the same seeded inputs; nothing computed by the GPU is fed
+to the oracle.  Runs are free-running: the oracle keeps its own state through
+every window.  Pass bar per compared field:
+  compensator indices        exact
+  int8 codes                 bit-exact, except codes whose oracle pre-rounding
+                             value lies within 1e-6 relative of a .5 boundary;
+                             those may differ by one and must be fewer than
+                             1e-6 of the compared codes
+  fp32 outputs, scales, lines, records   relative error <= 1e-4
+The harness also counts fp32 values that are not bitwise equal, which the
+canonical arithmetic is designed to make zero.
+"""
+import concurrent.futures as cf
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from quantized_recurrent_state_amd import leapq as lq
+from quantized_recurrent_state_amd import workloads
+
+D = 128
+TOL = 1e-4
+
+
+def progress(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)) / max(float(np.max(np.abs(b))), 1e-30))
+
+
+class Report:
+    def __init__(self):
+        self.worst = {}
+        self.nonbit = {}
+        self.code_total = 0
+        self.code_exempt = 0
+        self.code_bad = 0
+        self.idx_bad = 0
+
+    def fp(self, name, gpu, ref):
+        gpu = np.asarray(gpu, np.float32)
+        ref = np.asarray(ref, np.float32)
+        assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+        r = rel(gpu, ref)
+        self.worst[name] = max(self.worst.get(name, 0.0), r)
+        self.nonbit[name] = self.nonbit.get(name, 0) + int(np.sum(gpu.view(np.uint32) != ref.view(np.uint32)))
+
+    def codes(self, gpu, ref_head, ref_y=None):
+        gpu = np.asarray(gpu, np.int8)
+        diff = gpu != ref_head
+        self.code_total += gpu.size
+        nd = int(diff.sum())
+        if nd:
+            if ref_y is None:
+                self.code_bad += nd
+            else:
+                y = np.abs(ref_y[diff])
+                near = np.abs(y - np.floor(y) - 0.5) <= 1e-6 * y
+                off1 = np.abs(gpu[diff].astype(np.int32) - ref_head[diff].astype(np.int32)) == 1
+                ok = near & off1
+                self.code_exempt += int(ok.sum())
+                self.code_bad += int((~ok).sum())
+
+    def check(self):
+        msgs = []
+        for k, v in self.worst.items():
+            if not v <= TOL:
+                msgs.append(f"{k}: relative error {v:.3g} > {TOL}")
+        if self.idx_bad:
+            msgs.append(f"compensator indices differ in {self.idx_bad} slots")
+        if self.code_bad:
+            msgs.append(f"{self.code_bad} int8 codes differ outside the .5-boundary exemption")
+        if self.code_total and self.code_exempt >= 1e-6 * self.code_total:
+            msgs.append(f"{self.code_exempt} exempt code differences >= 1e-6 of {self.code_total}")
+        assert not msgs, "; ".join(msgs)
+
+    def summary(self):
+        return {"worst_rel": self.worst, "non_bitwise": self.nonbit, "codes": self.code_total,
+                "codes_exempt": self.code_exempt, "codes_bad": self.code_bad, "idx_bad": self.idx_bad}
+
+
+def compare_state(L, heads_ref, sample, rep, what="all"):
+    """Boundary state (and records) of sampled heads against the oracle."""
+    idx = torch.as_tensor(sample, device=L.device)
+    codes = L.codes()[idx].cpu().numpy()
+    rho = L.rho()[idx].cpu().numpy()
+    sig = L.sigma()[idx].cpu().numpy()
+    C = L.cfg.n_comp
+    cidx = L.comp_idx()[idx].cpu().numpy() if C else None
+    cvec = L.comp_vec()[idx].cpu().numpy() if C else None
+    n = L.n_records
+    if n:
+        rg = L.rec_gamma()[idx].cpu().numpy()
+        rk = L.rec_k()[idx].cpu().numpy()
+        ru = L.rec_u()[idx].cpu().numpy()
+    for s, h in enumerate(heads_ref):
+        assert h.n == n
+        # without the oracle's pre-rounding values every code difference
+        # counts against the bar (stricter than the .5-boundary exemption)
+        rep.codes(codes[s], h.Q, None)
+        rep.fp("rho", rho[s], h.rho)
+        rep.fp("sigma", sig[s], h.sigma)
+        if C:
+            if not np.array_equal(cidx[s], h.idx[:C]):
+                rep.idx_bad += int(np.sum(cidx[s] != h.idx[:C]))
+            rep.fp("comp_vec", cvec[s], h.vec[:C])
+        if n:
+            rep.fp("rec_gamma", rg[s, :n], h.gam[:n])
+            rep.fp("rec_k", rk[s, :n], h.rk[:n])
+            rep.fp("rec_u", ru[s, :n], h.ru[:n])
+
+
+def _pool():
+    return cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
+
+
+def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="cuda", check_every_token=True,
+              fold_at=None, report=None, log=True):
+    """Runs `tokens` decode tokens of one layer on the GPU and, for the
+    sampled heads, in the oracle; folds whenever the window is full (or at
+    the token counts in fold_at).  Returns the Report."""
+    rep = report or Report()
+    dev = torch.device(device)
+    H = wl.batch * wl.heads
+    T = wl.tokens if tokens is None else tokens
+    sample = list(range(H)) if sample is None else list(sample)
+    cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype)
+    L = lq.Layer(cfg, dev)
+    S0 = workloads.initial_state(wl, layer, device=gen_device).reshape(H, D, D)
+    lq.leapq_init_state(L, S0.to(dev))
+    S0h = S0[sample].cpu().numpy()
+    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor) for _ in sample]
+    with _pool() as pool:
+        list(pool.map(lambda a: a[0].init(a[1]), zip(refs, S0h)))
+        torch.cuda.synchronize(dev)
+        compare_state(L, refs, sample, rep)
+        o = torch.empty(H, D, dtype=torch.float32, device=dev)
+        sidx = torch.as_tensor(sample)
+        for t in range(T):
+            q, k, v, a, b = workloads.token_inputs(wl, layer, t, device=gen_device)
+            qd, kd, vd = (x.reshape(H, D).to(dev) for x in (q, k, v))
+            ad, bd = a.reshape(H).to(dev), b.reshape(H).to(dev)
+            lq.leapq_append(L, qd, kd, vd, ad, bd, o)
+            qh = workloads.widen(q.reshape(H, D)[sidx]).cpu().numpy()
+            kh = workloads.widen(k.reshape(H, D)[sidx]).cpu().numpy()
+            vh = workloads.widen(v.reshape(H, D)[sidx]).cpu().numpy()
+            ah = a.reshape(H)[sidx].cpu().numpy()
+            bh = b.reshape(H)[sidx].cpu().numpy()
+            outs = list(pool.map(lambda s: refs[s].append(qh[s], kh[s], vh[s], ah[s], bh[s])[0],
+                                 range(len(sample))))
+            og = o[sidx.to(dev)].cpu().numpy()
+            rep.fp("o", og, np.stack(outs))
+            if check_every_token:
+                compare_state(L, refs, sample, rep)
+            full = L.n_records == wl.window
+            if full or (fold_at is not None and (t + 1) in fold_at):
+                lq.leapq_fold(L)
+                list(pool.map(lambda h: h.fold(), refs))
+                torch.cuda.synchronize(dev)
+                compare_state(L, refs, sample, rep)
+                if log:
+                    progress(f"  [{wl.name} layer {layer}] token {t + 1}/{T}: folded; "
+                             f"worst {max(rep.worst.values()):.2e}, non-bitwise {sum(rep.nonbit.values())}, "
+                             f"codes bad {rep.code_bad}, idx bad {rep.idx_bad}")
+    return rep, L, refs

@@ -1,0 +1,200 @@
+"""Host-side checks of the C ABI (no GPU): symbols, layout, validation.
+
+Every call here returns before any HIP call (validation failures and the
+host-only layout query), so it runs on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_recurrent_state_amd import leapq as lq
+from quantized_recurrent_state_amd import metrics
+from tests.pins import golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # a 256-byte-aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "leapq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(leapq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert set(names) == set(lq.SYMBOLS), names
+    L = lq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert lq.leapq_version() == 100
+    for st in range(0, -8, -1):
+        s = lq.status_str(st)
+        assert s and s != "unknown status", st
+    assert lq.status_str(-99) == "unknown status"
+
+
+def layout(**kw):
+    return lq.leapq_query_layout(lq.make_config(**kw))
+
+
+def test_layout_sections_aligned_and_disjoint():
+    for (B, H, W, C) in ((1, 4, 16, 4), (512, 32, 16, 4), (3, 5, 1, 0), (2, 7, 64, 8)):
+        L = layout(batch=B, heads=H, window=W, n_comp=C)
+        heads = B * H
+        secs = [("off_codes", heads * 128 * 128), ("off_row_scale", heads * 512), ("off_col_scale", heads * 512),
+                ("off_comp_idx", heads * C * 4), ("off_comp_vec", heads * C * 512),
+                ("off_rec_gamma", heads * W * 4), ("off_rec_k", heads * W * 512), ("off_rec_u", heads * W * 512)]
+        end = 0
+        for name, size in secs:
+            off = getattr(L, name)
+            assert off % 256 == 0 and off >= end, (name, off, end)
+            end = off + size
+        assert L.total_bytes >= end and L.total_bytes % 256 == 0
+        assert L.boundary_bytes_per_head == metrics.boundary_bytes(C)
+        assert L.record_bytes_per_head == W * metrics.record_bytes()
+
+
+def test_layout_matches_page_figures():
+    g = golden("page_figures.json")
+    L = layout(batch=1, heads=1)
+    bpe = L.boundary_bytes_per_head / (128 * 128)
+    f = g["boundary_bytes_per_element"]
+    assert abs(bpe - f["value"]) <= f["printed_digits_tol"], bpe
+    assert abs(f["fp32_bytes_per_element"] / bpe - f["storage_ratio"]) <= f["ratio_tol"]
+    r = g["fp32_state_bytes_per_request"]
+    s = r["shape"]
+    fp32 = s["layers"] * s["heads"] * s["dk"] * s["dv"] * s["bytes_per_number"]
+    assert abs(fp32 - r["value"]) <= r["printed_digits_tol"], fp32
+    e = g["gpu_entries_matched"]
+    assert e["folds"] * e["heads"] * e["entries_per_head"] == e["value"]
+    assert e["entries_per_head"] == 128 * 128
+    d = g["defaults"]
+    assert (lq.make_config(1, 1).window, lq.make_config(1, 1).n_comp) == (d["window"], d["n_comp"])
+
+
+def test_step_definition_matches_page():
+    s = golden("page_figures.json")["step_definition"]
+    step = metrics.step_ms(s["append_ms"], s["fold_extra_ms"], s["window"])
+    assert abs(step - s["table_step_ms"]) <= s["tol_ms"], step
+    budget = metrics.fold_budget_ms(s["append_ms"], s["window_kernel_ms"], s["window"])
+    assert abs(budget - s["fold_budget_ms"]) <= s["budget_tol_ms"], budget
+
+
+def test_bytes_model_values():
+    # one head, bf16 inputs, W=16, C=4
+    assert metrics.append_bytes(0) == 21788
+    assert sum(metrics.append_bytes(n) for n in range(16)) / 16 == 29498
+    assert metrics.fold_bytes(16) == 55392
+    assert metrics.window_bytes() / 16 == 32960
+    assert metrics.gdn_step_bytes(4) == 132360 and metrics.gdn_step_bytes(2) == 66824
+
+
+# ---------------------------------------------------------------- validation
+
+def cfg(**kw):
+    base = dict(batch=2, heads=4, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32")
+    base.update(kw)
+    return lq.make_config(**base)
+
+
+def fake_layer(c, n=0, state=FAKE):
+    L = lq.leapq_layer()
+    L.cfg = c
+    L.state = state
+    L.n_records = n
+    return L
+
+
+def call_append(L, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, o=FAKE):
+    vp = ctypes.c_void_p
+    return lq.lib().leapq_append(ctypes.byref(L), vp(q), vp(k), vp(v), vp(a), vp(b), vp(o), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), lq.LEAPQ_ERR_RANGE), (dict(heads=0), lq.LEAPQ_ERR_RANGE),
+    (dict(window=0), lq.LEAPQ_ERR_RANGE), (dict(window=65), lq.LEAPQ_ERR_RANGE),
+    (dict(n_comp=-1), lq.LEAPQ_ERR_RANGE), (dict(n_comp=9), lq.LEAPQ_ERR_RANGE),
+    (dict(sigma_floor=0.0), lq.LEAPQ_ERR_RANGE), (dict(sigma_floor=float("nan")), lq.LEAPQ_ERR_RANGE),
+])
+def test_config_ranges(kw, status):
+    c = cfg(**kw)
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(lq.leapq_layout())) == status
+    L = fake_layer(c)
+    assert call_append(L) == status and L.n_records == 0
+
+
+def test_config_shape_dtype_reserved():
+    L_out = lq.leapq_layout()
+    c = cfg()
+    c.dk = 64
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_SHAPE
+    c = cfg()
+    c.in_dtype = 7
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_DTYPE
+    c = cfg()
+    c.smoothing = 2
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
+    c = cfg()
+    c.reserved[1] = 1
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
+    assert lq.lib().leapq_query_layout(None, ctypes.byref(L_out)) == lq.LEAPQ_ERR_NULL
+    assert lq.lib().leapq_query_layout(ctypes.byref(cfg()), None) == lq.LEAPQ_ERR_NULL
+
+
+def test_append_pointer_checks():
+    c = cfg()
+    assert call_append(fake_layer(c, state=0)) == lq.LEAPQ_ERR_NULL
+    assert call_append(fake_layer(c, state=FAKE + 16)) == lq.LEAPQ_ERR_ALIGN
+    for key in ("q", "k", "v", "a", "b", "o"):
+        assert call_append(fake_layer(c), **{key: 0}) == lq.LEAPQ_ERR_NULL, key
+    for key in ("q", "k", "v", "o"):
+        assert call_append(fake_layer(c), **{key: FAKE + 4}) == lq.LEAPQ_ERR_ALIGN, key
+    assert lq.lib().leapq_append(None, *([ctypes.c_void_p(FAKE)] * 6), None) == lq.LEAPQ_ERR_NULL
+
+
+def test_append_window_full_and_record_range():
+    c = cfg(window=16)
+    L = fake_layer(c, n=16)
+    assert call_append(L) == lq.LEAPQ_ERR_WINDOW_FULL and L.n_records == 16
+    L = fake_layer(c, n=17)
+    assert call_append(L) == lq.LEAPQ_ERR_RANGE
+    L = fake_layer(c, n=-1)
+    assert lq.lib().leapq_fold(ctypes.byref(L), None) == lq.LEAPQ_ERR_RANGE and L.n_records == -1
+
+
+def test_init_fold_dequant_checks():
+    c = cfg()
+    lib = lq.lib()
+    vp = ctypes.c_void_p
+    L = fake_layer(c)
+    assert lib.leapq_init_state(ctypes.byref(L), None, None) == lq.LEAPQ_ERR_NULL
+    assert lib.leapq_init_state(ctypes.byref(L), vp(FAKE + 8), None) == lq.LEAPQ_ERR_ALIGN
+    assert lib.leapq_fold(None, None) == lq.LEAPQ_ERR_NULL
+    assert lib.leapq_fold(ctypes.byref(fake_layer(c, state=FAKE + 128)), None) == lq.LEAPQ_ERR_ALIGN
+    for what in (-1, 3):
+        assert lib.leapq_dequant(ctypes.byref(L), what, vp(FAKE), None) == lq.LEAPQ_ERR_RANGE
+    assert lib.leapq_dequant(ctypes.byref(L), 0, None, None) == lq.LEAPQ_ERR_NULL
+    assert lib.leapq_dequant(ctypes.byref(L), 2, vp(FAKE + 4), None) == lq.LEAPQ_ERR_ALIGN
+
+
+def test_gdn_decode_checks():
+    lib = lq.lib()
+    vp = ctypes.c_void_p
+    c = cfg()
+    args = [vp(FAKE)] * 8
+    assert lib.leapq_gdn_decode(ctypes.byref(c), 5, *args, None) == lq.LEAPQ_ERR_DTYPE
+    assert lib.leapq_gdn_decode(None, 0, *args, None) == lq.LEAPQ_ERR_NULL
+    bad = list(args)
+    bad[0] = None
+    assert lib.leapq_gdn_decode(ctypes.byref(c), 0, *bad, None) == lq.LEAPQ_ERR_NULL
+    bad = list(args)
+    bad[1] = vp(FAKE + 2)
+    assert lib.leapq_gdn_decode(ctypes.byref(c), 1, *bad, None) == lq.LEAPQ_ERR_ALIGN
+    c.dv = 96
+    assert lib.leapq_gdn_decode(ctypes.byref(c), 0, *args, None) == lq.LEAPQ_ERR_SHAPE
