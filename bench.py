@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s and HBM GB/s (% of peak), append+fold, 24Lx32H, batch 512"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "quantized_recurrent_state_amd", "csrc", "leapq_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "quantized_recurrent_state_amd", "csrc", "leapq_append.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_b512_traffic.json")
 
 

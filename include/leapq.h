@@ -88,8 +88,11 @@ typedef struct leapq_config {
  *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
  *                                      over r for a column)
  *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
- *   rec_k     fp32  [heads][W][128]    record keys
- *   rec_u     fp32  [heads][W][128]    record corrections
+ *   rec_k     fp32  [heads][W][128]    record keys; key row r is stored at
+ *                                      4*(r % 32) + r / 32
+ *   rec_u     fp32  [heads][W][128]    record corrections; value column c is
+ *                                      stored at 16*(c % 8) + c / 8 (the
+ *                                      interleave of a code row)
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
  * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 512 + 512). */
 typedef struct leapq_layout {

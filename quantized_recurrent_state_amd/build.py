@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libleapq.so")
-SOURCES = [os.path.join(CSRC, "leapq_kernels.hip"), os.path.join(CSRC, "leapq_abi.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("leapq_append.hip", "leapq_fold.hip", "leapq_dense.hip", "leapq_abi.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -192,13 +192,23 @@ class Layer:
         W = self.cfg.window
         return self._sec(self.layout.off_rec_gamma, self.heads * W, torch.float32, (self.heads, W))
 
-    def rec_k(self):
+    def rec_k_physical(self):
         W = self.cfg.window
         return self._sec(self.layout.off_rec_k, self.heads * W * D, torch.float32, (self.heads, W, D))
 
-    def rec_u(self):
+    def rec_u_physical(self):
         W = self.cfg.window
         return self._sec(self.layout.off_rec_u, self.heads * W * D, torch.float32, (self.heads, W, D))
+
+    def rec_k(self):
+        """Record keys [heads, W, 128] in logical key-row order."""
+        r = torch.arange(D, device=self.device)
+        return self.rec_k_physical()[:, :, 4 * (r % 32) + r // 32]
+
+    def rec_u(self):
+        """Record corrections [heads, W, 128] in logical value-column order."""
+        c = torch.arange(D, device=self.device)
+        return self.rec_u_physical()[:, :, 16 * (c % 8) + c // 8]
 
 
 def leapq_init_state(layer, S0, stream=None):
