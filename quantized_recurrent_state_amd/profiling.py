@@ -1,0 +1,171 @@
+"""Short GPU programs for rocprofv3 runs, and the reduction of its CSV output.
+
+Programs (each is what comes after `rocprofv3 ... --`):
+
+  python3 -m quantized_recurrent_state_amd.profiling run [--workload b512] [--windows 2]
+      one layer of the workload: init, then `windows` x (W appends + fold)
+  python3 -m quantized_recurrent_state_amd.profiling copy [--mib 1024] [--reps 4]
+      a copy-shaped elementwise kernel (y = -x: 4 bytes read and 4 written
+      per element; torch's same-dtype copy_ is a DMA blit, not a kernel) of
+      known size, to calibrate FETCH_SIZE and WRITE_SIZE against bytes moved
+
+Reductions (CPU only, read the CSV files rocprofv3 wrote):
+
+  python3 -m quantized_recurrent_state_amd.profiling traffic \
+      --kernel k_append --fetch F.csv --write W.csv \
+      --copy-fetch CF.csv --copy-write CW.csv --copy-mib 1024 --workload b512 --out X.json
+  python3 -m quantized_recurrent_state_amd.profiling stats --csv kernel_stats.csv
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+
+def kernel_sha(src="leapq_append.hip"):
+    with open(os.path.join(PKG, "csrc", src), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- programs
+def run_layer(workload, windows):
+    import torch
+
+    from . import leapq as lq
+    from . import workloads
+
+    wl = workloads.WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    H, D = wl.batch * wl.heads, 128
+    toks = []
+    for pos in range(wl.window):
+        q, k, v, a, b = workloads.token_inputs(wl, 0, pos, device=dev)
+        toks.append((q.reshape(H, D), k.reshape(H, D), v.reshape(H, D), a.reshape(H), b.reshape(H)))
+    S0 = workloads.initial_state(wl, 0, device=dev).reshape(H, D, D)
+    o = torch.empty(H, D, dtype=torch.float32, device=dev)
+    L = lq.Layer(lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing,
+                                wl.sigma_floor, wl.in_dtype), dev)
+    lq.leapq_init_state(L, S0)
+    for w in range(windows):
+        for n in range(wl.window):
+            q, k, v, a, b = toks[n]
+            lq.leapq_append(L, q, k, v, a, b, o)
+        lq.leapq_fold(L)
+        torch.cuda.synchronize(dev)
+        print(f"[profiling] {wl.name} layer 0: window {w + 1}/{windows} done", flush=True)
+
+
+def run_copy(mib, reps):
+    import torch
+
+    n = mib * 2**20 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for r in range(reps):
+        torch.neg(x, out=y)  # an elementwise kernel: one read and one write per element
+    torch.cuda.synchronize()
+    print(f"[profiling] copy {mib} MiB x {reps} done", flush=True)
+
+
+# ---------------------------------------------------------------- reductions
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def counter_per_dispatch(path, kernel, counter):
+    """Mean over dispatches of `kernel` (substring of the kernel name) of the
+    counter's value (summed over the CSV's rows of one dispatch)."""
+    per = {}
+    for r in _rows(path):
+        if kernel not in r.get("Kernel_Name", "") or r.get("Counter_Name") != counter:
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernel {kernel!r} in {path}")
+    vals = list(per.values())
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic(args):
+    """HBM bytes per launch of `kernel` from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by bytes-moved / counter of a plain copy."""
+    copy_bytes = args.copy_mib * 2**20
+    cf, _ = counter_per_dispatch(args.copy_fetch, args.copy_kernel, "FETCH_SIZE")
+    cw, _ = counter_per_dispatch(args.copy_write, args.copy_kernel, "WRITE_SIZE")
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    kf, nf = counter_per_dispatch(args.fetch, args.kernel, "FETCH_SIZE")
+    kw, nw = counter_per_dispatch(args.write, args.kernel, "WRITE_SIZE")
+    fetch_b = kf * 1024.0 * f_scale
+    write_b = kw * 1024.0 * w_scale
+    out = {
+        "kernel": args.kernel,
+        "kernel_sha": kernel_sha(args.kernel_src),
+        "workload": args.workload,
+        "dispatches": [nf, nw],
+        "fetch_kib_raw": kf,
+        "write_kib_raw": kw,
+        "copy_mib": args.copy_mib,
+        "copy_fetch_scale": f_scale,
+        "copy_write_scale": w_scale,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b,
+    }
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def stats(args):
+    """Kernel-trace stats CSV -> a short table (name, calls, mean us, total ms)."""
+    rows = _rows(args.csv)
+    print(f"{'kernel':60s} {'calls':>6s} {'mean_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    for r in rows:
+        name = r["Name"][:60]
+        print(f"{name:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+              f"{float(r['TotalDurationNs']) / 1e6:10.3f} {float(r['Percentage']):6.2f}")
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", default="b512")
+    r.add_argument("--windows", type=int, default=2)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=4)
+    t = sub.add_parser("traffic")
+    t.add_argument("--kernel", default="k_append")
+    t.add_argument("--kernel-src", default="leapq_append.hip")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-kernel", default="neg_kernel")
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--workload", default="b512")
+    t.add_argument("--out", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    a = p.parse_args(argv)
+    if a.cmd == "run":
+        run_layer(a.workload, a.windows)
+    elif a.cmd == "copy":
+        run_copy(a.mib, a.reps)
+    elif a.cmd == "traffic":
+        traffic(a)
+    else:
+        stats(a)
+
+
+if __name__ == "__main__":
+    main()
