@@ -77,22 +77,26 @@ typedef struct leapq_config {
 
 /* Byte layout of one layer's state buffer.  Sections are "structure of
  * arrays" over heads; each section starts on a 256-byte boundary and head h's
- * slice starts at off_X + h * (per-head size of X).
- *   codes     int8  [heads][128][128]  per head 16384 B.  Row r occupies bytes
- *                                      128r..128r+127; within a row, byte
- *                                      16*j + m (j < 8, m < 16) holds value
- *                                      column j + 8*m (column-interleaved).
+ * slice starts at off_X + h * (per-head size of X).  With
+ * iperm(x) = x ^ (x & 4 ? 3 : 0) for x < 32:
+ *   codes     int8  [heads][16384]     the code of (key row r, value column c)
+ *                                      is byte 4096 (c % 4) + 1024 (r / 32)
+ *                                      + 16 (iperm(r % 32) + 32 ((c / 4) % 2))
+ *                                      + c / 8 of the head's block
  *   row_scale fp32  [heads][128]       rho_r
  *   col_scale fp32  [heads][128]       sigma_c
  *   comp_idx  int32 [heads][C]         -1 unused, 0..127 row r, 128+c column c
  *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
- *                                      over r for a column)
+ *                                      over r for a column), natural order
  *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
  *   rec_k     fp32  [heads][W][128]    record keys; key row r is stored at
- *                                      4*(r % 32) + r / 32
+ *                                      32 (r / 32) + iperm(r % 32)
  *   rec_u     fp32  [heads][W][128]    record corrections; value column c is
- *                                      stored at 16*(c % 8) + c / 8 (the
- *                                      interleave of a code row)
+ *                                      stored at 32 (c % 4) + 8 (c / 32)
+ *                                      + 4 ((c / 4) % 2) + (c / 8) % 4
+ * These orders are the thread map of the kernels (each thread's 64 codes are
+ * four 16-byte loads, each wave's loads 1 KB contiguous; the record keys and
+ * corrections are the operand orders of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
  * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 512 + 512). */
 typedef struct leapq_layout {

@@ -2,6 +2,8 @@
 
 Flags that matter for the numbers:
   -ffp-contract=off   no fused multiply-add except the explicit ones
+  -amdgpu-mfma-vgpr-form  matrix-instruction accumulators in ordinary VGPRs
+                      (no AGPR copies of the fold's state tile)
   packed-fp32-ops off the kernels are written for unpacked fp32 VALU
   (no fast-math, no denormal flush; '/' and sqrtf stay correctly rounded,
    which is hipcc's default for HIP)
@@ -23,6 +25,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",

@@ -18,12 +18,13 @@
 // (T = the canonical 128-term tree) and the record (gamma_t, k, u_t) is
 // stored at slot n.
 //
-// Memory: each thread loads its 64 codes as four 16-byte loads; every other
-// per-head operand (records, compensator lines, rho and sigma, k, q, v, the
-// compensator indices and the record decays) is copied straight into LDS by
-// a few LDS-direct loads per wave.  The residual read is reduced inside each
-// wave; barriers separate the copies, the per-head dot products and the
-// per-column tail.
+// Memory: each thread loads its 64 codes as four 16-byte loads (1 KB
+// contiguous per wave and load); every other per-head operand (records,
+// compensator lines, rho and sigma, k, q, v, the compensator indices and the
+// record decays) is copied straight into LDS by a few LDS-direct loads per
+// wave.  The residual read is reduced inside each wave (thread map of
+// leapq_device.h); barriers separate the copies, the per-head dot products
+// and the per-column tail.
 #include "leapq_device.h"
 
 namespace leapq {
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     float *cdot = coef + 128;                                    // [2][8]
     float *kqd = cdot + 16;                                      // [1]
 
-    const AMap a = amap();
+    const MMap a = mmap();
     const int l = a.l, w = a.w;
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     // ---- loads: codes to registers, every other operand to LDS
     uint4 qc[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + a.row(p) * D + 16 * a.j);
+    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
     for (int rr = w; rr < n; rr += 4)
         lds_copy16(l < 32 ? hs.rk + rr * D + 4 * l : hs.ru + rr * D + 4 * (l - 32), rec + rr * 256);
     for (int pair = 2 * w; pair < C; pair += 8)
@@ -111,10 +112,10 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // ---- operands from LDS
-    const int vec = l >> 5;
-    const int mfin = (((l >> 4) & 1) << 3) | (((l >> 3) & 1) << 2) | (((l >> 1) & 1) << 1) | (l & 1);
-    const int c = a.j + 8 * mfin;
+    // ---- operands from LDS; after the residual read lane l holds vector
+    // vec = bit 4 of l (0: k, 1: q) of column w + 4h + 8 (l & 15)
+    const int vec = (l >> 4) & 1;
+    const int c = a.col(l & 15);
     float rh[4], kr[4], qr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -130,11 +131,11 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     const float ci_l = l < n ? gt / sgam[l] : 0.0f;  // c_i of record i = lane, for the dot jobs
 
     // ---- residual read of column m for k and q: rows (i, i+64) and
-    // (i+32, i+96) by fused level 0, then level 1; the first exchange (tree
-    // level h = 16 on lane bit 5: k stays in lanes < 32, q in lanes >= 32)
-    // follows at once so only 16 partials stay live.  Then levels h = 8, 4,
-    // 2, 1 on lane bits 4, 3, 1, 0.  Lane l ends with vector l>>5 of column
-    // j + 8 * mfin.
+    // (i+32, i+96) by fused level 0, then level 32; the next exchange (tree
+    // level 16 on lane bit 4: k stays in lanes with bit 4 clear, q in the
+    // others) follows at once so only 16 partials stay live.  Then levels 8,
+    // 4, 2, 1 on lane bits 3, 2 (lane ^ 7 is row ^ 4), 1, 0, each keeping half
+    // of the columns.
     float red;
     {
         float wk[4], wq[4];
@@ -153,14 +154,14 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
             for (int p = 0; p < 4; ++p) f[p] = code_f(cw[p][m >> 2], m & 3);
             const float sk = fma_(wk[0], f[0], wk[2] * f[2]) + fma_(wk[1], f[1], wk[3] * f[3]);
             const float sq = fma_(wq[0], f[0], wq[2] * f[2]) + fma_(wq[1], f[1], wq[3] * f[3]);
-            a16[m] = xhalf32(sk, sq);
+            a16[m] = xhalf16(sk, sq);
         }
         float a8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a8[e] = xhalf16(a16[e], a16[e + 8]);
+        for (int e = 0; e < 8; ++e) a8[e] = xhalf_dpp<DPP_ROR8>(a16[e], a16[e + 8], (l >> 3) & 1);
         float a4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a4[e] = xhalf_dpp<DPP_ROR8>(a8[e], a8[e + 4], (l >> 3) & 1);
+        for (int e = 0; e < 4; ++e) a4[e] = xhalf_dpp<DPP_HMIR>(a8[e], a8[e + 4], (l >> 2) & 1);
         float a2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) a2[e] = xhalf_dpp<DPP_XOR2>(a4[e], a4[e + 2], (l >> 1) & 1);
@@ -212,9 +213,9 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     float acc = gt * b;
     const int uc = upos(c);
     for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * 256 + 128 + uc], acc);
-    // k lanes form u; q lanes receive it from lane l-32 and finish o
+    // k lanes form u; q lanes receive it from lane l-16 and finish o
     const float u = b_h * (v_c - acc);
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
     const float u_from_k = __uint_as_float(sw[0]);
     if (vec == 0) {
         hs.ru[n * D + uc] = u;

@@ -11,16 +11,24 @@
 // commutative, so any lane order that pairs the same partials gives the same
 // bits.
 //
-// Thread map of a 256-thread workgroup that owns one head: wave w (0..3),
-// lane l (0..63),
-//     i  = (l & 3) | (l >> 3) << 2      key rows  i + 32p,  p = 0..3
-//     hb = (l >> 2) & 1,  j = w + 4 hb  value columns j + 8m, m = 0..15
-// A column sum over the 128 rows therefore runs: levels 0 and 1 inside the
-// thread (rows i, i+64 and i+32, i+96), then levels h = 16, 8, 4, 2, 1 on
-// lane bits 5, 4, 3, 1, 0: a v_permlane32_swap, a v_permlane16_swap and three
-// exact-xor DPP moves, all inside one wave.  A row sum over the 128 columns
-// runs: levels 0..3 inside the thread (columns j+8m), level 4 on lane bit 2
-// (DPP), levels 5 and 6 across waves w^2, w^1 through LDS.
+// Thread map of the quantized-state kernels (init, append, fold, dequant):
+// a 256-thread workgroup owns one head; wave w (0..3), lane l (0..63),
+//     h = l >> 5,  jp = l & 31,  i = jp ^ (jp & 4 ? 3 : 0)
+//     key rows      i + 32 p,         p = 0..3
+//     value columns w + 4 h + 8 m,    m = 0..15
+// This is the accumulator layout of v_mfma_f32_32x32x1_2b_f32 with the key
+// on the B operand (B lane 32b + jp carries row i + 32 (2q + b) of matrix
+// instruction q) and the value on the A operand (A lane a carries column
+// w + 4 ((a >> 2) & 1) + 8 ((a & 3) | (a >> 3 & 3) << 2)), so the fold's
+// rank-one record updates run on the matrix cores, one K = 1 step each, which
+// rounds exactly like an fma.
+// A column sum over the 128 rows runs levels 0 and h = 32 inside the thread
+// (rows i, i+64 and i+32, i+96), then h = 16, 8, 4, 2, 1 on lane bits 4, 3,
+// 2, 1, 0: a v_permlane16_swap, row_ror:8, row_half_mirror (lane ^ 7, which
+// is row ^ 4 because of the xor in i), quad_perm ^2 and ^1.  A row sum over
+// the 128 columns runs levels 0, 32, 16, 8 inside the thread (columns
+// w + 4h + 8m), level 4 on lane bit 5 (v_permlane32_swap) and levels 2, 1
+// across waves w ^ 2, w ^ 1 through LDS.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,12 +43,36 @@ constexpr int D = 128;
 constexpr int NT = 256;
 
 __device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+// value select (kept as a function so selects between array elements stay
+// selects of values, not of addresses)
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
 // ---------------------------------------------------------------- thread map
+struct MMap {
+    int w, l, h, jp, i;
+    __device__ __forceinline__ int row(int p) const { return i + 32 * p; }
+    __device__ __forceinline__ int col(int m) const { return w + 4 * h + 8 * m; }
+};
+
+__host__ __device__ __forceinline__ int iperm(int x) { return x ^ ((x & 4) ? 3 : 0); }
+
+__device__ __forceinline__ MMap mmap()
+{
+    MMap a;
+    a.l = threadIdx.x & 63;
+    a.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    a.h = a.l >> 5;
+    a.jp = a.l & 31;
+    a.i = iperm(a.jp);
+    return a;
+}
+
+// Thread map of the dense baselines (leapq_dense.hip): rows i + 32p and
+// contiguous columns 16 j + m, with i = (l & 3) | (l >> 3) << 2 and
+// j = w + 4 ((l >> 2) & 1); column sums run on lane bits 5, 4, 3, 1, 0.
 struct AMap {
     int w, l, i, hb, j;
     __device__ __forceinline__ int row(int p) const { return i + 32 * p; }
-    __device__ __forceinline__ int col(int m) const { return j + 8 * m; }
 };
 
 __device__ __forceinline__ AMap amap()
@@ -55,12 +87,19 @@ __device__ __forceinline__ AMap amap()
 }
 
 // ---------------------------------------------------------------- layouts
-// Record keys are stored with key row r at 4*(r % 32) + r / 32 (a thread's 4
-// rows are one float4); record corrections with value column c at
-// 16*(c % 8) + c / 8 (a thread's 16 columns are four float4s), the same
-// interleave as the codes of a row.
-__device__ __forceinline__ int kpos(int r) { return 4 * (r & 31) + (r >> 5); }
-__device__ __forceinline__ int upos(int c) { return 16 * (c & 7) + (c >> 3); }
+// Codes of a head (16384 bytes): the 16 codes of thread (w, l), row p, are
+// the bytes code_off(w, l, p) + m, m = 0..15 (column w + 4h + 8m), so each
+// 16-byte load of a wave reads 1 KB contiguous.
+__host__ __device__ __forceinline__ int code_off(int w, int l, int p) { return w * 4096 + p * 1024 + l * 16; }
+// Record keys: row r at kpos(r), the B operand order of the matrix
+// instruction (lane L of instruction q reads kpos = 64 q + L).
+__host__ __device__ __forceinline__ int kpos(int r) { return 32 * (r >> 5) + iperm(r & 31); }
+// Record corrections: column c at upos(c), the A operand order (lane a of
+// wave w reads 32 w + (a & 31)).
+__host__ __device__ __forceinline__ int upos(int c)
+{
+    return 32 * (c & 3) + 8 * (c >> 5) + 4 * ((c >> 2) & 1) + ((c >> 3) & 3);
+}
 
 struct HeadState {
     int8_t *codes;
@@ -207,8 +246,8 @@ __device__ __forceinline__ int wave_min(int x)
     return min(x, dppi<DPP_XOR1>(x));
 }
 
-// Column sum over the 128 rows, from the 16 level-1 partials v[m] (column
-// j+8m) of each thread.  Returns the sum of the lane's column
+// AMap column sum over the 128 rows, from the 16 level-1 partials v[m]
+// (column j+8m) of each thread.  Returns the sum of the lane's column
 // j + 8 * colm(l), colm(l) = (l>>5&1)<<3 | (l>>4&1)<<2 | (l>>3&1)<<1 | (l>>1&1);
 // lanes l and l^1 hold the same column.
 __device__ __forceinline__ int colm_of(int l)
@@ -228,6 +267,36 @@ __device__ __forceinline__ float colsum16(const float (&v)[16], int l)
     for (int e = 0; e < 2; ++e) a2[e] = xhalf_dpp<DPP_ROR8>(a4[e], a4[e + 2], (l >> 3) & 1);
     const float a1 = xhalf_dpp<DPP_XOR2>(a2[0], a2[1], (l >> 1) & 1);
     return a1 + dpp<DPP_XOR1>(a1);
+}
+
+// MMap column sum over the 128 rows, from the 16 level-32 partials v[m]
+// (column w + 4h + 8m, rows i, i+32, i+64, i+96 already combined) of each
+// thread: exchange-and-add on lane bits 4 (permlane16 swap), 3 (row_ror:8),
+// 2 (row_half_mirror: lane ^ 7, row ^ 4) and 1 (quad ^2), then a butterfly
+// on bit 0.  Returns the sum of column w + 4h + 8 mcol(l), mcol(l) =
+// (l >> 1) & 15; lanes l and l ^ 1 hold the same column.
+__device__ __forceinline__ int mcol_of(int l) { return (l >> 1) & 15; }
+__device__ __forceinline__ float mcolsum16(const float (&v)[16], int l)
+{
+    float a8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a8[e] = xhalf16(v[e], v[e + 8]);
+    float a4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a4[e] = xhalf_dpp<DPP_ROR8>(a8[e], a8[e + 4], (l >> 3) & 1);
+    float a2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) a2[e] = xhalf_dpp<DPP_HMIR>(a4[e], a4[e + 2], (l >> 2) & 1);
+    const float a1 = xhalf_dpp<DPP_XOR2>(a2[0], a2[1], (l >> 1) & 1);
+    return a1 + dpp<DPP_XOR1>(a1);
+}
+
+// Exchange-and-max on lane bit 5: the lower lane keeps max(K, partner K),
+// the upper lane max(G, partner G).
+__device__ __forceinline__ float xhalf32max(float K, float G)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(K), __float_as_uint(G), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Row partial over a thread's 16 columns of one row (levels 0..3 of the

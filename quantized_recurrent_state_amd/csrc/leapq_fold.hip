@@ -21,14 +21,27 @@
 //             code = rint(x * (127 / M_r)) (rows with M_r < 2^-120: zeros)
 // The clamp to +-127 of the plain statement is a no-op here: |x| <= M_r
 // gives |x * RN(127 / M_r)| <= 127 (1 + 2^-23) < 127.5.
+//
+// The records are applied on the matrix cores: with the thread map of
+// leapq_device.h a record is two v_mfma_f32_32x32x1_2b_f32 per wave (A = the
+// correction over the wave's 32 columns, B = c_i k_i over 64 rows each), and
+// a K = 1 matrix step rounds exactly like fma(c_i k_i[r], u_i[c], S), so the
+// chain over the records is the same sequence of fused multiply-adds.
 #include "leapq_device.h"
 
 namespace leapq {
 namespace {
 using namespace dev;
 
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+// The thread's 64 entries S[p][m] = (row i + 32p, column w + 4h + 8m); in
+// the matrix instructions' accumulators they are register 16 (p & 1) + m of
+// accumulator p >> 1 (instruction q = p >> 1, block b = p & 1).
+#define TS(T, p, m) ((T)[p][m])
+
 struct FoldLds {
-    float rec[16 * 256];  // a chunk of up to 16 records: keys | corrections (stored layouts)
+    float rec[16 * 256];  // a chunk of up to 16 records: keys | corrections (stored orders)
     float lines[8 * 128];
     float rho[128];
     float sig[128];
@@ -43,7 +56,7 @@ struct FoldLds {
 };
 
 // Copies boundary fields (lines, rho, sigma, indices) and n decays to LDS.
-__device__ __forceinline__ void stage_small(const AMap &a, const HeadState &hs, int C, int n, FoldLds &sm)
+__device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, int C, int n, FoldLds &sm)
 {
     const int l = a.l, w = a.w;
     for (int pair = 2 * w; pair < C; pair += 8)
@@ -57,7 +70,7 @@ __device__ __forceinline__ void stage_small(const AMap &a, const HeadState &hs, 
     }
 }
 
-__device__ __forceinline__ void stage_records(const AMap &a, const HeadState &hs, int base, int cnt, FoldLds &sm)
+__device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, FoldLds &sm)
 {
     const int l = a.l;
     for (int rr = a.w; rr < cnt; rr += 4) {
@@ -66,11 +79,16 @@ __device__ __forceinline__ void stage_records(const AMap &a, const HeadState &hs
     }
 }
 
-// Current state in registers: S[p][m] = entry (row i+32p, column j+8m).
-// qc: the thread's 4 code chunks.  Expects stage_small() done and visible
-// and, if n > 0, records 0..min(n,16)-1 staged and visible.  Contains
-// barriers when n > 16.
-__device__ __forceinline__ void rebuild(const AMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
+__device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, uint4 (&qc)[4])
+{
+#pragma unroll
+    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(a.w, a.l, p));
+}
+
+// Current state in the tile.  qc: the thread's 4 code chunks.  Expects
+// stage_small() done and visible and, if n > 0, records 0..min(n,16)-1
+// staged and visible.  Contains barriers when n > 16.
+__device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
                                         bool lines, FoldLds &sm, float (&S)[4][16])
 {
     const float gn = n > 0 ? sm.gam[n - 1] : 1.0f;
@@ -82,37 +100,46 @@ __device__ __forceinline__ void rebuild(const AMap &a, const HeadState &hs, cons
         const float ap = gn * sm.rho[a.row(p)];
         const uint32_t cw[4] = {qc[p].x, qc[p].y, qc[p].z, qc[p].w};
 #pragma unroll
-        for (int m = 0; m < 16; ++m) S[p][m] = (code_f(cw[m >> 2], m & 3) * ap) * sg[m];
+        for (int m = 0; m < 16; ++m) TS(S, p, m) = (code_f(cw[m >> 2], m & 3) * ap) * sg[m];
     }
-    if (lines) {
+    if (lines && C > 0) {
+        // line of each of the thread's rows / columns (-1: none).  An entry
+        // on a row line and a column line is +0 in the line extracted second
+        // (it was zeroed by the first), so adding only one of the two gives
+        // the same bits as adding both in order.
+        int rl[4] = {-1, -1, -1, -1}, cl[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) cl[m] = -1;
         for (int jj = 0; jj < C; ++jj) {
             const int id = sm.idx[jj];
-            const float *v = sm.lines + jj * D;
-            if (id < 0) continue;
-            if (id < D) {
-                const int pp = id >> 5;
-                if (a.i == (id & 31)) {
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        if (p == pp) {
+            for (int p = 0; p < 4; ++p) rl[p] = (id == a.row(p)) ? jj : rl[p];
 #pragma unroll
-                            for (int m = 0; m < 16; ++m) S[p][m] = S[p][m] + gn * v[a.col(m)];
-                        }
-                }
-            } else {
-                const int c = id - D, mm = c >> 3;
-                if (a.j == (c & 7)) {
-#pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        if (m == mm) {
-#pragma unroll
-                            for (int p = 0; p < 4; ++p) S[p][m] = S[p][m] + gn * v[a.row(p)];
-                        }
-                }
-            }
+            for (int m = 0; m < 16; ++m) cl[m] = (id == D + a.col(m)) ? jj : cl[m];
         }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            if (rl[p] >= 0) {
+                const float *v = sm.lines + rl[p] * D;
+#pragma unroll
+                for (int m = 0; m < 16; ++m) TS(S, p, m) = TS(S, p, m) + gn * v[a.col(m)];
+            }
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            if (cl[m] >= 0) {
+                const float *v = sm.lines + cl[m] * D;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) TS(S, p, m) = TS(S, p, m) + gn * v[a.row(p)];
+            }
     }
+    // through the accumulators even when n == 0: one definition of S after
+    // this point keeps it in one set of registers
     const float ci_l = a.l < n ? gn / sm.gam[a.l] : 0.0f;  // c_i for record i = lane
+    f32x32 acc[2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[p >> 1][16 * (p & 1) + m] = S[p][m];
     for (int base = 0; base < n; base += 16) {
         const int cnt = n - base < 16 ? n - base : 16;
         if (base > 0) {
@@ -123,23 +150,18 @@ __device__ __forceinline__ void rebuild(const AMap &a, const HeadState &hs, cons
         }
         for (int r = 0; r < cnt; ++r) {
             const float ci = rdl(ci_l, base + r);
-            const float4 kk = *reinterpret_cast<const float4 *>(sm.rec + r * 256 + 4 * a.i);
-            const float wv[4] = {ci * kk.x, ci * kk.y, ci * kk.z, ci * kk.w};
-            float u[16];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const float4 uu = *reinterpret_cast<const float4 *>(sm.rec + r * 256 + 128 + 16 * a.j + 4 * d);
-                u[4 * d] = uu.x;
-                u[4 * d + 1] = uu.y;
-                u[4 * d + 2] = uu.z;
-                u[4 * d + 3] = uu.w;
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int m = 0; m < 16; ++m) S[p][m] = fma_(wv[p], u[m], S[p][m]);
+            const float *rr = sm.rec + r * 256;
+            const float b0 = ci * rr[a.l];       // key row of B lane l, instruction 0
+            const float b1 = ci * rr[64 + a.l];  // instruction 1
+            const float au = rr[128 + 32 * a.w + a.jp];
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
         }
     }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int m = 0; m < 16; ++m) S[p][m] = acc[p >> 1][16 * (p & 1) + m];
 }
 
 // ---------------------------------------------------------------- energies
@@ -147,26 +169,39 @@ __device__ __forceinline__ void col_partials(const float (&S)[4][16], float (&cp
 {
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-        cp[m] = fma_(S[0][m], S[0][m], S[2][m] * S[2][m]) + fma_(S[1][m], S[1][m], S[3][m] * S[3][m]);
+        cp[m] = fma_(TS(S, 0, m), TS(S, 0, m), TS(S, 2, m) * TS(S, 2, m)) +
+                fma_(TS(S, 1, m), TS(S, 1, m), TS(S, 3, m) * TS(S, 3, m));
+}
+
+__device__ __forceinline__ float row_partial(const float (&S)[4][16], int p)
+{
+    float x[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) x[m] = TS(S, p, m);
+    return row_energy16(x);
 }
 
 // Publishes the 128 column energies from the cached column partials.
-__device__ __forceinline__ void publish_cols(const AMap &a, const float (&cp)[16], FoldLds &sm)
+__device__ __forceinline__ void publish_cols(const MMap &a, const float (&cp)[16], FoldLds &sm)
 {
-    const float e = colsum16(cp, a.l);
-    if ((a.l & 1) == 0) sm.score[D + a.j + 8 * colm_of(a.l)] = e;
+    const float e = mcolsum16(cp, a.l);
+    if ((a.l & 1) == 0) sm.score[D + a.col(mcol_of(a.l))] = e;
+}
+
+// Writes a per-row value pair to the cross-wave buffer: the lower lane half
+// holds rows i, i+32, the upper rows i+64, i+96.
+__device__ __forceinline__ void put_rows(const MMap &a, float r0, float r1, FoldLds &sm)
+{
+    sm.part[a.w * D + a.i + 64 * a.h] = r0;
+    sm.part[a.w * D + a.i + 64 * a.h + 32] = r1;
 }
 
 // Publishes the 128 row energies from the cached row partials (levels 0..3);
-// level 4 across lane bit 2, levels 5 and 6 across waves.  Ends with a
+// level 4 across lane bit 5, levels 2 and 1 across waves.  Ends with a
 // barrier after which score[0..127] is written (by threads < 128).
-__device__ __forceinline__ void publish_rows(const AMap &a, const float (&rp)[4], FoldLds &sm)
+__device__ __forceinline__ void publish_rows(const MMap &a, const float (&rp)[4], FoldLds &sm)
 {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float s = rp[p] + xor4(rp[p]);
-        if (a.hb == 0) sm.part[a.w * D + a.row(p)] = s;
-    }
+    put_rows(a, xhalf32(rp[0], rp[2]), xhalf32(rp[1], rp[3]), sm);
     __syncthreads();
     const int t = threadIdx.x;
     if (t < D) sm.score[t] = (sm.part[t] + sm.part[2 * D + t]) + (sm.part[D + t] + sm.part[3 * D + t]);
@@ -174,7 +209,7 @@ __device__ __forceinline__ void publish_rows(const AMap &a, const float (&rp)[4]
 
 // Block argmax of score[0..255]: largest score, lowest candidate on ties;
 // -1 when no score is positive.  Starts and ends with barriers.
-__device__ __forceinline__ int pick_line(const AMap &a, FoldLds &sm)
+__device__ __forceinline__ int pick_line(const MMap &a, FoldLds &sm)
 {
     __syncthreads();
     const int t = threadIdx.x;
@@ -190,10 +225,22 @@ __device__ __forceinline__ int pick_line(const AMap &a, FoldLds &sm)
     return min(min(sm.redi[0], sm.redi[1]), min(sm.redi[2], sm.redi[3]));
 }
 
+// Low byte of rint(y) for |y| < 2^22: adding 1.5 * 2^23 rounds y to an
+// integer (to nearest even) in the low mantissa bits.
+__device__ __forceinline__ uint32_t rint_bits(float y) { return __float_as_uint(y + 12582912.0f); }
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 // Steps after the rebuild, shared by init and fold.  Writes the head's new
-// boundary state (codes, rho, sigma, indices, lines).
-__device__ void quantize_state(const AMap &a, float (&S)[4][16], const HeadState &hs, int C, int smoothing,
-                               float floor_, FoldLds &sm)
+// boundary state (codes, rho, sigma, indices, lines).  CT >= 0: the number of
+// compensators as a compile-time constant (C == CT), unrolling the rounds.
+template <int CT>
+__device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16], const HeadState &hs, int C, int smoothing,
+                                               float floor_, FoldLds &sm)
 {
     const int t = threadIdx.x, l = a.l;
     // ---- compensator tokens
@@ -201,54 +248,75 @@ __device__ void quantize_state(const AMap &a, float (&S)[4][16], const HeadState
         float cp[16], rp[4];
         col_partials(S, cp);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) rp[p] = row_energy16(S[p]);
+        for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
         publish_cols(a, cp, sm);
         publish_rows(a, rp, sm);
-        for (int jj = 0; jj < C; ++jj) {
+        // one greedy round per compensator: pick, store and zero the line,
+        // rescore the other axis (skipped after the last round).  The rounds
+        // are unrolled (C <= 8); the body is written out here, not called, so
+        // S stays in registers.
+        constexpr int NR = CT >= 0 ? CT : 8;
+        const int nrounds = CT >= 0 ? CT : C;
+#pragma unroll
+        for (int jj = 0; jj < NR; ++jj) {
+            if (jj >= nrounds) break;
             const int pick = pick_line(a, sm);
             float *vec = hs.cvec + jj * D;
             if (t == 0) hs.cidx[jj] = pick;
-            if (pick < 0) {
-                if (t < D) vec[t] = 0.0f;
-                continue;
-            }
-            if (pick < D) {
-                const int pp = pick >> 5;
-                const bool own = a.i == (pick & 31);
+            // a row pick is owned by the two lanes per wave with i == pick % 32
+            // (row p = pick / 32); a column pick by lane half h of wave w
+            // (m = c / 8).  One straight pass over S per round: S keeps its
+            // registers across the loop.
+            const bool isrow = pick >= 0 && pick < D, iscol = pick >= D;
+            const int pr = pick >> 5, cc = pick - D, mm = cc >> 3;
+            const bool own_r = isrow && a.i == (pick & 31);
+            const bool own_c = iscol && a.w == (cc & 3) && a.h == ((cc >> 2) & 1);
+            if (pick < 0 && t < D) vec[t] = 0.0f;
+            if (own_r) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    if (p == pp && own) {
+                    if (p == pr) {
 #pragma unroll
-                        for (int m = 0; m < 16; ++m) {
-                            vec[a.col(m)] = S[p][m];
-                            S[p][m] = 0.0f;
-                        }
-                        rp[p] = 0.0f;
+                        for (int m = 0; m < 16; ++m) vec[a.col(m)] = TS(S, p, m);
                     }
-                if (jj + 1 < C) {
-                    if (own) col_partials(S, cp);
-                    if (t == 0) sm.score[pick] = 0.0f;
-                    publish_cols(a, cp, sm);
+            }
+            if (own_c) {
+                // S[p][mm] by a select tree on the bits of mm (value selects;
+                // a branch per m would turn into a runtime index into S)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    float x8[8], x4[4], x2[2];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x8[e] = sel((mm & 8) != 0, TS(S, p, e + 8), TS(S, p, e));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x4[e] = sel((mm & 4) != 0, x8[e + 4], x8[e]);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) x2[e] = sel((mm & 2) != 0, x4[e + 2], x4[e]);
+                    vec[a.row(p)] = sel((mm & 1) != 0, x2[1], x2[0]);
                 }
-            } else {
-                const int cc = pick - D, mm = cc >> 3;
-                const bool own = a.j == (cc & 7);
+            }
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (m == mm && own) {
+            for (int p = 0; p < 4; ++p) {
+                const bool zr = own_r && p == pr;
 #pragma unroll
-                        for (int p = 0; p < 4; ++p) {
-                            vec[a.row(p)] = S[p][m];
-                            S[p][m] = 0.0f;
-                        }
-                        cp[m] = 0.0f;
+                for (int m = 0; m < 16; ++m) {
+                    const bool zc = own_c && m == mm;
+                    TS(S, p, m) = (zr || zc) ? 0.0f : TS(S, p, m);
+                }
+                rp[p] = zr ? 0.0f : rp[p];
+            }
+#pragma unroll
+            for (int m = 0; m < 16; ++m) cp[m] = (own_c && m == mm) ? 0.0f : cp[m];
+            if (jj + 1 < nrounds && pick >= 0) {
+                if (t == 0) sm.score[pick] = 0.0f;
+                if (isrow) {
+                    col_partials(S, cp);
+                    publish_cols(a, cp, sm);
+                } else {
+                    if (a.w == (cc & 3)) {
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
                     }
-                if (jj + 1 < C) {
-                    if (own) {
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) rp[p] = row_energy16(S[p]);
-                    }
-                    if (t == 0) sm.score[pick] = 0.0f;
                     publish_rows(a, rp, sm);
                 }
             }
@@ -259,10 +327,10 @@ __device__ void quantize_state(const AMap &a, float (&S)[4][16], const HeadState
         float v[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            v[m] = (fabsf(S[0][m]) + fabsf(S[2][m])) + (fabsf(S[1][m]) + fabsf(S[3][m]));
-        const float msum = colsum16(v, l);
+            v[m] = (fabsf(TS(S, 0, m)) + fabsf(TS(S, 2, m))) + (fabsf(TS(S, 1, m)) + fabsf(TS(S, 3, m)));
+        const float msum = mcolsum16(v, l);
         if ((l & 1) == 0) {
-            const int c = a.j + 8 * colm_of(l);
+            const int c = a.col(mcol_of(l));
             float s = 1.0f;
             if (smoothing) {
                 s = sqrtf(msum * 0.0078125f);
@@ -274,19 +342,22 @@ __device__ void quantize_state(const AMap &a, float (&S)[4][16], const HeadState
     }
     __syncthreads();
     // ---- per-row symmetric int8, round half to even
-    float inv[16];
+    {
+        float inv[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) inv[m] = sm.sinv[a.col(m)];
+        for (int m = 0; m < 16; ++m) inv[m] = sm.sinv[a.col(m)];
+        float mx[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        float Mx = 0.0f;
+        for (int p = 0; p < 4; ++p) {
+            float Mx = 0.0f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            S[p][m] = S[p][m] * inv[m];
-            Mx = fmaxf(Mx, fabsf(S[p][m]));
+            for (int m = 0; m < 16; ++m) {
+                TS(S, p, m) = TS(S, p, m) * inv[m];
+                Mx = fmaxf(Mx, fabsf(TS(S, p, m)));
+            }
+            mx[p] = Mx;
         }
-        Mx = fmaxf(Mx, xor4(Mx));
-        if (a.hb == 0) sm.part[a.w * D + a.row(p)] = Mx;
+        put_rows(a, xhalf32max(mx[0], mx[2]), xhalf32max(mx[1], mx[3]), sm);
     }
     __syncthreads();
     if (t < D) {
@@ -299,21 +370,21 @@ __device__ void quantize_state(const AMap &a, float (&S)[4][16], const HeadState
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const float g = sm.rowg[a.row(p)];
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        uint32_t b[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const float y = rintf(S[p][m] * g);
-            w4[m >> 2] |= ((uint32_t)(int32_t)y & 0xffu) << (8 * (m & 3));
-        }
-        *reinterpret_cast<uint4 *>(hs.codes + a.row(p) * D + 16 * a.j) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        for (int m = 0; m < 16; ++m) b[m] = rint_bits(TS(S, p, m) * g);
+        *reinterpret_cast<uint4 *>(hs.codes + code_off(a.w, a.l, p)) =
+            make_uint4(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]),
+                       pack4(b[8], b[9], b[10], b[11]), pack4(b[12], b[13], b[14], b[15]));
     }
 }
 
+template <int CT>
 __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restrict__ S0, int smoothing,
                                               float floor_)
 {
     __shared__ FoldLds sm;
-    const AMap a = amap();
+    const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     const float *src = S0 + (size_t)h * D * D;
@@ -321,19 +392,19 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int m = 0; m < 16; ++m) S[p][m] = src[a.row(p) * D + a.col(m)];
-    quantize_state(a, S, hs, sv.C, smoothing, floor_, sm);
+        for (int m = 0; m < 16; ++m) TS(S, p, m) = src[a.row(p) * D + a.col(m)];
+    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, sm);
 }
 
+template <int CT>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
     __shared__ FoldLds sm;
-    const AMap a = amap();
+    const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     uint4 qc[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + a.row(p) * D + 16 * a.j);
+    load_codes(a, hs, qc);
     stage_small(a, hs, sv.C, n, sm);
     stage_records(a, hs, 0, n < 16 ? n : 16, sm);
     __builtin_amdgcn_s_waitcnt(0);
@@ -341,19 +412,18 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     float S[4][16];
     rebuild(a, hs, qc, sv.C, n, true, sm, S);
     __syncthreads();  // every thread has read the old boundary from LDS
-    quantize_state(a, S, hs, sv.C, smoothing, floor_, sm);
+    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, sm);
 }
 
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
     __shared__ FoldLds sm;
-    const AMap a = amap();
+    const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     const int nr = what == 2 ? n : 0;
     uint4 qc[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + a.row(p) * D + 16 * a.j);
+    load_codes(a, hs, qc);
     stage_small(a, hs, sv.C, nr, sm);
     stage_records(a, hs, 0, nr < 16 ? nr : 16, sm);
     __builtin_amdgcn_s_waitcnt(0);
@@ -364,7 +434,7 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int m = 0; m < 16; ++m) dst[a.row(p) * D + a.col(m)] = S[p][m];
+        for (int m = 0; m < 16; ++m) dst[a.row(p) * D + a.col(m)] = TS(S, p, m);
 }
 
 }  // namespace
@@ -372,13 +442,19 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
 hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
                        hipStream_t s)
 {
-    hipLaunchKernelGGL(k_init, dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    if (sv.C == 4)
+        hipLaunchKernelGGL(k_init<4>, dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    else
+        hipLaunchKernelGGL(k_init<-1>, dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
     return hipGetLastError();
 }
 
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_fold, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+    if (sv.C == 4)
+        hipLaunchKernelGGL(k_fold<4>, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+    else
+        hipLaunchKernelGGL(k_fold<-1>, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     return hipGetLastError();
 }
 

@@ -126,6 +126,27 @@ def _dev_tensor(t, name, dtype, shape, device):
                          f"{t.dtype} {tuple(t.shape)} on {t.device} (contiguous={t.is_contiguous()})")
 
 
+# ---- stored orders of the state sections (include/leapq.h); r, c are
+# integer tensors (or ints) of key rows / value columns.
+def _iperm(x):
+    return x ^ (((x >> 2) & 1) * 3)
+
+
+def code_offset(r, c):
+    """Byte of code (r, c) within its head's 16384-byte block."""
+    return (c & 3) * 4096 + (r >> 5) * 1024 + (_iperm(r & 31) + 32 * ((c >> 2) & 1)) * 16 + (c >> 3)
+
+
+def key_pos(r):
+    """Position of key row r within a stored record key."""
+    return 32 * (r >> 5) + _iperm(r & 31)
+
+
+def corr_pos(c):
+    """Position of value column c within a stored record correction."""
+    return 32 * (c & 3) + 8 * (c >> 5) + 4 * ((c >> 2) & 1) + ((c >> 3) & 3)
+
+
 class Layer:
     """One layer: config + its state buffer (torch uint8 tensor) + window count."""
 
@@ -164,15 +185,15 @@ class Layer:
         return self.state[off:off + nbytes].view(dtype).view(*shape)
 
     def codes_physical(self):
+        """int8 [heads, 16384]: each head's codes in stored order."""
         H = self.heads
-        return self._sec(self.layout.off_codes, H * D * D, torch.int8, (H, D, D))
+        return self._sec(self.layout.off_codes, H * D * D, torch.int8, (H, D * D))
 
     def codes(self):
-        """int8 [heads, 128(row), 128(column)] in logical column order."""
-        phys = self.codes_physical()
-        col = torch.arange(D, device=self.device)
-        pos = (col % 8) * 16 + col // 8  # byte position of column c in a row
-        return phys[:, :, pos]
+        """int8 [heads, 128(row), 128(column)] in logical order."""
+        r = torch.arange(D, device=self.device).view(D, 1)
+        c = torch.arange(D, device=self.device).view(1, D)
+        return self.codes_physical()[:, code_offset(r, c)]
 
     def rho(self):
         return self._sec(self.layout.off_row_scale, self.heads * D, torch.float32, (self.heads, D))
@@ -203,12 +224,12 @@ class Layer:
     def rec_k(self):
         """Record keys [heads, W, 128] in logical key-row order."""
         r = torch.arange(D, device=self.device)
-        return self.rec_k_physical()[:, :, 4 * (r % 32) + r // 32]
+        return self.rec_k_physical()[:, :, key_pos(r)]
 
     def rec_u(self):
         """Record corrections [heads, W, 128] in logical value-column order."""
         c = torch.arange(D, device=self.device)
-        return self.rec_u_physical()[:, :, 16 * (c % 8) + c // 8]
+        return self.rec_u_physical()[:, :, corr_pos(c)]
 
 
 def leapq_init_state(layer, S0, stream=None):
