@@ -47,71 +47,91 @@ struct InLds<uint16_t> {
     }
 };
 
-// LDS in floats: records [n][256] (keys | corrections, stored layouts),
-// lines [C][128], rho [128], sigma [128], inputs, indices [8], decays [64],
-// coefficients [2][64], column-token dots [2][8], k.q [1] (+3 pad)
-__host__ __device__ constexpr int append_lds_floats(int n, int C, int in_floats)
+// LDS of one head in floats: records [n][256] (keys | corrections, stored
+// orders), lines [C][128], rho [128], sigma [128], inputs (k, q, v),
+// indices [8], decays [64]
+__host__ __device__ constexpr int head_lds_floats(int n, int C, int in_floats)
 {
-    return n * 256 + C * 128 + 256 + in_floats + 8 + 64 + 128 + 16 + 4;
+    return n * 256 + C * 128 + 256 + in_floats + 8 + 64;
 }
+// per-workgroup results of the dot jobs: coefficients [2][64], column-token
+// dots [2][8], k.q [1] (+3 pad)
+constexpr int kDotFloats = 128 + 16 + 4;
 
 template <typename T>
-__global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__restrict__ qin,
-                                                const T *__restrict__ kin, const T *__restrict__ vin,
-                                                const float *__restrict__ alpha, const float *__restrict__ beta,
-                                                float *__restrict__ o)
+struct HeadLds {
+    float *rec, *cv, *srho, *ssig, *sin_, *sgam;
+    int *sidx;
+    __device__ HeadLds(float *base, int n, int C)
+    {
+        rec = base;
+        cv = rec + n * 256;
+        srho = cv + C * D;
+        ssig = srho + D;
+        sin_ = ssig + D;
+        sidx = reinterpret_cast<int *>(sin_ + InLds<T>::floats);
+        sgam = reinterpret_cast<float *>(sidx + 8);
+    }
+};
+
+// Barrier between LDS phases of one workgroup: this wave's LDS writes are
+// complete, then s_barrier (no wait on vector memory: the record and output
+// stores of the tail are not held back by it).
+__device__ __forceinline__ void lds_barrier()
 {
-    extern __shared__ float dsm[];
-    const int C = sv.C;
-    float *rec = dsm;                                            // [n][256]
-    float *cv = rec + n * 256;                                   // [C][128]
-    float *srho = cv + C * D;                                    // [128]
-    float *ssig = srho + D;                                      // [128]
-    float *sin_ = ssig + D;                                      // k, q, v
-    int *sidx = reinterpret_cast<int *>(sin_ + InLds<T>::floats);  // [8]
-    float *sgam = reinterpret_cast<float *>(sidx + 8);           // [64]
-    float *coef = sgam + 64;                                     // [2][64]
-    float *cdot = coef + 128;                                    // [2][8]
-    float *kqd = cdot + 16;                                      // [1]
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited
+    __builtin_amdgcn_s_barrier();
+}
 
-    const MMap a = mmap();
-    const int l = a.l, w = a.w;
-    const int h = blockIdx.x;
+// Issues every global load of head h: its 64 codes per thread into qc, every
+// other operand into the LDS buffer L by LDS-direct copies.
+template <typename T>
+__device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
+                                             const T *__restrict__ kin, const T *__restrict__ vin,
+                                             const MMap &a, const HeadLds<T> &L, uint4 (&qc)[4])
+{
+    const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
-
-    // ---- loads: codes to registers, every other operand to LDS
-    uint4 qc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
     for (int rr = w; rr < n; rr += 4)
-        lds_copy16(l < 32 ? hs.rk + rr * D + 4 * l : hs.ru + rr * D + 4 * (l - 32), rec + rr * 256);
+        lds_copy16(l < 32 ? hs.rk + rr * D + 4 * l : hs.ru + rr * D + 4 * (l - 32), L.rec + rr * 256);
     for (int pair = 2 * w; pair < C; pair += 8)
-        if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), cv + pair * D);
+        if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
     if (w == 0) {
-        lds_copy16(l < 32 ? hs.rho + 4 * l : hs.sigma + 4 * (l - 32), srho);
+        lds_copy16(l < 32 ? hs.rho + 4 * l : hs.sigma + 4 * (l - 32), L.srho);
     } else if (w == 1) {
         // inputs as 16-byte pieces of k, q, v in that order
         constexpr int per = (int)(128 * sizeof(T) / 16);
         if (l < 3 * per) {
             const int vecno = l / per, piece = l % per;
             const T *src = (vecno == 0 ? kin : vecno == 1 ? qin : vin) + (size_t)h * D;
-            lds_copy16(reinterpret_cast<const char *>(src) + 16 * piece, sin_);
+            lds_copy16(reinterpret_cast<const char *>(src) + 16 * piece, L.sin_);
         }
         if (3 * per > 64 && l < 3 * per - 64) {
             const int f = 64 + l, vecno = f / per, piece = f % per;
             const T *src = (vecno == 0 ? kin : vecno == 1 ? qin : vin) + (size_t)h * D;
-            lds_copy16(reinterpret_cast<const char *>(src) + 16 * piece, sin_ + 256);
+            lds_copy16(reinterpret_cast<const char *>(src) + 16 * piece, L.sin_ + 256);
         }
     } else if (w == 2) {
-        if (l < C) lds_copy4(hs.cidx + l, sidx);
+        if (l < C) lds_copy4(hs.cidx + l, L.sidx);
     } else {
-        if (l < n) lds_copy4(hs.rgam + l, sgam);
+        if (l < n) lds_copy4(hs.rgam + l, L.sgam);
     }
-    const float a_h = alpha[h];
-    const float b_h = beta[h];
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+}
 
+// The token for head h from its staged operands (L, qc); writes o and the
+// record.  Contains one lds_barrier (dot jobs -> tail).
+template <typename T>
+__device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a, const HeadLds<T> &L,
+                                               float *dots, const uint4 (&qc)[4], float a_h, float b_h,
+                                               float *__restrict__ o)
+{
+    const int C = sv.C, l = a.l, w = a.w;
+    const HeadState hs = head_state(sv, h);
+    const float *rec = L.rec, *cv = L.cv, *srho = L.srho, *ssig = L.ssig, *sin_ = L.sin_, *sgam = L.sgam;
+    const int *sidx = L.sidx;
+    float *coef = dots, *cdot = dots + 128, *kqd = dots + 144;
     // ---- operands from LDS; after the residual read lane l holds vector
     // vec = bit 4 of l (0: k, 1: q) of column w + 4h + 8 (l & 15)
     const int vec = (l >> 4) & 1;
@@ -198,7 +218,7 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- per-column tail: lane (vec, c)
     float b = sig_c * red;
@@ -229,22 +249,44 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     }
 }
 
+template <typename T>
+__global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__restrict__ qin,
+                                                const T *__restrict__ kin, const T *__restrict__ vin,
+                                                const float *__restrict__ alpha, const float *__restrict__ beta,
+                                                float *__restrict__ o)
+{
+    extern __shared__ float dsm[];
+    const MMap a = mmap();
+    const int h = blockIdx.x;
+    const HeadLds<T> L(dsm, n, sv.C);
+    float *dots = dsm + head_lds_floats(n, sv.C, InLds<T>::floats);
+    uint4 qc[4];
+    append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
+    const float a_h = alpha[h];
+    const float b_h = beta[h];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    append_compute<T>(sv, n, h, a, L, dots, qc, a_h, b_h, o);
+}
+
 }  // namespace
+
+template <typename T>
+static void launch_append_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
+                            const float *alpha, const float *beta, float *o, hipStream_t s)
+{
+    const size_t lds = sizeof(float) * (head_lds_floats(n, sv.C, InLds<T>::floats) + kDotFloats);
+    hipLaunchKernelGGL(k_append<T>, dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
+                       (const T *)v, alpha, beta, o);
+}
 
 hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
                          const void *v, const float *alpha, const float *beta, float *o, hipStream_t s)
 {
-    if (bf16) {
-        using T = uint16_t;
-        const size_t lds = sizeof(float) * append_lds_floats(n, sv.C, InLds<T>::floats);
-        hipLaunchKernelGGL(k_append<T>, dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
-                           (const T *)v, alpha, beta, o);
-    } else {
-        using T = float;
-        const size_t lds = sizeof(float) * append_lds_floats(n, sv.C, InLds<T>::floats);
-        hipLaunchKernelGGL(k_append<T>, dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
-                           (const T *)v, alpha, beta, o);
-    }
+    if (bf16)
+        launch_append_t<uint16_t>(sv, heads, n, q, k, v, alpha, beta, o, s);
+    else
+        launch_append_t<float>(sv, heads, n, q, k, v, alpha, beta, o, s);
     return hipGetLastError();
 }
 

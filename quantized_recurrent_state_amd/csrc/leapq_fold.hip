@@ -111,11 +111,15 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
 #pragma unroll
         for (int m = 0; m < 16; ++m) cl[m] = -1;
         for (int jj = 0; jj < C; ++jj) {
-            const int id = sm.idx[jj];
+            const int id = __builtin_amdgcn_readfirstlane(sm.idx[jj]);
+            const bool isrow = id >= 0 && id < D, iscol = id >= D;
+            const int c = id - D;
+            const bool own_r = isrow && a.i == (id & 31);
+            const bool own_c = iscol && a.w == (c & 3) && a.h == ((c >> 2) & 1);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) rl[p] = (id == a.row(p)) ? jj : rl[p];
+            for (int p = 0; p < 4; ++p) rl[p] = (own_r && (id >> 5) == p) ? jj : rl[p];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) cl[m] = (id == D + a.col(m)) ? jj : cl[m];
+            for (int m = 0; m < 16; ++m) cl[m] = (own_c && (c >> 3) == m) ? jj : cl[m];
         }
 #pragma unroll
         for (int p = 0; p < 4; ++p)
@@ -148,11 +152,25 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        for (int r = 0; r < cnt; ++r) {
+        // records r of the chunk in order; four per iteration, then the rest
+        int r = 0;
+        for (; r + 4 <= cnt; r += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float ci = rdl(ci_l, base + r + u);
+                const float *rr = sm.rec + (r + u) * 256;
+                const float b0 = ci * rr[a.l];       // key row of B lane l, instruction 0
+                const float b1 = ci * rr[64 + a.l];  // instruction 1
+                const float au = rr[128 + 32 * a.w + a.jp];
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
+            }
+        }
+        for (; r < cnt; ++r) {
             const float ci = rdl(ci_l, base + r);
             const float *rr = sm.rec + r * 256;
-            const float b0 = ci * rr[a.l];       // key row of B lane l, instruction 0
-            const float b1 = ci * rr[64 + a.l];  // instruction 1
+            const float b0 = ci * rr[a.l];
+            const float b1 = ci * rr[64 + a.l];
             const float au = rr[128 + 32 * a.w + a.jp];
             acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
@@ -208,21 +226,26 @@ __device__ __forceinline__ void publish_rows(const MMap &a, const float (&rp)[4]
 }
 
 // Block argmax of score[0..255]: largest score, lowest candidate on ties;
-// -1 when no score is positive.  Starts and ends with barriers.
+// -1 when no score is positive.  Each wave reduces its 64 candidates to
+// (max, lowest index at the max); starts and ends with a barrier.
 __device__ __forceinline__ int pick_line(const MMap &a, FoldLds &sm)
 {
     __syncthreads();
     const int t = threadIdx.x;
     const float s = sm.score[t];
     const float mw = wave_max(s);
-    if (a.l == 0) sm.redf[a.w] = mw;
+    const int iw = wave_min(s == mw ? t : 1 << 20);
+    if (a.l == 0) {
+        sm.redf[a.w] = mw;
+        sm.redi[a.w] = iw;
+    }
     __syncthreads();
     const float M = fmaxf(fmaxf(sm.redf[0], sm.redf[1]), fmaxf(sm.redf[2], sm.redf[3]));
     if (!(M > 0.0f)) return -1;  // uniform
-    const int cw = wave_min(s == M ? t : 1 << 20);
-    if (a.l == 0) sm.redi[a.w] = cw;
-    __syncthreads();
-    return min(min(sm.redi[0], sm.redi[1]), min(sm.redi[2], sm.redi[3]));
+    int pick = 1 << 20;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pick = sm.redf[k] == M ? min(pick, sm.redi[k]) : pick;
+    return pick;
 }
 
 // Low byte of rint(y) for |y| < 2^22: adding 1.5 * 2^23 rounds y to an
