@@ -74,15 +74,6 @@ struct HeadLds {
     }
 };
 
-// Barrier between LDS phases of one workgroup: this wave's LDS writes are
-// complete, then s_barrier (no wait on vector memory: the record and output
-// stores of the tail are not held back by it).
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited
-    __builtin_amdgcn_s_barrier();
-}
-
 // Issues every global load of head h: its 64 codes per thread into qc, every
 // other operand into the LDS buffer L by LDS-direct copies.
 template <typename T>

@@ -313,6 +313,15 @@ __device__ __forceinline__ float row_energy16(const float (&x)[16])
     return t[0] + t[1];
 }
 
+// Barrier between LDS phases of one workgroup: this wave's LDS writes are
+// complete, then s_barrier.  Unlike __syncthreads() it does not wait for the
+// wave's outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited
+    __builtin_amdgcn_s_barrier();
+}
+
 // ---------------------------------------------------------------- LDS-direct copies
 __device__ __forceinline__ void lds_copy16(const void *g, float *lds)
 {

@@ -47,12 +47,11 @@ struct FoldLds {
     float sig[128];
     int idx[8];
     float gam[64];
-    float part[4 * 128];  // cross-wave row partials / row maxima
-    float score[256];     // row energies, then column energies
-    float rowg[128];      // 127 / M_r per row (0 for zero rows)
-    float sinv[128];      // 1 / sigma_c
-    float redf[4];
-    int redi[4];
+    float colE[2][128];      // column energies (two buffers, see extraction)
+    float rowP[2][4 * 128];  // per-wave row-energy partials (two buffers)
+    float part[4 * 128];     // cross-wave row maxima
+    float rowg[128];         // 127 / M_r per row (0 for zero rows)
+    float sinv[128];         // 1 / sigma_c
 };
 
 // Copies boundary fields (lines, rho, sigma, indices) and n decays to LDS.
@@ -199,53 +198,56 @@ __device__ __forceinline__ float row_partial(const float (&S)[4][16], int p)
     return row_energy16(x);
 }
 
-// Publishes the 128 column energies from the cached column partials.
-__device__ __forceinline__ void publish_cols(const MMap &a, const float (&cp)[16], FoldLds &sm)
+// Column energies from the cached column partials (tree levels 16..1 across
+// lanes); lane pairs (l, l ^ 1) hold one column, the even lane writes it.
+__device__ __forceinline__ void put_cols(const MMap &a, const float (&cp)[16], float *colE)
 {
     const float e = mcolsum16(cp, a.l);
-    if ((a.l & 1) == 0) sm.score[D + a.col(mcol_of(a.l))] = e;
+    if ((a.l & 1) == 0) colE[a.col(mcol_of(a.l))] = e;
 }
 
-// Writes a per-row value pair to the cross-wave buffer: the lower lane half
-// holds rows i, i+32, the upper rows i+64, i+96.
-__device__ __forceinline__ void put_rows(const MMap &a, float r0, float r1, FoldLds &sm)
+// Writes a per-row value pair to a per-wave row buffer [4][128]: the lower
+// lane half holds rows i, i+32, the upper rows i+64, i+96.
+__device__ __forceinline__ void put_rows(const MMap &a, float r0, float r1, float *buf)
 {
-    sm.part[a.w * D + a.i + 64 * a.h] = r0;
-    sm.part[a.w * D + a.i + 64 * a.h + 32] = r1;
+    buf[a.w * D + a.i + 64 * a.h] = r0;
+    buf[a.w * D + a.i + 64 * a.h + 32] = r1;
 }
 
-// Publishes the 128 row energies from the cached row partials (levels 0..3);
-// level 4 across lane bit 5, levels 2 and 1 across waves.  Ends with a
-// barrier after which score[0..127] is written (by threads < 128).
-__device__ __forceinline__ void publish_rows(const MMap &a, const float (&rp)[4], FoldLds &sm)
+// This wave's row-energy partials: levels 0..3 cached in rp, level 4 across
+// lane bit 5.  Levels 2 and 1 (across waves) are taken by the reader.
+__device__ __forceinline__ void put_row_energies(const MMap &a, const float (&rp)[4], float *rowP)
 {
-    put_rows(a, xhalf32(rp[0], rp[2]), xhalf32(rp[1], rp[3]), sm);
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t < D) sm.score[t] = (sm.part[t] + sm.part[2 * D + t]) + (sm.part[D + t] + sm.part[3 * D + t]);
+    put_rows(a, xhalf32(rp[0], rp[2]), xhalf32(rp[1], rp[3]), rowP);
 }
 
-// Block argmax of score[0..255]: largest score, lowest candidate on ties;
-// -1 when no score is positive.  Each wave reduces its 64 candidates to
-// (max, lowest index at the max); starts and ends with a barrier.
-__device__ __forceinline__ int pick_line(const MMap &a, FoldLds &sm)
+// Greedy pick over the 256 candidates (rows 0..127, then columns 128..255):
+// largest energy, lowest candidate on ties, the candidates in pk[0..npk)
+// (earlier picks) excluded; -1 when no energy is positive.  Every wave
+// computes it from LDS; the row energy is the canonical sum of the four
+// waves' partials (w, w ^ 2 first, then the two pairs).
+template <int NP>
+__device__ __forceinline__ int pick_all(const MMap &a, const float *colE, const float *rowP, const int (&pk)[NP],
+                                        int npk)
 {
-    __syncthreads();
-    const int t = threadIdx.x;
-    const float s = sm.score[t];
-    const float mw = wave_max(s);
-    const int iw = wave_min(s == mw ? t : 1 << 20);
-    if (a.l == 0) {
-        sm.redf[a.w] = mw;
-        sm.redi[a.w] = iw;
-    }
-    __syncthreads();
-    const float M = fmaxf(fmaxf(sm.redf[0], sm.redf[1]), fmaxf(sm.redf[2], sm.redf[3]));
-    if (!(M > 0.0f)) return -1;  // uniform
-    int pick = 1 << 20;
+    const int l = a.l;
+    float e[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pick = sm.redf[k] == M ? min(pick, sm.redi[k]) : pick;
-    return pick;
+    for (int k = 0; k < 2; ++k) {
+        const int r = l + 64 * k;
+        e[k] = (rowP[r] + rowP[2 * D + r]) + (rowP[D + r] + rowP[3 * D + r]);
+        e[2 + k] = colE[r];
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+        if (j < npk) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) e[k] = (pk[j] == 64 * k + l) ? -1.0f : e[k];
+        }
+    const float M = wave_max(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])));
+    if (!(M > 0.0f)) return -1;
+    const int cand = e[0] == M ? l : e[1] == M ? 64 + l : e[2] == M ? 128 + l : e[3] == M ? 192 + l : 1 << 20;
+    return __builtin_amdgcn_readfirstlane(wave_min(cand));
 }
 
 // Low byte of rint(y) for |y| < 2^22: adding 1.5 * 2^23 rounds y to an
@@ -266,30 +268,35 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
                                                float floor_, FoldLds &sm)
 {
     const int t = threadIdx.x, l = a.l;
-    // ---- compensator tokens
+    // ---- compensator tokens: one greedy round per compensator (pick, store
+    // and zero the line, rescore the other axis).  Every wave takes the same
+    // pick from the energies in LDS, so a round needs one barrier: the
+    // rescored axis is written to the other of its two buffers, which no
+    // wave reads until that barrier.  The rounds are unrolled (C <= 8) and
+    // written out here, not called, so S stays in registers.
     if (C > 0) {
+        constexpr int NR = CT >= 0 ? CT : 8;
+        const int nrounds = CT >= 0 ? CT : C;
         float cp[16], rp[4];
+        int pk[NR];
+        int cb = 0, rb = 0;
         col_partials(S, cp);
 #pragma unroll
         for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
-        publish_cols(a, cp, sm);
-        publish_rows(a, rp, sm);
-        // one greedy round per compensator: pick, store and zero the line,
-        // rescore the other axis (skipped after the last round).  The rounds
-        // are unrolled (C <= 8); the body is written out here, not called, so
-        // S stays in registers.
-        constexpr int NR = CT >= 0 ? CT : 8;
-        const int nrounds = CT >= 0 ? CT : C;
+        put_cols(a, cp, sm.colE[0]);
+        put_row_energies(a, rp, sm.rowP[0]);
+        lds_barrier();
 #pragma unroll
         for (int jj = 0; jj < NR; ++jj) {
             if (jj >= nrounds) break;
-            const int pick = pick_line(a, sm);
+            const int pick = pick_all(a, sm.colE[cb], sm.rowP[rb], pk, jj);
+            pk[jj] = pick;
             float *vec = hs.cvec + jj * D;
             if (t == 0) hs.cidx[jj] = pick;
             // a row pick is owned by the two lanes per wave with i == pick % 32
             // (row p = pick / 32); a column pick by lane half h of wave w
             // (m = c / 8).  One straight pass over S per round: S keeps its
-            // registers across the loop.
+            // registers across the rounds.
             const bool isrow = pick >= 0 && pick < D, iscol = pick >= D;
             const int pr = pick >> 5, cc = pick - D, mm = cc >> 3;
             const bool own_r = isrow && a.i == (pick & 31);
@@ -331,17 +338,19 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
 #pragma unroll
             for (int m = 0; m < 16; ++m) cp[m] = (own_c && m == mm) ? 0.0f : cp[m];
             if (jj + 1 < nrounds && pick >= 0) {
-                if (t == 0) sm.score[pick] = 0.0f;
                 if (isrow) {
                     col_partials(S, cp);
-                    publish_cols(a, cp, sm);
+                    put_cols(a, cp, sm.colE[cb ^ 1]);
+                    cb ^= 1;
                 } else {
                     if (a.w == (cc & 3)) {
 #pragma unroll
                         for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
                     }
-                    publish_rows(a, rp, sm);
+                    put_row_energies(a, rp, sm.rowP[rb ^ 1]);
+                    rb ^= 1;
                 }
+                lds_barrier();
             }
         }
     }
@@ -380,7 +389,7 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
             }
             mx[p] = Mx;
         }
-        put_rows(a, xhalf32max(mx[0], mx[2]), xhalf32max(mx[1], mx[3]), sm);
+        put_rows(a, xhalf32max(mx[0], mx[2]), xhalf32max(mx[1], mx[3]), sm.part);
     }
     __syncthreads();
     if (t < D) {
