@@ -40,22 +40,26 @@ typedef float f32x32 __attribute__((ext_vector_type(32)));
 // accumulator p >> 1 (instruction q = p >> 1, block b = p & 1).
 #define TS(T, p, m) ((T)[p][m])
 
-struct FoldLds {
+// Operands of one head staged from HBM, and the work arrays of the steps
+// after the rebuild.
+struct FoldStage {
     float rec[16 * 256];  // a chunk of up to 16 records: keys | corrections (stored orders)
     float lines[8 * 128];
     float rho[128];
     float sig[128];
     int idx[8];
     float gam[64];
+};
+struct FoldWork {
     float colE[2][128];      // column energies (two buffers, see extraction)
     float rowP[2][4 * 128];  // per-wave row-energy partials (two buffers)
     float part[4 * 128];     // cross-wave row maxima
-    float rowg[128];         // 127 / M_r per row (0 for zero rows)
+    float rowg[4][128];      // per wave: 127 / M_r per row (0 for zero rows)
     float sinv[128];         // 1 / sigma_c
 };
 
 // Copies boundary fields (lines, rho, sigma, indices) and n decays to LDS.
-__device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, int C, int n, FoldLds &sm)
+__device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, int C, int n, FoldStage &sm)
 {
     const int l = a.l, w = a.w;
     for (int pair = 2 * w; pair < C; pair += 8)
@@ -69,7 +73,7 @@ __device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, 
     }
 }
 
-__device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, FoldLds &sm)
+__device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, FoldStage &sm)
 {
     const int l = a.l;
     for (int rr = a.w; rr < cnt; rr += 4) {
@@ -88,7 +92,7 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 // stage_small() done and visible and, if n > 0, records 0..min(n,16)-1
 // staged and visible.  Contains barriers when n > 16.
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
-                                        bool lines, FoldLds &sm, float (&S)[4][16])
+                                        bool lines, FoldStage &sm, float (&S)[4][16])
 {
     const float gn = n > 0 ? sm.gam[n - 1] : 1.0f;
     float sg[16];
@@ -265,7 +269,7 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 // compensators as a compile-time constant (C == CT), unrolling the rounds.
 template <int CT>
 __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16], const HeadState &hs, int C, int smoothing,
-                                               float floor_, FoldLds &sm)
+                                               float floor_, FoldWork &sm)
 {
     const int t = threadIdx.x, l = a.l;
     // ---- compensator tokens: one greedy round per compensator (pick, store
@@ -277,13 +281,16 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
     if (C > 0) {
         constexpr int NR = CT >= 0 ? CT : 8;
         const int nrounds = CT >= 0 ? CT : C;
-        float cp[16], rp[4];
+        float rp[4];
         int pk[NR];
         int cb = 0, rb = 0;
-        col_partials(S, cp);
+        {
+            float cp[16];
+            col_partials(S, cp);
+            put_cols(a, cp, sm.colE[0]);
+        }
 #pragma unroll
         for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
-        put_cols(a, cp, sm.colE[0]);
         put_row_energies(a, rp, sm.rowP[0]);
         lds_barrier();
 #pragma unroll
@@ -335,10 +342,10 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
                 }
                 rp[p] = zr ? 0.0f : rp[p];
             }
-#pragma unroll
-            for (int m = 0; m < 16; ++m) cp[m] = (own_c && m == mm) ? 0.0f : cp[m];
             if (jj + 1 < nrounds && pick >= 0) {
                 if (isrow) {
+                    // column energies from S (picked lines already zeroed)
+                    float cp[16];
                     col_partials(S, cp);
                     put_cols(a, cp, sm.colE[cb ^ 1]);
                     cb ^= 1;
@@ -372,7 +379,9 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
             sm.sinv[c] = 1.0f / s;
         }
     }
-    __syncthreads();
+    // the wave reads back only its own columns: LDS order within the wave
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
     // ---- per-row symmetric int8, round half to even
     {
         float inv[16];
@@ -391,17 +400,25 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
         }
         put_rows(a, xhalf32max(mx[0], mx[2]), xhalf32max(mx[1], mx[3]), sm.part);
     }
-    __syncthreads();
-    if (t < D) {
-        const float M = fmaxf(fmaxf(sm.part[t], sm.part[D + t]), fmaxf(sm.part[2 * D + t], sm.part[3 * D + t]));
-        const bool live = M >= 0x1p-120f;
-        hs.rho[t] = live ? M / 127.0f : 0.0f;
-        sm.rowg[t] = live ? 127.0f / M : 0.0f;
+    lds_barrier();
+    // every wave forms 127 / M_r for all rows (lane l: rows l, l + 64) in its
+    // own buffer; wave 0 also stores rho
+    {
+        float *rg = sm.rowg[a.w];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = l + 64 * k;
+            const float M = fmaxf(fmaxf(sm.part[r], sm.part[D + r]), fmaxf(sm.part[2 * D + r], sm.part[3 * D + r]));
+            const bool live = M >= 0x1p-120f;
+            if (a.w == 0) hs.rho[r] = live ? M / 127.0f : 0.0f;
+            rg[r] = live ? 127.0f / M : 0.0f;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const float g = sm.rowg[a.row(p)];
+        const float g = sm.rowg[a.w][a.row(p)];
         uint32_t b[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) b[m] = rint_bits(TS(S, p, m) * g);
@@ -415,7 +432,7 @@ template <int CT>
 __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restrict__ S0, int smoothing,
                                               float floor_)
 {
-    __shared__ FoldLds sm;
+    __shared__ FoldWork wk;
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
@@ -425,43 +442,45 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int m = 0; m < 16; ++m) TS(S, p, m) = src[a.row(p) * D + a.col(m)];
-    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, sm);
+    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
 template <int CT>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
-    __shared__ FoldLds sm;
+    __shared__ FoldStage st;
+    __shared__ FoldWork wk;
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     uint4 qc[4];
     load_codes(a, hs, qc);
-    stage_small(a, hs, sv.C, n, sm);
-    stage_records(a, hs, 0, n < 16 ? n : 16, sm);
+    stage_small(a, hs, sv.C, n, st);
+    stage_records(a, hs, 0, n < 16 ? n : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild(a, hs, qc, sv.C, n, true, sm, S);
-    __syncthreads();  // every thread has read the old boundary from LDS
-    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, sm);
+    rebuild(a, hs, qc, sv.C, n, true, st, S);
+    // no barrier: the quantization writes only LDS arrays the rebuild does
+    // not read, and each thread rewrites only the codes it loaded
+    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
-    __shared__ FoldLds sm;
+    __shared__ FoldStage st;
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     const int nr = what == 2 ? n : 0;
     uint4 qc[4];
     load_codes(a, hs, qc);
-    stage_small(a, hs, sv.C, nr, sm);
-    stage_records(a, hs, 0, nr < 16 ? nr : 16, sm);
+    stage_small(a, hs, sv.C, nr, st);
+    stage_records(a, hs, 0, nr < 16 ? nr : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild(a, hs, qc, sv.C, nr, what >= 1, sm, S);
+    rebuild(a, hs, qc, sv.C, nr, what >= 1, st, S);
     float *dst = out + (size_t)h * D * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
