@@ -8,7 +8,8 @@
 // with S[r][c] indexed (key row, value column).  A bf16 state is widened,
 // updated in fp32 and rounded to nearest even on store.  The reads are
 // canonical-tree dot products over the rows; the update is one fma per
-// entry.
+// entry.  A bf16 state is stored with the hardware round-to-nearest-even
+// conversion.
 //
 // Thread map: rows i + 32p as in leapq_device.h, but the 16 columns of a
 // thread are contiguous (16 j + m) to match the natural state layout.
@@ -55,6 +56,17 @@ __device__ __forceinline__ void store_row16<float>(float *p, const float (&x)[16
     for (int d = 0; d < 4; ++d)
         reinterpret_cast<float4 *>(p)[d] = make_float4(x[4 * d], x[4 * d + 1], x[4 * d + 2], x[4 * d + 3]);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even as packed bf16 (one
+// v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 template <>
 __device__ __forceinline__ void store_row16<uint16_t>(uint16_t *p, const float (&x)[16])
 {
@@ -62,9 +74,7 @@ __device__ __forceinline__ void store_row16<uint16_t>(uint16_t *p, const float (
     for (int d = 0; d < 2; ++d) {
         uint32_t w4[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            w4[b] = (uint32_t)f32_to_bf16_rne(x[8 * d + 2 * b]) |
-                    ((uint32_t)f32_to_bf16_rne(x[8 * d + 2 * b + 1]) << 16);
+        for (int b = 0; b < 4; ++b) w4[b] = pack_bf16x2(x[8 * d + 2 * b], x[8 * d + 2 * b + 1]);
         reinterpret_cast<uint4 *>(p)[d] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
 }
