@@ -1,7 +1,8 @@
 """Decode benchmark of the LeapQuant append + fold path on one MI355X.
 
 One step = one window of the whole hot path: for each of the window's 16
-tokens, the append of all 24 layers; after the 16th token each layer's fold.
+tokens, the append of all 24 layers; each layer's 16th token and its fold run
+as one leapq_append_fold call (--separate: append, then fold).
 Workload (default "b512"): 24 GDN layers x 32 heads x 128x128 state, batch
 512, W=16, C=4, bf16 q/k/v, fp32 records; seeded synthetic inputs (a pool of
 16 tokens per layer, cycled every window), resident in HBM before timing.
@@ -9,7 +10,7 @@ Workload (default "b512"): 24 GDN layers x 32 heads x 128x128 state, batch
 Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps 64] [--warmup 2] [--workload b512]
-                  [--no-baselines] [--no-cpu]
+                  [--no-baselines] [--no-cpu] [--separate]
 """
 import argparse
 import hashlib
@@ -41,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--baseline-tokens", type=int, default=16)
     p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--separate", action="store_true",
+                   help="leapq_append then leapq_fold for each window's last token (no fused call)")
     return p.parse_args()
 
 
@@ -94,14 +97,21 @@ def main():
     log(f"[bench] states and input pool resident: "
         f"{torch.cuda.memory_allocated(dev) / 2**30:.1f} GiB allocated")
 
-    def window(events=None):
+    def window(events=None, fused=True):
+        """One window: W tokens through every layer.  With fused, each layer's
+        last token and its fold are one leapq_append_fold call; otherwise
+        leapq_append, then leapq_fold after the W-th token."""
         for pos in range(W):
             for l in range(Lyr):
                 q, k, v, a, b = pool[l][pos]
+                kind = "append_fold" if fused and layers[l].n_records == W - 1 else "append"
                 if events is not None:
-                    events.append(("append", pos, torch.cuda.Event(enable_timing=True)))
+                    events.append((kind, pos, torch.cuda.Event(enable_timing=True)))
                     events[-1][2].record(stream)
-                lq.leapq_append(layers[l], q, k, v, a, b, outs[l], stream)
+                if kind == "append_fold":
+                    lq.leapq_append_fold(layers[l], q, k, v, a, b, outs[l], stream)
+                else:
+                    lq.leapq_append(layers[l], q, k, v, a, b, outs[l], stream)
                 if events is not None:
                     events.append(("end", pos, torch.cuda.Event(enable_timing=True)))
                     events[-1][2].record(stream)
@@ -114,8 +124,9 @@ def main():
                         events.append(("end", pos, torch.cuda.Event(enable_timing=True)))
                         events[-1][2].record(stream)
 
+    fused = not args.separate
     for _ in range(args.warmup):
-        window()
+        window(fused=fused)
     torch.cuda.synchronize(dev)
     log(f"[bench] warmup {args.warmup} windows done")
 
@@ -126,7 +137,7 @@ def main():
     wall0 = time.perf_counter()
     t0.record(stream)
     for s in range(args.steps):
-        window()
+        window(fused=fused)
         if (s + 1) % 16 == 0:
             log(f"[bench] timed windows enqueued: {s + 1}/{args.steps}")
     t1.record(stream)
@@ -138,27 +149,41 @@ def main():
     log(f"[bench] {args.steps} windows: {total_ms:.1f} ms on the GPU clock ({wall:.2f} s wall); "
         f"{ms_per_step:.3f} ms per window, {tokens_per_s:,.0f} tokens/s")
 
-    # ---- per-launch durations (HIP events on the launch stream), 2 windows
+    # ---- per-launch durations (HIP events on the launch stream): 2 windows
+    # of separate appends and folds, then 2 windows timing the fused launch
     ev_app = {pos: [] for pos in range(W)}
-    ev_fold = []
-    for _ in range(2):
+    ev_fold, ev_fused = [], []
+    for mode in (False, False, True, True):
         events = []
-        window(events)
+        window(events, fused=mode)
         torch.cuda.synchronize(dev)
         for (kind, pos, e0), (_, _, e1) in zip(events[0::2], events[1::2]):
-            (ev_app[pos] if kind == "append" else ev_fold).append(e0.elapsed_time(e1))
+            dt = e0.elapsed_time(e1)
+            if kind == "append_fold":
+                ev_fused.append(dt)
+            elif kind == "fold":
+                ev_fold.append(dt)
+            elif not mode:
+                ev_app[pos].append(dt)
     app_us = {pos: 1e3 * float(np.mean(v)) for pos, v in ev_app.items()}
     append_us = float(np.mean(list(app_us.values())))
     fold_us = 1e3 * float(np.mean(ev_fold))
+    fused_us = 1e3 * float(np.mean(ev_fused)) if ev_fused else None
     app_bytes_avg = float(np.mean([metrics.append_bytes(n, C, in_bytes) for n in range(W)])) * H
     fold_bytes = metrics.fold_bytes(W, C) * H
     append_gbps = app_bytes_avg / (append_us * 1e-6) / 1e9
     fold_gbps = fold_bytes / (fold_us * 1e-6) / 1e9
-    share = metrics.fold_share(W * append_us, fold_us)
+    share_sep = metrics.fold_share(W * append_us, fold_us)
+    # fused schedule: the fold's cost is what the fused launch adds to the
+    # window's last append
+    share = share_sep
+    if fused and fused_us is not None:
+        share = (fused_us - app_us[W - 1]) / (sum(app_us[p] for p in range(W - 1)) + fused_us)
     window_bytes = metrics.window_bytes(W, C, in_bytes) * H * Lyr
     path_gbps = window_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] append {append_us:.1f} us ({append_gbps:.0f} GB/s algorithmic), fold {fold_us:.1f} us "
-        f"({fold_gbps:.0f} GB/s), fold share {100 * share:.1f}%, whole path {path_gbps:.0f} GB/s")
+        f"({fold_gbps:.0f} GB/s), last append + fold in one launch {fused_us:.1f} us; fold share "
+        f"{100 * share:.1f}% ({100 * share_sep:.1f}% with a separate fold), whole path {path_gbps:.0f} GB/s")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -221,11 +246,15 @@ def main():
         "config": {"workload": f"{wl.name}: {wl.notes}", "batch": B, "layers": Lyr, "heads": Hh,
                    "dk": D, "dv": D, "window": W, "n_comp": C, "in_dtype": wl.in_dtype,
                    "state": "int8 residual + fp32 compensators + fp32 records",
-                   "tokens_per_step": W},
+                   "tokens_per_step": W,
+                   "schedule": ("W-1 appends + leapq_append_fold per layer and window" if fused
+                                else "W appends + leapq_fold per layer and window")},
         "append_us": append_us,
         "append_us_by_position": [round(app_us[p], 2) for p in range(W)],
         "fold_us": fold_us,
+        "append_fold_us": fused_us,
         "fold_share": share,
+        "fold_share_separate_fold": share_sep,
         "hbm_gbps_path_algorithmic": path_gbps,
         "roofline": {"bound": "hbm", "kernel": "leapq append", "achieved": append_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": append_gbps / HBM_PEAK_GBPS,

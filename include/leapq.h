@@ -139,6 +139,19 @@ int32_t leapq_init_state(leapq_layer *layer, const float *S0, void *stream);
 int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const void *v,
                      const float *alpha, const float *beta, float *o, void *stream);
 
+/* The window's last token and its fold in one call: exactly leapq_append
+ * followed by leapq_fold ("Recurrent-state quantization for linear
+ * attention: a first GPU kernel", What we built: the append adds the
+ * token's record and computes its output; the fold then rebuilds, selects
+ * compensators, rescales, rounds and empties the buffer).  Requires
+ * n_records == window - 1 (else LEAPQ_ERR_RANGE); arguments as for
+ * leapq_append.  With window <= 16 this is one launch in which the
+ * boundary and the records are read once and the token's record never
+ * reaches HBM; otherwise the two steps are launched in turn.  Sets
+ * n_records := 0. */
+int32_t leapq_append_fold(leapq_layer *layer, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, float *o, void *stream);
+
 /* Closes the window ("Recurrent-state quantization for linear attention: a
  * first GPU kernel", What we built: rebuild, select compensators, rescale,
  * round, empty the buffer; "LeapQuant" B.3): rebuilds the current state from

@@ -139,6 +139,33 @@ int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const voi
     return st;
 }
 
+int32_t leapq_append_fold(leapq_layer *layer, const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, float *o, void *stream)
+{
+    leapq::StateView sv;
+    int32_t st = view_of(layer, &sv);
+    if (st != LEAPQ_OK) return st;
+    if (!q || !k || !v || !alpha || !beta || !o) return LEAPQ_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 4) ||
+        !aligned(beta, 4))
+        return LEAPQ_ERR_ALIGN;
+    if (layer->n_records != layer->cfg.window - 1) return LEAPQ_ERR_RANGE;
+    const int heads = heads_of(&layer->cfg);
+    const int bf16 = layer->cfg.in_dtype == LEAPQ_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    if (layer->cfg.window <= 16) {
+        st = hip_status(leapq::launch_append_fold(sv, heads, layer->n_records, bf16, q, k, v, alpha, beta, o,
+                                                  layer->cfg.smoothing, layer->cfg.sigma_floor, s));
+    } else {
+        st = hip_status(leapq::launch_append(sv, heads, layer->n_records, bf16, q, k, v, alpha, beta, o, s));
+        if (st == LEAPQ_OK)
+            st = hip_status(leapq::launch_fold(sv, heads, layer->n_records + 1, layer->cfg.smoothing,
+                                               layer->cfg.sigma_floor, s));
+    }
+    if (st == LEAPQ_OK) layer->n_records = 0;
+    return st;
+}
+
 int32_t leapq_fold(leapq_layer *layer, void *stream)
 {
     leapq::StateView sv;

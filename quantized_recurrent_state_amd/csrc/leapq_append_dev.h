@@ -1,0 +1,230 @@
+// Device code of the append (one decode token per head), shared by the
+// append kernel and the fused last-append-and-fold kernel.  See
+// leapq_append.hip for the method and its sources.
+#pragma once
+
+#include "leapq_device.h"
+
+namespace leapq {
+namespace {
+using namespace dev;
+
+template <typename T>
+struct InLds;
+template <>
+struct InLds<float> {
+    static constexpr int floats = 3 * 128;
+    __device__ static float get(const float *base, int vecno, int e) { return base[vecno * 128 + e]; }
+};
+template <>
+struct InLds<uint16_t> {
+    static constexpr int floats = 3 * 64;
+    __device__ static float get(const float *base, int vecno, int e)
+    {
+        return bf16_to_f32(reinterpret_cast<const uint16_t *>(base)[vecno * 128 + e]);
+    }
+};
+
+// LDS of one head in floats: records [n][256] (keys | corrections, stored
+// orders), lines [C][128], rho [128], sigma [128], inputs (k, q, v),
+// indices [8], decays [64]
+__host__ __device__ constexpr int head_lds_floats(int n, int C, int in_floats)
+{
+    return n * 256 + C * 128 + 256 + in_floats + 8 + 64;
+}
+// per-workgroup results of the dot jobs: coefficients [2][64], column-token
+// dots [2][8], k.q [1] (+3 pad)
+constexpr int kDotFloats = 128 + 16 + 4;
+
+template <typename T>
+struct HeadLds {
+    float *rec, *cv, *srho, *ssig, *sin_, *sgam;
+    int *sidx;
+    __device__ HeadLds(float *rec_, float *cv_, float *rho_sigma, float *in_, int *idx_, float *gam_)
+        : rec(rec_), cv(cv_), srho(rho_sigma), ssig(rho_sigma + D), sin_(in_), sgam(gam_), sidx(idx_)
+    {
+    }
+    __device__ HeadLds(float *base, int n, int C)
+    {
+        rec = base;
+        cv = rec + n * 256;
+        srho = cv + C * D;
+        ssig = srho + D;
+        sin_ = ssig + D;
+        sidx = reinterpret_cast<int *>(sin_ + InLds<T>::floats);
+        sgam = reinterpret_cast<float *>(sidx + 8);
+    }
+};
+
+// Issues every global load of head h: its 64 codes per thread into qc, every
+// other operand into the LDS buffer L by LDS-direct copies.
+template <typename T>
+__device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
+                                             const T *__restrict__ kin, const T *__restrict__ vin,
+                                             const MMap &a, const HeadLds<T> &L, uint4 (&qc)[4])
+{
+    const int C = sv.C, l = a.l, w = a.w;
+    const HeadState hs = head_state(sv, h);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
+    for (int rr = w; rr < n; rr += 4)
+        lds_copy16(l < 32 ? hs.rk + rr * D + 4 * l : hs.ru + rr * D + 4 * (l - 32), L.rec + rr * 256);
+    for (int pair = 2 * w; pair < C; pair += 8)
+        if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
+    if (w == 0) {
+        lds_copy16(l < 32 ? hs.rho + 4 * l : hs.sigma + 4 * (l - 32), L.srho);
+    } else if (w == 1) {
+        // inputs as 16-byte pieces of k, q, v in that order
+        constexpr int per = (int)(128 * sizeof(T) / 16);
+        if (l < 3 * per) {
+            const int vecno = l / per, piece = l % per;
+            const T *src = (vecno == 0 ? kin : vecno == 1 ? qin : vin) + (size_t)h * D;
+            lds_copy16(reinterpret_cast<const char *>(src) + 16 * piece, L.sin_);
+        }
+        if (3 * per > 64 && l < 3 * per - 64) {
+            const int f = 64 + l, vecno = f / per, piece = f % per;
+            const T *src = (vecno == 0 ? kin : vecno == 1 ? qin : vin) + (size_t)h * D;
+            lds_copy16(reinterpret_cast<const char *>(src) + 16 * piece, L.sin_ + 256);
+        }
+    } else if (w == 2) {
+        if (l < C) lds_copy4(hs.cidx + l, L.sidx);
+    } else {
+        if (l < n) lds_copy4(hs.rgam + l, L.sgam);
+    }
+}
+
+// The token for head h from its staged operands (L, qc); writes o and the
+// record.  Contains one lds_barrier (dot jobs -> tail).
+template <typename T, bool REC_LDS = false>
+__device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a, const HeadLds<T> &L,
+                                               float *dots, const uint4 (&qc)[4], float a_h, float b_h,
+                                               float *__restrict__ o)
+{
+    const int C = sv.C, l = a.l, w = a.w;
+    const HeadState hs = head_state(sv, h);
+    const float *rec = L.rec, *cv = L.cv, *srho = L.srho, *ssig = L.ssig, *sin_ = L.sin_, *sgam = L.sgam;
+    const int *sidx = L.sidx;
+    float *coef = dots, *cdot = dots + 128, *kqd = dots + 144;
+    // ---- operands from LDS; after the residual read lane l holds vector
+    // vec = bit 4 of l (0: k, 1: q) of column w + 4h + 8 (l & 15)
+    const int vec = (l >> 4) & 1;
+    const int c = a.col(l & 15);
+    float rh[4], kr[4], qr[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        rh[p] = srho[a.row(p)];
+        kr[p] = InLds<T>::get(sin_, 0, a.row(p));
+        qr[p] = InLds<T>::get(sin_, 1, a.row(p));
+    }
+    const float k0 = InLds<T>::get(sin_, 0, l), k1 = InLds<T>::get(sin_, 0, l + 64);
+    const float q0 = InLds<T>::get(sin_, 1, l), q1 = InLds<T>::get(sin_, 1, l + 64);
+    const float sig_c = ssig[c];
+    const float v_c = InLds<T>::get(sin_, 2, c);
+    const float gt = (n > 0 ? sgam[n - 1] : 1.0f) * a_h;
+    const float ci_l = l < n ? gt / sgam[l] : 0.0f;  // c_i of record i = lane, for the dot jobs
+
+    // ---- residual read of column m for k and q: rows (i, i+64) and
+    // (i+32, i+96) by fused level 0, then level 32; the next exchange (tree
+    // level 16 on lane bit 4: k stays in lanes with bit 4 clear, q in the
+    // others) follows at once so only 16 partials stay live.  Then levels 8,
+    // 4, 2, 1 on lane bits 3, 2 (lane ^ 7 is row ^ 4), 1, 0, each keeping half
+    // of the columns.
+    float red;
+    {
+        float wk[4], wq[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            wk[p] = kr[p] * rh[p];
+            wq[p] = qr[p] * rh[p];
+        }
+        const uint32_t cw[4][4] = {{qc[0].x, qc[0].y, qc[0].z, qc[0].w}, {qc[1].x, qc[1].y, qc[1].z, qc[1].w},
+                                   {qc[2].x, qc[2].y, qc[2].z, qc[2].w}, {qc[3].x, qc[3].y, qc[3].z, qc[3].w}};
+        float a16[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            float f[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) f[p] = code_f(cw[p][m >> 2], m & 3);
+            const float sk = fma_(wk[0], f[0], wk[2] * f[2]) + fma_(wk[1], f[1], wk[3] * f[3]);
+            const float sq = fma_(wq[0], f[0], wq[2] * f[2]) + fma_(wq[1], f[1], wq[3] * f[3]);
+            a16[m] = xhalf16(sk, sq);
+        }
+        float a8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = xhalf_dpp<DPP_ROR8>(a16[e], a16[e + 8], (l >> 3) & 1);
+        float a4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a4[e] = xhalf_dpp<DPP_HMIR>(a8[e], a8[e + 4], (l >> 2) & 1);
+        float a2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) a2[e] = xhalf_dpp<DPP_XOR2>(a4[e], a4[e + 2], (l >> 1) & 1);
+        red = xhalf_dpp<DPP_XOR1>(a2[0], a2[1], l & 1);
+    }
+
+    // ---- per-head dot products, one wave per job:
+    // job r < n: c_r * (k_r . k), c_r * (k_r . q); job n: (k . q);
+    // job n+1+jj: (line_jj . k), (line_jj . q) for column tokens
+    const int njobs = n + 1 + C;
+    for (int job = w; job < njobs; job += 4) {
+        if (job < n) {
+            const float a0 = rec[job * 256 + kpos(l)], a1 = rec[job * 256 + kpos(l + 64)];
+            const float dk = wdot(a0, a1, k0, k1);
+            const float dq = wdot(a0, a1, q0, q1);
+            const float ci = rdl(ci_l, job);
+            if (l == 0) {
+                coef[job] = ci * dk;
+                coef[64 + job] = ci * dq;
+            }
+        } else if (job == n) {
+            const float d = wdot(k0, k1, q0, q1);
+            if (l == 0) kqd[0] = d;
+        } else {
+            const int jj = job - n - 1;
+            if (sidx[jj] >= D) {
+                const float a0 = cv[jj * D + l], a1 = cv[jj * D + l + 64];
+                const float dk = wdot(a0, a1, k0, k1);
+                const float dq = wdot(a0, a1, q0, q1);
+                if (l == 0) {
+                    cdot[jj] = dk;
+                    cdot[8 + jj] = dq;
+                }
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- per-column tail: lane (vec, c)
+    float b = sig_c * red;
+    for (int jj = 0; jj < C; ++jj) {
+        const int id = sidx[jj];
+        if (id < 0) continue;
+        if (id < D)
+            b = fma_(InLds<T>::get(sin_, vec, id), cv[jj * D + c], b);
+        else if (id - D == c)
+            b = b + cdot[vec * 8 + jj];
+    }
+    float acc = gt * b;
+    const int uc = upos(c);
+    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * 256 + 128 + uc], acc);
+    // k lanes form u; q lanes receive it from lane l-16 and finish o
+    const float u = b_h * (v_c - acc);
+    auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+    const float u_from_k = __uint_as_float(sw[0]);
+    // the record goes to HBM, or (REC_LDS) into slot n of the staged records
+    float *ru = REC_LDS ? L.rec + n * 256 + 128 : hs.ru + n * D;
+    float *rk = REC_LDS ? L.rec + n * 256 : hs.rk + n * D;
+    float *rg = REC_LDS ? L.sgam : hs.rgam;
+    if (vec == 0) {
+        ru[uc] = u;
+    } else {
+        o[(size_t)h * D + c] = fma_(kqd[0], u_from_k, acc);
+    }
+    if (w == 0) {
+        rk[kpos(l)] = k0;
+        rk[kpos(l + 64)] = k1;
+        if (l == 0) rg[n] = gt;
+    }
+}
+
+}  // namespace
+}  // namespace leapq

@@ -27,6 +27,7 @@
 // correction over the wave's 32 columns, B = c_i k_i over 64 rows each), and
 // a K = 1 matrix step rounds exactly like fma(c_i k_i[r], u_i[c], S), so the
 // chain over the records is the same sequence of fused multiply-adds.
+#include "leapq_append_dev.h"
 #include "leapq_device.h"
 
 namespace leapq {
@@ -466,6 +467,41 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
+// The last token of a full window and the fold, in one launch (W <= 16).
+// The append's staging (codes in registers, records and the other operands
+// in LDS) serves both steps: the token's output is written as by the append,
+// its record goes into LDS slot n instead of HBM (the fold consumes it and
+// empties the buffer), and the fold rebuilds from the same registers and LDS
+// instead of reading the boundary and the records again.  The results are
+// those of leapq_append followed by leapq_fold.
+template <typename T, int CT>
+__global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
+                                                     const T *__restrict__ kin, const T *__restrict__ vin,
+                                                     const float *__restrict__ alpha,
+                                                     const float *__restrict__ beta, float *__restrict__ o,
+                                                     int smoothing, float floor_)
+{
+    __shared__ FoldStage st;
+    __shared__ float sin_[InLds<T>::floats];
+    __shared__ float dots[kDotFloats];
+    __shared__ FoldWork wk;
+    const MMap a = mmap();
+    const int h = blockIdx.x;
+    const HeadLds<T> L(st.rec, st.lines, st.rho, sin_, st.idx, st.gam);
+    uint4 qc[4];
+    append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
+    const float a_h = alpha[h];
+    const float b_h = beta[h];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    append_compute<T, true>(sv, n, h, a, L, dots, qc, a_h, b_h, o);
+    lds_barrier();  // record n is in LDS for every wave
+    const HeadState hs = head_state(sv, h);
+    float S[4][16];
+    rebuild(a, hs, qc, sv.C, n + 1, true, st, S);
+    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
+}
+
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
     __shared__ FoldStage st;
@@ -506,6 +542,30 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
         hipLaunchKernelGGL(k_fold<4>, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     else
         hipLaunchKernelGGL(k_fold<-1>, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+    return hipGetLastError();
+}
+
+template <typename T>
+static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *beta, float *o, int smoothing, float floor_,
+                                 hipStream_t s)
+{
+    if (sv.C == 4)
+        hipLaunchKernelGGL((k_append_fold<T, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q, (const T *)k,
+                           (const T *)v, alpha, beta, o, smoothing, floor_);
+    else
+        hipLaunchKernelGGL((k_append_fold<T, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q, (const T *)k,
+                           (const T *)v, alpha, beta, o, smoothing, floor_);
+}
+
+hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
+                              const void *v, const float *alpha, const float *beta, float *o, int smoothing,
+                              float floor_, hipStream_t s)
+{
+    if (bf16)
+        launch_append_fold_t<uint16_t>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, s);
+    else
+        launch_append_fold_t<float>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, s);
     return hipGetLastError();
 }
 

@@ -27,6 +27,11 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s);
 hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
                          const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
+// The window's last append and the fold in one launch; requires n + 1 == W
+// and W <= 16 (the records fit one LDS chunk).
+hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
+                              const void *v, const float *alpha, const float *beta, float *o, int smoothing,
+                              float floor_, hipStream_t s);
 hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, void *S, const void *q, const void *k,
                              const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
 

@@ -30,8 +30,8 @@ LEAPQ_DEQ_RESIDUAL = 0
 LEAPQ_DEQ_BOUNDARY = 1
 LEAPQ_DEQ_CURRENT = 2
 
-SYMBOLS = ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_fold", "leapq_dequant",
-           "leapq_gdn_decode", "leapq_status_str", "leapq_version")
+SYMBOLS = ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold", "leapq_fold",
+           "leapq_dequant", "leapq_gdn_decode", "leapq_status_str", "leapq_version")
 
 
 class leapq_config(ctypes.Structure):
@@ -73,11 +73,12 @@ def lib():
         L.leapq_query_layout.argtypes = [ctypes.POINTER(leapq_config), ctypes.POINTER(leapq_layout)]
         L.leapq_init_state.argtypes = [ctypes.POINTER(leapq_layer), vp, vp]
         L.leapq_append.argtypes = [ctypes.POINTER(leapq_layer), vp, vp, vp, vp, vp, vp, vp]
+        L.leapq_append_fold.argtypes = [ctypes.POINTER(leapq_layer), vp, vp, vp, vp, vp, vp, vp]
         L.leapq_fold.argtypes = [ctypes.POINTER(leapq_layer), vp]
         L.leapq_dequant.argtypes = [ctypes.POINTER(leapq_layer), i32, vp, vp]
         L.leapq_gdn_decode.argtypes = [ctypes.POINTER(leapq_config), i32, vp, vp, vp, vp, vp, vp, vp, vp]
-        for f in ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_fold", "leapq_dequant",
-                  "leapq_gdn_decode", "leapq_version"):
+        for f in ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold", "leapq_fold",
+                  "leapq_dequant", "leapq_gdn_decode", "leapq_version"):
             getattr(L, f).restype = i32
         L.leapq_status_str.argtypes = [i32]
         L.leapq_status_str.restype = ctypes.c_char_p
@@ -247,6 +248,18 @@ def leapq_append(layer, q, k, v, alpha, beta, o, stream=None):
     _dev_tensor(o, "o", torch.float32, (H, D), dev)
     _check(lib().leapq_append(ctypes.byref(layer.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                               _ptr(o), _stream(stream, dev)), "leapq_append")
+
+
+def leapq_append_fold(layer, q, k, v, alpha, beta, o, stream=None):
+    """The window's last token and the fold (leapq_append then leapq_fold)."""
+    H, dt, dev = layer.heads, layer.in_dtype, layer.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, dt, (H, D), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, (H,), dev)
+    _dev_tensor(beta, "beta", torch.float32, (H,), dev)
+    _dev_tensor(o, "o", torch.float32, (H, D), dev)
+    _check(lib().leapq_append_fold(ctypes.byref(layer.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(o), _stream(stream, dev)), "leapq_append_fold")
 
 
 def leapq_fold(layer, stream=None):

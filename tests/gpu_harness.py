@@ -127,10 +127,12 @@ def _pool():
 
 
 def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="cuda", check_every_token=True,
-              fold_at=None, report=None, log=True):
+              fold_at=None, report=None, log=True, fused=False):
     """Runs `tokens` decode tokens of one layer on the GPU and, for the
     sampled heads, in the oracle; folds whenever the window is full (or at
-    the token counts in fold_at).  Returns the Report."""
+    the token counts in fold_at).  With fused, the GPU takes each window's
+    last token and its fold in one leapq_append_fold call (the oracle still
+    appends, then folds).  Returns the Report."""
     rep = report or Report()
     dev = torch.device(device)
     H = wl.batch * wl.heads
@@ -152,7 +154,11 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
             q, k, v, a, b = workloads.token_inputs(wl, layer, t, device=gen_device)
             qd, kd, vd = (x.reshape(H, D).to(dev) for x in (q, k, v))
             ad, bd = a.reshape(H).to(dev), b.reshape(H).to(dev)
-            lq.leapq_append(L, qd, kd, vd, ad, bd, o)
+            last = fused and L.n_records == wl.window - 1
+            if last:
+                lq.leapq_append_fold(L, qd, kd, vd, ad, bd, o)
+            else:
+                lq.leapq_append(L, qd, kd, vd, ad, bd, o)
             qh = workloads.widen(q.reshape(H, D)[sidx]).cpu().numpy()
             kh = workloads.widen(k.reshape(H, D)[sidx]).cpu().numpy()
             vh = workloads.widen(v.reshape(H, D)[sidx]).cpu().numpy()
@@ -162,11 +168,12 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
                                  range(len(sample))))
             og = o[sidx.to(dev)].cpu().numpy()
             rep.fp("o", og, np.stack(outs))
-            if check_every_token:
+            if check_every_token and not last:
                 compare_state(L, refs, sample, rep)
-            full = L.n_records == wl.window
+            full = last or L.n_records == wl.window
             if full or (fold_at is not None and (t + 1) in fold_at):
-                lq.leapq_fold(L)
+                if not last:
+                    lq.leapq_fold(L)
                 list(pool.map(lambda h: h.fold(), refs))
                 torch.cuda.synchronize(dev)
                 compare_state(L, refs, sample, rep)

@@ -198,3 +198,28 @@ def test_gdn_decode_checks():
     assert lib.leapq_gdn_decode(ctypes.byref(c), 1, *bad, None) == lq.LEAPQ_ERR_ALIGN
     c.dv = 96
     assert lib.leapq_gdn_decode(ctypes.byref(c), 0, *args, None) == lq.LEAPQ_ERR_SHAPE
+
+
+def call_append_fold(L, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, o=FAKE):
+    vp = ctypes.c_void_p
+    return lq.lib().leapq_append_fold(ctypes.byref(L), vp(q), vp(k), vp(v), vp(a), vp(b), vp(o), None)
+
+
+def test_append_fold_checks():
+    """The fused last append + fold needs n_records == window - 1; failures
+    leave n_records unchanged."""
+    for W in (1, 16, 20, 64):
+        c = cfg(window=W)
+        for n in (0, W - 2, W, W + 1):
+            if n == W - 1 or n < 0:
+                continue
+            L = fake_layer(c, n=n)
+            assert call_append_fold(L) == lq.LEAPQ_ERR_RANGE and L.n_records == n, (W, n)
+    c = cfg(window=16)
+    assert call_append_fold(fake_layer(c, n=15, state=0)) == lq.LEAPQ_ERR_NULL
+    assert call_append_fold(fake_layer(c, n=15, state=FAKE + 16)) == lq.LEAPQ_ERR_ALIGN
+    for key in ("q", "k", "v", "a", "b", "o"):
+        L = fake_layer(c, n=15)
+        assert call_append_fold(L, **{key: 0}) == lq.LEAPQ_ERR_NULL and L.n_records == 15, key
+    for key in ("q", "k", "v", "o"):
+        assert call_append_fold(fake_layer(c, n=15), **{key: FAKE + 4}) == lq.LEAPQ_ERR_ALIGN, key
