@@ -170,7 +170,7 @@ def main():
     fold_us = 1e3 * float(np.mean(ev_fold))
     fused_us = 1e3 * float(np.mean(ev_fused)) if ev_fused else None
     app_bytes_avg = float(np.mean([metrics.append_bytes(n, C, in_bytes) for n in range(W)])) * H
-    fold_bytes = metrics.fold_bytes(W, C) * H
+    fold_bytes = metrics.fold_bytes(W, C, in_bytes) * H
     append_gbps = app_bytes_avg / (append_us * 1e-6) / 1e9
     fold_gbps = fold_bytes / (fold_us * 1e-6) / 1e9
     share_sep = metrics.fold_share(W * append_us, fold_us)
@@ -245,7 +245,7 @@ def main():
         "data": "synthetic (seeded; 16-token input pool per layer, cycled every window)",
         "config": {"workload": f"{wl.name}: {wl.notes}", "batch": B, "layers": Lyr, "heads": Hh,
                    "dk": D, "dv": D, "window": W, "n_comp": C, "in_dtype": wl.in_dtype,
-                   "state": "int8 residual + fp32 compensators + fp32 records",
+                   "state": "int8 residual + fp32 compensators + records (fp32 decays and corrections, keys in the input dtype)",
                    "tokens_per_step": W,
                    "schedule": ("W-1 appends + leapq_append_fold per layer and window" if fused
                                 else "W appends + leapq_fold per layer and window")},

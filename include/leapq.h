@@ -89,16 +89,19 @@ typedef struct leapq_config {
  *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
  *                                      over r for a column), natural order
  *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
- *   rec_k     fp32  [heads][W][128]    record keys; key row r is stored at
- *                                      32 (r / 32) + iperm(r % 32)
+ *   rec_k     in_dtype [heads][W][128] record keys in key-row order, in the
+ *                                      input dtype: a record's key is the
+ *                                      token's k as given, so bf16 storage
+ *                                      of bf16 inputs is exact
  *   rec_u     fp32  [heads][W][128]    record corrections; value column c is
  *                                      stored at 32 (c % 4) + 8 (c / 32)
  *                                      + 4 ((c / 4) % 2) + (c / 8) % 4
  * These orders are the thread map of the kernels (each thread's 64 codes are
  * four 16-byte loads, each wave's loads 1 KB contiguous; the record keys and
- * corrections are the operand orders of the fold's matrix instructions).
+ * corrections are the A operand order of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
- * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 512 + 512). */
+ * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 128 e + 512)
+ * with e = 4 (fp32 inputs) or 2 (bf16 inputs). */
 typedef struct leapq_layout {
     uint64_t total_bytes;
     uint64_t off_codes, off_row_scale, off_col_scale, off_comp_idx, off_comp_vec;

@@ -45,6 +45,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
 {
     const uint64_t H = (uint64_t)c->batch * (uint64_t)c->heads;
     const uint64_t C = (uint64_t)c->n_comp, W = (uint64_t)c->window;
+    const uint64_t kb = c->in_dtype == LEAPQ_BF16 ? 2 : 4;  // record key element
     uint64_t off = 0;
     L->off_codes = off;
     off = round_up(off + H * kD * kD);
@@ -59,12 +60,12 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_rec_gamma = off;
     off = round_up(off + H * W * 4);
     L->off_rec_k = off;
-    off = round_up(off + H * W * kD * 4);
+    off = round_up(off + H * W * kD * kb);
     L->off_rec_u = off;
     off = round_up(off + H * W * kD * 4);
     L->total_bytes = off;
     L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * kD * 4;
-    L->record_bytes_per_head = W * (4 + 2 * kD * 4);
+    L->record_bytes_per_head = W * (4 + kD * kb + kD * 4);
 }
 
 int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
@@ -84,10 +85,11 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->cidx = (int32_t *)(b + L.off_comp_idx);
     sv->cvec = (float *)(b + L.off_comp_vec);
     sv->rgam = (float *)(b + L.off_rec_gamma);
-    sv->rk = (float *)(b + L.off_rec_k);
+    sv->rk = b + L.off_rec_k;
     sv->ru = (float *)(b + L.off_rec_u);
     sv->C = layer->cfg.n_comp;
     sv->W = layer->cfg.window;
+    sv->key_bf16 = layer->cfg.in_dtype == LEAPQ_BF16;
     return LEAPQ_OK;
 }
 

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadLds<T> L(dsm, n, sv.C);
-    float *dots = dsm + head_lds_floats(n, sv.C, InLds<T>::floats);
+    float *dots = dsm + head_lds_floats<T>(n, sv.C);
     uint4 qc[4];
     append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
     const float a_h = alpha[h];
@@ -57,7 +57,7 @@ template <typename T>
 static void launch_append_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, float *o, hipStream_t s)
 {
-    const size_t lds = sizeof(float) * (head_lds_floats(n, sv.C, InLds<T>::floats) + kDotFloats);
+    const size_t lds = sizeof(float) * (head_lds_floats<T>(n, sv.C) + kDotFloats);
     hipLaunchKernelGGL(k_append<T>, dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
                        (const T *)v, alpha, beta, o);
 }

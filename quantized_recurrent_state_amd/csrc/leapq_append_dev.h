@@ -25,12 +25,36 @@ struct InLds<uint16_t> {
     }
 };
 
-// LDS of one head in floats: records [n][256] (keys | corrections, stored
-// orders), lines [C][128], rho [128], sigma [128], inputs (k, q, v),
-// indices [8], decays [64]
-__host__ __device__ constexpr int head_lds_floats(int n, int C, int in_floats)
+// A record as stored and as staged in LDS: the key in the input dtype T (row
+// order, exact: the append's key is an input), then the correction (fp32,
+// stored order); keys take kbytes, a staged record stride floats.
+template <typename T>
+struct Rec {
+    static constexpr int kbytes = D * (int)sizeof(T);
+    static constexpr int kf = kbytes / 4;
+    static constexpr int stride = kf + D;
+    static constexpr int kpieces = kbytes / 16;
+    __device__ static float key(const float *rec, int r) { return InLds<T>::get(rec, 0, r); }
+};
+
+// Copies record g of a head into LDS at dst (stride floats) with one
+// LDS-direct load per lane: the key's 16-byte pieces, then the correction's.
+template <typename T>
+__device__ __forceinline__ void copy_record(const HeadState &hs, int g, int l, float *dst)
 {
-    return n * 256 + C * 128 + 256 + in_floats + 8 + 64;
+    constexpr int kp = Rec<T>::kpieces;
+    if (kp + 32 >= 64 || l < kp + 32)
+        lds_copy16(l < kp ? static_cast<const void *>(hs.rk + g * Rec<T>::kbytes + 16 * l)
+                          : static_cast<const void *>(hs.ru + g * D + 4 * (l - kp)),
+                   dst);
+}
+
+// LDS of one head in floats: records [n][stride], lines [C][128], rho [128],
+// sigma [128], inputs (k, q, v), indices [8], decays [64]
+template <typename T>
+__host__ __device__ constexpr int head_lds_floats(int n, int C)
+{
+    return n * Rec<T>::stride + C * 128 + 256 + InLds<T>::floats + 8 + 64;
 }
 // per-workgroup results of the dot jobs: coefficients [2][64], column-token
 // dots [2][8], k.q [1] (+3 pad)
@@ -47,7 +71,7 @@ struct HeadLds {
     __device__ HeadLds(float *base, int n, int C)
     {
         rec = base;
-        cv = rec + n * 256;
+        cv = rec + n * Rec<T>::stride;
         srho = cv + C * D;
         ssig = srho + D;
         sin_ = ssig + D;
@@ -67,8 +91,7 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
     const HeadState hs = head_state(sv, h);
 #pragma unroll
     for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
-    for (int rr = w; rr < n; rr += 4)
-        lds_copy16(l < 32 ? hs.rk + rr * D + 4 * l : hs.ru + rr * D + 4 * (l - 32), L.rec + rr * 256);
+    for (int rr = w; rr < n; rr += 4) copy_record<T>(hs, rr, l, L.rec + rr * Rec<T>::stride);
     for (int pair = 2 * w; pair < C; pair += 8)
         if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
     if (w == 0) {
@@ -167,7 +190,8 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     const int njobs = n + 1 + C;
     for (int job = w; job < njobs; job += 4) {
         if (job < n) {
-            const float a0 = rec[job * 256 + kpos(l)], a1 = rec[job * 256 + kpos(l + 64)];
+            const float *kj = rec + job * Rec<T>::stride;
+            const float a0 = Rec<T>::key(kj, l), a1 = Rec<T>::key(kj, l + 64);
             const float dk = wdot(a0, a1, k0, k1);
             const float dq = wdot(a0, a1, q0, q1);
             const float ci = rdl(ci_l, job);
@@ -205,14 +229,15 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     }
     float acc = gt * b;
     const int uc = upos(c);
-    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * 256 + 128 + uc], acc);
+    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * Rec<T>::stride + Rec<T>::kf + uc], acc);
     // k lanes form u; q lanes receive it from lane l-16 and finish o
     const float u = b_h * (v_c - acc);
     auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
     const float u_from_k = __uint_as_float(sw[0]);
     // the record goes to HBM, or (REC_LDS) into slot n of the staged records
-    float *ru = REC_LDS ? L.rec + n * 256 + 128 : hs.ru + n * D;
-    float *rk = REC_LDS ? L.rec + n * 256 : hs.rk + n * D;
+    float *ru = REC_LDS ? L.rec + n * Rec<T>::stride + Rec<T>::kf : hs.ru + n * D;
+    uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * Rec<T>::stride)
+                           : reinterpret_cast<uint32_t *>(hs.rk + n * Rec<T>::kbytes);
     float *rg = REC_LDS ? L.sgam : hs.rgam;
     if (vec == 0) {
         ru[uc] = u;
@@ -220,8 +245,10 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
         o[(size_t)h * D + c] = fma_(kqd[0], u_from_k, acc);
     }
     if (w == 0) {
-        rk[kpos(l)] = k0;
-        rk[kpos(l + 64)] = k1;
+        // the key is the token's k as staged (the first kbytes of the inputs)
+        const uint32_t *kw = reinterpret_cast<const uint32_t *>(sin_);
+        rk[l] = kw[l];
+        if (Rec<T>::kf > 64) rk[l + 64] = kw[l + 64];
         if (l == 0) rg[n] = gt;
     }
 }

@@ -91,9 +91,6 @@ __device__ __forceinline__ AMap amap()
 // the bytes code_off(w, l, p) + m, m = 0..15 (column w + 4h + 8m), so each
 // 16-byte load of a wave reads 1 KB contiguous.
 __host__ __device__ __forceinline__ int code_off(int w, int l, int p) { return w * 4096 + p * 1024 + l * 16; }
-// Record keys: row r at kpos(r), the B operand order of the matrix
-// instruction (lane L of instruction q reads kpos = 64 q + L).
-__host__ __device__ __forceinline__ int kpos(int r) { return 32 * (r >> 5) + iperm(r & 31); }
 // Record corrections: column c at upos(c), the A operand order (lane a of
 // wave w reads 32 w + (a & 31)).
 __host__ __device__ __forceinline__ int upos(int c)
@@ -106,7 +103,8 @@ struct HeadState {
     float *rho, *sigma;
     int32_t *cidx;
     float *cvec;
-    float *rgam, *rk, *ru;
+    float *rgam, *ru;
+    char *rk;  // keys in the input dtype, row order; key_bytes per record
 };
 
 __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
@@ -118,7 +116,7 @@ __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
     s.cidx = sv.cidx + (size_t)h * sv.C;
     s.cvec = sv.cvec + (size_t)h * sv.C * D;
     s.rgam = sv.rgam + (size_t)h * sv.W;
-    s.rk = sv.rk + (size_t)h * sv.W * D;
+    s.rk = static_cast<char *>(sv.rk) + (size_t)h * sv.W * D * (sv.key_bf16 ? 2 : 4);
     s.ru = sv.ru + (size_t)h * sv.W * D;
     return s;
 }

@@ -44,7 +44,7 @@ typedef float f32x32 __attribute__((ext_vector_type(32)));
 // Operands of one head staged from HBM, and the work arrays of the steps
 // after the rebuild.
 struct FoldStage {
-    float rec[16 * 256];  // a chunk of up to 16 records: keys | corrections (stored orders)
+    float rec[16 * 256];  // a chunk of up to 16 records (Rec<T>::stride floats each)
     float lines[8 * 128];
     float rho[128];
     float sig[128];
@@ -74,13 +74,10 @@ __device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, 
     }
 }
 
+template <typename T>
 __device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, FoldStage &sm)
 {
-    const int l = a.l;
-    for (int rr = a.w; rr < cnt; rr += 4) {
-        const int g = base + rr;
-        lds_copy16(l < 32 ? hs.rk + g * D + 4 * l : hs.ru + g * D + 4 * (l - 32), sm.rec + rr * 256);
-    }
+    for (int rr = a.w; rr < cnt; rr += 4) copy_record<T>(hs, base + rr, a.l, sm.rec + rr * Rec<T>::stride);
 }
 
 __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, uint4 (&qc)[4])
@@ -91,7 +88,8 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 
 // Current state in the tile.  qc: the thread's 4 code chunks.  Expects
 // stage_small() done and visible and, if n > 0, records 0..min(n,16)-1
-// staged and visible.  Contains barriers when n > 16.
+// staged and visible.  Contains barriers when n > 16.  T: the key dtype.
+template <typename T>
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
                                         bool lines, FoldStage &sm, float (&S)[4][16])
 {
@@ -152,30 +150,32 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
         const int cnt = n - base < 16 ? n - base : 16;
         if (base > 0) {
             __syncthreads();  // the previous chunk is consumed
-            stage_records(a, hs, base, cnt, sm);
+            stage_records<T>(a, hs, base, cnt, sm);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        // records r of the chunk in order; four per iteration, then the rest
+        // records r of the chunk in order; four per iteration, then the rest.
+        // B lane l of instruction q carries key row a.i + 32 (a.h + 2q).
+        const int kr0 = a.i + 32 * a.h;
         int r = 0;
         for (; r + 4 <= cnt; r += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float ci = rdl(ci_l, base + r + u);
-                const float *rr = sm.rec + (r + u) * 256;
-                const float b0 = ci * rr[a.l];       // key row of B lane l, instruction 0
-                const float b1 = ci * rr[64 + a.l];  // instruction 1
-                const float au = rr[128 + 32 * a.w + a.jp];
+                const float *rr = sm.rec + (r + u) * Rec<T>::stride;
+                const float b0 = ci * Rec<T>::key(rr, kr0);
+                const float b1 = ci * Rec<T>::key(rr, kr0 + 64);
+                const float au = rr[Rec<T>::kf + 32 * a.w + a.jp];
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
             }
         }
         for (; r < cnt; ++r) {
             const float ci = rdl(ci_l, base + r);
-            const float *rr = sm.rec + r * 256;
-            const float b0 = ci * rr[a.l];
-            const float b1 = ci * rr[64 + a.l];
-            const float au = rr[128 + 32 * a.w + a.jp];
+            const float *rr = sm.rec + r * Rec<T>::stride;
+            const float b0 = ci * Rec<T>::key(rr, kr0);
+            const float b1 = ci * Rec<T>::key(rr, kr0 + 64);
+            const float au = rr[Rec<T>::kf + 32 * a.w + a.jp];
             acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
         }
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <int CT>
+template <typename T, int CT>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
     __shared__ FoldStage st;
@@ -457,11 +457,11 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     uint4 qc[4];
     load_codes(a, hs, qc);
     stage_small(a, hs, sv.C, n, st);
-    stage_records(a, hs, 0, n < 16 ? n : 16, st);
+    stage_records<T>(a, hs, 0, n < 16 ? n : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild(a, hs, qc, sv.C, n, true, st, S);
+    rebuild<T>(a, hs, qc, sv.C, n, true, st, S);
     // no barrier: the quantization writes only LDS arrays the rebuild does
     // not read, and each thread rewrites only the codes it loaded
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
@@ -498,10 +498,11 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild(a, hs, qc, sv.C, n + 1, true, st, S);
+    rebuild<T>(a, hs, qc, sv.C, n + 1, true, st, S);
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
+template <typename T>
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
     __shared__ FoldStage st;
@@ -512,11 +513,11 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
     uint4 qc[4];
     load_codes(a, hs, qc);
     stage_small(a, hs, sv.C, nr, st);
-    stage_records(a, hs, 0, nr < 16 ? nr : 16, st);
+    stage_records<T>(a, hs, 0, nr < 16 ? nr : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild(a, hs, qc, sv.C, nr, what >= 1, st, S);
+    rebuild<T>(a, hs, qc, sv.C, nr, what >= 1, st, S);
     float *dst = out + (size_t)h * D * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -536,12 +537,21 @@ hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoo
     return hipGetLastError();
 }
 
-hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
+template <typename T>
+static void launch_fold_t(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL(k_fold<4>, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<T, 4>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     else
-        hipLaunchKernelGGL(k_fold<-1>, dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<T, -1>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+}
+
+hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
+{
+    if (sv.key_bf16)
+        launch_fold_t<uint16_t>(sv, heads, n, smoothing, floor_, s);
+    else
+        launch_fold_t<float>(sv, heads, n, smoothing, floor_, s);
     return hipGetLastError();
 }
 
@@ -571,7 +581,10 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
 
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_dequant, dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    if (sv.key_bf16)
+        hipLaunchKernelGGL(k_dequant<uint16_t>, dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    else
+        hipLaunchKernelGGL(k_dequant<float>, dim3(heads), dim3(NT), 0, s, sv, n, what, out);
     return hipGetLastError();
 }
 

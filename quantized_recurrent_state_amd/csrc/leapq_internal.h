@@ -15,10 +15,11 @@ struct StateView {
     int32_t *cidx;
     float *cvec;
     float *rgam;
-    float *rk;
+    void *rk;  // record keys in the input dtype (fp32 or bf16)
     float *ru;
     int C;  // compensator lines per head
     int W;  // record slots per head
+    int key_bf16;  // record keys (and inputs) are bf16
 };
 
 hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,

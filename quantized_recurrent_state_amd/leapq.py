@@ -138,11 +138,6 @@ def code_offset(r, c):
     return (c & 3) * 4096 + (r >> 5) * 1024 + (_iperm(r & 31) + 32 * ((c >> 2) & 1)) * 16 + (c >> 3)
 
 
-def key_pos(r):
-    """Position of key row r within a stored record key."""
-    return 32 * (r >> 5) + _iperm(r & 31)
-
-
 def corr_pos(c):
     """Position of value column c within a stored record correction."""
     return 32 * (c & 3) + 8 * (c >> 5) + 4 * ((c >> 2) & 1) + ((c >> 3) & 3)
@@ -215,17 +210,17 @@ class Layer:
         return self._sec(self.layout.off_rec_gamma, self.heads * W, torch.float32, (self.heads, W))
 
     def rec_k_physical(self):
+        """Record keys [heads, W, 128] as stored: the input dtype, key-row order."""
         W = self.cfg.window
-        return self._sec(self.layout.off_rec_k, self.heads * W * D, torch.float32, (self.heads, W, D))
+        return self._sec(self.layout.off_rec_k, self.heads * W * D, self.in_dtype, (self.heads, W, D))
 
     def rec_u_physical(self):
         W = self.cfg.window
         return self._sec(self.layout.off_rec_u, self.heads * W * D, torch.float32, (self.heads, W, D))
 
     def rec_k(self):
-        """Record keys [heads, W, 128] in logical key-row order."""
-        r = torch.arange(D, device=self.device)
-        return self.rec_k_physical()[:, :, key_pos(r)]
+        """Record keys [heads, W, 128] as fp32 (exact)."""
+        return self.rec_k_physical().float()
 
     def rec_u(self):
         """Record corrections [heads, W, 128] in logical value-column order."""

@@ -5,8 +5,10 @@ for one head (no re-reads, no dense fp32 state):
 
   append, with n records already in the window (token n+1):
       read   codes 128*128 + rho, sigma 2*512 + compensators C*(4+512)
-             + q, k, v 3*128*e_in + alpha, beta 8 + records n*(4+512+512)
-      write  record 4+512+512 + output 512
+             + q, k, v 3*128*e_in + alpha, beta 8 + records n*(4+128*e_in+512)
+      write  record 4+128*e_in+512 + output 512
+  (a record holds gamma and u in fp32 and the key in the input dtype e_in,
+  which stores the token's k exactly)
   fold of n records:
       read   boundary (codes, scales, compensators) + n records
       write  boundary
@@ -26,20 +28,20 @@ def boundary_bytes(C=4):
     return D * D + 2 * D * 4 + C * (4 + D * 4)
 
 
-def record_bytes():
-    """Bytes of one record: gamma, k, u in fp32."""
-    return 4 + 2 * D * 4
+def record_bytes(in_bytes=2):
+    """Bytes of one record: gamma and u in fp32, k in the input dtype."""
+    return 4 + D * in_bytes + D * 4
 
 
 def append_bytes(n, C=4, in_bytes=2):
     """Algorithmic bytes of one head's append with n records present."""
-    read = boundary_bytes(C) + 3 * D * in_bytes + 8 + n * record_bytes()
-    write = record_bytes() + D * 4
+    read = boundary_bytes(C) + 3 * D * in_bytes + 8 + n * record_bytes(in_bytes)
+    write = record_bytes(in_bytes) + D * 4
     return read + write
 
 
-def fold_bytes(n, C=4):
-    return 2 * boundary_bytes(C) + n * record_bytes()
+def fold_bytes(n, C=4, in_bytes=2):
+    return 2 * boundary_bytes(C) + n * record_bytes(in_bytes)
 
 
 def init_bytes(C=4):
@@ -48,7 +50,7 @@ def init_bytes(C=4):
 
 def window_bytes(W=16, C=4, in_bytes=2):
     """Bytes of one head over a whole window: W appends and one fold."""
-    return sum(append_bytes(n, C, in_bytes) for n in range(W)) + fold_bytes(W, C)
+    return sum(append_bytes(n, C, in_bytes) for n in range(W)) + fold_bytes(W, C, in_bytes)
 
 
 def gdn_step_bytes(state_bytes=4, in_bytes=2):

@@ -44,12 +44,14 @@ def layout(**kw):
 
 
 def test_layout_sections_aligned_and_disjoint():
-    for (B, H, W, C) in ((1, 4, 16, 4), (512, 32, 16, 4), (3, 5, 1, 0), (2, 7, 64, 8)):
-        L = layout(batch=B, heads=H, window=W, n_comp=C)
+    for (B, H, W, C, dt) in ((1, 4, 16, 4, "f32"), (512, 32, 16, 4, "bf16"), (3, 5, 1, 0, "bf16"),
+                             (2, 7, 64, 8, "f32")):
+        L = layout(batch=B, heads=H, window=W, n_comp=C, in_dtype=dt)
         heads = B * H
+        e = 2 if dt == "bf16" else 4  # record keys are stored in the input dtype
         secs = [("off_codes", heads * 128 * 128), ("off_row_scale", heads * 512), ("off_col_scale", heads * 512),
                 ("off_comp_idx", heads * C * 4), ("off_comp_vec", heads * C * 512),
-                ("off_rec_gamma", heads * W * 4), ("off_rec_k", heads * W * 512), ("off_rec_u", heads * W * 512)]
+                ("off_rec_gamma", heads * W * 4), ("off_rec_k", heads * W * 128 * e), ("off_rec_u", heads * W * 512)]
         end = 0
         for name, size in secs:
             off = getattr(L, name)
@@ -57,7 +59,7 @@ def test_layout_sections_aligned_and_disjoint():
             end = off + size
         assert L.total_bytes >= end and L.total_bytes % 256 == 0
         assert L.boundary_bytes_per_head == metrics.boundary_bytes(C)
-        assert L.record_bytes_per_head == W * metrics.record_bytes()
+        assert L.record_bytes_per_head == W * metrics.record_bytes(e)
 
 
 def test_layout_matches_page_figures():
@@ -87,11 +89,15 @@ def test_step_definition_matches_page():
 
 
 def test_bytes_model_values():
-    # one head, bf16 inputs, W=16, C=4
-    assert metrics.append_bytes(0) == 21788
-    assert sum(metrics.append_bytes(n) for n in range(16)) / 16 == 29498
-    assert metrics.fold_bytes(16) == 55392
-    assert metrics.window_bytes() / 16 == 32960
+    # one head, bf16 inputs (bf16 record keys), W=16, C=4
+    assert metrics.record_bytes() == 4 + 256 + 512
+    assert metrics.append_bytes(0) == 21532
+    assert sum(metrics.append_bytes(n) for n in range(16)) / 16 == 27322
+    assert metrics.fold_bytes(16) == 51296
+    assert metrics.window_bytes() / 16 == 30528
+    # fp32 inputs: fp32 keys, 1,028-byte records
+    assert metrics.append_bytes(0, in_bytes=4) == 22556
+    assert metrics.fold_bytes(16, in_bytes=4) == 55392
     assert metrics.gdn_step_bytes(4) == 132360 and metrics.gdn_step_bytes(2) == 66824
 
 
