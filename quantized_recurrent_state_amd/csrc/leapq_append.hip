@@ -18,13 +18,13 @@
 // (T = the canonical 128-term tree) and the record (gamma_t, k, u_t) is
 // stored at slot n.
 //
-// Memory: each thread loads its 64 codes as four 16-byte loads (1 KB
-// contiguous per wave and load); every other per-head operand (records,
-// compensator lines, rho and sigma, k, q, v, the compensator indices and the
-// record decays) is copied straight into LDS by a few LDS-direct loads per
-// wave.  The residual read is reduced inside each wave (thread map of
-// leapq_device.h); barriers separate the copies, the per-head dot products
-// and the per-column tail.
+// Memory: every per-head operand but the codes (records, compensator lines,
+// rho and sigma, k, q, v, the compensator indices and the record decays) is
+// copied straight into LDS by a few LDS-direct loads per wave; then each
+// thread loads its 64 codes as four 16-byte loads (1 KB contiguous per wave
+// and load).  Once the copies have landed the per-head dot products run
+// while the codes are still in flight; the residual read is then reduced
+// inside each wave (thread map of leapq_device.h) and finished per column.
 #include "leapq_append_dev.h"
 
 namespace leapq {
@@ -46,8 +46,8 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
     const float a_h = alpha[h];
     const float b_h = beta[h];
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    wait_lds_copies();
+    lds_barrier();
     append_compute<T>(sv, n, h, a, L, dots, qc, a_h, b_h, o);
 }
 

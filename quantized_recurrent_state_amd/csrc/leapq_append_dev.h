@@ -80,8 +80,20 @@ struct HeadLds {
     }
 };
 
-// Issues every global load of head h: its 64 codes per thread into qc, every
-// other operand into the LDS buffer L by LDS-direct copies.
+// Wait until at most kCodeLoads vector loads of this wave are outstanding:
+// with the codes issued last, every LDS-direct copy of append_issue() has
+// landed (vector loads complete in issue order) while the codes may still be
+// in flight.  Other waves' copies need a barrier after this.
+constexpr int kCodeLoads = 4;
+__device__ __forceinline__ void wait_lds_copies()
+{
+    // vmcnt(4) (bits 3:0 and 15:14), expcnt(7), lgkmcnt(15): not waited
+    __builtin_amdgcn_s_waitcnt((kCodeLoads & 15) | ((kCodeLoads >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Issues every global load of head h: every operand other than the codes
+// into the LDS buffer L by LDS-direct copies, then the thread's 64 codes into
+// qc as the wave's last kCodeLoads vector loads.
 template <typename T>
 __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
                                              const T *__restrict__ kin, const T *__restrict__ vin,
@@ -89,8 +101,6 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
 {
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
     for (int rr = w; rr < n; rr += 4) copy_record<T>(hs, rr, l, L.rec + rr * Rec<T>::stride);
     for (int pair = 2 * w; pair < C; pair += 8)
         if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
@@ -114,10 +124,17 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
     } else {
         if (l < n) lds_copy4(hs.rgam + l, L.sgam);
     }
+    // the code loads stay behind every copy (wait_lds_copies counts on it)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // The token for head h from its staged operands (L, qc); writes o and the
-// record.  Contains one lds_barrier (dot jobs -> tail).
+// record.  Expects the LDS copies landed and visible (wait_lds_copies() and a
+// barrier); the codes are waited for at their first use.  Contains one
+// lds_barrier (dot jobs -> residual read and tail).
 template <typename T, bool REC_LDS = false>
 __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a, const HeadLds<T> &L,
                                                float *dots, const uint4 (&qc)[4], float a_h, float b_h,
@@ -145,6 +162,40 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     const float v_c = InLds<T>::get(sin_, 2, c);
     const float gt = (n > 0 ? sgam[n - 1] : 1.0f) * a_h;
     const float ci_l = l < n ? gt / sgam[l] : 0.0f;  // c_i of record i = lane, for the dot jobs
+
+    // ---- per-head dot products (operands in LDS; the codes may still be in
+    // flight), one wave per job:
+    // job r < n: c_r * (k_r . k), c_r * (k_r . q); job n: (k . q);
+    // job n+1+jj: (line_jj . k), (line_jj . q) for column tokens
+    const int njobs = n + 1 + C;
+    for (int job = w; job < njobs; job += 4) {
+        if (job < n) {
+            const float *kj = rec + job * Rec<T>::stride;
+            const float a0 = Rec<T>::key(kj, l), a1 = Rec<T>::key(kj, l + 64);
+            const float dk = wdot(a0, a1, k0, k1);
+            const float dq = wdot(a0, a1, q0, q1);
+            const float ci = rdl(ci_l, job);
+            if (l == 0) {
+                coef[job] = ci * dk;
+                coef[64 + job] = ci * dq;
+            }
+        } else if (job == n) {
+            const float d = wdot(k0, k1, q0, q1);
+            if (l == 0) kqd[0] = d;
+        } else {
+            const int jj = job - n - 1;
+            if (sidx[jj] >= D) {
+                const float a0 = cv[jj * D + l], a1 = cv[jj * D + l + 64];
+                const float dk = wdot(a0, a1, k0, k1);
+                const float dq = wdot(a0, a1, q0, q1);
+                if (l == 0) {
+                    cdot[jj] = dk;
+                    cdot[8 + jj] = dq;
+                }
+            }
+        }
+    }
+    lds_barrier();  // the coefficients of every wave's jobs
 
     // ---- residual read of column m for k and q: rows (i, i+64) and
     // (i+32, i+96) by fused level 0, then level 32; the next exchange (tree
@@ -183,39 +234,6 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
         for (int e = 0; e < 2; ++e) a2[e] = xhalf_dpp<DPP_XOR2>(a4[e], a4[e + 2], (l >> 1) & 1);
         red = xhalf_dpp<DPP_XOR1>(a2[0], a2[1], l & 1);
     }
-
-    // ---- per-head dot products, one wave per job:
-    // job r < n: c_r * (k_r . k), c_r * (k_r . q); job n: (k . q);
-    // job n+1+jj: (line_jj . k), (line_jj . q) for column tokens
-    const int njobs = n + 1 + C;
-    for (int job = w; job < njobs; job += 4) {
-        if (job < n) {
-            const float *kj = rec + job * Rec<T>::stride;
-            const float a0 = Rec<T>::key(kj, l), a1 = Rec<T>::key(kj, l + 64);
-            const float dk = wdot(a0, a1, k0, k1);
-            const float dq = wdot(a0, a1, q0, q1);
-            const float ci = rdl(ci_l, job);
-            if (l == 0) {
-                coef[job] = ci * dk;
-                coef[64 + job] = ci * dq;
-            }
-        } else if (job == n) {
-            const float d = wdot(k0, k1, q0, q1);
-            if (l == 0) kqd[0] = d;
-        } else {
-            const int jj = job - n - 1;
-            if (sidx[jj] >= D) {
-                const float a0 = cv[jj * D + l], a1 = cv[jj * D + l + 64];
-                const float dk = wdot(a0, a1, k0, k1);
-                const float dq = wdot(a0, a1, q0, q1);
-                if (l == 0) {
-                    cdot[jj] = dk;
-                    cdot[8 + jj] = dq;
-                }
-            }
-        }
-    }
-    lds_barrier();
 
     // ---- per-column tail: lane (vec, c)
     float b = sig_c * red;

@@ -492,8 +492,8 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
     const float a_h = alpha[h];
     const float b_h = beta[h];
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    wait_lds_copies();
+    lds_barrier();
     append_compute<T, true>(sv, n, h, a, L, dots, qc, a_h, b_h, o);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
