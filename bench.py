@@ -13,7 +13,6 @@ Prints ONE JSON line on stdout; progress goes to stderr.
                   [--no-baselines] [--no-cpu] [--separate]
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -24,7 +23,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s and HBM GB/s (% of peak), append+fold, 24Lx32H, batch 512"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "quantized_recurrent_state_amd", "csrc", "leapq_append.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_b512_traffic.json")
 
 
@@ -48,8 +46,8 @@ def parse():
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    from quantized_recurrent_state_amd.profiling import kernel_sha as sha
+    return sha()
 
 
 def main():

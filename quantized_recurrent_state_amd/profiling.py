@@ -2,8 +2,9 @@
 
 Programs (each is what comes after `rocprofv3 ... --`):
 
-  python3 -m quantized_recurrent_state_amd.profiling run [--workload b512] [--windows 2]
-      one layer of the workload: init, then `windows` x (W appends + fold)
+  python3 -m quantized_recurrent_state_amd.profiling run [--workload b512] [--windows 2] [--fused]
+      one layer of the workload: init, then `windows` x (W appends + fold), or
+      with --fused x (W-1 appends + the last append and fold in one launch)
   python3 -m quantized_recurrent_state_amd.profiling copy [--mib 1024] [--reps 4]
       a copy-shaped elementwise kernel (y = -x: 4 bytes read and 4 written
       per element; torch's same-dtype copy_ is a DMA blit, not a kernel) of
@@ -27,13 +28,20 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 
-def kernel_sha(src="leapq_append.hip"):
-    with open(os.path.join(PKG, "csrc", src), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the sources of the append kernel: its traffic figure holds while they are unchanged
+APPEND_SOURCES = ("leapq_append.hip", "leapq_append_dev.h", "leapq_device.h")
+
+
+def kernel_sha(srcs=APPEND_SOURCES):
+    h = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(PKG, "csrc", src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------- programs
-def run_layer(workload, windows):
+def run_layer(workload, windows, fused=False):
     import torch
 
     from . import leapq as lq
@@ -54,8 +62,12 @@ def run_layer(workload, windows):
     for w in range(windows):
         for n in range(wl.window):
             q, k, v, a, b = toks[n]
-            lq.leapq_append(L, q, k, v, a, b, o)
-        lq.leapq_fold(L)
+            if fused and n == wl.window - 1:
+                lq.leapq_append_fold(L, q, k, v, a, b, o)
+            else:
+                lq.leapq_append(L, q, k, v, a, b, o)
+        if not fused:
+            lq.leapq_fold(L)
         torch.cuda.synchronize(dev)
         print(f"[profiling] {wl.name} layer 0: window {w + 1}/{windows} done", flush=True)
 
@@ -140,12 +152,13 @@ def main(argv=None):
     r = sub.add_parser("run")
     r.add_argument("--workload", default="b512")
     r.add_argument("--windows", type=int, default=2)
+    r.add_argument("--fused", action="store_true")
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=4)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", default="k_append")
-    t.add_argument("--kernel-src", default="leapq_append.hip")
+    t.add_argument("--kernel-src", nargs="+", default=list(APPEND_SOURCES))
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-kernel", default="neg_kernel")
@@ -158,7 +171,7 @@ def main(argv=None):
     s.add_argument("--csv", required=True)
     a = p.parse_args(argv)
     if a.cmd == "run":
-        run_layer(a.workload, a.windows)
+        run_layer(a.workload, a.windows, a.fused)
     elif a.cmd == "copy":
         run_copy(a.mib, a.reps)
     elif a.cmd == "traffic":
