@@ -50,6 +50,8 @@ def _bind(L):
         "lqo_gdn_step_f64": (None, [f64p, f64p, f64p, f64p, cd, cd, f64p, f64p]),
         "lqo_gdn_step_bf16": (None, [u16p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
         "lqo_f32_to_bf16": (ctypes.c_uint16, [cf]),
+        "lqo_gate": (None, [cf, cf, cf, cf, f32p, f32p]),
+        "lqo_l2norm": (None, [f32p, cf, cf, f32p]),
         "lqo_dim": (ci, []),
     }
     for name, (res, args) in sig.items():
@@ -82,6 +84,35 @@ def t128_sum(f, L=None):
 def t128_dot(a, b, L=None):
     L = L or lib()
     return float(L.lqo_t128_dot(_p(f32(a), ctypes.c_float), _p(f32(b), ctypes.c_float)))
+
+
+def gate(a, b, A_log, dt_bias, L=None):
+    """Decay and step size from the raw gate inputs (fp32 scalars)."""
+    L = L or lib()
+    al, be = ctypes.c_float(), ctypes.c_float()
+    L.lqo_gate(float(np.float32(a)), float(np.float32(b)), float(np.float32(A_log)), float(np.float32(dt_bias)),
+               ctypes.byref(al), ctypes.byref(be))
+    return np.float32(al.value), np.float32(be.value)
+
+
+def l2norm(x, eps=1e-6, scale=1.0, L=None):
+    """(x * (1 / sqrt(T128(x . x) + eps))) * scale in fp32."""
+    L = L or lib()
+    out = np.zeros(D, np.float32)
+    L.lqo_l2norm(_p(f32(x), ctypes.c_float), float(np.float32(eps)), float(np.float32(scale)),
+                 _p(out, ctypes.c_float))
+    return out
+
+
+def gated_inputs(q, k, v, a, b, A_log, dt_bias, q_scale=1.0, eps=1e-6, normalize=True, L=None):
+    """One head's token as the append sees it after the gate arithmetic:
+    (q, k, v, alpha, beta), q and k L2-normalized (q also scaled) when
+    `normalize`."""
+    alpha, beta = gate(a, b, A_log, dt_bias, L)
+    if normalize:
+        q = l2norm(q, eps, q_scale, L)
+        k = l2norm(k, eps, 1.0, L)
+    return f32(q), f32(k), f32(v), alpha, beta
 
 
 class Head:

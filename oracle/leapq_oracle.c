@@ -334,6 +334,38 @@ void lqo_append(const int8_t *Q, const float *rho, const float *sigma, int C,
 }
 
 /* ------------------------------------------------------------------ */
+/* Gate arithmetic: the per-token step in front of the path ([RN4]       */
+/* Results: the column "with gate arithmetic").  The pages name the step */
+/* but print no formula; these are the Gated DeltaNet layer's gates (the */
+/* model family of [LQ] 3.1 and [RN4] Background).  Parity unpinned      */
+/* against the pages: the tests pin them by closed forms instead.        */
+/* ------------------------------------------------------------------ */
+
+/* Decay and step size of one head and token from the raw projections a, b
+ * and the head's parameters A_log, dt_bias:
+ *   alpha = exp(-exp(A_log) * softplus(a + dt_bias)),  beta = 1 / (1 + exp(-b)),
+ * softplus(x) = max(x, 0) + log1p(exp(-|x|)).  Evaluated in binary64 from
+ * the fp32 arguments and rounded once to fp32, so that two correct libm's
+ * agree on the fp32 result except where the binary64 value lies within a
+ * few units of its last place from an fp32 rounding boundary. */
+void lqo_gate(float a, float b, float A_log, float dt_bias, float *alpha, float *beta)
+{
+    double x = (double)a + (double)dt_bias;
+    double sp = fmax(x, 0.0) + log1p(exp(-fabs(x)));
+    *alpha = (float)exp(-exp((double)A_log) * sp);
+    *beta = (float)(1.0 / (1.0 + exp(-(double)b)));
+}
+
+/* L2 normalization of a 128-vector in fp32 with a scale:
+ *   s = T128(x . x),  inv = 1 / sqrt(s + eps),  out_r = (x_r * inv) * scale. */
+void lqo_l2norm(const float *x, float eps, float scale, float *out)
+{
+    float s = lqo_t128_dot(x, x);
+    float inv = 1.0f / sqrtf(s + eps);
+    for (int r = 0; r < D; ++r) out[r] = (x[r] * inv) * scale;
+}
+
+/* ------------------------------------------------------------------ */
 /* Dense per-token GDN recurrences: the brute-force checker of the       */
 /* windowed path and the unquantized quality references.                */
 /* ------------------------------------------------------------------ */

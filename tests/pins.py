@@ -428,10 +428,96 @@ def pin_window_one(L):
         h.fold()
 
 
+def _ulps(a, b):
+    """Distance in fp32 units in the last place (same-sign finite values)."""
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(a - b)
+
+
+def pin_gate_closed_forms(L):
+    """Gate arithmetic against closed forms: softplus(0) = ln 2, so A = 1 and
+    x = 0 give alpha = 1/2 and A = 2 gives 1/4; sigmoid(0) = 1/2 and
+    sigmoid(-b) = 1 - sigmoid(b); large x make softplus(x) = x, very negative
+    x make alpha round to 1; alpha falls as a grows.  Random arguments agree
+    within one ulp with numpy's float64 logaddexp / exp, a different route to
+    the same functions."""
+    assert oracle.gate(0.0, 0.0, 0.0, 0.0, L) == (np.float32(0.5), np.float32(0.5))
+    al, _ = oracle.gate(0.0, 0.0, np.float32(np.log(2.0)), 0.0, L)
+    assert _ulps(al, np.float32(0.25)) <= 1
+    al, _ = oracle.gate(30.0, 0.0, -3.0, 0.0, L)
+    assert _ulps(al, np.float32(np.exp(-np.exp(-3.0) * 30.0))) <= 1
+    al, be = oracle.gate(-40.0, 40.0, 2.0, 0.0, L)
+    assert al == np.float32(1.0) and be == np.float32(1.0)
+    al, _ = oracle.gate(0.5, 0.0, 0.0, -0.5, L)  # dt_bias shifts a
+    assert al == np.float32(0.5)
+    rng = np.random.default_rng(7)
+    prev = 2.0
+    for a in np.linspace(-6, 6, 49, dtype=np.float32):
+        al, _ = oracle.gate(a, 0.0, 0.3, -1.0, L)
+        assert al <= prev
+        prev = al
+    for _ in range(200):
+        a, b, Al, dt = (np.float32(x) for x in rng.normal(0, 3, 4))
+        al, be = oracle.gate(a, b, Al, dt, L)
+        x = np.float64(a) + np.float64(dt)
+        want_a = np.float32(np.exp(-np.exp(np.float64(Al)) * np.logaddexp(0.0, x)))
+        want_b = np.float32(1.0 / (1.0 + np.exp(-np.float64(b))))
+        assert _ulps(al, want_a) <= 1 and _ulps(be, want_b) <= 1, (a, b, Al, dt, al, want_a, be, want_b)
+        _, be_neg = oracle.gate(a, -b, Al, dt, L)
+        assert abs(np.float64(be) + np.float64(be_neg) - 1.0) <= 2.0 ** -23
+
+
+def pin_l2norm(L):
+    """L2 normalization: a power-of-two multiple of a unit vector comes back
+    exactly; random vectors get unit norm to rounding and match x / |x| in
+    float64 within 2 ulp; the scale applies after the normalization (exactly
+    the unscaled result times the scale); eps sits under the root (a vector
+    far below sqrt(eps) is divided by sqrt(eps), the zero vector stays 0)."""
+    e = np.zeros(D, np.float32)
+    e[37] = -8.0
+    out = oracle.l2norm(e, 0.0, 1.0, L)
+    assert out[37] == -1.0 and np.count_nonzero(out) == 1
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 3, D).astype(np.float32)
+    u = oracle.l2norm(x, 0.0, 1.0, L)
+    assert abs(np.linalg.norm(u.astype(np.float64)) - 1.0) < 1e-6
+    want = (x.astype(np.float64) / np.linalg.norm(x.astype(np.float64))).astype(np.float32)
+    assert np.max(_ulps(u, want)) <= 2
+    s = np.float32(128 ** -0.5)
+    assert np.array_equal(oracle.l2norm(x, 1e-6, s, L), oracle.l2norm(x, 1e-6, 1.0, L) * s)
+    tiny = np.full(D, 1e-6, np.float32)
+    got = oracle.l2norm(tiny, 1e-6, 1.0, L)
+    assert rel(got, tiny.astype(np.float64) / np.sqrt(1e-6 + 128e-12)) < 1e-5
+    assert not np.any(oracle.l2norm(np.zeros(D, np.float32), 1e-6, 1.0, L))
+
+
+def pin_gated_window(L):
+    """A window driven through the gate arithmetic equals the dense float64
+    recurrence on the same gated inputs (normalized in float64) to 1e-5."""
+    rng = np.random.default_rng(21)
+    S0 = (rng.normal(0, 0.02, (D, D))).astype(np.float32)
+    h = oracle.Head(C=4, W=16, L=L).init(S0)
+    S = h.dequant(1).astype(np.float64)
+    A_log, dt_bias = np.float32(np.log(4.0)), np.float32(-4.0)
+    for t in range(16):
+        q, k, v = (rng.normal(0, 1, D).astype(np.float32) for _ in range(3))
+        a, b = (np.float32(x) for x in rng.normal(0, 1, 2))
+        gq, gk, gv, al, be = oracle.gated_inputs(q, k, v, a, b, A_log, dt_bias, q_scale=0.125, L=L)
+        o, _ = h.append(gq, gk, gv, al, be)
+        q64 = q.astype(np.float64) / np.sqrt(np.sum(q.astype(np.float64) ** 2) + 1e-6) * 0.125
+        k64 = k.astype(np.float64) / np.sqrt(np.sum(k.astype(np.float64) ** 2) + 1e-6)
+        x = np.float64(a) + np.float64(dt_bias)
+        al64 = np.exp(-np.exp(np.float64(A_log)) * np.logaddexp(0.0, x))
+        be64 = 1.0 / (1.0 + np.exp(-np.float64(b)))
+        _, o64 = np_gdn_f64(S, q64, k64, v.astype(np.float64), al64, be64)
+        assert rel(o, o64) < 1e-5, (t, rel(o, o64))
+
+
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
     pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
-    pin_tiny_rows, pin_dense_steps, pin_window_one,
+    pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
 ]

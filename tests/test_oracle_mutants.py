@@ -47,6 +47,13 @@ MUTANTS = [
      "    float u[D];"),
     ("step_read_output_with_k", "oc = fmaf(S[r * D + c], q[r], oc);", "oc = fmaf(S[r * D + c], k[r], oc);"),
     ("bf16_truncate", "b += 0x7fffu + lsb;", "b += 0u * lsb;"),
+    ("gate_softplus_sign", "log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
+    ("gate_rate_not_exponentiated", "exp(-exp((double)A_log) * sp)", "exp(-(double)A_log * sp)"),
+    ("gate_drop_dt_bias", "double x = (double)a + (double)dt_bias;", "double x = (double)a;"),
+    ("gate_beta_sign", "exp(-(double)b)", "exp((double)b)"),
+    ("l2norm_no_sqrt", "1.0f / sqrtf(s + eps)", "1.0f / (s + eps)"),
+    ("l2norm_eps_outside_root", "sqrtf(s + eps)", "(sqrtf(s) + eps)"),
+    ("l2norm_scale_folded", "(x[r] * inv) * scale", "x[r] * (inv * scale)"),
 ]
 
 
