@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--workload", default="b512")
     p.add_argument("--no-baselines", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-gated", action="store_true",
+                   help="skip the gated-path measurement (gate arithmetic and q/k normalization in the append)")
     p.add_argument("--baseline-tokens", type=int, default=16)
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--separate", action="store_true",
@@ -175,8 +177,12 @@ def main():
     # fused schedule: the fold's cost is what the fused launch adds to the
     # window's last append
     share = share_sep
-    if fused and fused_us is not None:
-        share = (fused_us - app_us[W - 1]) / (sum(app_us[p] for p in range(W - 1)) + fused_us)
+    if fused and fused_us is not None and W >= 3:
+        # the plain append at the last position, extrapolated from positions
+        # 0..W-2: the measured one follows the previous layer's fold and
+        # carries part of that fold's write-back
+        last_app = float(np.polyval(np.polyfit(np.arange(W - 1), [app_us[p] for p in range(W - 1)], 1), W - 1))
+        share = (fused_us - last_app) / (sum(app_us[p] for p in range(W - 1)) + fused_us)
     window_bytes = metrics.window_bytes(W, C, in_bytes) * H * Lyr
     path_gbps = window_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"[bench] append {append_us:.1f} us ({append_gbps:.0f} GB/s algorithmic), fold {fold_us:.1f} us "
@@ -189,6 +195,65 @@ def main():
             tr = json.load(f)
         if tr.get("kernel_sha") == kernel_sha() and tr.get("workload") == wl.name:
             traffic = tr.get("bytes_per_launch")
+
+    # ---- the gated path: raw projections in, gate arithmetic and q / k
+    # normalization in the append (fp32 record keys), same schedule
+    gated = None
+    if not args.no_gated:
+        gcfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, qk_norm=True)
+        glayers, gpool, gates = [], [], []
+        for l in range(Lyr):
+            L = lq.Layer(gcfg, dev)
+            S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
+            lq.leapq_init_state(L, S0)
+            del S0
+            glayers.append(L)
+            gates.append(lq.Gate(*workloads.gate_params(wl, l, device=dev)))
+            toks = []
+            for pos in range(W):
+                q, k, v, a, b = workloads.gated_token_inputs(wl, l, pos, device=dev)
+                toks.append((q.reshape(H, D), k.reshape(H, D), v.reshape(H, D), a.reshape(H), b.reshape(H)))
+            gpool.append(toks)
+
+        def gwindow(ev=None):
+            for pos in range(W):
+                for l in range(Lyr):
+                    q, k, v, a, b = gpool[l][pos]
+                    if ev is not None:
+                        ev.append((pos, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                        ev[-1][1].record(stream)
+                    if glayers[l].n_records == W - 1:
+                        lq.leapq_append_fold_gated(glayers[l], gates[l], q, k, v, a, b, outs[l], stream)
+                    else:
+                        lq.leapq_append_gated(glayers[l], gates[l], q, k, v, a, b, outs[l], stream)
+                    if ev is not None:
+                        ev[-1][2].record(stream)
+
+        gwindow()
+        torch.cuda.synchronize(dev)
+        gsteps = max(4, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(gsteps):
+            gwindow()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        g_ms = e0.elapsed_time(e1) / gsteps
+        gev = []
+        gwindow(gev)
+        torch.cuda.synchronize(dev)
+        g_app = [1e3 * e0_.elapsed_time(e1_) for pos, e0_, e1_ in gev if pos < W - 1]
+        g_fused = [1e3 * e0_.elapsed_time(e1_) for pos, e0_, e1_ in gev if pos == W - 1]
+        gated = {"tokens_per_s": B * W / (g_ms / 1e3), "ms_per_step": g_ms, "steps": gsteps,
+                 "ratio_to_plain": (B * W / (g_ms / 1e3)) / tokens_per_s,
+                 "append_us": float(np.mean(g_app)), "append_fold_us": float(np.mean(g_fused)),
+                 "inputs": "raw bf16 q/k/v and fp32 gate projections a, b; alpha, beta from A_log, dt_bias; "
+                           "q, k L2-normalized in the append; fp32 record keys"}
+        log(f"[bench] gated path: {g_ms:.3f} ms per window, {gated['tokens_per_s']:,.0f} tokens/s "
+            f"({gated['ratio_to_plain']:.3f} of the plain path); append {gated['append_us']:.1f} us "
+            f"(positions 0..{W - 2}), last append + fold {gated['append_fold_us']:.1f} us")
+        del glayers, gpool, gates
+        torch.cuda.empty_cache()
 
     # ---- baselines at the same shape: dense fp32-state and bf16-state decode
     baselines = None
@@ -259,6 +324,7 @@ def main():
                      "traffic": traffic,
                      "bytes_per_launch_algorithmic": app_bytes_avg},
         "fold_roofline": {"bound": "alu", "achieved_gbps_algorithmic": fold_gbps},
+        "gated": gated,
         "baselines": baselines,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),

@@ -47,8 +47,9 @@ extern "C" {
 #define LEAPQ_ERR_NULL (-1)        /* a required pointer is NULL */
 #define LEAPQ_ERR_SHAPE (-2)       /* dk or dv is not 128 */
 #define LEAPQ_ERR_RANGE (-3)       /* batch/heads < 1, window not in [1,64], n_comp not in [0,8],
-                                      smoothing not 0/1, sigma_floor not > 0, what not in {0,1,2},
-                                      heads*batch too large, n_records out of [0, window] */
+                                      smoothing or qk_norm not 0/1, sigma_floor not > 0, what not
+                                      in {0,1,2}, heads*batch too large, n_records out of
+                                      [0, window], reserved fields not zero */
 #define LEAPQ_ERR_ALIGN (-4)       /* state not 256-byte aligned, or a tensor not 16-byte aligned */
 #define LEAPQ_ERR_WINDOW_FULL (-5) /* append with n_records == window: fold first */
 #define LEAPQ_ERR_DTYPE (-6)       /* in_dtype / state_dtype not LEAPQ_F32 or LEAPQ_BF16 */
@@ -72,7 +73,8 @@ typedef struct leapq_config {
     int32_t smoothing;   /* 1: per-column residual smoothing; 0: sigma = 1 */
     float sigma_floor;   /* positive floor of the smoothing scale (1e-6) */
     int32_t in_dtype;    /* LEAPQ_F32 or LEAPQ_BF16 for q, k, v */
-    int32_t reserved[3]; /* must be zero */
+    int32_t qk_norm;     /* 1: the gated appends L2-normalize q and k (record keys are then fp32); 0 or 1 */
+    int32_t reserved[2]; /* must be zero */
 } leapq_config;
 
 /* Byte layout of one layer's state buffer.  Sections are "structure of
@@ -89,10 +91,11 @@ typedef struct leapq_config {
  *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
  *                                      over r for a column), natural order
  *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
- *   rec_k     in_dtype [heads][W][128] record keys in key-row order, in the
- *                                      input dtype: a record's key is the
+ *   rec_k     e     [heads][W][128]    record keys in key-row order, in the
+ *                                      input dtype (a record's key is the
  *                                      token's k as given, so bf16 storage
- *                                      of bf16 inputs is exact
+ *                                      of bf16 inputs is exact), or fp32
+ *                                      when qk_norm = 1
  *   rec_u     fp32  [heads][W][128]    record corrections; value column c is
  *                                      stored at 32 (c % 4) + 8 (c / 32)
  *                                      + 4 ((c / 4) % 2) + (c / 8) % 4
@@ -101,7 +104,7 @@ typedef struct leapq_config {
  * corrections are the A operand order of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
  * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 128 e + 512)
- * with e = 4 (fp32 inputs) or 2 (bf16 inputs). */
+ * with e = 2 for bf16 inputs and qk_norm = 0, else 4. */
 typedef struct leapq_layout {
     uint64_t total_bytes;
     uint64_t off_codes, off_row_scale, off_col_scale, off_comp_idx, off_comp_vec;
@@ -154,6 +157,40 @@ int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const voi
  * n_records := 0. */
 int32_t leapq_append_fold(leapq_layer *layer, const void *q, const void *k, const void *v,
                           const float *alpha, const float *beta, float *o, void *stream);
+
+/* Gate arithmetic in front of the append: the decay and step size are
+ * computed from the layer's raw projections per head and token, and q, k
+ * are L2-normalized when the layer has qk_norm = 1 ("Recurrent-state
+ * quantization for linear attention: a first GPU kernel", Results: the
+ * column with gate arithmetic; the pages give no formula, these are the
+ * Gated DeltaNet layer's gates):
+ *   alpha = exp(-exp(A_log[j]) * softplus(a + dt_bias[j])),  beta = 1 / (1 + exp(-b)),
+ *   softplus(x) = max(x, 0) + log1p(exp(-|x|)), evaluated in binary64 from the
+ *   fp32 arguments and rounded once to fp32 (j = head index within a request);
+ *   k <- k * (1 / sqrt(k . k + norm_eps)),
+ *   q <- (q * (1 / sqrt(q . q + norm_eps))) * q_scale, in fp32 with the
+ *   canonical 128-term dot. */
+typedef struct leapq_gate {
+    const float *A_log;   /* [cfg.heads] fp32 (device), per model head, shared by the batch */
+    const float *dt_bias; /* [cfg.heads] fp32 (device) */
+    float q_scale;        /* multiplies the normalized query (used when qk_norm = 1), e.g. 128^-1/2 */
+    float norm_eps;       /* >= 0, added under the root of the L2 norm (used when qk_norm = 1) */
+    int32_t reserved[2];  /* must be zero */
+} leapq_gate;
+
+/* leapq_append with the gate arithmetic fused in front: a, b [heads] fp32
+ * (device) are the raw decay and step-size projections of this token, and q,
+ * k are the raw projections (normalized in the kernel when qk_norm = 1).
+ * Everything else, including the record written and the output, is as for
+ * leapq_append with the gated alpha, beta, q and k.  gate must not be NULL
+ * (LEAPQ_ERR_NULL), its pointers 4-byte aligned (LEAPQ_ERR_ALIGN), norm_eps
+ * finite and >= 0, q_scale finite and reserved zero (LEAPQ_ERR_RANGE). */
+int32_t leapq_append_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
+                           const void *v, const float *a, const float *b, float *o, void *stream);
+
+/* leapq_append_fold with the gate arithmetic of leapq_append_gated. */
+int32_t leapq_append_fold_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
+                                const void *v, const float *a, const float *b, float *o, void *stream);
 
 /* Closes the window ("Recurrent-state quantization for linear attention: a
  * first GPU kernel", What we built: rebuild, select compensators, rescale,

@@ -37,15 +37,20 @@ int32_t check_method_config(const leapq_config *c)
     if (c->n_comp < 0 || c->n_comp > 8) return LEAPQ_ERR_RANGE;
     if (c->smoothing != 0 && c->smoothing != 1) return LEAPQ_ERR_RANGE;
     if (!(c->sigma_floor > 0.0f) || c->sigma_floor > 3.0e38f) return LEAPQ_ERR_RANGE;
-    if (c->reserved[0] || c->reserved[1] || c->reserved[2]) return LEAPQ_ERR_RANGE;
+    if (c->qk_norm != 0 && c->qk_norm != 1) return LEAPQ_ERR_RANGE;
+    if (c->reserved[0] || c->reserved[1]) return LEAPQ_ERR_RANGE;
     return LEAPQ_OK;
 }
+
+// Record keys are stored in the input dtype, which holds the token's k
+// exactly, unless the layer's gated appends normalize k (then fp32).
+bool key_bf16(const leapq_config *c) { return c->in_dtype == LEAPQ_BF16 && !c->qk_norm; }
 
 void compute_layout(const leapq_config *c, leapq_layout *L)
 {
     const uint64_t H = (uint64_t)c->batch * (uint64_t)c->heads;
     const uint64_t C = (uint64_t)c->n_comp, W = (uint64_t)c->window;
-    const uint64_t kb = c->in_dtype == LEAPQ_BF16 ? 2 : 4;  // record key element
+    const uint64_t kb = key_bf16(c) ? 2 : 4;  // record key element
     uint64_t off = 0;
     L->off_codes = off;
     off = round_up(off + H * kD * kD);
@@ -89,7 +94,7 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->ru = (float *)(b + L.off_rec_u);
     sv->C = layer->cfg.n_comp;
     sv->W = layer->cfg.window;
-    sv->key_bf16 = layer->cfg.in_dtype == LEAPQ_BF16;
+    sv->key_bf16 = key_bf16(&layer->cfg);
     return LEAPQ_OK;
 }
 
@@ -123,49 +128,103 @@ int32_t leapq_init_state(leapq_layer *layer, const float *S0, void *stream)
     return st;
 }
 
-int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const void *v, const float *alpha,
-                     const float *beta, float *o, void *stream)
+}  // extern "C"
+
+namespace {
+
+leapq::GateArgs plain_gate(const leapq_config &c) { return {nullptr, nullptr, 1.0f, 0.0f, c.heads, 0, 0}; }
+
+int32_t gate_of(const leapq_layer *layer, const leapq_gate *g, leapq::GateArgs *out)
+{
+    if (!g || !g->A_log || !g->dt_bias) return LEAPQ_ERR_NULL;
+    if (!aligned(g->A_log, 4) || !aligned(g->dt_bias, 4)) return LEAPQ_ERR_ALIGN;
+    if (g->reserved[0] || g->reserved[1]) return LEAPQ_ERR_RANGE;
+    if (!(g->norm_eps >= 0.0f) || g->norm_eps > 3.0e38f) return LEAPQ_ERR_RANGE;
+    if (!(g->q_scale == g->q_scale) || g->q_scale > 3.0e38f || g->q_scale < -3.0e38f) return LEAPQ_ERR_RANGE;
+    *out = {g->A_log, g->dt_bias, g->q_scale, g->norm_eps, layer->cfg.heads, 1, layer->cfg.qk_norm};
+    return LEAPQ_OK;
+}
+
+int32_t check_token(const void *q, const void *k, const void *v, const float *a, const float *b, const float *o)
+{
+    if (!q || !k || !v || !a || !b || !o) return LEAPQ_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(a, 4) ||
+        !aligned(b, 4))
+        return LEAPQ_ERR_ALIGN;
+    return LEAPQ_OK;
+}
+
+int32_t append_impl(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k, const void *v,
+                    const float *alpha, const float *beta, float *o, void *stream)
 {
     leapq::StateView sv;
     int32_t st = view_of(layer, &sv);
     if (st != LEAPQ_OK) return st;
-    if (!q || !k || !v || !alpha || !beta || !o) return LEAPQ_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 4) ||
-        !aligned(beta, 4))
-        return LEAPQ_ERR_ALIGN;
+    leapq::GateArgs g = plain_gate(layer->cfg);
+    if (gate && (st = gate_of(layer, gate, &g)) != LEAPQ_OK) return st;
+    if ((st = check_token(q, k, v, alpha, beta, o)) != LEAPQ_OK) return st;
     if (layer->n_records >= layer->cfg.window) return LEAPQ_ERR_WINDOW_FULL;
     st = hip_status(leapq::launch_append(sv, heads_of(&layer->cfg), layer->n_records,
-                                         layer->cfg.in_dtype == LEAPQ_BF16, q, k, v, alpha, beta, o,
+                                         layer->cfg.in_dtype == LEAPQ_BF16, q, k, v, alpha, beta, o, g,
                                          (hipStream_t)stream));
     if (st == LEAPQ_OK) layer->n_records += 1;
     return st;
 }
 
-int32_t leapq_append_fold(leapq_layer *layer, const void *q, const void *k, const void *v, const float *alpha,
-                          const float *beta, float *o, void *stream)
+int32_t append_fold_impl(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta, float *o, void *stream)
 {
     leapq::StateView sv;
     int32_t st = view_of(layer, &sv);
     if (st != LEAPQ_OK) return st;
-    if (!q || !k || !v || !alpha || !beta || !o) return LEAPQ_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(alpha, 4) ||
-        !aligned(beta, 4))
-        return LEAPQ_ERR_ALIGN;
+    leapq::GateArgs g = plain_gate(layer->cfg);
+    if (gate && (st = gate_of(layer, gate, &g)) != LEAPQ_OK) return st;
+    if ((st = check_token(q, k, v, alpha, beta, o)) != LEAPQ_OK) return st;
     if (layer->n_records != layer->cfg.window - 1) return LEAPQ_ERR_RANGE;
     const int heads = heads_of(&layer->cfg);
     const int bf16 = layer->cfg.in_dtype == LEAPQ_BF16;
     hipStream_t s = (hipStream_t)stream;
     if (layer->cfg.window <= 16) {
         st = hip_status(leapq::launch_append_fold(sv, heads, layer->n_records, bf16, q, k, v, alpha, beta, o,
-                                                  layer->cfg.smoothing, layer->cfg.sigma_floor, s));
+                                                  layer->cfg.smoothing, layer->cfg.sigma_floor, g, s));
     } else {
-        st = hip_status(leapq::launch_append(sv, heads, layer->n_records, bf16, q, k, v, alpha, beta, o, s));
+        st = hip_status(leapq::launch_append(sv, heads, layer->n_records, bf16, q, k, v, alpha, beta, o, g, s));
         if (st == LEAPQ_OK)
             st = hip_status(leapq::launch_fold(sv, heads, layer->n_records + 1, layer->cfg.smoothing,
                                                layer->cfg.sigma_floor, s));
     }
     if (st == LEAPQ_OK) layer->n_records = 0;
     return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const void *v, const float *alpha,
+                     const float *beta, float *o, void *stream)
+{
+    return append_impl(layer, nullptr, q, k, v, alpha, beta, o, stream);
+}
+
+int32_t leapq_append_fold(leapq_layer *layer, const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, float *o, void *stream)
+{
+    return append_fold_impl(layer, nullptr, q, k, v, alpha, beta, o, stream);
+}
+
+int32_t leapq_append_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k, const void *v,
+                           const float *a, const float *b, float *o, void *stream)
+{
+    if (!gate) return LEAPQ_ERR_NULL;
+    return append_impl(layer, gate, q, k, v, a, b, o, stream);
+}
+
+int32_t leapq_append_fold_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
+                                const void *v, const float *a, const float *b, float *o, void *stream)
+{
+    if (!gate) return LEAPQ_ERR_NULL;
+    return append_fold_impl(layer, gate, q, k, v, a, b, o, stream);
 }
 
 int32_t leapq_fold(leapq_layer *layer, void *stream)

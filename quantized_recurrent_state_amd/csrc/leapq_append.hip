@@ -31,44 +31,68 @@ namespace leapq {
 namespace {
 using namespace dev;
 
-template <typename T>
+template <typename T, typename K, bool GATED, bool NORM>
 __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__restrict__ qin,
                                                 const T *__restrict__ kin, const T *__restrict__ vin,
                                                 const float *__restrict__ alpha, const float *__restrict__ beta,
-                                                float *__restrict__ o)
+                                                float *__restrict__ o, GateArgs g)
 {
     extern __shared__ float dsm[];
     const MMap a = mmap();
     const int h = blockIdx.x;
-    const HeadLds<T> L(dsm, n, sv.C);
-    float *dots = dsm + head_lds_floats<T>(n, sv.C);
+    const HeadLds<T, K> L(dsm, n, sv.C);
+    float *dots = dsm + head_lds_floats<T, K>(n, sv.C);
     uint4 qc[4];
-    append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
-    const float a_h = alpha[h];
-    const float b_h = beta[h];
+    append_issue<T, K>(sv, n, h, qin, kin, vin, a, L, qc);
+    float a_h = sload(alpha, h);
+    float b_h = sload(beta, h);
+    if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
     wait_lds_copies();
     lds_barrier();
-    append_compute<T>(sv, n, h, a, L, dots, qc, a_h, b_h, o);
+    if constexpr (GATED) {
+        a_h = dots[kGateSlot];
+        b_h = dots[kGateSlot + 1];
+    }
+    append_compute<T, K, false, NORM>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
 }
 
 }  // namespace
 
-template <typename T>
+template <typename T, typename K, bool GATED, bool NORM>
 static void launch_append_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
-                            const float *alpha, const float *beta, float *o, hipStream_t s)
+                            const float *alpha, const float *beta, float *o, const GateArgs &g, hipStream_t s)
 {
-    const size_t lds = sizeof(float) * (head_lds_floats<T>(n, sv.C) + kDotFloats);
-    hipLaunchKernelGGL(k_append<T>, dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
-                       (const T *)v, alpha, beta, o);
+    const size_t lds = sizeof(float) * (head_lds_floats<T, K>(n, sv.C) + kDotFloats);
+    hipLaunchKernelGGL((k_append<T, K, GATED, NORM>), dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
+                       (const T *)v, alpha, beta, o, g);
 }
 
 hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
-                         const void *v, const float *alpha, const float *beta, float *o, hipStream_t s)
+                         const void *v, const float *alpha, const float *beta, float *o, const GateArgs &g,
+                         hipStream_t s)
 {
-    if (bf16)
-        launch_append_t<uint16_t>(sv, heads, n, q, k, v, alpha, beta, o, s);
-    else
-        launch_append_t<float>(sv, heads, n, q, k, v, alpha, beta, o, s);
+    // (inputs, keys): (fp32, fp32), (bf16, bf16), or (bf16, fp32) for a layer
+    // whose keys are fp32 because its gated appends normalize k
+    const bool kb = sv.key_bf16;
+    if (!g.gated) {
+        if (!bf16)
+            launch_append_t<float, float, false, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+        else if (kb)
+            launch_append_t<uint16_t, uint16_t, false, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+        else
+            launch_append_t<uint16_t, float, false, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+    } else if (!bf16) {
+        if (g.normalize)
+            launch_append_t<float, float, true, true>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+        else
+            launch_append_t<float, float, true, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+    } else if (kb) {
+        launch_append_t<uint16_t, uint16_t, true, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+    } else if (g.normalize) {
+        launch_append_t<uint16_t, float, true, true>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+    } else {
+        launch_append_t<uint16_t, float, true, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+    }
     return hipGetLastError();
 }
 

@@ -3,6 +3,8 @@
 // leapq_append.hip for the method and its sources.
 #pragma once
 
+#include <type_traits>
+
 #include "leapq_device.h"
 
 namespace leapq {
@@ -25,9 +27,10 @@ struct InLds<uint16_t> {
     }
 };
 
-// A record as stored and as staged in LDS: the key in the input dtype T (row
-// order, exact: the append's key is an input), then the correction (fp32,
-// stored order); keys take kbytes, a staged record stride floats.
+// A record as stored and as staged in LDS: the key in dtype T (row order;
+// the input dtype stores the token's k exactly unless the append normalizes
+// it, which needs fp32), then the correction (fp32, stored order); keys take
+// kbytes, a staged record stride floats.
 template <typename T>
 struct Rec {
     static constexpr int kbytes = D * (int)sizeof(T);
@@ -49,18 +52,19 @@ __device__ __forceinline__ void copy_record(const HeadState &hs, int g, int l, f
                    dst);
 }
 
-// LDS of one head in floats: records [n][stride], lines [C][128], rho [128],
-// sigma [128], inputs (k, q, v), indices [8], decays [64]
-template <typename T>
+// LDS of one head in floats: records [n][stride] (keys K), lines [C][128],
+// rho [128], sigma [128], inputs (k, q, v as T), indices [8], decays [64]
+template <typename T, typename K>
 __host__ __device__ constexpr int head_lds_floats(int n, int C)
 {
-    return n * Rec<T>::stride + C * 128 + 256 + InLds<T>::floats + 8 + 64;
+    return n * Rec<K>::stride + C * 128 + 256 + InLds<T>::floats + 8 + 64;
 }
 // per-workgroup results of the dot jobs: coefficients [2][64], column-token
-// dots [2][8], k.q [1] (+3 pad)
+// dots [2][8], k.q [1], then the gated alpha and beta [2] (+1 pad)
 constexpr int kDotFloats = 128 + 16 + 4;
+constexpr int kGateSlot = 145;
 
-template <typename T>
+template <typename T, typename K>
 struct HeadLds {
     float *rec, *cv, *srho, *ssig, *sin_, *sgam;
     int *sidx;
@@ -71,7 +75,7 @@ struct HeadLds {
     __device__ HeadLds(float *base, int n, int C)
     {
         rec = base;
-        cv = rec + n * Rec<T>::stride;
+        cv = rec + n * Rec<K>::stride;
         srho = cv + C * D;
         ssig = srho + D;
         sin_ = ssig + D;
@@ -94,14 +98,14 @@ __device__ __forceinline__ void wait_lds_copies()
 // Issues every global load of head h: every operand other than the codes
 // into the LDS buffer L by LDS-direct copies, then the thread's 64 codes into
 // qc as the wave's last kCodeLoads vector loads.
-template <typename T>
+template <typename T, typename K>
 __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
                                              const T *__restrict__ kin, const T *__restrict__ vin,
-                                             const MMap &a, const HeadLds<T> &L, uint4 (&qc)[4])
+                                             const MMap &a, const HeadLds<T, K> &L, uint4 (&qc)[4])
 {
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
-    for (int rr = w; rr < n; rr += 4) copy_record<T>(hs, rr, l, L.rec + rr * Rec<T>::stride);
+    for (int rr = w; rr < n; rr += 4) copy_record<K>(hs, rr, l, L.rec + rr * Rec<K>::stride);
     for (int pair = 2 * w; pair < C; pair += 8)
         if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
     if (w == 0) {
@@ -131,14 +135,48 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Gate arithmetic of one head and token, in binary64 from the fp32
+// arguments and rounded once to fp32: alpha = exp(-exp(A_log) softplus(a +
+// dt_bias)) with softplus(x) = max(x, 0) + log1p(exp(-|x|)), beta =
+// 1 / (1 + exp(-b)).  The pages time this step ("Recurrent-state
+// quantization for linear attention: a first GPU kernel", Results: the
+// column with gate arithmetic) without printing it; these are the gates of
+// the Gated DeltaNet layer.
+__device__ __forceinline__ void gate_eval(float a, float b, float A_log, float dt_bias, float &alpha, float &beta)
+{
+    const double x = (double)a + (double)dt_bias;
+    const double sp = fmax(x, 0.0) + log1p(exp(-fabs(x)));
+    alpha = (float)exp(-exp((double)A_log) * sp);
+    beta = (float)(1.0 / (1.0 + exp(-(double)b)));
+}
+
+// The gates of head h by wave 0 alone, while the loads are in flight, into
+// dots[kGateSlot..+1]; every wave reads them back after the next barrier
+// (gate_read).  a_h, b_h: the raw projections.
+__device__ __forceinline__ void gate_issue(const GateArgs &g, int h, const MMap &a, float a_h, float b_h, float *dots)
+{
+    if (a.w == 0) {
+        const int j = h % g.heads;
+        float al, be;
+        gate_eval(a_h, b_h, sload(g.A_log, j), sload(g.dt_bias, j), al, be);
+        if (a.l == 0) {
+            dots[kGateSlot] = al;
+            dots[kGateSlot + 1] = be;
+        }
+    }
+}
+
 // The token for head h from its staged operands (L, qc); writes o and the
-// record.  Expects the LDS copies landed and visible (wait_lds_copies() and a
+// record.  NORM: q and k are L2-normalized first, k_r * (1 / sqrt(k . k +
+// eps)) and (q_r * (1 / sqrt(q . q + eps))) * q_scale, with the canonical
+// dot (the record key is then the normalized k in fp32).  Expects the LDS copies landed and visible (wait_lds_copies() and a
 // barrier); the codes are waited for at their first use.  Contains one
 // lds_barrier (dot jobs -> residual read and tail).
-template <typename T, bool REC_LDS = false>
-__device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a, const HeadLds<T> &L,
-                                               float *dots, const uint4 (&qc)[4], float a_h, float b_h,
-                                               float *__restrict__ o)
+template <typename T, typename K, bool REC_LDS = false, bool NORM = false>
+__device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a,
+                                               const HeadLds<T, K> &L, float *dots, const uint4 (&qc)[4], float a_h,
+                                               float b_h, float *__restrict__ o, float q_scale = 1.0f,
+                                               float eps = 0.0f)
 {
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
@@ -149,15 +187,26 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     // vec = bit 4 of l (0: k, 1: q) of column w + 4h + 8 (l & 15)
     const int vec = (l >> 4) & 1;
     const int c = a.col(l & 15);
+    float kn = 1.0f, qn = 1.0f;  // normalization factors (NORM)
+    float k0 = InLds<T>::get(sin_, 0, l), k1 = InLds<T>::get(sin_, 0, l + 64);
+    float q0 = InLds<T>::get(sin_, 1, l), q1 = InLds<T>::get(sin_, 1, l + 64);
+    if constexpr (NORM) {
+        kn = 1.0f / sqrtf(wdot(k0, k1, k0, k1) + eps);
+        qn = 1.0f / sqrtf(wdot(q0, q1, q0, q1) + eps);
+    }
+    auto nk = [&](float x) { return NORM ? x * kn : x; };
+    auto nq = [&](float x) { return NORM ? (x * qn) * q_scale : x; };
+    k0 = nk(k0);
+    k1 = nk(k1);
+    q0 = nq(q0);
+    q1 = nq(q1);
     float rh[4], kr[4], qr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         rh[p] = srho[a.row(p)];
-        kr[p] = InLds<T>::get(sin_, 0, a.row(p));
-        qr[p] = InLds<T>::get(sin_, 1, a.row(p));
+        kr[p] = nk(InLds<T>::get(sin_, 0, a.row(p)));
+        qr[p] = nq(InLds<T>::get(sin_, 1, a.row(p)));
     }
-    const float k0 = InLds<T>::get(sin_, 0, l), k1 = InLds<T>::get(sin_, 0, l + 64);
-    const float q0 = InLds<T>::get(sin_, 1, l), q1 = InLds<T>::get(sin_, 1, l + 64);
     const float sig_c = ssig[c];
     const float v_c = InLds<T>::get(sin_, 2, c);
     const float gt = (n > 0 ? sgam[n - 1] : 1.0f) * a_h;
@@ -170,8 +219,8 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     const int njobs = n + 1 + C;
     for (int job = w; job < njobs; job += 4) {
         if (job < n) {
-            const float *kj = rec + job * Rec<T>::stride;
-            const float a0 = Rec<T>::key(kj, l), a1 = Rec<T>::key(kj, l + 64);
+            const float *kj = rec + job * Rec<K>::stride;
+            const float a0 = Rec<K>::key(kj, l), a1 = Rec<K>::key(kj, l + 64);
             const float dk = wdot(a0, a1, k0, k1);
             const float dq = wdot(a0, a1, q0, q1);
             const float ci = rdl(ci_l, job);
@@ -240,22 +289,24 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     for (int jj = 0; jj < C; ++jj) {
         const int id = sidx[jj];
         if (id < 0) continue;
-        if (id < D)
-            b = fma_(InLds<T>::get(sin_, vec, id), cv[jj * D + c], b);
+        if (id < D) {
+            const float x = InLds<T>::get(sin_, vec, id);
+            b = fma_(vec ? nq(x) : nk(x), cv[jj * D + c], b);
+        }
         else if (id - D == c)
             b = b + cdot[vec * 8 + jj];
     }
     float acc = gt * b;
     const int uc = upos(c);
-    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * Rec<T>::stride + Rec<T>::kf + uc], acc);
+    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * Rec<K>::stride + Rec<K>::kf + uc], acc);
     // k lanes form u; q lanes receive it from lane l-16 and finish o
     const float u = b_h * (v_c - acc);
     auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
     const float u_from_k = __uint_as_float(sw[0]);
     // the record goes to HBM, or (REC_LDS) into slot n of the staged records
-    float *ru = REC_LDS ? L.rec + n * Rec<T>::stride + Rec<T>::kf : hs.ru + n * D;
-    uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * Rec<T>::stride)
-                           : reinterpret_cast<uint32_t *>(hs.rk + n * Rec<T>::kbytes);
+    float *ru = REC_LDS ? L.rec + n * Rec<K>::stride + Rec<K>::kf : hs.ru + n * D;
+    uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * Rec<K>::stride)
+                           : reinterpret_cast<uint32_t *>(hs.rk + n * Rec<K>::kbytes);
     float *rg = REC_LDS ? L.sgam : hs.rgam;
     if (vec == 0) {
         ru[uc] = u;
@@ -263,10 +314,16 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
         o[(size_t)h * D + c] = fma_(kqd[0], u_from_k, acc);
     }
     if (w == 0) {
-        // the key is the token's k as staged (the first kbytes of the inputs)
-        const uint32_t *kw = reinterpret_cast<const uint32_t *>(sin_);
-        rk[l] = kw[l];
-        if (Rec<T>::kf > 64) rk[l + 64] = kw[l + 64];
+        if constexpr (std::is_same<K, T>::value && !NORM) {
+            // the key is the token's k as staged (the first kbytes of the inputs)
+            const uint32_t *kw = reinterpret_cast<const uint32_t *>(sin_);
+            rk[l] = kw[l];
+            if (Rec<K>::kf > 64) rk[l + 64] = kw[l + 64];
+        } else {
+            static_assert(std::is_same<K, float>::value, "normalized or widened keys are fp32");
+            rk[l] = __float_as_uint(k0);
+            rk[l + 64] = __float_as_uint(k1);
+        }
         if (l == 0) rg[n] = gt;
     }
 }

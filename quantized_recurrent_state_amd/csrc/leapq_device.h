@@ -329,6 +329,15 @@ __device__ __forceinline__ void lds_copy4(const void *g, void *lds)
 {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
 }
+// A read-only fp32 value at a wave-uniform index, as a scalar load (constant
+// address space): waited for by lgkmcnt, so it does not wait behind the
+// wave's vector loads.
+__device__ __forceinline__ float sload(const float *p, int i)
+{
+    typedef const __attribute__((address_space(4))) float *cptr;
+    return ((cptr)(uintptr_t)p)[i];
+}
+
 __device__ __forceinline__ float rdl(float x, int lane)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(x), lane));

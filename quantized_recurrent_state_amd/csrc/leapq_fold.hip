@@ -474,12 +474,12 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
 // empties the buffer), and the fold rebuilds from the same registers and LDS
 // instead of reading the boundary and the records again.  The results are
 // those of leapq_append followed by leapq_fold.
-template <typename T, int CT>
+template <typename T, typename K, bool GATED, bool NORM, int CT>
 __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
                                                      const T *__restrict__ kin, const T *__restrict__ vin,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ beta, float *__restrict__ o,
-                                                     int smoothing, float floor_)
+                                                     int smoothing, float floor_, GateArgs g)
 {
     __shared__ FoldStage st;
     __shared__ float sin_[InLds<T>::floats];
@@ -487,18 +487,23 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     __shared__ FoldWork wk;
     const MMap a = mmap();
     const int h = blockIdx.x;
-    const HeadLds<T> L(st.rec, st.lines, st.rho, sin_, st.idx, st.gam);
+    const HeadLds<T, K> L(st.rec, st.lines, st.rho, sin_, st.idx, st.gam);
     uint4 qc[4];
-    append_issue<T>(sv, n, h, qin, kin, vin, a, L, qc);
-    const float a_h = alpha[h];
-    const float b_h = beta[h];
+    append_issue<T, K>(sv, n, h, qin, kin, vin, a, L, qc);
+    float a_h = sload(alpha, h);
+    float b_h = sload(beta, h);
+    if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
     wait_lds_copies();
     lds_barrier();
-    append_compute<T, true>(sv, n, h, a, L, dots, qc, a_h, b_h, o);
+    if constexpr (GATED) {
+        a_h = dots[kGateSlot];
+        b_h = dots[kGateSlot + 1];
+    }
+    append_compute<T, K, true, NORM>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<T>(a, hs, qc, sv.C, n + 1, true, st, S);
+    rebuild<K>(a, hs, qc, sv.C, n + 1, true, st, S);
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
@@ -555,27 +560,46 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename K, bool GATED, bool NORM>
 static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, float *o, int smoothing, float floor_,
-                                 hipStream_t s)
+                                 const GateArgs &g, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_append_fold<T, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q, (const T *)k,
-                           (const T *)v, alpha, beta, o, smoothing, floor_);
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
+                           (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
     else
-        hipLaunchKernelGGL((k_append_fold<T, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q, (const T *)k,
-                           (const T *)v, alpha, beta, o, smoothing, floor_);
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
+                           (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
 }
 
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
                               const void *v, const float *alpha, const float *beta, float *o, int smoothing,
-                              float floor_, hipStream_t s)
+                              float floor_, const GateArgs &g, hipStream_t s)
 {
-    if (bf16)
-        launch_append_fold_t<uint16_t>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, s);
-    else
-        launch_append_fold_t<float>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, s);
+    // the (inputs, keys, gated, normalize) combinations of launch_append
+    const bool kb = sv.key_bf16;
+#define LQ_AF(T, K, G, N) launch_append_fold_t<T, K, G, N>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
+    if (!g.gated) {
+        if (!bf16)
+            LQ_AF(float, float, false, false);
+        else if (kb)
+            LQ_AF(uint16_t, uint16_t, false, false);
+        else
+            LQ_AF(uint16_t, float, false, false);
+    } else if (!bf16) {
+        if (g.normalize)
+            LQ_AF(float, float, true, true);
+        else
+            LQ_AF(float, float, true, false);
+    } else if (kb) {
+        LQ_AF(uint16_t, uint16_t, true, false);
+    } else if (g.normalize) {
+        LQ_AF(uint16_t, float, true, true);
+    } else {
+        LQ_AF(uint16_t, float, true, false);
+    }
+#undef LQ_AF
     return hipGetLastError();
 }
 

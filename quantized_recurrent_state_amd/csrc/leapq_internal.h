@@ -22,17 +22,31 @@ struct StateView {
     int key_bf16;  // record keys (and inputs) are bf16
 };
 
+// Gate arithmetic in front of the append (mode 0: alpha and beta are given;
+// LEAPQ_GATE_*: they are computed from the raw projections, and q and k
+// are L2-normalized when `normalize`).
+struct GateArgs {
+    const float *A_log;    // [heads] per model head
+    const float *dt_bias;  // [heads]
+    float q_scale;
+    float eps;
+    int heads;  // model heads per request: head h uses parameters h % heads
+    int gated;
+    int normalize;
+};
+
 hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
                        hipStream_t s);
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s);
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s);
 hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
-                         const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
+                         const void *v, const float *alpha, const float *beta, float *o, const GateArgs &g,
+                         hipStream_t s);
 // The window's last append and the fold in one launch; requires n + 1 == W
 // and W <= 16 (the records fit one LDS chunk).
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
                               const void *v, const float *alpha, const float *beta, float *o, int smoothing,
-                              float floor_, hipStream_t s);
+                              float floor_, const GateArgs &g, hipStream_t s);
 hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, void *S, const void *q, const void *k,
                              const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
 

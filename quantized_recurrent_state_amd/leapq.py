@@ -30,15 +30,21 @@ LEAPQ_DEQ_RESIDUAL = 0
 LEAPQ_DEQ_BOUNDARY = 1
 LEAPQ_DEQ_CURRENT = 2
 
-SYMBOLS = ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold", "leapq_fold",
-           "leapq_dequant", "leapq_gdn_decode", "leapq_status_str", "leapq_version")
+SYMBOLS = ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold", "leapq_append_gated",
+           "leapq_append_fold_gated", "leapq_fold", "leapq_dequant", "leapq_gdn_decode", "leapq_status_str",
+           "leapq_version")
 
 
 class leapq_config(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
                 ("smoothing", ctypes.c_int32), ("sigma_floor", ctypes.c_float),
-                ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("in_dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+
+
+class leapq_gate(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("q_scale", ctypes.c_float),
+                ("norm_eps", ctypes.c_float), ("reserved", ctypes.c_int32 * 2)]
 
 
 class leapq_layout(ctypes.Structure):
@@ -74,11 +80,15 @@ def lib():
         L.leapq_init_state.argtypes = [ctypes.POINTER(leapq_layer), vp, vp]
         L.leapq_append.argtypes = [ctypes.POINTER(leapq_layer), vp, vp, vp, vp, vp, vp, vp]
         L.leapq_append_fold.argtypes = [ctypes.POINTER(leapq_layer), vp, vp, vp, vp, vp, vp, vp]
+        for f in ("leapq_append_gated", "leapq_append_fold_gated"):
+            getattr(L, f).argtypes = [ctypes.POINTER(leapq_layer), ctypes.POINTER(leapq_gate), vp, vp, vp, vp, vp,
+                                      vp, vp]
         L.leapq_fold.argtypes = [ctypes.POINTER(leapq_layer), vp]
         L.leapq_dequant.argtypes = [ctypes.POINTER(leapq_layer), i32, vp, vp]
         L.leapq_gdn_decode.argtypes = [ctypes.POINTER(leapq_config), i32, vp, vp, vp, vp, vp, vp, vp, vp]
-        for f in ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold", "leapq_fold",
-                  "leapq_dequant", "leapq_gdn_decode", "leapq_version"):
+        for f in ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold",
+                  "leapq_append_gated", "leapq_append_fold_gated", "leapq_fold", "leapq_dequant",
+                  "leapq_gdn_decode", "leapq_version"):
             getattr(L, f).restype = i32
         L.leapq_status_str.argtypes = [i32]
         L.leapq_status_str.restype = ctypes.c_char_p
@@ -96,13 +106,32 @@ def _check(status, what):
         raise LeapqError(status, what)
 
 
-def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32"):
+def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32",
+                qk_norm=False):
     c = leapq_config()
     c.batch, c.heads, c.dk, c.dv = int(batch), int(heads), D, D
     c.window, c.n_comp, c.smoothing = int(window), int(n_comp), int(bool(smoothing))
     c.sigma_floor = float(sigma_floor)
     c.in_dtype = LEAPQ_BF16 if in_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
+    c.qk_norm = int(bool(qk_norm))
     return c
+
+
+class Gate:
+    """Gate parameters of a layer (leapq_gate): A_log and dt_bias are fp32
+    device tensors [heads] (per model head); q_scale and norm_eps apply when
+    the layer normalizes q and k (qk_norm)."""
+
+    def __init__(self, A_log, dt_bias, q_scale=D ** -0.5, norm_eps=1e-6):
+        if A_log.shape != dt_bias.shape or A_log.dim() != 1:
+            raise ValueError("A_log and dt_bias: fp32 [heads]")
+        for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"{name}: expected a contiguous float32 tensor")
+        self.A_log, self.dt_bias = A_log, dt_bias
+        self.c = leapq_gate()
+        self.c.A_log, self.c.dt_bias = A_log.data_ptr(), dt_bias.data_ptr()
+        self.c.q_scale, self.c.norm_eps = float(q_scale), float(norm_eps)
 
 
 def leapq_query_layout(cfg):
@@ -175,6 +204,11 @@ class Layer:
     def in_dtype(self):
         return torch.bfloat16 if self.cfg.in_dtype == LEAPQ_BF16 else torch.float32
 
+    @property
+    def key_dtype(self):
+        """Element type of the stored record keys (include/leapq.h layout)."""
+        return torch.bfloat16 if self.cfg.in_dtype == LEAPQ_BF16 and not self.cfg.qk_norm else torch.float32
+
     # ---- read-only views of the state sections (layout of include/leapq.h)
     def _sec(self, off, count, dtype, shape):
         nbytes = count * torch.tensor([], dtype=dtype).element_size()
@@ -210,9 +244,9 @@ class Layer:
         return self._sec(self.layout.off_rec_gamma, self.heads * W, torch.float32, (self.heads, W))
 
     def rec_k_physical(self):
-        """Record keys [heads, W, 128] as stored: the input dtype, key-row order."""
+        """Record keys [heads, W, 128] as stored (key_dtype, key-row order)."""
         W = self.cfg.window
-        return self._sec(self.layout.off_rec_k, self.heads * W * D, self.in_dtype, (self.heads, W, D))
+        return self._sec(self.layout.off_rec_k, self.heads * W * D, self.key_dtype, (self.heads, W, D))
 
     def rec_u_physical(self):
         W = self.cfg.window
@@ -255,6 +289,30 @@ def leapq_append_fold(layer, q, k, v, alpha, beta, o, stream=None):
     _dev_tensor(o, "o", torch.float32, (H, D), dev)
     _check(lib().leapq_append_fold(ctypes.byref(layer.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                    _ptr(o), _stream(stream, dev)), "leapq_append_fold")
+
+
+def _gated_args(layer, gate, q, k, v, a, b, o):
+    H, dt, dev = layer.heads, layer.in_dtype, layer.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, dt, (H, D), dev)
+    _dev_tensor(a, "a", torch.float32, (H,), dev)
+    _dev_tensor(b, "b", torch.float32, (H,), dev)
+    _dev_tensor(o, "o", torch.float32, (H, D), dev)
+    for name, t in (("A_log", gate.A_log), ("dt_bias", gate.dt_bias)):
+        _dev_tensor(t, name, torch.float32, (layer.cfg.heads,), dev)
+    return (ctypes.byref(layer.c), ctypes.byref(gate.c), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(o))
+
+
+def leapq_append_gated(layer, gate, q, k, v, a, b, o, stream=None):
+    """leapq_append with the gate arithmetic: a, b are the raw projections."""
+    _check(lib().leapq_append_gated(*_gated_args(layer, gate, q, k, v, a, b, o), _stream(stream, layer.device)),
+           "leapq_append_gated")
+
+
+def leapq_append_fold_gated(layer, gate, q, k, v, a, b, o, stream=None):
+    """leapq_append_fold with the gate arithmetic."""
+    _check(lib().leapq_append_fold_gated(*_gated_args(layer, gate, q, k, v, a, b, o),
+                                         _stream(stream, layer.device)), "leapq_append_fold_gated")
 
 
 def leapq_fold(layer, stream=None):

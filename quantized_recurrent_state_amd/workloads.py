@@ -28,12 +28,23 @@ Initial states:
              above, scale 2 rows and 2 columns x200 (a hard, slowly decaying
              late layer).
 
+Gated inputs (the raw projections that the gate arithmetic of the gated
+entry points consumes) follow the Gated DeltaNet layer's parameterization:
+
+  q, k, v ~ N(0, 1)^128 (q and k not normalized),  a, b ~ N(0, 1)
+  per layer and model head: A_log = log(A), A ~ U[1, 16];
+  dt_bias = softplus^-1(dt), log dt ~ U[log 1e-3, log 1e-1]
+
+so that alpha = exp(-A softplus(a + dt_bias)) spreads over (0, 1) with most
+heads decaying slowly.
+
 Every draw comes from a torch generator seeded by a 64-bit mix of
 (seed, stream, layer, token), so any (layer, token) slice can be regenerated
 on demand, on the CPU or on the GPU.  The CPU and GPU generators produce
 different numbers for the same seed; a comparison always hands both sides the
 same tensor.
 """
+import math
 from dataclasses import dataclass, field
 
 import torch
@@ -98,7 +109,7 @@ WORKLOADS = {
 }
 
 # stream ids
-_S_INIT, _S_TOK, _S_HARD = 1, 2, 3
+_S_INIT, _S_TOK, _S_HARD, _S_GTOK, _S_GPAR = 1, 2, 3, 4, 5
 
 
 def _normal(shape, g, device, mean=0.0, std=1.0):
@@ -183,6 +194,31 @@ def token_inputs(wl, layer, token, device="cpu"):
     dt = wl.torch_dtype()
     return (q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous(),
             alpha.contiguous(), beta.contiguous())
+
+
+def gate_params(wl, layer, device="cpu"):
+    """Gate parameters of one layer: A_log, dt_bias as fp32 [heads]."""
+    g = _gen(device, wl.seed, _S_GPAR, layer)
+    A = 1.0 + 15.0 * torch.rand(wl.heads, generator=g, device=device, dtype=torch.float64)
+    u = torch.rand(wl.heads, generator=g, device=device, dtype=torch.float64)
+    dt = torch.exp(math.log(1e-3) + u * (math.log(1e-1) - math.log(1e-3)))
+    dt_bias = dt + torch.log(-torch.expm1(-dt))  # softplus(dt_bias) = dt
+    return torch.log(A).float().contiguous(), dt_bias.float().contiguous()
+
+
+def gated_token_inputs(wl, layer, token, device="cpu"):
+    """Raw inputs of one decode token for the gated entry points: q, k, v as
+    [batch, heads, 128] in the workload's input dtype (q, k not normalized)
+    and the raw gate projections a, b as fp32 [batch, heads]."""
+    B, H = wl.batch, wl.heads
+    g = _gen(device, wl.seed, _S_GTOK, layer, token)
+    q = _normal((B, H, D), g, device)
+    k = _normal((B, H, D), g, device)
+    v = _normal((B, H, D), g, device)
+    a = _normal((B, H), g, device)
+    b = _normal((B, H), g, device)
+    dt = wl.torch_dtype()
+    return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous(), a.contiguous(), b.contiguous()
 
 
 def widen(x):

@@ -127,19 +127,28 @@ def _pool():
 
 
 def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="cuda", check_every_token=True,
-              fold_at=None, report=None, log=True, fused=False):
+              fold_at=None, report=None, log=True, fused=False, gated=None, qk_norm=False):
     """Runs `tokens` decode tokens of one layer on the GPU and, for the
     sampled heads, in the oracle; folds whenever the window is full (or at
     the token counts in fold_at).  With fused, the GPU takes each window's
     last token and its fold in one leapq_append_fold call (the oracle still
-    appends, then folds).  Returns the Report."""
+    appends, then folds).  With gated = dict(q_scale=, eps=), the inputs are
+    the raw projections of workloads.gated_token_inputs and the GPU runs the
+    gated entry points (the oracle applies oracle.gated_inputs first); the
+    layer normalizes q and k when qk_norm.  Returns the Report."""
     rep = report or Report()
     dev = torch.device(device)
     H = wl.batch * wl.heads
     T = wl.tokens if tokens is None else tokens
     sample = list(range(H)) if sample is None else list(sample)
-    cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype)
+    cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype,
+                         qk_norm=qk_norm)
     L = lq.Layer(cfg, dev)
+    if gated is not None:
+        A_log, dt_bias = workloads.gate_params(wl, layer)
+        gate = lq.Gate(A_log.to(dev), dt_bias.to(dev), gated["q_scale"], gated["eps"])
+        jh = [h % wl.heads for h in sample]
+        pA, pdt = A_log.numpy(), dt_bias.numpy()
     S0 = workloads.initial_state(wl, layer, device=gen_device).reshape(H, D, D)
     lq.leapq_init_state(L, S0.to(dev))
     S0h = S0[sample].cpu().numpy()
@@ -151,11 +160,14 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
         o = torch.empty(H, D, dtype=torch.float32, device=dev)
         sidx = torch.as_tensor(sample)
         for t in range(T):
-            q, k, v, a, b = workloads.token_inputs(wl, layer, t, device=gen_device)
+            gen = workloads.gated_token_inputs if gated is not None else workloads.token_inputs
+            q, k, v, a, b = gen(wl, layer, t, device=gen_device)
             qd, kd, vd = (x.reshape(H, D).to(dev) for x in (q, k, v))
             ad, bd = a.reshape(H).to(dev), b.reshape(H).to(dev)
             last = fused and L.n_records == wl.window - 1
-            if last:
+            if gated is not None:
+                (lq.leapq_append_fold_gated if last else lq.leapq_append_gated)(L, gate, qd, kd, vd, ad, bd, o)
+            elif last:
                 lq.leapq_append_fold(L, qd, kd, vd, ad, bd, o)
             else:
                 lq.leapq_append(L, qd, kd, vd, ad, bd, o)
@@ -164,8 +176,15 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
             vh = workloads.widen(v.reshape(H, D)[sidx]).cpu().numpy()
             ah = a.reshape(H)[sidx].cpu().numpy()
             bh = b.reshape(H)[sidx].cpu().numpy()
-            outs = list(pool.map(lambda s: refs[s].append(qh[s], kh[s], vh[s], ah[s], bh[s])[0],
-                                 range(len(sample))))
+            if gated is not None:
+                def step(s):
+                    gq, gk, gv, al, be = oracle.gated_inputs(qh[s], kh[s], vh[s], ah[s], bh[s], pA[jh[s]],
+                                                             pdt[jh[s]], gated["q_scale"], gated["eps"], qk_norm)
+                    return refs[s].append(gq, gk, gv, al, be)[0]
+            else:
+                def step(s):
+                    return refs[s].append(qh[s], kh[s], vh[s], ah[s], bh[s])[0]
+            outs = list(pool.map(step, range(len(sample))))
             og = o[sidx.to(dev)].cpu().numpy()
             rep.fp("o", og, np.stack(outs))
             if check_every_token and not last:

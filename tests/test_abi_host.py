@@ -229,3 +229,54 @@ def test_append_fold_checks():
         assert call_append_fold(L, **{key: 0}) == lq.LEAPQ_ERR_NULL and L.n_records == 15, key
     for key in ("q", "k", "v", "o"):
         assert call_append_fold(fake_layer(c, n=15), **{key: FAKE + 4}) == lq.LEAPQ_ERR_ALIGN, key
+
+
+# ---------------------------------------------------------------- gated entry points
+
+def gate_struct(A=FAKE, dt=FAKE, q_scale=0.125, eps=1e-6):
+    g = lq.leapq_gate()
+    g.A_log, g.dt_bias, g.q_scale, g.norm_eps = A, dt, q_scale, eps
+    return g
+
+
+def call_gated(L, g, fused=False, q=FAKE, a=FAKE):
+    vp = ctypes.c_void_p
+    fn = lq.lib().leapq_append_fold_gated if fused else lq.lib().leapq_append_gated
+    gp = ctypes.byref(g) if g is not None else None
+    return fn(ctypes.byref(L), gp, vp(q), vp(FAKE), vp(FAKE), vp(a), vp(FAKE), vp(FAKE), None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_gated_checks(fused):
+    c = cfg(qk_norm=True)
+    n = 15 if fused else 0
+    assert call_gated(fake_layer(c, n), None, fused) == lq.LEAPQ_ERR_NULL
+    for kw, status in ((dict(A=0), lq.LEAPQ_ERR_NULL), (dict(dt=0), lq.LEAPQ_ERR_NULL),
+                       (dict(A=FAKE + 2), lq.LEAPQ_ERR_ALIGN), (dict(dt=FAKE + 1), lq.LEAPQ_ERR_ALIGN),
+                       (dict(eps=-1.0), lq.LEAPQ_ERR_RANGE), (dict(eps=float("nan")), lq.LEAPQ_ERR_RANGE),
+                       (dict(eps=float("inf")), lq.LEAPQ_ERR_RANGE),
+                       (dict(q_scale=float("nan")), lq.LEAPQ_ERR_RANGE),
+                       (dict(q_scale=float("inf")), lq.LEAPQ_ERR_RANGE)):
+        L = fake_layer(c, n)
+        assert call_gated(L, gate_struct(**kw), fused) == status, kw
+        assert L.n_records == n
+    g = gate_struct()
+    g.reserved[0] = 3
+    assert call_gated(fake_layer(c, n), g, fused) == lq.LEAPQ_ERR_RANGE
+    assert call_gated(fake_layer(c, n), gate_struct(), fused, q=0) == lq.LEAPQ_ERR_NULL
+    assert call_gated(fake_layer(c, n), gate_struct(), fused, a=FAKE + 2) == lq.LEAPQ_ERR_ALIGN
+    # window position
+    bad_n = 3 if fused else 16
+    expect = lq.LEAPQ_ERR_RANGE if fused else lq.LEAPQ_ERR_WINDOW_FULL
+    assert call_gated(fake_layer(c, bad_n), gate_struct(), fused) == expect
+
+
+def test_qk_norm_config_and_key_layout():
+    out = lq.leapq_layout()
+    c = cfg()
+    c.qk_norm = 2
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE
+    for dt, qk, e in (("bf16", False, 2), ("bf16", True, 4), ("f32", False, 4), ("f32", True, 4)):
+        L = layout(batch=2, heads=4, window=16, n_comp=4, in_dtype=dt, qk_norm=qk)
+        assert L.off_rec_u - L.off_rec_k >= 2 * 4 * 16 * 128 * e
+        assert L.record_bytes_per_head == 16 * (4 + 128 * e + 512), (dt, qk)
