@@ -13,7 +13,7 @@ Programs (each is what comes after `rocprofv3 ... --`):
 Reductions (CPU only, read the CSV files rocprofv3 wrote):
 
   python3 -m quantized_recurrent_state_amd.profiling traffic \
-      --kernel k_append --fetch F.csv --write W.csv \
+      --kernel 'k_append<' --fetch F.csv --write W.csv \
       --copy-fetch CF.csv --copy-write CW.csv --copy-mib 1024 --workload b512 --out X.json
   python3 -m quantized_recurrent_state_amd.profiling stats --csv kernel_stats.csv
 """
@@ -157,7 +157,7 @@ def main(argv=None):
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=4)
     t = sub.add_parser("traffic")
-    t.add_argument("--kernel", default="k_append")
+    t.add_argument("--kernel", default="k_append<", help="substring of the kernel name")
     t.add_argument("--kernel-src", nargs="+", default=list(APPEND_SOURCES))
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
