@@ -46,6 +46,11 @@ def _bind(L):
         "lqo_fold": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
         "lqo_append": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p,
                               f32p, f32p, f32p, cf, cf, f32p]),
+        "lqo_current_kda": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, f32p]),
+        "lqo_fold_kda": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
+        "lqo_append_kda": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p,
+                                  f32p, f32p, f32p, f32p, cf, f32p]),
+        "lqo_kda_step_f32": (None, [f32p, f32p, f32p, f32p, f32p, cf, f32p, f32p]),
         "lqo_gdn_step_f32": (None, [f32p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
         "lqo_gdn_step_f64": (None, [f64p, f64p, f64p, f64p, cd, cd, f64p, f64p]),
         "lqo_gdn_step_bf16": (None, [u16p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
@@ -119,19 +124,24 @@ class Head:
     """One head's LeapQuant state held in numpy arrays, driven by the oracle.
 
     Q is int8 [128][128] in logical (key row, value column) order; rho and
-    sigma are fp32 [128]; idx int32 [C]; vec fp32 [C][128]; records gam [W],
-    rk [W][128], ru [W][128]; n is the number of records in the window.
+    sigma are fp32 [128]; idx int32 [C]; vec fp32 [C][128]; records gam [W]
+    (decay="scalar", GDN) or [W][128] (decay="channel", KDA), rk [W][128],
+    ru [W][128]; n is the number of records in the window.
     """
 
-    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None):
+    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None, decay="scalar"):
         self.L = L or lib()
         self.C, self.W, self.smoothing, self.floor = int(C), int(W), int(smoothing), float(sigma_floor)
+        if decay not in ("scalar", "channel"):
+            raise ValueError("decay must be 'scalar' or 'channel'")
+        self.decay = decay
+        self.kda = decay == "channel"
         self.Q = np.zeros((D, D), np.int8)
         self.rho = np.zeros(D, np.float32)
         self.sigma = np.ones(D, np.float32)
         self.idx = np.full(max(self.C, 1), -1, np.int32)
         self.vec = np.zeros((max(self.C, 1), D), np.float32)
-        self.gam = np.zeros(max(self.W, 1), np.float32)
+        self.gam = np.zeros((max(self.W, 1), D) if self.kda else max(self.W, 1), np.float32)
         self.rk = np.zeros((max(self.W, 1), D), np.float32)
         self.ru = np.zeros((max(self.W, 1), D), np.float32)
         self.n = 0
@@ -161,13 +171,19 @@ class Head:
         q, k, v = f32(q), f32(k), f32(v)
         o = np.zeros(D, np.float32)
         fp = ctypes.c_float
-        self.L.lqo_append(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp),
-                          float(np.float32(alpha)), float(np.float32(beta)), _p(o, fp))
+        if self.kda:
+            al = f32(alpha).reshape(D)
+            self.L.lqo_append_kda(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp), _p(al, fp),
+                                  float(np.float32(beta)), _p(o, fp))
+        else:
+            self.L.lqo_append(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp),
+                              float(np.float32(alpha)), float(np.float32(beta)), _p(o, fp))
         self.n += 1
         return o, self.ru[self.n - 1].copy()
 
     def fold(self):
-        self.L.lqo_fold(*self._st(), *self._rec(), self.smoothing, self.floor)
+        fn = self.L.lqo_fold_kda if self.kda else self.L.lqo_fold
+        fn(*self._st(), *self._rec(), self.smoothing, self.floor)
         self.n = 0
         return self
 
@@ -180,13 +196,14 @@ class Head:
         elif what == 1:
             self.L.lqo_boundary(*self._st(), _p(out, fp))
         elif what == 2:
-            self.L.lqo_current(*self._st(), *self._rec(), _p(out, fp))
+            fn = self.L.lqo_current_kda if self.kda else self.L.lqo_current
+            fn(*self._st(), *self._rec(), _p(out, fp))
         else:
             raise ValueError("what must be 0, 1 or 2")
         return out
 
     def copy(self):
-        h = Head(self.C, self.W, self.smoothing, self.floor, self.L)
+        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay)
         for name in ("Q", "rho", "sigma", "idx", "vec", "gam", "rk", "ru"):
             setattr(h, name, getattr(self, name).copy())
         h.n = self.n
@@ -207,6 +224,18 @@ def gdn_step_f32(S, q, k, v, alpha, beta, L=None):
     fp = ctypes.c_float
     L.lqo_gdn_step_f32(_p(S, fp), _p(f32(q), fp), _p(f32(k), fp), _p(f32(v), fp),
                        float(np.float32(alpha)), float(np.float32(beta)), _p(u, fp), _p(o, fp))
+    return u, o
+
+
+def kda_step_f32(S, q, k, v, alpha, beta, L=None):
+    """Dense fp32 KDA token step (per-row decay alpha [128]), in place on S; returns (u, o)."""
+    L = L or lib()
+    assert S.dtype == np.float32 and S.flags["C_CONTIGUOUS"]
+    u = np.zeros(D, np.float32)
+    o = np.zeros(D, np.float32)
+    fp = ctypes.c_float
+    L.lqo_kda_step_f32(_p(S, fp), _p(f32(q), fp), _p(f32(k), fp), _p(f32(v), fp), _p(f32(alpha), fp),
+                       float(np.float32(beta)), _p(u, fp), _p(o, fp))
     return u, o
 
 

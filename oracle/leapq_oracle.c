@@ -334,6 +334,139 @@ void lqo_append(const int8_t *Q, const float *rho, const float *sigma, int C,
 }
 
 /* ------------------------------------------------------------------ */
+/* Per-channel decay (KDA): [LQ] App. A writes the general update with   */
+/* a diagonal decay D_t = Diag(alpha_t), alpha_t a d_k-vector for Kimi   */
+/* Delta Attention, and one rank-one record per token as for GDN; [LQ]   */
+/* B.2: cumulative diagonal decays are kept incrementally.  The state    */
+/* rows are key coordinates, so the decay scales rows.  Records hold the */
+/* cumulative decay as a vector, gam[i][r].                              */
+/* ------------------------------------------------------------------ */
+
+/* The cumulative decay after n records (all ones at n = 0) into g. */
+static void gamma_vec_of(int n, const float *gam, float *g)
+{
+    for (int r = 0; r < D; ++r) g[r] = n > 0 ? gam[(size_t)(n - 1) * D + r] : 1.0f;
+}
+
+/* Compensator lines scaled per row: entry (r, c) of a line receives
+ * g[r] * (its value). */
+static void add_lines_rows(float *M, int C, const int32_t *idx, const float *vec, const float *g)
+{
+    for (int j = 0; j < C; ++j) {
+        const float *v = vec + (size_t)j * D;
+        if (idx[j] < 0) continue;
+        if (idx[j] < D) {
+            int r = idx[j];
+            for (int c = 0; c < D; ++c) M[r * D + c] = M[r * D + c] + g[r] * v[c];
+        } else {
+            int c = idx[j] - D;
+            for (int r = 0; r < D; ++r) M[r * D + c] = M[r * D + c] + g[r] * v[r];
+        }
+    }
+}
+
+/* Current state after n records with per-row cumulative decays:
+ *   S = Diag(gamma_n) B + sum_i Diag(gamma_n / gamma_i) k_i u_i^T,
+ * formed as for lqo_current with gamma_n[r] in place of the scalar:
+ * (code * (gamma_n[r] * rho_r)) * sigma_c, lines gamma_n[r] * line, then
+ * record i in order by fma((gamma_n[r] / gamma_i[r]) * k_i[r], u_i[c], S). */
+void lqo_current_kda(const int8_t *Q, const float *rho, const float *sigma, int C,
+                     const int32_t *idx, const float *vec, int n, const float *gam,
+                     const float *rk, const float *ru, float *out)
+{
+    float gn[D];
+    gamma_vec_of(n, gam, gn);
+    for (int r = 0; r < D; ++r) {
+        float a = gn[r] * rho[r];
+        for (int c = 0; c < D; ++c) out[r * D + c] = ((float)Q[r * D + c] * a) * sigma[c];
+    }
+    add_lines_rows(out, C, idx, vec, gn);
+    for (int i = 0; i < n; ++i) {
+        float w[D];
+        for (int r = 0; r < D; ++r) w[r] = (gn[r] / gam[(size_t)i * D + r]) * rk[(size_t)i * D + r];
+        for (int r = 0; r < D; ++r)
+            for (int c = 0; c < D; ++c)
+                out[r * D + c] = fmaf(w[r], ru[(size_t)i * D + c], out[r * D + c]);
+    }
+}
+
+/* Fold with per-channel decays: rebuild (lqo_current_kda), then the same
+ * quantization as every fold.  The caller sets n = 0. */
+void lqo_fold_kda(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *vec,
+                  int n, const float *gam, const float *rk, const float *ru,
+                  int smoothing, float sigma_floor)
+{
+    float R[D * D];
+    lqo_current_kda(Q, rho, sigma, C, idx, vec, n, gam, rk, ru, R);
+    lqo_quantize(R, C, smoothing, sigma_floor, Q, rho, sigma, idx, vec);
+}
+
+/* One token with per-channel decay alpha[r] (n records present, n < W):
+ *   gamma_t[r] = gamma_n[r] * alpha[r],  x = gamma_t (.) k,  y = gamma_t (.) q
+ *   w_i[r] = (gamma_t[r] / gamma_i[r]) * k_i[r]
+ *   r   = B^T x + sum_i (w_i . k) u_i            (read of Diag(alpha) S_{t-1})
+ *   u_t = beta * (v - r)
+ *   o   = B^T y + sum_i (w_i . q) u_i + (k . q) u_t
+ * with the boundary reads of lqo_append (residual scales on the residual
+ * only, compensators as tokens) and the record (gamma_t, k, u_t) at slot n. */
+void lqo_append_kda(const int8_t *Q, const float *rho, const float *sigma, int C,
+                    const int32_t *idx, const float *vec, int n, float *gam, float *rk,
+                    float *ru, const float *q, const float *k, const float *v, const float *alpha,
+                    float beta, float *o)
+{
+    float gp[D], gt[D], x[D], y[D], r[D], u[D];
+    gamma_vec_of(n, gam, gp);
+    for (int e = 0; e < D; ++e) {
+        gt[e] = gp[e] * alpha[e];
+        x[e] = gt[e] * k[e];
+        y[e] = gt[e] * q[e];
+    }
+    boundary_read(Q, rho, sigma, C, idx, vec, x, r);
+    boundary_read(Q, rho, sigma, C, idx, vec, y, o);
+    for (int i = 0; i < n; ++i) {
+        const float *ki = rk + (size_t)i * D, *ui = ru + (size_t)i * D, *gi = gam + (size_t)i * D;
+        float w[D];
+        for (int e = 0; e < D; ++e) w[e] = (gt[e] / gi[e]) * ki[e];
+        float ak = lqo_t128_dot(w, k);
+        float aq = lqo_t128_dot(w, q);
+        for (int c = 0; c < D; ++c) {
+            r[c] = fmaf(ak, ui[c], r[c]);
+            o[c] = fmaf(aq, ui[c], o[c]);
+        }
+    }
+    for (int cc = 0; cc < D; ++cc) u[cc] = beta * (v[cc] - r[cc]);
+    float kq = lqo_t128_dot(k, q);
+    for (int cc = 0; cc < D; ++cc) o[cc] = fmaf(kq, u[cc], o[cc]);
+
+    memcpy(gam + (size_t)n * D, gt, D * sizeof(float));
+    memcpy(rk + (size_t)n * D, k, D * sizeof(float));
+    memcpy(ru + (size_t)n * D, u, D * sizeof(float));
+}
+
+/* One KDA token on a dense fp32 state: S = Diag(alpha) S; r = S^T k;
+ * u = beta (v - r); S += k u^T; o = S^T q.  Plain sequential sums. */
+void lqo_kda_step_f32(float *S, const float *q, const float *k, const float *v,
+                      const float *alpha, float beta, float *u_out, float *o)
+{
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c) S[r * D + c] = alpha[r] * S[r * D + c];
+    float u[D];
+    for (int c = 0; c < D; ++c) {
+        float rc = 0.0f;
+        for (int r = 0; r < D; ++r) rc = fmaf(S[r * D + c], k[r], rc);
+        u[c] = beta * (v[c] - rc);
+    }
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c) S[r * D + c] = fmaf(k[r], u[c], S[r * D + c]);
+    for (int c = 0; c < D; ++c) {
+        float oc = 0.0f;
+        for (int rr = 0; rr < D; ++rr) oc = fmaf(S[rr * D + c], q[rr], oc);
+        o[c] = oc;
+    }
+    if (u_out) memcpy(u_out, u, sizeof u);
+}
+
+/* ------------------------------------------------------------------ */
 /* Gate arithmetic: the per-token step in front of the path ([RN4]       */
 /* Results: the column "with gate arithmetic").  The pages name the step */
 /* but print no formula; these are the Gated DeltaNet layer's gates (the */

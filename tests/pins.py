@@ -514,10 +514,85 @@ def pin_gated_window(L):
         assert rel(o, o64) < 1e-5, (t, rel(o, o64))
 
 
+def _kda_tokens(rng, T, spread=1.0):
+    toks = []
+    for _ in range(T):
+        q = rng.normal(0, 1, D)
+        k = rng.normal(0, 1, D)
+        q, k = (x / np.linalg.norm(x) for x in (q, k))
+        v = rng.normal(0, 1, D)
+        alpha = np.exp(-np.logaddexp(0.0, rng.normal(-3.0, spread, D)))
+        beta = 1.0 / (1.0 + np.exp(-rng.normal()))
+        toks.append(tuple(np.float32(x) if np.ndim(x) == 0 else x.astype(np.float32)
+                          for x in (q, k, v, alpha, beta)))
+    return toks
+
+
+def pin_kda_window_vs_dense_f64(L):
+    """Per-channel decay ([LQ] App. A, D_t = Diag(alpha_t)): a window of
+    appends equals the float64 dense recurrence with row-wise decay from the
+    dequantized boundary (outputs and the rebuilt state to 1e-5), and the
+    fold leaves an empty buffer whose boundary is the quantized state."""
+    S0, _ = tiny_inputs(seed=31, tokens=1, init="gauss")
+    rng = np.random.default_rng(31)
+    h = oracle.Head(C=4, W=16, L=L, decay="channel").init(S0[0])
+    S = h.dequant(1).astype(np.float64)
+    for (q, k, v, a, b) in _kda_tokens(rng, 16, spread=1.5):
+        o, u = h.append(q, k, v, a, b)
+        S *= a.astype(np.float64)[:, None]
+        r = S.T @ k.astype(np.float64)
+        u64 = float(b) * (v.astype(np.float64) - r)
+        S += np.outer(k.astype(np.float64), u64)
+        o64 = S.T @ q.astype(np.float64)
+        assert rel(o, o64) < 1e-5 and rel(u, u64) < 1e-5
+    cur = h.dequant(2)
+    assert rel(cur, S) < 1e-5
+    want = oracle.quantize(cur, C=4, L=L)
+    h.fold()
+    assert h.n == 0 and np.array_equal(h.Q, want.Q) and np.array_equal(h.idx, want.idx)
+    assert np.array_equal(h.dequant(2), h.dequant(1))
+
+
+def pin_kda_uniform_is_gdn(L):
+    """With the same decay on every channel, per-channel decay is the scalar
+    (GDN) decay: the dense steps agree bit for bit, and the windowed paths,
+    which round in different orders, agree to 1e-6."""
+    S0, _ = tiny_inputs(seed=32, tokens=1, init="gauss")
+    rng = np.random.default_rng(32)
+    hk = oracle.Head(C=4, W=16, L=L, decay="channel").init(S0[0])
+    hg = oracle.Head(C=4, W=16, L=L).init(S0[0])
+    Sk = hk.dequant(1)
+    Sg = Sk.copy()
+    for (q, k, v, a, b) in _kda_tokens(rng, 16):
+        a0 = np.float32(a[0])
+        ok, _ = hk.append(q, k, v, np.full(D, a0, np.float32), b)
+        og, _ = hg.append(q, k, v, a0, b)
+        assert rel(ok, og) < 1e-6
+        uk, dk = oracle.kda_step_f32(Sk, q, k, v, np.full(D, a0, np.float32), b, L)
+        ug, dg = oracle.gdn_step_f32(Sg, q, k, v, a0, b, L)
+        assert np.array_equal(dk, dg) and np.array_equal(uk, ug) and np.array_equal(Sk, Sg)
+    assert rel(hk.dequant(2), hg.dequant(2)) < 1e-6
+
+
+def pin_kda_dense_step(L):
+    """The fp32 dense KDA step against numpy float64 (row-wise decay)."""
+    rng = np.random.default_rng(33)
+    S = rng.normal(0, 0.1, (D, D)).astype(np.float32)
+    S64 = S.astype(np.float64)
+    for (q, k, v, a, b) in _kda_tokens(rng, 8, spread=2.0):
+        u, o = oracle.kda_step_f32(S, q, k, v, a, b, L)
+        S64 *= a.astype(np.float64)[:, None]
+        u64 = float(b) * (v.astype(np.float64) - S64.T @ k.astype(np.float64))
+        S64 += np.outer(k.astype(np.float64), u64)
+        assert rel(u, u64) < 1e-5 and rel(o, S64.T @ q.astype(np.float64)) < 1e-5
+    assert rel(S, S64) < 1e-5
+
+
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
     pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
+    pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step,
 ]

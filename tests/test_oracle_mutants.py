@@ -54,6 +54,14 @@ MUTANTS = [
     ("l2norm_no_sqrt", "1.0f / sqrtf(s + eps)", "1.0f / (s + eps)"),
     ("l2norm_eps_outside_root", "sqrtf(s + eps)", "(sqrtf(s) + eps)"),
     ("l2norm_scale_folded", "(x[r] * inv) * scale", "x[r] * (inv * scale)"),
+    ("kda_ratio_inverted", "w[e] = (gt[e] / gi[e]) * ki[e];", "w[e] = (gi[e] / gt[e]) * ki[e];"),
+    ("kda_read_undecayed", "x[e] = gt[e] * k[e];", "x[e] = k[e];"),
+    ("kda_gamma_not_cumulative", "gt[e] = gp[e] * alpha[e];", "gt[e] = alpha[e];"),
+    ("kda_rebuild_ratio_inverted", "w[r] = (gn[r] / gam[(size_t)i * D + r]) * rk[(size_t)i * D + r];",
+     "w[r] = (gam[(size_t)i * D + r] / gn[r]) * rk[(size_t)i * D + r];"),
+    ("kda_lines_unscaled", "M[r * D + c] = M[r * D + c] + g[r] * v[c];", "M[r * D + c] = M[r * D + c] + v[c];"),
+    ("kda_rebuild_no_gamma", "float a = gn[r] * rho[r];", "float a = rho[r];"),
+    ("kda_step_column_decay", "S[r * D + c] = alpha[r] * S[r * D + c];", "S[r * D + c] = alpha[c] * S[r * D + c];"),
 ]
 
 
