@@ -59,6 +59,12 @@ extern "C" {
 #define LEAPQ_F32 0
 #define LEAPQ_BF16 1
 
+/* decay of the recurrence ("LeapQuant" App. A: D_t = Diag(alpha_t)): one
+ * scalar per head and token (Gated DeltaNet), or one value per key channel
+ * (Kimi Delta Attention), which scales the state's rows */
+#define LEAPQ_DECAY_SCALAR 0
+#define LEAPQ_DECAY_CHANNEL 1
+
 /* what leapq_dequant writes */
 #define LEAPQ_DEQ_RESIDUAL 0 /* (code * rho_r) * sigma_c, compensator lines left at zero */
 #define LEAPQ_DEQ_BOUNDARY 1 /* residual + compensator lines: the window's fixed state B */
@@ -74,7 +80,9 @@ typedef struct leapq_config {
     float sigma_floor;   /* positive floor of the smoothing scale (1e-6) */
     int32_t in_dtype;    /* LEAPQ_F32 or LEAPQ_BF16 for q, k, v */
     int32_t qk_norm;     /* 1: the gated appends L2-normalize q and k (record keys are then fp32); 0 or 1 */
-    int32_t reserved[2]; /* must be zero */
+    int32_t decay;       /* LEAPQ_DECAY_SCALAR (GDN: alpha per head) or LEAPQ_DECAY_CHANNEL (KDA: alpha
+                            per head and key channel); channel decay excludes qk_norm */
+    int32_t reserved;    /* must be zero */
 } leapq_config;
 
 /* Byte layout of one layer's state buffer.  Sections are "structure of
@@ -91,6 +99,7 @@ typedef struct leapq_config {
  *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
  *                                      over r for a column), natural order
  *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
+ *                   ([heads][W][128] per key row with LEAPQ_DECAY_CHANNEL)
  *   rec_k     e     [heads][W][128]    record keys in key-row order, in the
  *                                      input dtype (a record's key is the
  *                                      token's k as given, so bf16 storage
@@ -103,8 +112,9 @@ typedef struct leapq_config {
  * four 16-byte loads, each wave's loads 1 KB contiguous; the record keys and
  * corrections are the A operand order of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
- * 1.19 bytes per state element); record_bytes_per_head = W * (4 + 128 e + 512)
- * with e = 2 for bf16 inputs and qk_norm = 0, else 4. */
+ * 1.19 bytes per state element); record_bytes_per_head = W * (4 g + 128 e + 512)
+ * with e = 2 for bf16 inputs and qk_norm = 0, else 4, and g = 1 (scalar
+ * decay) or 128 (channel decay). */
 typedef struct leapq_layout {
     uint64_t total_bytes;
     uint64_t off_codes, off_row_scale, off_col_scale, off_comp_idx, off_comp_vec;
@@ -137,11 +147,15 @@ int32_t leapq_init_state(leapq_layer *layer, const float *S0, void *stream);
  * read with the key, correction, rank-one write, read the output; "LeapQuant"
  * B.2-B.3: read from the fixed boundary plus the records).
  *   q, k [heads][128], v [heads][128] in cfg.in_dtype (device);
- *   alpha, beta [heads] fp32 (device): decay and step size of this token;
+ *   alpha [heads] fp32 (device; [heads][128], 16-byte aligned, with
+ *   LEAPQ_DECAY_CHANNEL): decay of this token; beta [heads] fp32: step size;
  *   o [heads][128] fp32 (device, written): the output S_t^T q_t.
  * Writes record n_records (gamma_t = gamma_{t-1} * alpha, k_t, u_t =
- * beta (v_t - (alpha S_{t-1})^T k_t)) and increments n_records.  Requires
- * n_records < window (else LEAPQ_ERR_WINDOW_FULL). */
+ * beta (v_t - (D_t S_{t-1})^T k_t) with D_t = alpha or Diag(alpha)) and
+ * increments n_records.  Requires n_records < window (else
+ * LEAPQ_ERR_WINDOW_FULL).  With channel decay ("LeapQuant" App. A, B.2) the
+ * read uses gamma_t (.) k against the boundary and (gamma_t / gamma_i) (.) k_i
+ * for record i, per key row. */
 int32_t leapq_append(leapq_layer *layer, const void *q, const void *k, const void *v,
                      const float *alpha, const float *beta, float *o, void *stream);
 
@@ -184,7 +198,9 @@ typedef struct leapq_gate {
  * Everything else, including the record written and the output, is as for
  * leapq_append with the gated alpha, beta, q and k.  gate must not be NULL
  * (LEAPQ_ERR_NULL), its pointers 4-byte aligned (LEAPQ_ERR_ALIGN), norm_eps
- * finite and >= 0, q_scale finite and reserved zero (LEAPQ_ERR_RANGE). */
+ * finite and >= 0, q_scale finite and reserved zero (LEAPQ_ERR_RANGE).  The
+ * gates are the scalar-decay (GDN) ones: a layer with LEAPQ_DECAY_CHANNEL
+ * gets LEAPQ_ERR_RANGE. */
 int32_t leapq_append_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
                            const void *v, const float *a, const float *b, float *o, void *stream);
 
@@ -208,9 +224,11 @@ int32_t leapq_dequant(const leapq_layer *layer, int32_t what, float *S_out, void
 /* Unquantized per-token GDN decode on a dense state, in place (the fp32-state
  * and bf16-state baselines).  S [heads][128][128] in state_dtype (device,
  * natural row-major layout); q, k, v in cfg->in_dtype; alpha, beta fp32;
- * o fp32.  Per token: S = alpha S; u = beta (v - S^T k); S += k u^T;
- * o = S^T q; a bf16 state is widened, updated in fp32 and rounded to nearest
- * even on store.  Uses batch, heads, dk, dv and in_dtype of cfg only. */
+ * o fp32.  Per token: S = alpha S (row r scaled by alpha[r] with cfg->decay
+ * = LEAPQ_DECAY_CHANNEL, alpha then [heads][128]); u = beta (v - S^T k);
+ * S += k u^T; o = S^T q; a bf16 state is widened, updated in fp32 and
+ * rounded to nearest even on store.  Uses batch, heads, dk, dv, in_dtype and
+ * decay of cfg only. */
 int32_t leapq_gdn_decode(const leapq_config *cfg, int32_t state_dtype, void *S, const void *q,
                          const void *k, const void *v, const float *alpha, const float *beta,
                          float *o, void *stream);

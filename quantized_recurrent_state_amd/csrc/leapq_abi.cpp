@@ -26,6 +26,7 @@ int32_t check_config(const leapq_config *c)
     if (c->batch < 1 || c->heads < 1) return LEAPQ_ERR_RANGE;
     if ((int64_t)c->batch * c->heads >= kMaxHeads) return LEAPQ_ERR_RANGE;
     if (c->in_dtype != LEAPQ_F32 && c->in_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
+    if (c->decay != LEAPQ_DECAY_SCALAR && c->decay != LEAPQ_DECAY_CHANNEL) return LEAPQ_ERR_RANGE;
     return LEAPQ_OK;
 }
 
@@ -38,7 +39,8 @@ int32_t check_method_config(const leapq_config *c)
     if (c->smoothing != 0 && c->smoothing != 1) return LEAPQ_ERR_RANGE;
     if (!(c->sigma_floor > 0.0f) || c->sigma_floor > 3.0e38f) return LEAPQ_ERR_RANGE;
     if (c->qk_norm != 0 && c->qk_norm != 1) return LEAPQ_ERR_RANGE;
-    if (c->reserved[0] || c->reserved[1]) return LEAPQ_ERR_RANGE;
+    if (c->decay == LEAPQ_DECAY_CHANNEL && c->qk_norm) return LEAPQ_ERR_RANGE;
+    if (c->reserved) return LEAPQ_ERR_RANGE;
     return LEAPQ_OK;
 }
 
@@ -51,6 +53,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     const uint64_t H = (uint64_t)c->batch * (uint64_t)c->heads;
     const uint64_t C = (uint64_t)c->n_comp, W = (uint64_t)c->window;
     const uint64_t kb = key_bf16(c) ? 2 : 4;  // record key element
+    const uint64_t gw = c->decay == LEAPQ_DECAY_CHANNEL ? kD : 1;  // record decay values
     uint64_t off = 0;
     L->off_codes = off;
     off = round_up(off + H * kD * kD);
@@ -63,14 +66,14 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_comp_vec = off;
     off = round_up(off + H * C * kD * 4);
     L->off_rec_gamma = off;
-    off = round_up(off + H * W * 4);
+    off = round_up(off + H * W * gw * 4);
     L->off_rec_k = off;
     off = round_up(off + H * W * kD * kb);
     L->off_rec_u = off;
     off = round_up(off + H * W * kD * 4);
     L->total_bytes = off;
     L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * kD * 4;
-    L->record_bytes_per_head = W * (4 + kD * kb + kD * 4);
+    L->record_bytes_per_head = W * (4 * gw + kD * kb + kD * 4);
 }
 
 int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
@@ -95,6 +98,7 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->C = layer->cfg.n_comp;
     sv->W = layer->cfg.window;
     sv->key_bf16 = key_bf16(&layer->cfg);
+    sv->kda = layer->cfg.decay == LEAPQ_DECAY_CHANNEL;
     return LEAPQ_OK;
 }
 
@@ -137,6 +141,7 @@ leapq::GateArgs plain_gate(const leapq_config &c) { return {nullptr, nullptr, 1.
 int32_t gate_of(const leapq_layer *layer, const leapq_gate *g, leapq::GateArgs *out)
 {
     if (!g || !g->A_log || !g->dt_bias) return LEAPQ_ERR_NULL;
+    if (layer->cfg.decay != LEAPQ_DECAY_SCALAR) return LEAPQ_ERR_RANGE;
     if (!aligned(g->A_log, 4) || !aligned(g->dt_bias, 4)) return LEAPQ_ERR_ALIGN;
     if (g->reserved[0] || g->reserved[1]) return LEAPQ_ERR_RANGE;
     if (!(g->norm_eps >= 0.0f) || g->norm_eps > 3.0e38f) return LEAPQ_ERR_RANGE;
@@ -145,10 +150,11 @@ int32_t gate_of(const leapq_layer *layer, const leapq_gate *g, leapq::GateArgs *
     return LEAPQ_OK;
 }
 
-int32_t check_token(const void *q, const void *k, const void *v, const float *a, const float *b, const float *o)
+int32_t check_token(const void *q, const void *k, const void *v, const float *a, const float *b, const float *o,
+                    bool kda)
 {
     if (!q || !k || !v || !a || !b || !o) return LEAPQ_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(a, 4) ||
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(a, kda ? 16 : 4) ||
         !aligned(b, 4))
         return LEAPQ_ERR_ALIGN;
     return LEAPQ_OK;
@@ -162,7 +168,7 @@ int32_t append_impl(leapq_layer *layer, const leapq_gate *gate, const void *q, c
     if (st != LEAPQ_OK) return st;
     leapq::GateArgs g = plain_gate(layer->cfg);
     if (gate && (st = gate_of(layer, gate, &g)) != LEAPQ_OK) return st;
-    if ((st = check_token(q, k, v, alpha, beta, o)) != LEAPQ_OK) return st;
+    if ((st = check_token(q, k, v, alpha, beta, o, sv.kda)) != LEAPQ_OK) return st;
     if (layer->n_records >= layer->cfg.window) return LEAPQ_ERR_WINDOW_FULL;
     st = hip_status(leapq::launch_append(sv, heads_of(&layer->cfg), layer->n_records,
                                          layer->cfg.in_dtype == LEAPQ_BF16, q, k, v, alpha, beta, o, g,
@@ -179,7 +185,7 @@ int32_t append_fold_impl(leapq_layer *layer, const leapq_gate *gate, const void 
     if (st != LEAPQ_OK) return st;
     leapq::GateArgs g = plain_gate(layer->cfg);
     if (gate && (st = gate_of(layer, gate, &g)) != LEAPQ_OK) return st;
-    if ((st = check_token(q, k, v, alpha, beta, o)) != LEAPQ_OK) return st;
+    if ((st = check_token(q, k, v, alpha, beta, o, sv.kda)) != LEAPQ_OK) return st;
     if (layer->n_records != layer->cfg.window - 1) return LEAPQ_ERR_RANGE;
     const int heads = heads_of(&layer->cfg);
     const int bf16 = layer->cfg.in_dtype == LEAPQ_BF16;
@@ -257,11 +263,12 @@ int32_t leapq_gdn_decode(const leapq_config *cfg, int32_t state_dtype, void *S, 
     if (st != LEAPQ_OK) return st;
     if (state_dtype != LEAPQ_F32 && state_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
     if (!S || !q || !k || !v || !alpha || !beta || !o) return LEAPQ_ERR_NULL;
+    const int kda = cfg->decay == LEAPQ_DECAY_CHANNEL;
     if (!aligned(S, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(alpha, 4) || !aligned(beta, 4))
+        !aligned(alpha, kda ? 16 : 4) || !aligned(beta, 4))
         return LEAPQ_ERR_ALIGN;
     return hip_status(leapq::launch_gdn_decode(heads_of(cfg), state_dtype == LEAPQ_BF16,
-                                               cfg->in_dtype == LEAPQ_BF16, S, q, k, v, alpha, beta, o,
+                                               cfg->in_dtype == LEAPQ_BF16, kda, S, q, k, v, alpha, beta, o,
                                                (hipStream_t)stream));
 }
 

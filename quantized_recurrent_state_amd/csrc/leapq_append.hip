@@ -31,7 +31,7 @@ namespace leapq {
 namespace {
 using namespace dev;
 
-template <typename T, typename K, bool GATED, bool NORM>
+template <typename T, typename K, bool GATED, bool NORM, bool CH>
 __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__restrict__ qin,
                                                 const T *__restrict__ kin, const T *__restrict__ vin,
                                                 const float *__restrict__ alpha, const float *__restrict__ beta,
@@ -40,11 +40,11 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     extern __shared__ float dsm[];
     const MMap a = mmap();
     const int h = blockIdx.x;
-    const HeadLds<T, K> L(dsm, n, sv.C);
-    float *dots = dsm + head_lds_floats<T, K>(n, sv.C);
+    const HeadLds<T, K, CH> L(dsm, n, sv.C);
+    float *dots = dsm + head_lds_floats<T, K, CH>(n, sv.C);
     uint4 qc[4];
-    append_issue<T, K>(sv, n, h, qin, kin, vin, a, L, qc);
-    float a_h = sload(alpha, h);
+    append_issue<T, K, CH>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    float a_h = CH ? 1.0f : sload(alpha, h);  // with CH the decay vector is staged in LDS
     float b_h = sload(beta, h);
     if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
     wait_lds_copies();
@@ -53,18 +53,18 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
         a_h = dots[kGateSlot];
         b_h = dots[kGateSlot + 1];
     }
-    append_compute<T, K, false, NORM>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    append_compute<T, K, false, NORM, CH>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
 }
 
 }  // namespace
 
-template <typename T, typename K, bool GATED, bool NORM>
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false>
 static void launch_append_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, float *o, const GateArgs &g, hipStream_t s)
 {
-    const size_t lds = sizeof(float) * (head_lds_floats<T, K>(n, sv.C) + kDotFloats);
-    hipLaunchKernelGGL((k_append<T, K, GATED, NORM>), dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q, (const T *)k,
-                       (const T *)v, alpha, beta, o, g);
+    const size_t lds = sizeof(float) * (head_lds_floats<T, K, CH>(n, sv.C) + kDotFloats);
+    hipLaunchKernelGGL((k_append<T, K, GATED, NORM, CH>), dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q,
+                       (const T *)k, (const T *)v, alpha, beta, o, g);
 }
 
 hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
@@ -72,9 +72,15 @@ hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const 
                          hipStream_t s)
 {
     // (inputs, keys): (fp32, fp32), (bf16, bf16), or (bf16, fp32) for a layer
-    // whose keys are fp32 because its gated appends normalize k
+    // whose keys are fp32 because its gated appends normalize k; per-channel
+    // decay comes with keys in the input dtype and no gates
     const bool kb = sv.key_bf16;
-    if (!g.gated) {
+    if (sv.kda) {
+        if (!bf16)
+            launch_append_t<float, float, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+        else
+            launch_append_t<uint16_t, uint16_t, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+    } else if (!g.gated) {
         if (!bf16)
             launch_append_t<float, float, false, false>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
         else if (kb)

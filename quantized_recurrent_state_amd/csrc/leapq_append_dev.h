@@ -31,40 +31,53 @@ struct InLds<uint16_t> {
 // the input dtype stores the token's k exactly unless the append normalizes
 // it, which needs fp32), then the correction (fp32, stored order); keys take
 // kbytes, a staged record stride floats.
-template <typename T>
+// With per-channel decay (CH) a record also holds its cumulative decay as a
+// 128-vector; the staged record is then [decay | correction | key].
+template <typename T, bool CH = false>
 struct Rec {
     static constexpr int kbytes = D * (int)sizeof(T);
     static constexpr int kf = kbytes / 4;
-    static constexpr int stride = kf + D;
+    static constexpr int goff = 0;               // CH: the decay vector
+    static constexpr int uoff = CH ? D : kf;     // the correction
+    static constexpr int koff = CH ? 2 * D : 0;  // the key
+    static constexpr int stride = kf + D + (CH ? D : 0);
     static constexpr int kpieces = kbytes / 16;
-    __device__ static float key(const float *rec, int r) { return InLds<T>::get(rec, 0, r); }
+    __device__ static float key(const float *rec, int r) { return InLds<T>::get(rec + koff, 0, r); }
 };
 
-// Copies record g of a head into LDS at dst (stride floats) with one
-// LDS-direct load per lane: the key's 16-byte pieces, then the correction's.
-template <typename T>
+// Copies record g of a head into LDS at dst (stride floats) with LDS-direct
+// loads of 16 bytes per lane: without CH, the key's pieces then the
+// correction's in one load; with CH, the decay's and the correction's in one
+// load, then the key's.
+template <typename T, bool CH = false>
 __device__ __forceinline__ void copy_record(const HeadState &hs, int g, int l, float *dst)
 {
-    constexpr int kp = Rec<T>::kpieces;
-    if (kp + 32 >= 64 || l < kp + 32)
-        lds_copy16(l < kp ? static_cast<const void *>(hs.rk + g * Rec<T>::kbytes + 16 * l)
-                          : static_cast<const void *>(hs.ru + g * D + 4 * (l - kp)),
-                   dst);
+    constexpr int kp = Rec<T, CH>::kpieces;
+    if constexpr (!CH) {
+        if (kp + 32 >= 64 || l < kp + 32)
+            lds_copy16(l < kp ? static_cast<const void *>(hs.rk + g * Rec<T>::kbytes + 16 * l)
+                              : static_cast<const void *>(hs.ru + g * D + 4 * (l - kp)),
+                       dst);
+    } else {
+        lds_copy16(l < 32 ? hs.rgam + g * D + 4 * l : hs.ru + g * D + 4 * (l - 32), dst);
+        if (kp >= 64 || l < kp) lds_copy16(hs.rk + g * Rec<T, CH>::kbytes + 16 * l, dst + Rec<T, CH>::koff);
+    }
 }
 
 // LDS of one head in floats: records [n][stride] (keys K), lines [C][128],
-// rho [128], sigma [128], inputs (k, q, v as T), indices [8], decays [64]
-template <typename T, typename K>
+// rho [128], sigma [128], inputs (k, q, v as T), indices [8], then the
+// record decays [64] or, with CH, the token's decay vector [128]
+template <typename T, typename K, bool CH = false>
 __host__ __device__ constexpr int head_lds_floats(int n, int C)
 {
-    return n * Rec<K>::stride + C * 128 + 256 + InLds<T>::floats + 8 + 64;
+    return n * Rec<K, CH>::stride + C * 128 + 256 + InLds<T>::floats + 8 + (CH ? 128 : 64);
 }
 // per-workgroup results of the dot jobs: coefficients [2][64], column-token
 // dots [2][8], k.q [1], then the gated alpha and beta [2] (+1 pad)
 constexpr int kDotFloats = 128 + 16 + 4;
 constexpr int kGateSlot = 145;
 
-template <typename T, typename K>
+template <typename T, typename K, bool CH = false>
 struct HeadLds {
     float *rec, *cv, *srho, *ssig, *sin_, *sgam;
     int *sidx;
@@ -75,7 +88,7 @@ struct HeadLds {
     __device__ HeadLds(float *base, int n, int C)
     {
         rec = base;
-        cv = rec + n * Rec<K>::stride;
+        cv = rec + n * Rec<K, CH>::stride;
         srho = cv + C * D;
         ssig = srho + D;
         sin_ = ssig + D;
@@ -98,14 +111,15 @@ __device__ __forceinline__ void wait_lds_copies()
 // Issues every global load of head h: every operand other than the codes
 // into the LDS buffer L by LDS-direct copies, then the thread's 64 codes into
 // qc as the wave's last kCodeLoads vector loads.
-template <typename T, typename K>
+template <typename T, typename K, bool CH = false>
 __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
                                              const T *__restrict__ kin, const T *__restrict__ vin,
-                                             const MMap &a, const HeadLds<T, K> &L, uint4 (&qc)[4])
+                                             const MMap &a, const HeadLds<T, K, CH> &L, uint4 (&qc)[4],
+                                             const float *__restrict__ alpha = nullptr)
 {
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
-    for (int rr = w; rr < n; rr += 4) copy_record<K>(hs, rr, l, L.rec + rr * Rec<K>::stride);
+    for (int rr = w; rr < n; rr += 4) copy_record<K, CH>(hs, rr, l, L.rec + rr * Rec<K, CH>::stride);
     for (int pair = 2 * w; pair < C; pair += 8)
         if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
     if (w == 0) {
@@ -125,6 +139,9 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
         }
     } else if (w == 2) {
         if (l < C) lds_copy4(hs.cidx + l, L.sidx);
+    } else if constexpr (CH) {
+        // the token's decay vector (the records carry their own)
+        if (l < 32) lds_copy16(alpha + (size_t)h * D + 4 * l, L.sgam);
     } else {
         if (l < n) lds_copy4(hs.rgam + l, L.sgam);
     }
@@ -172,12 +189,13 @@ __device__ __forceinline__ void gate_issue(const GateArgs &g, int h, const MMap 
 // dot (the record key is then the normalized k in fp32).  Expects the LDS copies landed and visible (wait_lds_copies() and a
 // barrier); the codes are waited for at their first use.  Contains one
 // lds_barrier (dot jobs -> residual read and tail).
-template <typename T, typename K, bool REC_LDS = false, bool NORM = false>
+template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool CH = false>
 __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a,
-                                               const HeadLds<T, K> &L, float *dots, const uint4 (&qc)[4], float a_h,
-                                               float b_h, float *__restrict__ o, float q_scale = 1.0f,
+                                               const HeadLds<T, K, CH> &L, float *dots, const uint4 (&qc)[4],
+                                               float a_h, float b_h, float *__restrict__ o, float q_scale = 1.0f,
                                                float eps = 0.0f)
 {
+    using R = Rec<K, CH>;
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
     const float *rec = L.rec, *cv = L.cv, *srho = L.srho, *ssig = L.ssig, *sin_ = L.sin_, *sgam = L.sgam;
@@ -200,33 +218,64 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     k1 = nk(k1);
     q0 = nq(q0);
     q1 = nq(q1);
+    // decay: the scalar gamma_t = gamma_{n-1} * alpha, or (CH) per row
+    // gamma_t[r] = gamma_{n-1}[r] * alpha[r] from the staged previous record
+    // and the token's staged alpha (sgam); with CH the boundary is read with
+    // gamma_t (.) k and gamma_t (.) q
+    const float *gprev = rec + (n > 0 ? n - 1 : 0) * R::stride + R::goff;
+    auto gt_row = [&](int r) { return (n > 0 ? gprev[r] : 1.0f) * sgam[r]; };
     float rh[4], kr[4], qr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         rh[p] = srho[a.row(p)];
         kr[p] = nk(InLds<T>::get(sin_, 0, a.row(p)));
         qr[p] = nq(InLds<T>::get(sin_, 1, a.row(p)));
+        if constexpr (CH) {
+            const float g = gt_row(a.row(p));
+            kr[p] = g * kr[p];
+            qr[p] = g * qr[p];
+        }
     }
     const float sig_c = ssig[c];
     const float v_c = InLds<T>::get(sin_, 2, c);
-    const float gt = (n > 0 ? sgam[n - 1] : 1.0f) * a_h;
-    const float ci_l = l < n ? gt / sgam[l] : 0.0f;  // c_i of record i = lane, for the dot jobs
+    float gt = 1.0f, ci_l = 0.0f, gt0 = 1.0f, gt1 = 1.0f;
+    if constexpr (CH) {
+        gt0 = gt_row(l);
+        gt1 = gt_row(l + 64);
+    } else {
+        gt = (n > 0 ? sgam[n - 1] : 1.0f) * a_h;
+        ci_l = l < n ? gt / sgam[l] : 0.0f;  // c_i of record i = lane, for the dot jobs
+    }
 
     // ---- per-head dot products (operands in LDS; the codes may still be in
     // flight), one wave per job:
-    // job r < n: c_r * (k_r . k), c_r * (k_r . q); job n: (k . q);
-    // job n+1+jj: (line_jj . k), (line_jj . q) for column tokens
+    // job r < n: c_r * (k_r . k), c_r * (k_r . q), or with CH
+    //            (w_r . k), (w_r . q) with w_r = (gamma_t / gamma_r) (.) k_r;
+    // job n: (k . q);
+    // job n+1+jj: (line_jj . x), (line_jj . y) for column tokens, x = k and
+    //            y = q, or with CH x = gamma_t (.) k and y = gamma_t (.) q
     const int njobs = n + 1 + C;
     for (int job = w; job < njobs; job += 4) {
         if (job < n) {
-            const float *kj = rec + job * Rec<K>::stride;
-            const float a0 = Rec<K>::key(kj, l), a1 = Rec<K>::key(kj, l + 64);
+            const float *kj = rec + job * R::stride;
+            float a0 = R::key(kj, l), a1 = R::key(kj, l + 64);
+            if constexpr (CH) {
+                a0 = (gt0 / kj[R::goff + l]) * a0;
+                a1 = (gt1 / kj[R::goff + l + 64]) * a1;
+            }
             const float dk = wdot(a0, a1, k0, k1);
             const float dq = wdot(a0, a1, q0, q1);
-            const float ci = rdl(ci_l, job);
-            if (l == 0) {
-                coef[job] = ci * dk;
-                coef[64 + job] = ci * dq;
+            if constexpr (CH) {
+                if (l == 0) {
+                    coef[job] = dk;
+                    coef[64 + job] = dq;
+                }
+            } else {
+                const float ci = rdl(ci_l, job);
+                if (l == 0) {
+                    coef[job] = ci * dk;
+                    coef[64 + job] = ci * dq;
+                }
             }
         } else if (job == n) {
             const float d = wdot(k0, k1, q0, q1);
@@ -235,8 +284,8 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
             const int jj = job - n - 1;
             if (sidx[jj] >= D) {
                 const float a0 = cv[jj * D + l], a1 = cv[jj * D + l + 64];
-                const float dk = wdot(a0, a1, k0, k1);
-                const float dq = wdot(a0, a1, q0, q1);
+                const float dk = wdot(a0, a1, CH ? gt0 * k0 : k0, CH ? gt1 * k1 : k1);
+                const float dq = wdot(a0, a1, CH ? gt0 * q0 : q0, CH ? gt1 * q1 : q1);
                 if (l == 0) {
                     cdot[jj] = dk;
                     cdot[8 + jj] = dq;
@@ -291,23 +340,24 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
         if (id < 0) continue;
         if (id < D) {
             const float x = InLds<T>::get(sin_, vec, id);
-            b = fma_(vec ? nq(x) : nk(x), cv[jj * D + c], b);
-        }
-        else if (id - D == c)
+            float xr = vec ? nq(x) : nk(x);
+            if constexpr (CH) xr = gt_row(id) * xr;
+            b = fma_(xr, cv[jj * D + c], b);
+        } else if (id - D == c) {
             b = b + cdot[vec * 8 + jj];
+        }
     }
-    float acc = gt * b;
+    float acc = CH ? b : gt * b;
     const int uc = upos(c);
-    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * Rec<K>::stride + Rec<K>::kf + uc], acc);
+    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * R::stride + R::uoff + uc], acc);
     // k lanes form u; q lanes receive it from lane l-16 and finish o
     const float u = b_h * (v_c - acc);
     auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
     const float u_from_k = __uint_as_float(sw[0]);
     // the record goes to HBM, or (REC_LDS) into slot n of the staged records
-    float *ru = REC_LDS ? L.rec + n * Rec<K>::stride + Rec<K>::kf : hs.ru + n * D;
-    uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * Rec<K>::stride)
-                           : reinterpret_cast<uint32_t *>(hs.rk + n * Rec<K>::kbytes);
-    float *rg = REC_LDS ? L.sgam : hs.rgam;
+    float *ru = REC_LDS ? L.rec + n * R::stride + R::uoff : hs.ru + n * D;
+    uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * R::stride + R::koff)
+                           : reinterpret_cast<uint32_t *>(hs.rk + n * R::kbytes);
     if (vec == 0) {
         ru[uc] = u;
     } else {
@@ -318,13 +368,20 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
             // the key is the token's k as staged (the first kbytes of the inputs)
             const uint32_t *kw = reinterpret_cast<const uint32_t *>(sin_);
             rk[l] = kw[l];
-            if (Rec<K>::kf > 64) rk[l + 64] = kw[l + 64];
+            if (R::kf > 64) rk[l + 64] = kw[l + 64];
         } else {
             static_assert(std::is_same<K, float>::value, "normalized or widened keys are fp32");
             rk[l] = __float_as_uint(k0);
             rk[l + 64] = __float_as_uint(k1);
         }
-        if (l == 0) rg[n] = gt;
+        if constexpr (CH) {
+            float *rg = REC_LDS ? L.rec + n * R::stride + R::goff : hs.rgam + n * D;
+            rg[l] = gt0;
+            rg[l + 64] = gt1;
+        } else {
+            float *rg = REC_LDS ? L.sgam : hs.rgam;
+            if (l == 0) rg[n] = gt;
+        }
     }
 }
 

@@ -3,8 +3,9 @@
 //
 // One token ("Recurrent-state quantization for linear attention: a first GPU
 // kernel", Background; "LeapQuant: Efficient Linear Attention with Accurate
-// Recurrent State Quantization", App. A with D_t = alpha I, b_t = beta):
-//   S = alpha S;  r = S^T k;  u = beta (v - r);  S = S + k u^T;  o = S^T q
+// Recurrent State Quantization", App. A with D_t = alpha I, or D_t =
+// Diag(alpha) per key row for per-channel decay (CH), and b_t = beta):
+//   S = D_t S;  r = S^T k;  u = beta (v - r);  S = S + k u^T;  o = S^T q
 // with S[r][c] indexed (key row, value column).  A bf16 state is widened,
 // updated in fp32 and rounded to nearest even on store.  The reads are
 // canonical-tree dot products over the rows; the update is one fma per
@@ -79,7 +80,7 @@ __device__ __forceinline__ void store_row16<uint16_t>(uint16_t *p, const float (
     }
 }
 
-template <typename TS, typename TI>
+template <typename TS, typename TI, bool CH>
 __global__ __launch_bounds__(NT) void k_gdn_decode(TS *__restrict__ Sg, const TI *__restrict__ qin,
                                                     const TI *__restrict__ kin, const TI *__restrict__ vin,
                                                     const float *__restrict__ alpha,
@@ -91,10 +92,10 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(TS *__restrict__ Sg, const TI
     const int h = blockIdx.x;
     TS *Sh = Sg + (size_t)h * D * D;
     const TI *qh = qin + (size_t)h * D, *kh = kin + (size_t)h * D;
-    const float al = alpha[h];
-    float S[4][16], kr[4], qr[4];
+    float S[4][16], kr[4], qr[4], al[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+        al[p] = CH ? alpha[(size_t)h * D + a.row(p)] : alpha[h];
         kr[p] = ld_in<TI>(kh, a.row(p));
         qr[p] = ld_in<TI>(qh, a.row(p));
         load_row16<TS>(Sh + a.row(p) * D + 16 * a.j, S[p]);
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(TS *__restrict__ Sg, const TI
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int m = 0; m < 16; ++m) S[p][m] = al * S[p][m];
+        for (int m = 0; m < 16; ++m) S[p][m] = al[p] * S[p][m];
     float v[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
@@ -137,24 +138,34 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(TS *__restrict__ Sg, const TI
 
 }  // namespace
 
-hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, void *S, const void *q, const void *k,
-                             const void *v, const float *alpha, const float *beta, float *o, hipStream_t s)
+template <bool CH>
+static void launch_gdn_t(int heads, int state_bf16, int in_bf16, void *S, const void *q, const void *k,
+                         const void *v, const float *alpha, const float *beta, float *o, hipStream_t s)
 {
     if (state_bf16) {
         if (in_bf16)
-            hipLaunchKernelGGL((k_gdn_decode<uint16_t, uint16_t>), dim3(heads), dim3(NT), 0, s, (uint16_t *)S,
+            hipLaunchKernelGGL((k_gdn_decode<uint16_t, uint16_t, CH>), dim3(heads), dim3(NT), 0, s, (uint16_t *)S,
                                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, beta, o);
         else
-            hipLaunchKernelGGL((k_gdn_decode<uint16_t, float>), dim3(heads), dim3(NT), 0, s, (uint16_t *)S,
+            hipLaunchKernelGGL((k_gdn_decode<uint16_t, float, CH>), dim3(heads), dim3(NT), 0, s, (uint16_t *)S,
                                (const float *)q, (const float *)k, (const float *)v, alpha, beta, o);
     } else {
         if (in_bf16)
-            hipLaunchKernelGGL((k_gdn_decode<float, uint16_t>), dim3(heads), dim3(NT), 0, s, (float *)S,
+            hipLaunchKernelGGL((k_gdn_decode<float, uint16_t, CH>), dim3(heads), dim3(NT), 0, s, (float *)S,
                                (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, alpha, beta, o);
         else
-            hipLaunchKernelGGL((k_gdn_decode<float, float>), dim3(heads), dim3(NT), 0, s, (float *)S,
+            hipLaunchKernelGGL((k_gdn_decode<float, float, CH>), dim3(heads), dim3(NT), 0, s, (float *)S,
                                (const float *)q, (const float *)k, (const float *)v, alpha, beta, o);
     }
+}
+
+hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, int kda, void *S, const void *q, const void *k,
+                             const void *v, const float *alpha, const float *beta, float *o, hipStream_t s)
+{
+    if (kda)
+        launch_gdn_t<true>(heads, state_bf16, in_bf16, S, q, k, v, alpha, beta, o, s);
+    else
+        launch_gdn_t<false>(heads, state_bf16, in_bf16, S, q, k, v, alpha, beta, o, s);
     return hipGetLastError();
 }
 

@@ -43,13 +43,15 @@ typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 // Operands of one head staged from HBM, and the work arrays of the steps
 // after the rebuild.
+template <int RS>
 struct FoldStage {
-    float rec[16 * 256];  // a chunk of up to 16 records (Rec<T>::stride floats each)
+    float rec[16 * RS];  // a chunk of up to 16 records (RS = Rec<K, CH>::stride floats each)
     float lines[8 * 128];
     float rho[128];
     float sig[128];
     int idx[8];
-    float gam[64];
+    float gam[64];   // record decays (scalar decay)
+    float gW[128];   // the last record's decay vector (per-channel decay)
 };
 struct FoldWork {
     float colE[2][128];      // column energies (two buffers, see extraction)
@@ -59,8 +61,10 @@ struct FoldWork {
     float sinv[128];         // 1 / sigma_c
 };
 
-// Copies boundary fields (lines, rho, sigma, indices) and n decays to LDS.
-__device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, int C, int n, FoldStage &sm)
+// Copies boundary fields (lines, rho, sigma, indices) and the decays to LDS:
+// the n record decays, or with CH the last record's decay vector.
+template <bool CH, typename Stage>
+__device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, int C, int n, Stage &sm)
 {
     const int l = a.l, w = a.w;
     for (int pair = 2 * w; pair < C; pair += 8)
@@ -70,14 +74,18 @@ __device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, 
     } else if (w == 1) {
         if (l < C) lds_copy4(hs.cidx + l, sm.idx);
     } else if (w == 2) {
-        if (l < n) lds_copy4(hs.rgam + l, sm.gam);
+        if constexpr (CH) {
+            if (n > 0 && l < 32) lds_copy16(hs.rgam + (size_t)(n - 1) * D + 4 * l, sm.gW);
+        } else {
+            if (l < n) lds_copy4(hs.rgam + l, sm.gam);
+        }
     }
 }
 
-template <typename T>
-__device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, FoldStage &sm)
+template <typename K, bool CH, typename Stage>
+__device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, Stage &sm)
 {
-    for (int rr = a.w; rr < cnt; rr += 4) copy_record<T>(hs, base + rr, a.l, sm.rec + rr * Rec<T>::stride);
+    for (int rr = a.w; rr < cnt; rr += 4) copy_record<K, CH>(hs, base + rr, a.l, sm.rec + rr * Rec<K, CH>::stride);
 }
 
 __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, uint4 (&qc)[4])
@@ -88,18 +96,24 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 
 // Current state in the tile.  qc: the thread's 4 code chunks.  Expects
 // stage_small() done and visible and, if n > 0, records 0..min(n,16)-1
-// staged and visible.  Contains barriers when n > 16.  T: the key dtype.
-template <typename T>
+// staged and visible.  Contains barriers when n > 16.  K: the key dtype.
+// CH: per-channel decay, gamma_n[r] read from gW (the last record's decay
+// vector), every scale and record coefficient taken per row.
+template <typename K, bool CH, typename Stage>
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
-                                        bool lines, FoldStage &sm, float (&S)[4][16])
+                                        bool lines, Stage &sm, float (&S)[4][16], const float *gW = nullptr)
 {
-    const float gn = n > 0 ? sm.gam[n - 1] : 1.0f;
+    using R = Rec<K, CH>;
+    const float gn = CH ? 1.0f : (n > 0 ? sm.gam[n - 1] : 1.0f);
+    float gr[4];  // gamma_n of the thread's rows
+#pragma unroll
+    for (int p = 0; p < 4; ++p) gr[p] = CH ? (n > 0 ? gW[a.row(p)] : 1.0f) : gn;
     float sg[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) sg[m] = sm.sig[a.col(m)];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const float ap = gn * sm.rho[a.row(p)];
+        const float ap = gr[p] * sm.rho[a.row(p)];
         const uint32_t cw[4] = {qc[p].x, qc[p].y, qc[p].z, qc[p].w};
 #pragma unroll
         for (int m = 0; m < 16; ++m) TS(S, p, m) = (code_f(cw[m >> 2], m & 3) * ap) * sg[m];
@@ -128,19 +142,19 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
             if (rl[p] >= 0) {
                 const float *v = sm.lines + rl[p] * D;
 #pragma unroll
-                for (int m = 0; m < 16; ++m) TS(S, p, m) = TS(S, p, m) + gn * v[a.col(m)];
+                for (int m = 0; m < 16; ++m) TS(S, p, m) = TS(S, p, m) + gr[p] * v[a.col(m)];
             }
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             if (cl[m] >= 0) {
                 const float *v = sm.lines + cl[m] * D;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) TS(S, p, m) = TS(S, p, m) + gn * v[a.row(p)];
+                for (int p = 0; p < 4; ++p) TS(S, p, m) = TS(S, p, m) + gr[p] * v[a.row(p)];
             }
     }
     // through the accumulators even when n == 0: one definition of S after
     // this point keeps it in one set of registers
-    const float ci_l = a.l < n ? gn / sm.gam[a.l] : 0.0f;  // c_i for record i = lane
+    const float ci_l = !CH && a.l < n ? gn / sm.gam[a.l] : 0.0f;  // c_i for record i = lane (scalar decay)
     f32x32 acc[2];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -150,32 +164,46 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
         const int cnt = n - base < 16 ? n - base : 16;
         if (base > 0) {
             __syncthreads();  // the previous chunk is consumed
-            stage_records<T>(a, hs, base, cnt, sm);
+            stage_records<K, CH>(a, hs, base, cnt, sm);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
         // records r of the chunk in order; four per iteration, then the rest.
-        // B lane l of instruction q carries key row a.i + 32 (a.h + 2q).
+        // B lane l of instruction q carries key row a.i + 32 (a.h + 2q); with
+        // CH its coefficient is gamma_n[row] / gamma_i[row].
         const int kr0 = a.i + 32 * a.h;
+        const float gw0 = CH && n > 0 ? gW[kr0] : 1.0f, gw1 = CH && n > 0 ? gW[kr0 + 64] : 1.0f;
         int r = 0;
         for (; r + 4 <= cnt; r += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float ci = rdl(ci_l, base + r + u);
-                const float *rr = sm.rec + (r + u) * Rec<T>::stride;
-                const float b0 = ci * Rec<T>::key(rr, kr0);
-                const float b1 = ci * Rec<T>::key(rr, kr0 + 64);
-                const float au = rr[Rec<T>::kf + 32 * a.w + a.jp];
+                const float *rr = sm.rec + (r + u) * R::stride;
+                float b0, b1;
+                if constexpr (CH) {
+                    b0 = (gw0 / rr[R::goff + kr0]) * R::key(rr, kr0);
+                    b1 = (gw1 / rr[R::goff + kr0 + 64]) * R::key(rr, kr0 + 64);
+                } else {
+                    const float ci = rdl(ci_l, base + r + u);
+                    b0 = ci * R::key(rr, kr0);
+                    b1 = ci * R::key(rr, kr0 + 64);
+                }
+                const float au = rr[R::uoff + 32 * a.w + a.jp];
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
             }
         }
         for (; r < cnt; ++r) {
-            const float ci = rdl(ci_l, base + r);
-            const float *rr = sm.rec + r * Rec<T>::stride;
-            const float b0 = ci * Rec<T>::key(rr, kr0);
-            const float b1 = ci * Rec<T>::key(rr, kr0 + 64);
-            const float au = rr[Rec<T>::kf + 32 * a.w + a.jp];
+            const float *rr = sm.rec + r * R::stride;
+            float b0, b1;
+            if constexpr (CH) {
+                b0 = (gw0 / rr[R::goff + kr0]) * R::key(rr, kr0);
+                b1 = (gw1 / rr[R::goff + kr0 + 64]) * R::key(rr, kr0 + 64);
+            } else {
+                const float ci = rdl(ci_l, base + r);
+                b0 = ci * R::key(rr, kr0);
+                b1 = ci * R::key(rr, kr0 + 64);
+            }
+            const float au = rr[R::uoff + 32 * a.w + a.jp];
             acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
         }
@@ -446,22 +474,22 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename T, int CT>
+template <typename K, int CT, bool CH>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
-    __shared__ FoldStage st;
+    __shared__ FoldStage<Rec<K, CH>::stride> st;
     __shared__ FoldWork wk;
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     uint4 qc[4];
     load_codes(a, hs, qc);
-    stage_small(a, hs, sv.C, n, st);
-    stage_records<T>(a, hs, 0, n < 16 ? n : 16, st);
+    stage_small<CH>(a, hs, sv.C, n, st);
+    stage_records<K, CH>(a, hs, 0, n < 16 ? n : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<T>(a, hs, qc, sv.C, n, true, st, S);
+    rebuild<K, CH>(a, hs, qc, sv.C, n, true, st, S, st.gW);
     // no barrier: the quantization writes only LDS arrays the rebuild does
     // not read, and each thread rewrites only the codes it loaded
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
@@ -474,23 +502,26 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
 // empties the buffer), and the fold rebuilds from the same registers and LDS
 // instead of reading the boundary and the records again.  The results are
 // those of leapq_append followed by leapq_fold.
-template <typename T, typename K, bool GATED, bool NORM, int CT>
+template <typename T, typename K, bool GATED, bool NORM, bool CH, int CT>
 __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
                                                      const T *__restrict__ kin, const T *__restrict__ vin,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ beta, float *__restrict__ o,
                                                      int smoothing, float floor_, GateArgs g)
 {
-    __shared__ FoldStage st;
+    using R = Rec<K, CH>;
+    __shared__ FoldStage<R::stride> st;
     __shared__ float sin_[InLds<T>::floats];
     __shared__ float dots[kDotFloats];
     __shared__ FoldWork wk;
     const MMap a = mmap();
     const int h = blockIdx.x;
-    const HeadLds<T, K> L(st.rec, st.lines, st.rho, sin_, st.idx, st.gam);
+    // with CH the token's decay vector is staged in gW (the fold then reads
+    // gamma_n from the token's own record slot)
+    const HeadLds<T, K, CH> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
     uint4 qc[4];
-    append_issue<T, K>(sv, n, h, qin, kin, vin, a, L, qc);
-    float a_h = sload(alpha, h);
+    append_issue<T, K, CH>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    float a_h = CH ? 1.0f : sload(alpha, h);
     float b_h = sload(beta, h);
     if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
     wait_lds_copies();
@@ -499,30 +530,30 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
         a_h = dots[kGateSlot];
         b_h = dots[kGateSlot + 1];
     }
-    append_compute<T, K, true, NORM>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    append_compute<T, K, true, NORM, CH>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<K>(a, hs, qc, sv.C, n + 1, true, st, S);
+    rebuild<K, CH>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename T>
+template <typename K, bool CH>
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
-    __shared__ FoldStage st;
+    __shared__ FoldStage<Rec<K, CH>::stride> st;
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     const int nr = what == 2 ? n : 0;
     uint4 qc[4];
     load_codes(a, hs, qc);
-    stage_small(a, hs, sv.C, nr, st);
-    stage_records<T>(a, hs, 0, nr < 16 ? nr : 16, st);
+    stage_small<CH>(a, hs, sv.C, nr, st);
+    stage_records<K, CH>(a, hs, 0, nr < 16 ? nr : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<T>(a, hs, qc, sv.C, nr, what >= 1, st, S);
+    rebuild<K, CH>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
     float *dst = out + (size_t)h * D * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -542,34 +573,40 @@ hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoo
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename K, bool CH>
 static void launch_fold_t(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_fold<T, 4>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, 4, CH>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     else
-        hipLaunchKernelGGL((k_fold<T, -1>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, -1, CH>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
 }
 
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
-    if (sv.key_bf16)
-        launch_fold_t<uint16_t>(sv, heads, n, smoothing, floor_, s);
-    else
-        launch_fold_t<float>(sv, heads, n, smoothing, floor_, s);
+    if (sv.kda) {
+        if (sv.key_bf16)
+            launch_fold_t<uint16_t, true>(sv, heads, n, smoothing, floor_, s);
+        else
+            launch_fold_t<float, true>(sv, heads, n, smoothing, floor_, s);
+    } else if (sv.key_bf16) {
+        launch_fold_t<uint16_t, false>(sv, heads, n, smoothing, floor_, s);
+    } else {
+        launch_fold_t<float, false>(sv, heads, n, smoothing, floor_, s);
+    }
     return hipGetLastError();
 }
 
-template <typename T, typename K, bool GATED, bool NORM>
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false>
 static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, float *o, int smoothing, float floor_,
                                  const GateArgs &g, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
                            (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
     else
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
                            (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
 }
 
@@ -580,7 +617,14 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
     // the (inputs, keys, gated, normalize) combinations of launch_append
     const bool kb = sv.key_bf16;
 #define LQ_AF(T, K, G, N) launch_append_fold_t<T, K, G, N>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
-    if (!g.gated) {
+    if (sv.kda) {
+        if (!bf16)
+            launch_append_fold_t<float, float, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o, smoothing,
+                                                                 floor_, g, s);
+        else
+            launch_append_fold_t<uint16_t, uint16_t, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o,
+                                                                       smoothing, floor_, g, s);
+    } else if (!g.gated) {
         if (!bf16)
             LQ_AF(float, float, false, false);
         else if (kb)
@@ -605,10 +649,16 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
 
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s)
 {
-    if (sv.key_bf16)
-        hipLaunchKernelGGL(k_dequant<uint16_t>, dim3(heads), dim3(NT), 0, s, sv, n, what, out);
-    else
-        hipLaunchKernelGGL(k_dequant<float>, dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    if (sv.kda) {
+        if (sv.key_bf16)
+            hipLaunchKernelGGL((k_dequant<uint16_t, true>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+        else
+            hipLaunchKernelGGL((k_dequant<float, true>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    } else if (sv.key_bf16) {
+        hipLaunchKernelGGL((k_dequant<uint16_t, false>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    } else {
+        hipLaunchKernelGGL((k_dequant<float, false>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    }
     return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ struct StateView {
     int C;  // compensator lines per head
     int W;  // record slots per head
     int key_bf16;  // record keys (and inputs) are bf16
+    int kda;       // per-channel decay: alpha [heads][128], record decays [W][128]
 };
 
 // Gate arithmetic in front of the append (mode 0: alpha and beta are given;
@@ -47,7 +48,7 @@ hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const 
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
                               const void *v, const float *alpha, const float *beta, float *o, int smoothing,
                               float floor_, const GateArgs &g, hipStream_t s);
-hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, void *S, const void *q, const void *k,
+hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, int kda, void *S, const void *q, const void *k,
                              const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
 
 }  // namespace leapq

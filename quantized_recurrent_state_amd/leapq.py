@@ -26,6 +26,9 @@ LEAPQ_ERR_HIP = -7
 LEAPQ_F32 = 0
 LEAPQ_BF16 = 1
 
+LEAPQ_DECAY_SCALAR = 0
+LEAPQ_DECAY_CHANNEL = 1
+
 LEAPQ_DEQ_RESIDUAL = 0
 LEAPQ_DEQ_BOUNDARY = 1
 LEAPQ_DEQ_CURRENT = 2
@@ -39,7 +42,8 @@ class leapq_config(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
                 ("smoothing", ctypes.c_int32), ("sigma_floor", ctypes.c_float),
-                ("in_dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("in_dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("decay", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class leapq_gate(ctypes.Structure):
@@ -107,14 +111,20 @@ def _check(status, what):
 
 
 def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32",
-                qk_norm=False):
+                qk_norm=False, decay="scalar"):
     c = leapq_config()
     c.batch, c.heads, c.dk, c.dv = int(batch), int(heads), D, D
     c.window, c.n_comp, c.smoothing = int(window), int(n_comp), int(bool(smoothing))
     c.sigma_floor = float(sigma_floor)
     c.in_dtype = LEAPQ_BF16 if in_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
     c.qk_norm = int(bool(qk_norm))
+    c.decay = LEAPQ_DECAY_CHANNEL if decay in ("channel", LEAPQ_DECAY_CHANNEL) else LEAPQ_DECAY_SCALAR
     return c
+
+
+def _alpha_shape(cfg):
+    H = cfg.batch * cfg.heads
+    return (H, D) if cfg.decay == LEAPQ_DECAY_CHANNEL else (H,)
 
 
 class Gate:
@@ -240,7 +250,10 @@ class Layer:
         return self._sec(self.layout.off_comp_vec, self.heads * C * D, torch.float32, (self.heads, C, D))
 
     def rec_gamma(self):
+        """Record decays [heads, W] (scalar decay) or [heads, W, 128] (channel decay)."""
         W = self.cfg.window
+        if self.cfg.decay == LEAPQ_DECAY_CHANNEL:
+            return self._sec(self.layout.off_rec_gamma, self.heads * W * D, torch.float32, (self.heads, W, D))
         return self._sec(self.layout.off_rec_gamma, self.heads * W, torch.float32, (self.heads, W))
 
     def rec_k_physical(self):
@@ -272,7 +285,7 @@ def leapq_append(layer, q, k, v, alpha, beta, o, stream=None):
     H, dt, dev = layer.heads, layer.in_dtype, layer.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(t, name, dt, (H, D), dev)
-    _dev_tensor(alpha, "alpha", torch.float32, (H,), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, _alpha_shape(layer.cfg), dev)
     _dev_tensor(beta, "beta", torch.float32, (H,), dev)
     _dev_tensor(o, "o", torch.float32, (H, D), dev)
     _check(lib().leapq_append(ctypes.byref(layer.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -284,7 +297,7 @@ def leapq_append_fold(layer, q, k, v, alpha, beta, o, stream=None):
     H, dt, dev = layer.heads, layer.in_dtype, layer.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(t, name, dt, (H, D), dev)
-    _dev_tensor(alpha, "alpha", torch.float32, (H,), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, _alpha_shape(layer.cfg), dev)
     _dev_tensor(beta, "beta", torch.float32, (H,), dev)
     _dev_tensor(o, "o", torch.float32, (H, D), dev)
     _check(lib().leapq_append_fold(ctypes.byref(layer.c), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -335,7 +348,7 @@ def leapq_gdn_decode(cfg, S, q, k, v, alpha, beta, o, stream=None):
     dt = torch.bfloat16 if cfg.in_dtype == LEAPQ_BF16 else torch.float32
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(t, name, dt, (H, D), dev)
-    _dev_tensor(alpha, "alpha", torch.float32, (H,), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, _alpha_shape(cfg), dev)
     _dev_tensor(beta, "beta", torch.float32, (H,), dev)
     _dev_tensor(o, "o", torch.float32, (H, D), dev)
     sd = LEAPQ_BF16 if S.dtype == torch.bfloat16 else LEAPQ_F32

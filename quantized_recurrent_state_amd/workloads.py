@@ -12,7 +12,8 @@ distributions stand in for them:
   q, k   ~ N(0, 1)^128, each L2-normalized per head and token
   v      ~ N(0, 1)^128
   beta   = sigmoid(z),         z ~ N(0, 1)
-  alpha  = exp(-softplus(z)),  z ~ N(-3, 1)     (median 0.953)
+  alpha  = exp(-softplus(z)),  z ~ N(-3, 1)     (median 0.953); with
+           per-channel decay (KDA) one independent draw per key channel
 
 Initial states:
   "gauss":   N(0, 0.02^2) entries with 2 random rows and 2 random columns
@@ -85,6 +86,7 @@ class Workload:
     seed: int = 0
     smoothing: bool = True
     sigma_floor: float = 1e-6
+    decay: str = "scalar"          # "scalar" (GDN) or "channel" (KDA: alpha per key channel)
     notes: str = field(default="", compare=False)
 
     @property
@@ -104,6 +106,10 @@ WORKLOADS = {
                      notes="24 layers x 32 heads, batch 128, 512 tokens"),
     "b512": Workload("b512", 512, 24, 32, 1024, in_dtype="bf16", seed=3,
                      notes="24 layers x 32 heads, batch 512, 1024 tokens, bf16 q/k/v"),
+    "tiny_kda": Workload("tiny_kda", 1, 1, 4, 64, init="gauss", seed=5, decay="channel",
+                         notes="tiny with per-channel decay (KDA)"),
+    "b512_kda": Workload("b512_kda", 512, 24, 32, 1024, in_dtype="bf16", seed=6, decay="channel",
+                         notes="b512 shape with per-channel decay (KDA), bf16 q/k/v"),
     "long": Workload("long", 8, 3, 32, 4095, init="hard", seed=4,
                      notes="batch 8, 3 layers x 32 heads, 4095 tokens (255 folds)"),
 }
@@ -174,7 +180,8 @@ def token_inputs(wl, layer, token, device="cpu"):
     """Inputs of one decode token for one layer.
 
     Returns q, k, v as [batch, heads, 128] in the workload's input dtype and
-    alpha, beta as fp32 [batch, heads].
+    alpha, beta as fp32 [batch, heads]; with per-channel decay alpha is
+    [batch, heads, 128], drawn per channel from the same distribution.
     """
     B, H = wl.batch, wl.heads
     g = _gen(device, wl.seed, _S_TOK, layer, token)
@@ -184,8 +191,10 @@ def token_inputs(wl, layer, token, device="cpu"):
     q = q / q.norm(dim=-1, keepdim=True)
     k = k / k.norm(dim=-1, keepdim=True)
     zb = _normal((B, H), g, device)
-    za = _normal((B, H), g, device, mean=-3.0)
+    za = _normal((B, H, D) if wl.decay == "channel" else (B, H), g, device, mean=-3.0)
     if wl.init == "hard":
+        if wl.decay != "scalar":
+            raise ValueError("the hard heads are defined for scalar decay")
         zh = _normal((B, H), g, device, mean=-6.9, std=0.25)
         za = za.clone()
         za[:, 24:] = zh[:, 24:]

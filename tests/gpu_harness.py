@@ -142,7 +142,8 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     T = wl.tokens if tokens is None else tokens
     sample = list(range(H)) if sample is None else list(sample)
     cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype,
-                         qk_norm=qk_norm)
+                         qk_norm=qk_norm, decay=wl.decay)
+    ash = (H, D) if wl.decay == "channel" else (H,)
     L = lq.Layer(cfg, dev)
     if gated is not None:
         A_log, dt_bias = workloads.gate_params(wl, layer)
@@ -152,7 +153,7 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     S0 = workloads.initial_state(wl, layer, device=gen_device).reshape(H, D, D)
     lq.leapq_init_state(L, S0.to(dev))
     S0h = S0[sample].cpu().numpy()
-    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor) for _ in sample]
+    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay) for _ in sample]
     with _pool() as pool:
         list(pool.map(lambda a: a[0].init(a[1]), zip(refs, S0h)))
         torch.cuda.synchronize(dev)
@@ -163,7 +164,7 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
             gen = workloads.gated_token_inputs if gated is not None else workloads.token_inputs
             q, k, v, a, b = gen(wl, layer, t, device=gen_device)
             qd, kd, vd = (x.reshape(H, D).to(dev) for x in (q, k, v))
-            ad, bd = a.reshape(H).to(dev), b.reshape(H).to(dev)
+            ad, bd = a.reshape(ash).to(dev), b.reshape(H).to(dev)
             last = fused and L.n_records == wl.window - 1
             if gated is not None:
                 (lq.leapq_append_fold_gated if last else lq.leapq_append_gated)(L, gate, qd, kd, vd, ad, bd, o)
@@ -174,7 +175,7 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
             qh = workloads.widen(q.reshape(H, D)[sidx]).cpu().numpy()
             kh = workloads.widen(k.reshape(H, D)[sidx]).cpu().numpy()
             vh = workloads.widen(v.reshape(H, D)[sidx]).cpu().numpy()
-            ah = a.reshape(H)[sidx].cpu().numpy()
+            ah = a.reshape(ash)[sidx].cpu().numpy()
             bh = b.reshape(H)[sidx].cpu().numpy()
             if gated is not None:
                 def step(s):

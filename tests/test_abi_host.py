@@ -147,7 +147,12 @@ def test_config_shape_dtype_reserved():
     c.smoothing = 2
     assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
     c = cfg()
-    c.reserved[1] = 1
+    c.reserved = 1
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
+    c = cfg()
+    c.decay = 2
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
+    c = cfg(decay="channel", qk_norm=True)  # channel decay excludes normalized keys
     assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
     assert lq.lib().leapq_query_layout(None, ctypes.byref(L_out)) == lq.LEAPQ_ERR_NULL
     assert lq.lib().leapq_query_layout(ctypes.byref(cfg()), None) == lq.LEAPQ_ERR_NULL
@@ -280,3 +285,22 @@ def test_qk_norm_config_and_key_layout():
         L = layout(batch=2, heads=4, window=16, n_comp=4, in_dtype=dt, qk_norm=qk)
         assert L.off_rec_u - L.off_rec_k >= 2 * 4 * 16 * 128 * e
         assert L.record_bytes_per_head == 16 * (4 + 128 * e + 512), (dt, qk)
+
+
+# ---------------------------------------------------------------- per-channel decay
+
+def test_channel_decay_layout_and_checks():
+    for dt, e in (("bf16", 2), ("f32", 4)):
+        L = layout(batch=2, heads=4, window=16, n_comp=4, in_dtype=dt, decay="channel")
+        assert L.off_rec_k - L.off_rec_gamma >= 2 * 4 * 16 * 128 * 4
+        assert L.record_bytes_per_head == 16 * (4 * 128 + 128 * e + 512), dt
+    c = cfg(decay="channel")
+    # the decay vector is read in 16-byte pieces
+    assert call_append(fake_layer(c), a=FAKE + 4) == lq.LEAPQ_ERR_ALIGN
+    assert call_append(fake_layer(c, n=16)) == lq.LEAPQ_ERR_WINDOW_FULL
+    # the gates are scalar-decay gates
+    assert call_gated(fake_layer(c), gate_struct()) == lq.LEAPQ_ERR_RANGE
+    vp = ctypes.c_void_p
+    args = [vp(FAKE)] * 8
+    args[4] = vp(FAKE + 4)  # alpha
+    assert lq.lib().leapq_gdn_decode(ctypes.byref(c), 0, *args, None) == lq.LEAPQ_ERR_ALIGN
