@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-gated", action="store_true",
                    help="skip the gated-path measurement (gate arithmetic and q/k normalization in the append)")
+    p.add_argument("--no-kda", action="store_true",
+                   help="skip the per-channel decay (KDA) measurement at the same shape")
     p.add_argument("--baseline-tokens", type=int, default=16)
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--separate", action="store_true",
@@ -258,6 +260,97 @@ def main():
         del glayers, gpool, gates
         torch.cuda.empty_cache()
 
+    # ---- per-channel decay (KDA): the same shape and schedule with alpha a
+    # 128-vector per head and token, and the dense KDA baselines
+    kda = None
+    kname = wl.name + "_kda"
+    if not args.no_kda and kname in workloads.WORKLOADS:
+        kwl = workloads.WORKLOADS[kname]
+        kcfg = lq.make_config(B, Hh, W, C, kwl.smoothing, kwl.sigma_floor, kwl.in_dtype, decay="channel")
+        klayers, kpool = [], []
+        for l in range(Lyr):
+            L = lq.Layer(kcfg, dev)
+            S0 = workloads.initial_state(kwl, l, device=dev).reshape(H, D, D)
+            lq.leapq_init_state(L, S0)
+            del S0
+            klayers.append(L)
+            toks = []
+            for pos in range(W):
+                q, k, v, a, b = workloads.token_inputs(kwl, l, pos, device=dev)
+                toks.append((q.reshape(H, D), k.reshape(H, D), v.reshape(H, D), a.reshape(H, D), b.reshape(H)))
+            kpool.append(toks)
+
+        def kwindow(ev=None):
+            for pos in range(W):
+                for l in range(Lyr):
+                    q, k, v, a, b = kpool[l][pos]
+                    if ev is not None:
+                        ev.append((pos, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                        ev[-1][1].record(stream)
+                    if klayers[l].n_records == W - 1:
+                        lq.leapq_append_fold(klayers[l], q, k, v, a, b, outs[l], stream)
+                    else:
+                        lq.leapq_append(klayers[l], q, k, v, a, b, outs[l], stream)
+                    if ev is not None:
+                        ev[-1][2].record(stream)
+
+        kwindow()
+        torch.cuda.synchronize(dev)
+        ksteps = max(4, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(ksteps):
+            kwindow()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        k_ms = e0.elapsed_time(e1) / ksteps
+        kev = []
+        kwindow(kev)
+        torch.cuda.synchronize(dev)
+        k_app = [1e3 * e0_.elapsed_time(e1_) for pos, e0_, e1_ in kev if pos < W - 1]
+        k_fused = [1e3 * e0_.elapsed_time(e1_) for pos, e0_, e1_ in kev if pos == W - 1]
+        k_app_us = float(np.mean(k_app))
+        k_bytes = float(np.mean([metrics.append_bytes(n, C, in_bytes, channel=True) for n in range(W - 1)])) * H
+        kda = {"workload": f"{kwl.name}: {kwl.notes}", "tokens_per_s": B * W / (k_ms / 1e3), "ms_per_step": k_ms,
+               "steps": ksteps, "append_us": k_app_us, "append_fold_us": float(np.mean(k_fused)),
+               "append_gbps_algorithmic": k_bytes / (k_app_us * 1e-6) / 1e9,
+               "hbm_gbps_path_algorithmic": metrics.window_bytes(W, C, in_bytes, channel=True) * H * Lyr
+               / (k_ms * 1e-3) / 1e9}
+        del klayers
+        log(f"[bench] kda path: {k_ms:.3f} ms per window, {kda['tokens_per_s']:,.0f} tokens/s; append "
+            f"{k_app_us:.1f} us ({kda['append_gbps_algorithmic']:.0f} GB/s algorithmic), last append + fold "
+            f"{kda['append_fold_us']:.1f} us")
+        if not args.no_baselines:
+            for name, sdt, sbytes in (("fp32_state", torch.float32, 4), ("bf16_state", torch.bfloat16, 2)):
+                states = []
+                for l in range(Lyr):
+                    S0 = workloads.initial_state(kwl, l, device=dev).reshape(H, D, D)
+                    states.append(S0.to(sdt).contiguous())
+                    del S0
+                for pos in range(2):
+                    for l in range(Lyr):
+                        q, k, v, a, b = kpool[l][pos]
+                        lq.leapq_gdn_decode(kcfg, states[l], q, k, v, a, b, outs[l], stream)
+                torch.cuda.synchronize(dev)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                T = args.baseline_tokens
+                e0.record(stream)
+                for t in range(T):
+                    for l in range(Lyr):
+                        q, k, v, a, b = kpool[l][t % W]
+                        lq.leapq_gdn_decode(kcfg, states[l], q, k, v, a, b, outs[l], stream)
+                e1.record(stream)
+                torch.cuda.synchronize(dev)
+                ms_tok = e0.elapsed_time(e1) / T
+                kda[name] = {"tokens_per_s": B / (ms_tok * 1e-3), "ms_per_token": ms_tok,
+                             "hbm_gbps_algorithmic": metrics.gdn_step_bytes(sbytes, in_bytes, channel=True) * H * Lyr
+                             / (ms_tok * 1e-3) / 1e9}
+                kda[f"speedup_vs_{name}"] = kda["tokens_per_s"] / kda[name]["tokens_per_s"]
+                log(f"[bench] kda baseline {name}: {ms_tok:.3f} ms/token, {B / (ms_tok * 1e-3):,.0f} tokens/s")
+                del states
+        del kpool
+        torch.cuda.empty_cache()
+
     # ---- baselines at the same shape: dense fp32-state and bf16-state decode
     baselines = None
     if not args.no_baselines:
@@ -329,6 +422,7 @@ def main():
                      "bytes_per_launch_algorithmic": app_bytes_avg},
         "fold_roofline": {"bound": "alu", "achieved_gbps_algorithmic": fold_gbps},
         "gated": gated,
+        "kda": kda,
         "baselines": baselines,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),

@@ -8,7 +8,8 @@ for one head (no re-reads, no dense fp32 state):
              + q, k, v 3*128*e_in + alpha, beta 8 + records n*(4+128*e_in+512)
       write  record 4+128*e_in+512 + output 512
   (a record holds gamma and u in fp32 and the key in the input dtype e_in,
-  which stores the token's k exactly)
+  which stores the token's k exactly; with per-channel decay (KDA) alpha and
+  each record's gamma are 128-vectors: 512 bytes in place of 4)
   fold of n records:
       read   boundary (codes, scales, compensators) + n records
       write  boundary
@@ -28,34 +29,37 @@ def boundary_bytes(C=4):
     return D * D + 2 * D * 4 + C * (4 + D * 4)
 
 
-def record_bytes(in_bytes=2):
-    """Bytes of one record: gamma and u in fp32, k in the input dtype."""
-    return 4 + D * in_bytes + D * 4
+def record_bytes(in_bytes=2, channel=False):
+    """Bytes of one record: gamma (a 128-vector with per-channel decay) and u
+    in fp32, k in the input dtype."""
+    return 4 * (D if channel else 1) + D * in_bytes + D * 4
 
 
-def append_bytes(n, C=4, in_bytes=2):
+def append_bytes(n, C=4, in_bytes=2, channel=False):
     """Algorithmic bytes of one head's append with n records present."""
-    read = boundary_bytes(C) + 3 * D * in_bytes + 8 + n * record_bytes(in_bytes)
-    write = record_bytes(in_bytes) + D * 4
+    gates = 4 * (D if channel else 1) + 4
+    read = boundary_bytes(C) + 3 * D * in_bytes + gates + n * record_bytes(in_bytes, channel)
+    write = record_bytes(in_bytes, channel) + D * 4
     return read + write
 
 
-def fold_bytes(n, C=4, in_bytes=2):
-    return 2 * boundary_bytes(C) + n * record_bytes(in_bytes)
+def fold_bytes(n, C=4, in_bytes=2, channel=False):
+    return 2 * boundary_bytes(C) + n * record_bytes(in_bytes, channel)
 
 
 def init_bytes(C=4):
     return D * D * 4 + boundary_bytes(C)
 
 
-def window_bytes(W=16, C=4, in_bytes=2):
+def window_bytes(W=16, C=4, in_bytes=2, channel=False):
     """Bytes of one head over a whole window: W appends and one fold."""
-    return sum(append_bytes(n, C, in_bytes) for n in range(W)) + fold_bytes(W, C, in_bytes)
+    return (sum(append_bytes(n, C, in_bytes, channel) for n in range(W)) +
+            fold_bytes(W, C, in_bytes, channel))
 
 
-def gdn_step_bytes(state_bytes=4, in_bytes=2):
-    """Dense per-token GDN step: state read + write, inputs, output."""
-    return 2 * D * D * state_bytes + 3 * D * in_bytes + 8 + D * 4
+def gdn_step_bytes(state_bytes=4, in_bytes=2, channel=False):
+    """Dense per-token step: state read + write, inputs, output."""
+    return 2 * D * D * state_bytes + 3 * D * in_bytes + 4 * (D if channel else 1) + 4 + D * 4
 
 
 def step_ms(append_ms, fold_extra_ms, W=16):
