@@ -10,7 +10,8 @@ Efficient Linear Attention with Accurate Recurrent State Quantization", 1
 Introduction: a state rounded every step compounds its error; 3.2: rounding
 once per window keeps it bounded).  Heads are summarized separately for the
 regular heads and the hard heads of the "long" workload (slow decay, heavy
-outliers).
+outliers).  With per-channel decay ("long_kda") the references are the
+fp32-state and bf16-state KDA recurrences.
 
 A caller may pass `on_token(layer, t, inputs, o, folded)`, called after every
 token with that token's inputs (q, k, v, alpha, beta as handed to the GPU),
@@ -49,7 +50,8 @@ def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, o
     H = B * Hh
     nlayers = wl.layers if layers is None else layers
     T = wl.tokens if tokens is None else tokens
-    cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype)
+    cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, decay=wl.decay)
+    ash = (H, D) if wl.decay == "channel" else (H,)
     rel_q, rel_b, hard = [], [], []
     for layer in range(nlayers):
         S0 = workloads.initial_state(wl, layer, device=dev).reshape(H, D, D).contiguous()
@@ -67,7 +69,7 @@ def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, o
         for t in range(T):
             q, k, v, a, b = workloads.token_inputs(wl, layer, t, device=dev)
             q, k, v = q.reshape(H, D), k.reshape(H, D), v.reshape(H, D)
-            a, b = a.reshape(H), b.reshape(H)
+            a, b = a.reshape(ash), b.reshape(H)
             lq.leapq_append(L, q, k, v, a, b, oq)
             lq.leapq_gdn_decode(cfg, S32, q, k, v, a, b, o32)
             lq.leapq_gdn_decode(cfg, S16, q, k, v, a, b, o16)

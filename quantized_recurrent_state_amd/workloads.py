@@ -110,6 +110,8 @@ WORKLOADS = {
                          notes="tiny with per-channel decay (KDA)"),
     "b512_kda": Workload("b512_kda", 512, 24, 32, 1024, in_dtype="bf16", seed=6, decay="channel",
                          notes="b512 shape with per-channel decay (KDA), bf16 q/k/v"),
+    "long_kda": Workload("long_kda", 8, 3, 32, 4095, seed=7, decay="channel",
+                         notes="batch 8, 3 layers x 32 heads, 4095 tokens, per-channel decay (KDA)"),
     "long": Workload("long", 8, 3, 32, 4095, init="hard", seed=4,
                      notes="batch 8, 3 layers x 32 heads, 4095 tokens (255 folds)"),
 }

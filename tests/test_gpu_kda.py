@@ -99,3 +99,37 @@ def test_kda_full_size_b512_sampled():
     sample = list(range(9, 16384, 256))
     rep, _, _ = run_layer(wl, tokens=32, sample=sample, gen_device="cuda", check_every_token=False, fused=True)
     _finish(rep)
+
+
+def test_kda_long_horizon_layer0():
+    """4095 tokens (255 folds) of the per-channel decay study's first layer,
+    with 4 oracle heads run free beside the GPU through the per-token hook of
+    quantized_recurrent_state_amd.quality: bitwise equal outputs at every
+    token.  The error against the fp32-state KDA recurrence is printed for the
+    record and must be finite."""
+    from quantized_recurrent_state_amd import quality
+    wl = WL["long_kda"]
+    heads_idx = (0, 7, 100, 255)
+    S0 = workloads.initial_state(wl, 0, device="cuda").reshape(-1, D, D)[list(heads_idx)].cpu().numpy()
+    heads = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay="channel").init(S0[j])
+             for j in range(len(heads_idx))]
+    stat = {"non_bitwise": 0, "values": 0, "folds": 0}
+    idx = torch.tensor(heads_idx, device="cuda")
+
+    def on_token(layer, t, inputs, o, folded):
+        q, k, v, a, b = (x.index_select(0, idx).float().cpu().numpy() for x in inputs)
+        og = o.index_select(0, idx).cpu().numpy()
+        for j, st in enumerate(heads):
+            o_ref, _ = st.append(q[j], k[j], v[j], a[j], float(b[j]))
+            stat["non_bitwise"] += int(np.sum(og[j].view(np.uint32) != np.asarray(o_ref, np.float32).view(np.uint32)))
+            stat["values"] += D
+            if folded:
+                st.fold()
+        stat["folds"] += int(folded)
+        if (t + 1) % 1024 == 0:
+            progress(f"  token {t + 1}: oracle agreement so far {stat}")
+
+    res = quality.run("long_kda", layers=1, on_token=on_token, log=progress)
+    progress(f"  quality: {res}")
+    assert stat["folds"] == 255 and stat["non_bitwise"] == 0
+    assert res["finite"]
