@@ -55,6 +55,7 @@ def _bind(L):
         "lqo_gdn_step_f64": (None, [f64p, f64p, f64p, f64p, cd, cd, f64p, f64p]),
         "lqo_gdn_step_bf16": (None, [u16p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
         "lqo_f32_to_bf16": (ctypes.c_uint16, [cf]),
+        "lqo_round_bf16": (None, [f32p, ci]),
         "lqo_gate": (None, [cf, cf, cf, cf, f32p, f32p]),
         "lqo_l2norm": (None, [f32p, cf, cf, f32p]),
         "lqo_dim": (ci, []),
@@ -129,13 +130,16 @@ class Head:
     ru [W][128]; n is the number of records in the window.
     """
 
-    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None, decay="scalar"):
+    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None, decay="scalar", rec_u="f32"):
         self.L = L or lib()
         self.C, self.W, self.smoothing, self.floor = int(C), int(W), int(smoothing), float(sigma_floor)
         if decay not in ("scalar", "channel"):
             raise ValueError("decay must be 'scalar' or 'channel'")
         self.decay = decay
         self.kda = decay == "channel"
+        if rec_u not in ("f32", "bf16"):
+            raise ValueError("rec_u must be 'f32' or 'bf16'")
+        self.rec_u = rec_u
         self.Q = np.zeros((D, D), np.int8)
         self.rho = np.zeros(D, np.float32)
         self.sigma = np.ones(D, np.float32)
@@ -179,6 +183,10 @@ class Head:
             self.L.lqo_append(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp),
                               float(np.float32(alpha)), float(np.float32(beta)), _p(o, fp))
         self.n += 1
+        if self.rec_u == "bf16":
+            # the record keeps u rounded to bf16; this token's output used
+            # the fp32 u (lqo_append above)
+            self.L.lqo_round_bf16(_p(self.ru[self.n - 1], fp), D)
         return o, self.ru[self.n - 1].copy()
 
     def fold(self):
@@ -203,7 +211,7 @@ class Head:
         return out
 
     def copy(self):
-        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay)
+        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay, self.rec_u)
         for name in ("Q", "rho", "sigma", "idx", "vec", "gam", "rk", "ru"):
             setattr(h, name, getattr(self, name).copy())
         h.n = self.n

@@ -566,6 +566,15 @@ uint16_t lqo_f32_to_bf16(float f)
     return (uint16_t)(b >> 16);
 }
 
+/* bf16 record corrections (a lower-precision record option: [LQ] keeps
+ * records in higher precision than the state, [RN4] Why rounding the state
+ * is difficult; storing them narrower trades record traffic for error):
+ * rounds n values to bf16, nearest even, in place (the widened values). */
+void lqo_round_bf16(float *x, int n)
+{
+    for (int e = 0; e < n; ++e) x[e] = bf16_to_f32(lqo_f32_to_bf16(x[e]));
+}
+
 /* Per-token bf16 state ([RN4] Why rounding: a bf16 state rounded at every
  * token; [LQ] 4.2/4.4 per-step baselines): widen, take the fp32 step, keep
  * the output of the fp32 state, store the state rounded to bf16. */

@@ -588,11 +588,36 @@ def pin_kda_dense_step(L):
     assert rel(S, S64) < 1e-5
 
 
+def pin_bf16_records(L):
+    """Records whose corrections are kept in bf16: the token that makes a
+    record reads out with its fp32 u (outputs equal to the fp32-record path
+    until then), the stored u is that u rounded to nearest even in bf16
+    (torch's conversion as the independent reference), every stored value is
+    bf16, and a window stays within bf16 rounding of the float64 dense
+    recurrence."""
+    S0, toks = tiny_inputs(seed=41, tokens=16, init="gauss")
+    hf = oracle.Head(C=4, W=16, L=L).init(S0[0])
+    hb = oracle.Head(C=4, W=16, L=L, rec_u="bf16").init(S0[0])
+    S = hb.dequant(1).astype(np.float64)
+    for t, (q, k, v, a, b) in enumerate(toks):
+        of, uf = hf.append(q, k, v, a, b)
+        ob, ub = hb.append(q, k, v, a, b)
+        if t == 0:
+            assert np.array_equal(of, ob)
+            want = torch.from_numpy(uf).to(torch.bfloat16).float().numpy()
+            assert np.array_equal(ub, want)
+        assert not np.any(ub.view(np.uint32) & 0xFFFF)
+        _, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            float(a), float(b))
+        assert rel(ob, o64) < 5e-3
+    assert rel(hb.dequant(2), S) < 5e-3
+
+
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
     pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
-    pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step,
+    pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step, pin_bf16_records,
 ]

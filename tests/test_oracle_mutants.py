@@ -61,6 +61,7 @@ MUTANTS = [
      "w[r] = (gam[(size_t)i * D + r] / gn[r]) * rk[(size_t)i * D + r];"),
     ("kda_lines_unscaled", "M[r * D + c] = M[r * D + c] + g[r] * v[c];", "M[r * D + c] = M[r * D + c] + v[c];"),
     ("kda_rebuild_no_gamma", "float a = gn[r] * rho[r];", "float a = rho[r];"),
+    ("bf16_records_not_rounded", "x[e] = bf16_to_f32(lqo_f32_to_bf16(x[e]));", "x[e] = x[e];"),
     ("kda_step_column_decay", "S[r * D + c] = alpha[r] * S[r * D + c];", "S[r * D + c] = alpha[c] * S[r * D + c];"),
 ]
 
