@@ -82,7 +82,10 @@ typedef struct leapq_config {
     int32_t qk_norm;     /* 1: the gated appends L2-normalize q and k (record keys are then fp32); 0 or 1 */
     int32_t decay;       /* LEAPQ_DECAY_SCALAR (GDN: alpha per head) or LEAPQ_DECAY_CHANNEL (KDA: alpha
                             per head and key channel); channel decay excludes qk_norm */
-    int32_t reserved;    /* must be zero */
+    int32_t rec_dtype;   /* LEAPQ_F32 (the method's records) or LEAPQ_BF16: record corrections u kept in
+                            bf16, rounded to nearest even on store (a lossy lower-precision option; the
+                            token that makes a record reads out with its fp32 u); LEAPQ_BF16 requires
+                            scalar decay and qk_norm = 0 and is not taken by the gated entry points */
 } leapq_config;
 
 /* Byte layout of one layer's state buffer.  Sections are "structure of
@@ -105,16 +108,16 @@ typedef struct leapq_config {
  *                                      token's k as given, so bf16 storage
  *                                      of bf16 inputs is exact), or fp32
  *                                      when qk_norm = 1
- *   rec_u     fp32  [heads][W][128]    record corrections; value column c is
+ *   rec_u     fp32 or bf16 (rec_dtype) [heads][W][128]  record corrections; value column c is
  *                                      stored at 32 (c % 4) + 8 (c / 32)
  *                                      + 4 ((c / 4) % 2) + (c / 8) % 4
  * These orders are the thread map of the kernels (each thread's 64 codes are
  * four 16-byte loads, each wave's loads 1 KB contiguous; the record keys and
  * corrections are the A operand order of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
- * 1.19 bytes per state element); record_bytes_per_head = W * (4 g + 128 e + 512)
- * with e = 2 for bf16 inputs and qk_norm = 0, else 4, and g = 1 (scalar
- * decay) or 128 (channel decay). */
+ * 1.19 bytes per state element); record_bytes_per_head = W * (4 g + 128 e + 128 f)
+ * with e = 2 for bf16 inputs and qk_norm = 0, else 4, g = 1 (scalar decay)
+ * or 128 (channel decay), and f = 4, or 2 with rec_dtype = LEAPQ_BF16. */
 typedef struct leapq_layout {
     uint64_t total_bytes;
     uint64_t off_codes, off_row_scale, off_col_scale, off_comp_idx, off_comp_vec;

@@ -40,7 +40,8 @@ int32_t check_method_config(const leapq_config *c)
     if (!(c->sigma_floor > 0.0f) || c->sigma_floor > 3.0e38f) return LEAPQ_ERR_RANGE;
     if (c->qk_norm != 0 && c->qk_norm != 1) return LEAPQ_ERR_RANGE;
     if (c->decay == LEAPQ_DECAY_CHANNEL && c->qk_norm) return LEAPQ_ERR_RANGE;
-    if (c->reserved) return LEAPQ_ERR_RANGE;
+    if (c->rec_dtype != LEAPQ_F32 && c->rec_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
+    if (c->rec_dtype == LEAPQ_BF16 && (c->decay != LEAPQ_DECAY_SCALAR || c->qk_norm)) return LEAPQ_ERR_RANGE;
     return LEAPQ_OK;
 }
 
@@ -54,6 +55,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     const uint64_t C = (uint64_t)c->n_comp, W = (uint64_t)c->window;
     const uint64_t kb = key_bf16(c) ? 2 : 4;  // record key element
     const uint64_t gw = c->decay == LEAPQ_DECAY_CHANNEL ? kD : 1;  // record decay values
+    const uint64_t ub = c->rec_dtype == LEAPQ_BF16 ? 2 : 4;        // record correction element
     uint64_t off = 0;
     L->off_codes = off;
     off = round_up(off + H * kD * kD);
@@ -70,10 +72,10 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_rec_k = off;
     off = round_up(off + H * W * kD * kb);
     L->off_rec_u = off;
-    off = round_up(off + H * W * kD * 4);
+    off = round_up(off + H * W * kD * ub);
     L->total_bytes = off;
     L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * kD * 4;
-    L->record_bytes_per_head = W * (4 * gw + kD * kb + kD * 4);
+    L->record_bytes_per_head = W * (4 * gw + kD * kb + kD * ub);
 }
 
 int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
@@ -94,11 +96,12 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->cvec = (float *)(b + L.off_comp_vec);
     sv->rgam = (float *)(b + L.off_rec_gamma);
     sv->rk = b + L.off_rec_k;
-    sv->ru = (float *)(b + L.off_rec_u);
+    sv->ru = b + L.off_rec_u;
     sv->C = layer->cfg.n_comp;
     sv->W = layer->cfg.window;
     sv->key_bf16 = key_bf16(&layer->cfg);
     sv->kda = layer->cfg.decay == LEAPQ_DECAY_CHANNEL;
+    sv->u_bf16 = layer->cfg.rec_dtype == LEAPQ_BF16;
     return LEAPQ_OK;
 }
 
@@ -141,7 +144,7 @@ leapq::GateArgs plain_gate(const leapq_config &c) { return {nullptr, nullptr, 1.
 int32_t gate_of(const leapq_layer *layer, const leapq_gate *g, leapq::GateArgs *out)
 {
     if (!g || !g->A_log || !g->dt_bias) return LEAPQ_ERR_NULL;
-    if (layer->cfg.decay != LEAPQ_DECAY_SCALAR) return LEAPQ_ERR_RANGE;
+    if (layer->cfg.decay != LEAPQ_DECAY_SCALAR || layer->cfg.rec_dtype != LEAPQ_F32) return LEAPQ_ERR_RANGE;
     if (!aligned(g->A_log, 4) || !aligned(g->dt_bias, 4)) return LEAPQ_ERR_ALIGN;
     if (g->reserved[0] || g->reserved[1]) return LEAPQ_ERR_RANGE;
     if (!(g->norm_eps >= 0.0f) || g->norm_eps > 3.0e38f) return LEAPQ_ERR_RANGE;

@@ -32,52 +32,61 @@ struct InLds<uint16_t> {
 // it, which needs fp32), then the correction (fp32, stored order); keys take
 // kbytes, a staged record stride floats.
 // With per-channel decay (CH) a record also holds its cumulative decay as a
-// 128-vector; the staged record is then [decay | correction | key].
-template <typename T, bool CH = false>
+// 128-vector; the staged record is then [decay | correction | key].  U: the
+// correction's storage dtype (fp32, or bf16 as a lossy option).
+template <typename T, bool CH = false, typename U = float>
 struct Rec {
     static constexpr int kbytes = D * (int)sizeof(T);
     static constexpr int kf = kbytes / 4;
-    static constexpr int goff = 0;               // CH: the decay vector
-    static constexpr int uoff = CH ? D : kf;     // the correction
-    static constexpr int koff = CH ? 2 * D : 0;  // the key
-    static constexpr int stride = kf + D + (CH ? D : 0);
+    static constexpr int ubytes = D * (int)sizeof(U);
+    static constexpr int uf = ubytes / 4;
+    static constexpr int goff = 0;                   // CH: the decay vector
+    static constexpr int uoff = CH ? D : kf;         // the correction
+    static constexpr int koff = CH ? D + uf : 0;     // the key
+    static constexpr int stride = kf + uf + (CH ? D : 0);
     static constexpr int kpieces = kbytes / 16;
+    static constexpr int upieces = ubytes / 16;
     __device__ static float key(const float *rec, int r) { return InLds<T>::get(rec + koff, 0, r); }
+    __device__ static float u(const float *rec, int c) { return InLds<U>::get(rec + uoff, 0, c); }
 };
 
 // Copies record g of a head into LDS at dst (stride floats) with LDS-direct
 // loads of 16 bytes per lane: without CH, the key's pieces then the
 // correction's in one load; with CH, the decay's and the correction's in one
 // load, then the key's.
-template <typename T, bool CH = false>
+template <typename T, bool CH = false, typename U = float>
 __device__ __forceinline__ void copy_record(const HeadState &hs, int g, int l, float *dst)
 {
-    constexpr int kp = Rec<T, CH>::kpieces;
+    using R = Rec<T, CH, U>;
+    constexpr int kp = R::kpieces, up = R::upieces;
     if constexpr (!CH) {
-        if (kp + 32 >= 64 || l < kp + 32)
-            lds_copy16(l < kp ? static_cast<const void *>(hs.rk + g * Rec<T>::kbytes + 16 * l)
-                              : static_cast<const void *>(hs.ru + g * D + 4 * (l - kp)),
+        if (kp + up >= 64 || l < kp + up)
+            lds_copy16(l < kp ? static_cast<const void *>(hs.rk + g * R::kbytes + 16 * l)
+                              : static_cast<const void *>(hs.ru + g * R::ubytes + 16 * (l - kp)),
                        dst);
     } else {
-        lds_copy16(l < 32 ? hs.rgam + g * D + 4 * l : hs.ru + g * D + 4 * (l - 32), dst);
-        if (kp >= 64 || l < kp) lds_copy16(hs.rk + g * Rec<T, CH>::kbytes + 16 * l, dst + Rec<T, CH>::koff);
+        if (32 + up >= 64 || l < 32 + up)
+            lds_copy16(l < 32 ? static_cast<const void *>(hs.rgam + g * D + 4 * l)
+                              : static_cast<const void *>(hs.ru + g * R::ubytes + 16 * (l - 32)),
+                       dst);
+        if (kp >= 64 || l < kp) lds_copy16(hs.rk + g * R::kbytes + 16 * l, dst + R::koff);
     }
 }
 
 // LDS of one head in floats: records [n][stride] (keys K), lines [C][128],
 // rho [128], sigma [128], inputs (k, q, v as T), indices [8], then the
 // record decays [64] or, with CH, the token's decay vector [128]
-template <typename T, typename K, bool CH = false>
+template <typename T, typename K, bool CH = false, typename U = float>
 __host__ __device__ constexpr int head_lds_floats(int n, int C)
 {
-    return n * Rec<K, CH>::stride + C * 128 + 256 + InLds<T>::floats + 8 + (CH ? 128 : 64);
+    return n * Rec<K, CH, U>::stride + C * 128 + 256 + InLds<T>::floats + 8 + (CH ? 128 : 64);
 }
 // per-workgroup results of the dot jobs: coefficients [2][64], column-token
 // dots [2][8], k.q [1], then the gated alpha and beta [2] (+1 pad)
 constexpr int kDotFloats = 128 + 16 + 4;
 constexpr int kGateSlot = 145;
 
-template <typename T, typename K, bool CH = false>
+template <typename T, typename K, bool CH = false, typename U = float>
 struct HeadLds {
     float *rec, *cv, *srho, *ssig, *sin_, *sgam;
     int *sidx;
@@ -88,7 +97,7 @@ struct HeadLds {
     __device__ HeadLds(float *base, int n, int C)
     {
         rec = base;
-        cv = rec + n * Rec<K, CH>::stride;
+        cv = rec + n * Rec<K, CH, U>::stride;
         srho = cv + C * D;
         ssig = srho + D;
         sin_ = ssig + D;
@@ -111,15 +120,15 @@ __device__ __forceinline__ void wait_lds_copies()
 // Issues every global load of head h: every operand other than the codes
 // into the LDS buffer L by LDS-direct copies, then the thread's 64 codes into
 // qc as the wave's last kCodeLoads vector loads.
-template <typename T, typename K, bool CH = false>
+template <typename T, typename K, bool CH = false, typename U = float>
 __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
                                              const T *__restrict__ kin, const T *__restrict__ vin,
-                                             const MMap &a, const HeadLds<T, K, CH> &L, uint4 (&qc)[4],
+                                             const MMap &a, const HeadLds<T, K, CH, U> &L, uint4 (&qc)[4],
                                              const float *__restrict__ alpha = nullptr)
 {
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
-    for (int rr = w; rr < n; rr += 4) copy_record<K, CH>(hs, rr, l, L.rec + rr * Rec<K, CH>::stride);
+    for (int rr = w; rr < n; rr += 4) copy_record<K, CH, U>(hs, rr, l, L.rec + rr * Rec<K, CH, U>::stride);
     for (int pair = 2 * w; pair < C; pair += 8)
         if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
     if (w == 0) {
@@ -189,13 +198,13 @@ __device__ __forceinline__ void gate_issue(const GateArgs &g, int h, const MMap 
 // dot (the record key is then the normalized k in fp32).  Expects the LDS copies landed and visible (wait_lds_copies() and a
 // barrier); the codes are waited for at their first use.  Contains one
 // lds_barrier (dot jobs -> residual read and tail).
-template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool CH = false>
+template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool CH = false, typename U = float>
 __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a,
-                                               const HeadLds<T, K, CH> &L, float *dots, const uint4 (&qc)[4],
+                                               const HeadLds<T, K, CH, U> &L, float *dots, const uint4 (&qc)[4],
                                                float a_h, float b_h, float *__restrict__ o, float q_scale = 1.0f,
                                                float eps = 0.0f)
 {
-    using R = Rec<K, CH>;
+    using R = Rec<K, CH, U>;
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
     const float *rec = L.rec, *cv = L.cv, *srho = L.srho, *ssig = L.ssig, *sin_ = L.sin_, *sgam = L.sgam;
@@ -349,17 +358,22 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     }
     float acc = CH ? b : gt * b;
     const int uc = upos(c);
-    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], rec[r * R::stride + R::uoff + uc], acc);
+    for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], R::u(rec + r * R::stride, uc), acc);
     // k lanes form u; q lanes receive it from lane l-16 and finish o
     const float u = b_h * (v_c - acc);
     auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
     const float u_from_k = __uint_as_float(sw[0]);
     // the record goes to HBM, or (REC_LDS) into slot n of the staged records
-    float *ru = REC_LDS ? L.rec + n * R::stride + R::uoff : hs.ru + n * D;
+    char *ru = REC_LDS ? reinterpret_cast<char *>(L.rec + n * R::stride + R::uoff) : hs.ru + n * R::ubytes;
     uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * R::stride + R::koff)
                            : reinterpret_cast<uint32_t *>(hs.rk + n * R::kbytes);
     if (vec == 0) {
-        ru[uc] = u;
+        // the record's correction (rounded to nearest even with bf16 U); this
+        // token's own output below uses the fp32 u
+        if constexpr (std::is_same<U, float>::value)
+            reinterpret_cast<float *>(ru)[uc] = u;
+        else
+            reinterpret_cast<uint16_t *>(ru)[uc] = f32_to_bf16_rne(u);
     } else {
         o[(size_t)h * D + c] = fma_(kqd[0], u_from_k, acc);
     }

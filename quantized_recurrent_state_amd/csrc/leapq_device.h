@@ -103,8 +103,9 @@ struct HeadState {
     float *rho, *sigma;
     int32_t *cidx;
     float *cvec;
-    float *rgam, *ru;
-    char *rk;  // keys in the input dtype, row order; key_bytes per record
+    float *rgam;
+    char *rk;  // keys in the input dtype, row order
+    char *ru;  // corrections (fp32 or bf16), stored order
 };
 
 __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
@@ -117,7 +118,7 @@ __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
     s.cvec = sv.cvec + (size_t)h * sv.C * D;
     s.rgam = sv.rgam + (size_t)h * sv.W * (sv.kda ? D : 1);
     s.rk = static_cast<char *>(sv.rk) + (size_t)h * sv.W * D * (sv.key_bf16 ? 2 : 4);
-    s.ru = sv.ru + (size_t)h * sv.W * D;
+    s.ru = static_cast<char *>(sv.ru) + (size_t)h * sv.W * D * (sv.u_bf16 ? 2 : 4);
     return s;
 }
 

@@ -45,7 +45,7 @@ typedef float f32x32 __attribute__((ext_vector_type(32)));
 // after the rebuild.
 template <int RS>
 struct FoldStage {
-    float rec[16 * RS];  // a chunk of up to 16 records (RS = Rec<K, CH>::stride floats each)
+    float rec[16 * RS];  // a chunk of up to 16 records (RS = Rec<K, CH, U>::stride floats each)
     float lines[8 * 128];
     float rho[128];
     float sig[128];
@@ -82,10 +82,11 @@ __device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, 
     }
 }
 
-template <typename K, bool CH, typename Stage>
+template <typename K, bool CH, typename U, typename Stage>
 __device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs, int base, int cnt, Stage &sm)
 {
-    for (int rr = a.w; rr < cnt; rr += 4) copy_record<K, CH>(hs, base + rr, a.l, sm.rec + rr * Rec<K, CH>::stride);
+    for (int rr = a.w; rr < cnt; rr += 4)
+        copy_record<K, CH, U>(hs, base + rr, a.l, sm.rec + rr * Rec<K, CH, U>::stride);
 }
 
 __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, uint4 (&qc)[4])
@@ -99,11 +100,11 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 // staged and visible.  Contains barriers when n > 16.  K: the key dtype.
 // CH: per-channel decay, gamma_n[r] read from gW (the last record's decay
 // vector), every scale and record coefficient taken per row.
-template <typename K, bool CH, typename Stage>
+template <typename K, bool CH, typename U, typename Stage>
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
                                         bool lines, Stage &sm, float (&S)[4][16], const float *gW = nullptr)
 {
-    using R = Rec<K, CH>;
+    using R = Rec<K, CH, U>;
     const float gn = CH ? 1.0f : (n > 0 ? sm.gam[n - 1] : 1.0f);
     float gr[4];  // gamma_n of the thread's rows
 #pragma unroll
@@ -164,7 +165,7 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
         const int cnt = n - base < 16 ? n - base : 16;
         if (base > 0) {
             __syncthreads();  // the previous chunk is consumed
-            stage_records<K, CH>(a, hs, base, cnt, sm);
+            stage_records<K, CH, U>(a, hs, base, cnt, sm);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -187,7 +188,7 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
                     b0 = ci * R::key(rr, kr0);
                     b1 = ci * R::key(rr, kr0 + 64);
                 }
-                const float au = rr[R::uoff + 32 * a.w + a.jp];
+                const float au = R::u(rr, 32 * a.w + a.jp);
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
             }
@@ -203,7 +204,7 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
                 b0 = ci * R::key(rr, kr0);
                 b1 = ci * R::key(rr, kr0 + 64);
             }
-            const float au = rr[R::uoff + 32 * a.w + a.jp];
+            const float au = R::u(rr, 32 * a.w + a.jp);
             acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
         }
@@ -474,10 +475,10 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename K, int CT, bool CH>
+template <typename K, int CT, bool CH, typename U>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
-    __shared__ FoldStage<Rec<K, CH>::stride> st;
+    __shared__ FoldStage<Rec<K, CH, U>::stride> st;
     __shared__ FoldWork wk;
     const MMap a = mmap();
     const int h = blockIdx.x;
@@ -485,11 +486,11 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     uint4 qc[4];
     load_codes(a, hs, qc);
     stage_small<CH>(a, hs, sv.C, n, st);
-    stage_records<K, CH>(a, hs, 0, n < 16 ? n : 16, st);
+    stage_records<K, CH, U>(a, hs, 0, n < 16 ? n : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<K, CH>(a, hs, qc, sv.C, n, true, st, S, st.gW);
+    rebuild<K, CH, U>(a, hs, qc, sv.C, n, true, st, S, st.gW);
     // no barrier: the quantization writes only LDS arrays the rebuild does
     // not read, and each thread rewrites only the codes it loaded
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
@@ -502,14 +503,14 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
 // empties the buffer), and the fold rebuilds from the same registers and LDS
 // instead of reading the boundary and the records again.  The results are
 // those of leapq_append followed by leapq_fold.
-template <typename T, typename K, bool GATED, bool NORM, bool CH, int CT>
+template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, int CT>
 __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
                                                      const T *__restrict__ kin, const T *__restrict__ vin,
                                                      const float *__restrict__ alpha,
                                                      const float *__restrict__ beta, float *__restrict__ o,
                                                      int smoothing, float floor_, GateArgs g)
 {
-    using R = Rec<K, CH>;
+    using R = Rec<K, CH, U>;
     __shared__ FoldStage<R::stride> st;
     __shared__ float sin_[InLds<T>::floats];
     __shared__ float dots[kDotFloats];
@@ -518,9 +519,9 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     const int h = blockIdx.x;
     // with CH the token's decay vector is staged in gW (the fold then reads
     // gamma_n from the token's own record slot)
-    const HeadLds<T, K, CH> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
+    const HeadLds<T, K, CH, U> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
     uint4 qc[4];
-    append_issue<T, K, CH>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    append_issue<T, K, CH, U>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
     float a_h = CH ? 1.0f : sload(alpha, h);
     float b_h = sload(beta, h);
     if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
@@ -530,18 +531,18 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
         a_h = dots[kGateSlot];
         b_h = dots[kGateSlot + 1];
     }
-    append_compute<T, K, true, NORM, CH>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    append_compute<T, K, true, NORM, CH, U>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<K, CH>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
+    rebuild<K, CH, U>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
     quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename K, bool CH>
+template <typename K, bool CH, typename U>
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
-    __shared__ FoldStage<Rec<K, CH>::stride> st;
+    __shared__ FoldStage<Rec<K, CH, U>::stride> st;
     const MMap a = mmap();
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
@@ -549,11 +550,11 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
     uint4 qc[4];
     load_codes(a, hs, qc);
     stage_small<CH>(a, hs, sv.C, nr, st);
-    stage_records<K, CH>(a, hs, 0, nr < 16 ? nr : 16, st);
+    stage_records<K, CH, U>(a, hs, 0, nr < 16 ? nr : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<K, CH>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
+    rebuild<K, CH, U>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
     float *dst = out + (size_t)h * D * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -573,18 +574,23 @@ hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoo
     return hipGetLastError();
 }
 
-template <typename K, bool CH>
+template <typename K, bool CH, typename U = float>
 static void launch_fold_t(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_fold<K, 4, CH>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, 4, CH, U>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     else
-        hipLaunchKernelGGL((k_fold<K, -1, CH>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, -1, CH, U>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
 }
 
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
-    if (sv.kda) {
+    if (sv.u_bf16) {
+        if (sv.key_bf16)
+            launch_fold_t<uint16_t, false, uint16_t>(sv, heads, n, smoothing, floor_, s);
+        else
+            launch_fold_t<float, false, uint16_t>(sv, heads, n, smoothing, floor_, s);
+    } else if (sv.kda) {
         if (sv.key_bf16)
             launch_fold_t<uint16_t, true>(sv, heads, n, smoothing, floor_, s);
         else
@@ -597,16 +603,16 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
     return hipGetLastError();
 }
 
-template <typename T, typename K, bool GATED, bool NORM, bool CH = false>
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float>
 static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, float *o, int smoothing, float floor_,
                                  const GateArgs &g, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
                            (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
     else
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
                            (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
 }
 
@@ -617,7 +623,14 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
     // the (inputs, keys, gated, normalize) combinations of launch_append
     const bool kb = sv.key_bf16;
 #define LQ_AF(T, K, G, N) launch_append_fold_t<T, K, G, N>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
-    if (sv.kda) {
+    if (sv.u_bf16) {
+        if (!bf16)
+            launch_append_fold_t<float, float, false, false, false, uint16_t>(sv, heads, n, q, k, v, alpha, beta, o,
+                                                                            smoothing, floor_, g, s);
+        else
+            launch_append_fold_t<uint16_t, uint16_t, false, false, false, uint16_t>(
+                sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s);
+    } else if (sv.kda) {
         if (!bf16)
             launch_append_fold_t<float, float, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o, smoothing,
                                                                  floor_, g, s);
@@ -649,15 +662,20 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
 
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s)
 {
-    if (sv.kda) {
+    if (sv.u_bf16) {
         if (sv.key_bf16)
-            hipLaunchKernelGGL((k_dequant<uint16_t, true>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+            hipLaunchKernelGGL((k_dequant<uint16_t, false, uint16_t>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
         else
-            hipLaunchKernelGGL((k_dequant<float, true>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+            hipLaunchKernelGGL((k_dequant<float, false, uint16_t>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+    } else if (sv.kda) {
+        if (sv.key_bf16)
+            hipLaunchKernelGGL((k_dequant<uint16_t, true, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+        else
+            hipLaunchKernelGGL((k_dequant<float, true, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
     } else if (sv.key_bf16) {
-        hipLaunchKernelGGL((k_dequant<uint16_t, false>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+        hipLaunchKernelGGL((k_dequant<uint16_t, false, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
     } else {
-        hipLaunchKernelGGL((k_dequant<float, false>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+        hipLaunchKernelGGL((k_dequant<float, false, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
     }
     return hipGetLastError();
 }

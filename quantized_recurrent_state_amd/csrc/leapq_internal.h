@@ -16,11 +16,12 @@ struct StateView {
     float *cvec;
     float *rgam;
     void *rk;  // record keys in the input dtype (fp32 or bf16)
-    float *ru;
+    void *ru;  // record corrections (fp32, or bf16 with u_bf16)
     int C;  // compensator lines per head
     int W;  // record slots per head
     int key_bf16;  // record keys (and inputs) are bf16
     int kda;       // per-channel decay: alpha [heads][128], record decays [W][128]
+    int u_bf16;    // record corrections stored in bf16
 };
 
 // Gate arithmetic in front of the append (mode 0: alpha and beta are given;

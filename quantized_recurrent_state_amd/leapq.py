@@ -43,7 +43,7 @@ class leapq_config(ctypes.Structure):
                 ("dv", ctypes.c_int32), ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
                 ("smoothing", ctypes.c_int32), ("sigma_floor", ctypes.c_float),
                 ("in_dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("decay", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("rec_dtype", ctypes.c_int32)]
 
 
 class leapq_gate(ctypes.Structure):
@@ -111,7 +111,7 @@ def _check(status, what):
 
 
 def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32",
-                qk_norm=False, decay="scalar"):
+                qk_norm=False, decay="scalar", rec_dtype="f32"):
     c = leapq_config()
     c.batch, c.heads, c.dk, c.dv = int(batch), int(heads), D, D
     c.window, c.n_comp, c.smoothing = int(window), int(n_comp), int(bool(smoothing))
@@ -119,6 +119,7 @@ def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1
     c.in_dtype = LEAPQ_BF16 if in_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
     c.qk_norm = int(bool(qk_norm))
     c.decay = LEAPQ_DECAY_CHANNEL if decay in ("channel", LEAPQ_DECAY_CHANNEL) else LEAPQ_DECAY_SCALAR
+    c.rec_dtype = LEAPQ_BF16 if rec_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
     return c
 
 
@@ -262,8 +263,10 @@ class Layer:
         return self._sec(self.layout.off_rec_k, self.heads * W * D, self.key_dtype, (self.heads, W, D))
 
     def rec_u_physical(self):
+        """Record corrections [heads, W, 128] as stored (fp32, or bf16 with rec_dtype bf16)."""
         W = self.cfg.window
-        return self._sec(self.layout.off_rec_u, self.heads * W * D, torch.float32, (self.heads, W, D))
+        dt = torch.bfloat16 if self.cfg.rec_dtype == LEAPQ_BF16 else torch.float32
+        return self._sec(self.layout.off_rec_u, self.heads * W * D, dt, (self.heads, W, D))
 
     def rec_k(self):
         """Record keys [heads, W, 128] as fp32 (exact)."""
@@ -272,7 +275,7 @@ class Layer:
     def rec_u(self):
         """Record corrections [heads, W, 128] in logical value-column order."""
         c = torch.arange(D, device=self.device)
-        return self.rec_u_physical()[:, :, corr_pos(c)]
+        return self.rec_u_physical()[:, :, corr_pos(c)].float()
 
 
 def leapq_init_state(layer, S0, stream=None):

@@ -29,17 +29,18 @@ def boundary_bytes(C=4):
     return D * D + 2 * D * 4 + C * (4 + D * 4)
 
 
-def record_bytes(in_bytes=2, channel=False):
-    """Bytes of one record: gamma (a 128-vector with per-channel decay) and u
-    in fp32, k in the input dtype."""
-    return 4 * (D if channel else 1) + D * in_bytes + D * 4
+def record_bytes(in_bytes=2, channel=False, u_bytes=4):
+    """Bytes of one record: gamma (a 128-vector with per-channel decay) in
+    fp32, k in the input dtype, u in fp32 (or bf16 as a lossy option)."""
+    return 4 * (D if channel else 1) + D * in_bytes + D * u_bytes
 
 
-def append_bytes(n, C=4, in_bytes=2, channel=False):
+def append_bytes(n, C=4, in_bytes=2, channel=False, u_bytes=4):
     """Algorithmic bytes of one head's append with n records present."""
     gates = 4 * (D if channel else 1) + 4
-    read = boundary_bytes(C) + 3 * D * in_bytes + gates + n * record_bytes(in_bytes, channel)
-    write = record_bytes(in_bytes, channel) + D * 4
+    rec = record_bytes(in_bytes, channel, u_bytes)
+    read = boundary_bytes(C) + 3 * D * in_bytes + gates + n * rec
+    write = rec + D * 4
     return read + write
 
 

@@ -127,7 +127,7 @@ def _pool():
 
 
 def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="cuda", check_every_token=True,
-              fold_at=None, report=None, log=True, fused=False, gated=None, qk_norm=False):
+              fold_at=None, report=None, log=True, fused=False, gated=None, qk_norm=False, rec_u="f32"):
     """Runs `tokens` decode tokens of one layer on the GPU and, for the
     sampled heads, in the oracle; folds whenever the window is full (or at
     the token counts in fold_at).  With fused, the GPU takes each window's
@@ -142,7 +142,7 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     T = wl.tokens if tokens is None else tokens
     sample = list(range(H)) if sample is None else list(sample)
     cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype,
-                         qk_norm=qk_norm, decay=wl.decay)
+                         qk_norm=qk_norm, decay=wl.decay, rec_dtype=rec_u)
     ash = (H, D) if wl.decay == "channel" else (H,)
     L = lq.Layer(cfg, dev)
     if gated is not None:
@@ -153,7 +153,8 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     S0 = workloads.initial_state(wl, layer, device=gen_device).reshape(H, D, D)
     lq.leapq_init_state(L, S0.to(dev))
     S0h = S0[sample].cpu().numpy()
-    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay) for _ in sample]
+    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay, rec_u=rec_u)
+            for _ in sample]
     with _pool() as pool:
         list(pool.map(lambda a: a[0].init(a[1]), zip(refs, S0h)))
         torch.cuda.synchronize(dev)

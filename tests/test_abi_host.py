@@ -147,8 +147,8 @@ def test_config_shape_dtype_reserved():
     c.smoothing = 2
     assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
     c = cfg()
-    c.reserved = 1
-    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
+    c.rec_dtype = 5
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_DTYPE
     c = cfg()
     c.decay = 2
     assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(L_out)) == lq.LEAPQ_ERR_RANGE
@@ -304,3 +304,18 @@ def test_channel_decay_layout_and_checks():
     args = [vp(FAKE)] * 8
     args[4] = vp(FAKE + 4)  # alpha
     assert lq.lib().leapq_gdn_decode(ctypes.byref(c), 0, *args, None) == lq.LEAPQ_ERR_ALIGN
+
+
+# ---------------------------------------------------------------- bf16 record corrections
+
+def test_bf16_corrections_layout_and_checks():
+    for dt, e in (("bf16", 2), ("f32", 4)):
+        L = layout(batch=2, heads=4, window=16, n_comp=4, in_dtype=dt, rec_dtype="bf16")
+        assert L.total_bytes - L.off_rec_u >= 2 * 4 * 16 * 128 * 2
+        assert L.record_bytes_per_head == 16 * (4 + 128 * e + 256), dt
+    out = lq.leapq_layout()
+    for kw in (dict(decay="channel"), dict(qk_norm=True)):
+        c = cfg(rec_dtype="bf16", **kw)
+        assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
+    # the gated entry points keep fp32 corrections
+    assert call_gated(fake_layer(cfg(rec_dtype="bf16")), gate_struct()) == lq.LEAPQ_ERR_RANGE
