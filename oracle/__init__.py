@@ -57,6 +57,12 @@ def _bind(L):
         "lqo_f32_to_bf16": (ctypes.c_uint16, [cf]),
         "lqo_round_bf16": (None, [f32p, ci]),
         "lqo_gate": (None, [cf, cf, cf, cf, f32p, f32p]),
+        "lqo_quantize_r1": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_init_r1": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_fold_r1": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
+        "lqo_current_r1": (None, [i8p, f32p, f32p, ci, f32p, ci, f32p, f32p, f32p, f32p]),
+        "lqo_append_r1": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p,
+                                 f32p, f32p, f32p, cf, cf, f32p]),
         "lqo_l2norm": (None, [f32p, cf, cf, f32p]),
         "lqo_dim": (ci, []),
     }
@@ -130,7 +136,8 @@ class Head:
     ru [W][128]; n is the number of records in the window.
     """
 
-    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None, decay="scalar", rec_u="f32"):
+    def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None, decay="scalar", rec_u="f32",
+                 fit="lines"):
         self.L = L or lib()
         self.C, self.W, self.smoothing, self.floor = int(C), int(W), int(smoothing), float(sigma_floor)
         if decay not in ("scalar", "channel"):
@@ -140,11 +147,18 @@ class Head:
         if rec_u not in ("f32", "bf16"):
             raise ValueError("rec_u must be 'f32' or 'bf16'")
         self.rec_u = rec_u
+        if fit not in ("lines", "rank1"):
+            raise ValueError("fit must be 'lines' or 'rank1'")
+        if fit == "rank1" and self.kda:
+            raise ValueError("rank-one compensators are defined for scalar decay")
+        self.fit = fit
+        self.r1 = fit == "rank1"
         self.Q = np.zeros((D, D), np.int8)
         self.rho = np.zeros(D, np.float32)
         self.sigma = np.ones(D, np.float32)
         self.idx = np.full(max(self.C, 1), -1, np.int32)
-        self.vec = np.zeros((max(self.C, 1), D), np.float32)
+        # compensators: lines [C][128], or rank-one pairs [C][2 * 128] = [a | b]
+        self.vec = np.zeros((max(self.C, 1), 2 * D if self.r1 else D), np.float32)
         self.gam = np.zeros((max(self.W, 1), D) if self.kda else max(self.W, 1), np.float32)
         self.rk = np.zeros((max(self.W, 1), D), np.float32)
         self.ru = np.zeros((max(self.W, 1), D), np.float32)
@@ -162,9 +176,9 @@ class Head:
     def init(self, S0):
         S0 = f32(S0).reshape(D, D)
         fp = ctypes.c_float
-        self.L.lqo_init(_p(S0, fp), self.C, self.smoothing, self.floor, _p(self.Q, ctypes.c_int8),
-                        _p(self.rho, fp), _p(self.sigma, fp), _p(self.idx, ctypes.c_int32),
-                        _p(self.vec, fp))
+        fn = self.L.lqo_init_r1 if self.r1 else self.L.lqo_init
+        fn(_p(S0, fp), self.C, self.smoothing, self.floor, _p(self.Q, ctypes.c_int8),
+           _p(self.rho, fp), _p(self.sigma, fp), _p(self.idx, ctypes.c_int32), _p(self.vec, fp))
         self.n = 0
         return self
 
@@ -180,8 +194,9 @@ class Head:
             self.L.lqo_append_kda(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp), _p(al, fp),
                                   float(np.float32(beta)), _p(o, fp))
         else:
-            self.L.lqo_append(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp),
-                              float(np.float32(alpha)), float(np.float32(beta)), _p(o, fp))
+            fn = self.L.lqo_append_r1 if self.r1 else self.L.lqo_append
+            fn(*self._st(), *self._rec(), _p(q, fp), _p(k, fp), _p(v, fp),
+               float(np.float32(alpha)), float(np.float32(beta)), _p(o, fp))
         self.n += 1
         if self.rec_u == "bf16":
             # the record keeps u rounded to bf16; this token's output used
@@ -190,7 +205,7 @@ class Head:
         return o, self.ru[self.n - 1].copy()
 
     def fold(self):
-        fn = self.L.lqo_fold_kda if self.kda else self.L.lqo_fold
+        fn = self.L.lqo_fold_kda if self.kda else self.L.lqo_fold_r1 if self.r1 else self.L.lqo_fold
         fn(*self._st(), *self._rec(), self.smoothing, self.floor)
         self.n = 0
         return self
@@ -201,6 +216,11 @@ class Head:
         if what == 0:
             self.L.lqo_residual(_p(self.Q, ctypes.c_int8), _p(self.rho, fp), _p(self.sigma, fp),
                                 _p(out, fp))
+        elif what in (1, 2) and self.r1:
+            n = self.n if what == 2 else 0
+            self.L.lqo_current_r1(_p(self.Q, ctypes.c_int8), _p(self.rho, fp), _p(self.sigma, fp), self.C,
+                                  _p(self.vec, fp), n, _p(self.gam, fp), _p(self.rk, fp), _p(self.ru, fp),
+                                  _p(out, fp))
         elif what == 1:
             self.L.lqo_boundary(*self._st(), _p(out, fp))
         elif what == 2:
@@ -211,16 +231,16 @@ class Head:
         return out
 
     def copy(self):
-        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay, self.rec_u)
+        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay, self.rec_u, self.fit)
         for name in ("Q", "rho", "sigma", "idx", "vec", "gam", "rk", "ru"):
             setattr(h, name, getattr(self, name).copy())
         h.n = self.n
         return h
 
 
-def quantize(R, C=4, smoothing=True, sigma_floor=1e-6, L=None):
+def quantize(R, C=4, smoothing=True, sigma_floor=1e-6, L=None, fit="lines"):
     """Quantize a full fp32 matrix; returns a fresh Head at n = 0."""
-    return Head(C, 16, smoothing, sigma_floor, L).init(R)
+    return Head(C, 16, smoothing, sigma_floor, L, fit=fit).init(R)
 
 
 def gdn_step_f32(S, q, k, v, alpha, beta, L=None):

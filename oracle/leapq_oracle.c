@@ -133,16 +133,22 @@ void lqo_boundary(const int8_t *Q, const float *rho, const float *sigma, int C,
  * compensator lines as gamma_n * line, then each record i = 0..n-1 in order
  * is applied to every entry with one fused multiply-add of
  * w_i[r] = (gamma_n / gamma_i) * k_i[r] and u_i[c]. */
-void lqo_current(const int8_t *Q, const float *rho, const float *sigma, int C,
-                 const int32_t *idx, const float *vec, int n, const float *gam,
-                 const float *rk, const float *ru, float *out)
+static void add_rank1(float *M, int C, const float *ab, float g);
+
+/* r1: the compensators are rank-one pairs (see the rank-one fit below). */
+static void current_core(const int8_t *Q, const float *rho, const float *sigma, int C,
+                         const int32_t *idx, const float *vec, int r1, int n, const float *gam,
+                         const float *rk, const float *ru, float *out)
 {
     float gn = gamma_of(n, gam);
     for (int r = 0; r < D; ++r) {
         float a = gn * rho[r];
         for (int c = 0; c < D; ++c) out[r * D + c] = ((float)Q[r * D + c] * a) * sigma[c];
     }
-    add_lines(out, C, idx, vec, gn);
+    if (r1)
+        add_rank1(out, C, vec, gn);
+    else
+        add_lines(out, C, idx, vec, gn);
     for (int i = 0; i < n; ++i) {
         float ci = gn / gam[i];
         float w[D];
@@ -151,6 +157,13 @@ void lqo_current(const int8_t *Q, const float *rho, const float *sigma, int C,
             for (int c = 0; c < D; ++c)
                 out[r * D + c] = fmaf(w[r], ru[(size_t)i * D + c], out[r * D + c]);
     }
+}
+
+void lqo_current(const int8_t *Q, const float *rho, const float *sigma, int C,
+                 const int32_t *idx, const float *vec, int n, const float *gam,
+                 const float *rk, const float *ru, float *out)
+{
+    current_core(Q, rho, sigma, C, idx, vec, 0, n, gam, rk, ru, out);
 }
 
 /* ------------------------------------------------------------------ */
@@ -163,6 +176,8 @@ void lqo_current(const int8_t *Q, const float *rho, const float *sigma, int C,
 #define LQO_TINY 0x1p-120f
 
 /* R is consumed (extracted lines are zeroed in place). */
+static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t *Q, float *rho, float *sigma);
+
 void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
                   int8_t *Q, float *rho, float *sigma, int32_t *idx, float *vec)
 {
@@ -199,7 +214,13 @@ void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
             for (int r = 0; r < D; ++r) { v[r] = R[r * D + c]; R[r * D + c] = 0.0f; }
         }
     }
+    smooth_and_round(R, smoothing, sigma_floor, Q, rho, sigma);
+}
 
+/* Smoothing and per-row int8 of the residual R (what remains after the
+ * compensators), shared by both compensator fits. */
+static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t *Q, float *rho, float *sigma)
+{
     /* Residual smoothing ([LQ] 3.4): per value column, the square root of
      * the mean absolute value over the key rows, with a positive floor. */
     float inv_sigma[D];
@@ -263,6 +284,103 @@ void lqo_fold(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *v
 }
 
 /* ------------------------------------------------------------------ */
+/* Rank-one compensators fitted by power sweeps (a fold option): [RN4]   */
+/* Where the time goes describes four compensators found one at a time  */
+/* with eight sweeps each, starting from the longest row of the matrix; */
+/* [LQ] 3.3 keeps compensators as rank-one updates.  Compensator j is   */
+/* the pair (a_j, b_j) with a_j of unit norm; it sets aside a_j b_j^T.  */
+/* The pair sits in the line storage as [a_j | b_j] (2 x 128 values).  */
+/* ------------------------------------------------------------------ */
+
+#define LQO_SWEEPS 8
+
+/* Fits C rank-one compensators to R in order and deflates R by each:
+ *   r* = the row of largest canonical energy (lowest index on ties; none
+ *        if no energy is positive: the pair is zero and idx_j = -1)
+ *   b  = row r*;  then LQO_SWEEPS times:
+ *        a_r = T(R[r,:] . b),  a = a * (1 / sqrt(T(a . a))),  b_c = T(R[:,c] . a)
+ *   R[r][c] = fma(-a_r, b_c, R[r][c]);  idx_j = r*. */
+static void fit_rank1(float *R, int C, int32_t *idx, float *ab)
+{
+    for (int j = 0; j < C; ++j) {
+        float *a = ab + (size_t)j * 2 * D, *b = a + D;
+        float best = 0.0f;
+        int pick = -1;
+        for (int r = 0; r < D; ++r) {
+            float e = lqo_t128_dot(R + r * D, R + r * D);
+            if (e > best) { best = e; pick = r; }
+        }
+        idx[j] = pick;
+        for (int e = 0; e < D; ++e) { a[e] = 0.0f; b[e] = 0.0f; }
+        if (pick < 0) continue;
+        for (int c = 0; c < D; ++c) b[c] = R[pick * D + c];
+        for (int s = 0; s < LQO_SWEEPS; ++s) {
+            for (int r = 0; r < D; ++r) a[r] = lqo_t128_dot(R + r * D, b);
+            float na2 = lqo_t128_dot(a, a);
+            if (!(na2 > 0.0f)) {
+                for (int e = 0; e < D; ++e) { a[e] = 0.0f; b[e] = 0.0f; }
+                break;
+            }
+            float inv = 1.0f / sqrtf(na2);
+            for (int r = 0; r < D; ++r) a[r] = a[r] * inv;
+            for (int c = 0; c < D; ++c) {
+                float col[D];
+                for (int r = 0; r < D; ++r) col[r] = R[r * D + c];
+                b[c] = lqo_t128_dot(col, a);
+            }
+        }
+        for (int r = 0; r < D; ++r)
+            for (int c = 0; c < D; ++c) R[r * D + c] = fmaf(-a[r], b[c], R[r * D + c]);
+    }
+}
+
+/* Quantization with rank-one compensators: the fit, then the same smoothing
+ * and rounding as with lines.  ab: [C][2][128]. */
+void lqo_quantize_r1(float *R, int C, int smoothing, float sigma_floor,
+                     int8_t *Q, float *rho, float *sigma, int32_t *idx, float *ab)
+{
+    fit_rank1(R, C, idx, ab);
+    smooth_and_round(R, smoothing, sigma_floor, Q, rho, sigma);
+}
+
+/* Adds the compensators scaled by g: entry (r, c) gets fma(g a_j[r], b_j[c], .)
+ * for j in order. */
+static void add_rank1(float *M, int C, const float *ab, float g)
+{
+    for (int j = 0; j < C; ++j) {
+        const float *a = ab + (size_t)j * 2 * D, *b = a + D;
+        for (int r = 0; r < D; ++r) {
+            float w = g * a[r];
+            for (int c = 0; c < D; ++c) M[r * D + c] = fmaf(w, b[c], M[r * D + c]);
+        }
+    }
+}
+
+/* Current state with rank-one compensators: (code * (gamma_n rho_r)) *
+ * sigma_c, then the compensators scaled by gamma_n, then the records. */
+void lqo_current_r1(const int8_t *Q, const float *rho, const float *sigma, int C, const float *ab,
+                    int n, const float *gam, const float *rk, const float *ru, float *out)
+{
+    current_core(Q, rho, sigma, C, NULL, ab, 1, n, gam, rk, ru, out);
+}
+
+void lqo_init_r1(const float *S0, int C, int smoothing, float sigma_floor,
+                 int8_t *Q, float *rho, float *sigma, int32_t *idx, float *ab)
+{
+    float R[D * D];
+    memcpy(R, S0, sizeof R);
+    lqo_quantize_r1(R, C, smoothing, sigma_floor, Q, rho, sigma, idx, ab);
+}
+
+void lqo_fold_r1(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *ab,
+                 int n, const float *gam, const float *rk, const float *ru, int smoothing, float sigma_floor)
+{
+    float R[D * D];
+    lqo_current_r1(Q, rho, sigma, C, ab, n, gam, rk, ru, R);
+    lqo_quantize_r1(R, C, smoothing, sigma_floor, Q, rho, sigma, idx, ab);
+}
+
+/* ------------------------------------------------------------------ */
 /* Append: one decode token against the fixed boundary plus the records */
 /* ------------------------------------------------------------------ */
 
@@ -270,6 +388,23 @@ void lqo_fold(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *v
  * the residual's read only, sigma_c * sum_r (x_r * rho_r) * code[r][c];
  * each compensator then adds its read as a token: a row token r adds
  * x_r * line, a column token c adds (line . x) to column c. */
+static void boundary_read(const int8_t *Q, const float *rho, const float *sigma, int C,
+                          const int32_t *idx, const float *vec, const float *x, float *out);
+
+/* The read with rank-one compensators: the residual's read as above, then
+ * for each compensator in order (a_j . x) b_j, one fused multiply-add per
+ * column. */
+static void boundary_read_r1(const int8_t *Q, const float *rho, const float *sigma, int C, const float *ab,
+                             const float *x, float *out)
+{
+    boundary_read(Q, rho, sigma, 0, NULL, NULL, x, out);
+    for (int j = 0; j < C; ++j) {
+        const float *a = ab + (size_t)j * 2 * D, *b = a + D;
+        float d = lqo_t128_dot(a, x);
+        for (int c = 0; c < D; ++c) out[c] = fmaf(d, b[c], out[c]);
+    }
+}
+
 static void boundary_read(const int8_t *Q, const float *rho, const float *sigma, int C,
                           const int32_t *idx, const float *vec, const float *x, float *out)
 {
@@ -302,15 +437,20 @@ static void boundary_read(const int8_t *Q, const float *rho, const float *sigma,
  *   u_t = beta * (v - r)
  *   o   = gamma_t * B^T q + sum_i (c_i * (k_i . q)) u_i + (k . q) u_t  (read of S_t)
  * and the record (gamma_t, k, u_t) is stored at slot n. */
-void lqo_append(const int8_t *Q, const float *rho, const float *sigma, int C,
-                const int32_t *idx, const float *vec, int n, float *gam, float *rk,
-                float *ru, const float *q, const float *k, const float *v, float alpha,
-                float beta, float *o)
+static void append_core(const int8_t *Q, const float *rho, const float *sigma, int C,
+                        const int32_t *idx, const float *vec, int r1, int n, float *gam, float *rk,
+                        float *ru, const float *q, const float *k, const float *v, float alpha,
+                        float beta, float *o)
 {
     float gt = gamma_of(n, gam) * alpha;
     float bk[D], bq[D], u[D];
-    boundary_read(Q, rho, sigma, C, idx, vec, k, bk);
-    boundary_read(Q, rho, sigma, C, idx, vec, q, bq);
+    if (r1) {
+        boundary_read_r1(Q, rho, sigma, C, vec, k, bk);
+        boundary_read_r1(Q, rho, sigma, C, vec, q, bq);
+    } else {
+        boundary_read(Q, rho, sigma, C, idx, vec, k, bk);
+        boundary_read(Q, rho, sigma, C, idx, vec, q, bq);
+    }
 
     float r[D];
     for (int c = 0; c < D; ++c) { r[c] = gt * bk[c]; o[c] = gt * bq[c]; }
@@ -331,6 +471,24 @@ void lqo_append(const int8_t *Q, const float *rho, const float *sigma, int C,
     gam[n] = gt;
     memcpy(rk + (size_t)n * D, k, D * sizeof(float));
     memcpy(ru + (size_t)n * D, u, D * sizeof(float));
+}
+
+void lqo_append(const int8_t *Q, const float *rho, const float *sigma, int C,
+                const int32_t *idx, const float *vec, int n, float *gam, float *rk,
+                float *ru, const float *q, const float *k, const float *v, float alpha,
+                float beta, float *o)
+{
+    append_core(Q, rho, sigma, C, idx, vec, 0, n, gam, rk, ru, q, k, v, alpha, beta, o);
+}
+
+/* The append with rank-one compensators (ab: [C][2][128] in the line
+ * storage); everything else as lqo_append. */
+void lqo_append_r1(const int8_t *Q, const float *rho, const float *sigma, int C,
+                   const int32_t *idx, const float *ab, int n, float *gam, float *rk,
+                   float *ru, const float *q, const float *k, const float *v, float alpha,
+                   float beta, float *o)
+{
+    append_core(Q, rho, sigma, C, idx, ab, 1, n, gam, rk, ru, q, k, v, alpha, beta, o);
 }
 
 /* ------------------------------------------------------------------ */

@@ -613,6 +613,66 @@ def pin_bf16_records(L):
     assert rel(hb.dequant(2), S) < 5e-3
 
 
+def pin_rank1_fit(L):
+    """Rank-one compensators by power sweeps: the start is the fp64 argmax
+    row energy; after 8 sweeps a and b equal float64 power iteration from
+    that row to 1e-5; a has unit norm; a planted rank-one pattern is
+    captured (cosine > 0.99999) and the state is rebuilt from residual and
+    pairs within half an int8 step per entry."""
+    rng = np.random.default_rng(51)
+    u, v = rng.normal(size=D), rng.normal(size=D)
+    S = (3.0 * np.outer(u, v) + rng.normal(0, 0.05, (D, D))).astype(np.float32)
+    h = oracle.quantize(S, C=4, L=L, fit="rank1")
+    R = S.astype(np.float64)
+    for j in range(4):
+        a_j, b_j = h.vec[j, :D].astype(np.float64), h.vec[j, D:].astype(np.float64)
+        energy = np.sum(R * R, axis=1)
+        top = np.sort(energy)[::-1]
+        if top[0] - top[1] > 1e-6 * top[0]:
+            assert h.idx[j] == int(np.argmax(energy)), (j, h.idx[j])
+        b = R[h.idx[j]].copy()
+        for _ in range(8):
+            a = R @ b
+            a /= np.linalg.norm(a)
+            b = R.T @ a
+        assert rel(a_j, a) < 1e-5 and rel(b_j, b) < 1e-5, (j, rel(a_j, a), rel(b_j, b))
+        assert abs(np.linalg.norm(a_j) - 1.0) < 1e-6
+        R = R - np.outer(a_j, b_j)
+    a0, b0 = h.vec[0, :D].astype(np.float64), h.vec[0, D:].astype(np.float64)
+    assert abs(a0 @ u) / np.linalg.norm(u) > 0.99999
+    assert abs(b0 @ v) / (np.linalg.norm(b0) * np.linalg.norm(v)) > 0.99999
+    B = h.dequant(1).astype(np.float64)
+    step = np.outer(h.rho, h.sigma).astype(np.float64)
+    assert np.all(np.abs(B - S) <= 0.5 * step * (1 + 1e-5) + 1e-6 * np.abs(S).max())
+
+
+def pin_rank1_window_and_fold(L):
+    """A window with rank-one compensators equals the float64 dense
+    recurrence from its boundary to 1e-5; the fold equals fitting and
+    quantizing the current state, leaves an empty buffer, and the boundary
+    then equals the current state."""
+    S0, toks = tiny_inputs(seed=52, tokens=16, init="gauss")
+    h = oracle.Head(C=4, W=16, L=L, fit="rank1").init(S0[0])
+    S = h.dequant(1).astype(np.float64)
+    for (q, k, v, a, b) in toks:
+        o, _ = h.append(q, k, v, a, b)
+        _, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            float(a), float(b))
+        assert rel(o, o64) < 1e-5
+    cur = h.dequant(2)
+    assert rel(cur, S) < 1e-5
+    want = oracle.quantize(cur, C=4, L=L, fit="rank1")
+    h.fold()
+    assert h.n == 0 and np.array_equal(h.Q, want.Q) and np.array_equal(h.vec, want.vec)
+    assert np.array_equal(h.dequant(2), h.dequant(1))
+
+
+def pin_rank1_zero_state(L):
+    """An all-zero state: no start row, zero pairs, zero codes."""
+    h = oracle.quantize(np.zeros((D, D), np.float32), C=4, L=L, fit="rank1")
+    assert list(h.idx[:4]) == [-1] * 4 and not np.any(h.vec) and not np.any(h.Q)
+
+
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
@@ -620,4 +680,5 @@ ALL = [
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
     pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step, pin_bf16_records,
+    pin_rank1_fit, pin_rank1_window_and_fold, pin_rank1_zero_state,
 ]

@@ -62,6 +62,13 @@ MUTANTS = [
     ("kda_lines_unscaled", "M[r * D + c] = M[r * D + c] + g[r] * v[c];", "M[r * D + c] = M[r * D + c] + v[c];"),
     ("kda_rebuild_no_gamma", "float a = gn[r] * rho[r];", "float a = rho[r];"),
     ("bf16_records_not_rounded", "x[e] = bf16_to_f32(lqo_f32_to_bf16(x[e]));", "x[e] = x[e];"),
+    ("r1_sweep_rows_for_columns", "                for (int r = 0; r < D; ++r) col[r] = R[r * D + c];\n                b[c] = lqo_t128_dot(col, a);",
+     "                for (int r = 0; r < D; ++r) col[r] = R[c * D + r];\n                b[c] = lqo_t128_dot(col, a);"),
+    ("r1_not_normalized", "for (int r = 0; r < D; ++r) a[r] = a[r] * inv;", ";"),
+    ("r1_no_deflation", "for (int c = 0; c < D; ++c) R[r * D + c] = fmaf(-a[r], b[c], R[r * D + c]);", ";"),
+    ("r1_read_with_b", "float d = lqo_t128_dot(a, x);", "float d = lqo_t128_dot(b, x);"),
+    ("r1_rebuild_unscaled", "float w = g * a[r];", "float w = a[r];"),
+    ("r1_start_last_max", "if (e > best) { best = e; pick = r; }", "if (e >= best) { best = e; pick = r; }"),
     ("kda_step_column_decay", "S[r * D + c] = alpha[r] * S[r * D + c];", "S[r * D + c] = alpha[c] * S[r * D + c];"),
 ]
 
