@@ -42,6 +42,11 @@ int32_t check_method_config(const leapq_config *c)
     if (c->decay == LEAPQ_DECAY_CHANNEL && c->qk_norm) return LEAPQ_ERR_RANGE;
     if (c->rec_dtype != LEAPQ_F32 && c->rec_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
     if (c->rec_dtype == LEAPQ_BF16 && (c->decay != LEAPQ_DECAY_SCALAR || c->qk_norm)) return LEAPQ_ERR_RANGE;
+    if (c->comp_fit != LEAPQ_COMP_LINES && c->comp_fit != LEAPQ_COMP_RANK1) return LEAPQ_ERR_RANGE;
+    if (c->comp_fit == LEAPQ_COMP_RANK1 &&
+        (c->n_comp > 4 || c->decay != LEAPQ_DECAY_SCALAR || c->rec_dtype != LEAPQ_F32))
+        return LEAPQ_ERR_RANGE;
+    if (c->reserved[0] || c->reserved[1] || c->reserved[2]) return LEAPQ_ERR_RANGE;
     return LEAPQ_OK;
 }
 
@@ -56,6 +61,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     const uint64_t kb = key_bf16(c) ? 2 : 4;  // record key element
     const uint64_t gw = c->decay == LEAPQ_DECAY_CHANNEL ? kD : 1;  // record decay values
     const uint64_t ub = c->rec_dtype == LEAPQ_BF16 ? 2 : 4;        // record correction element
+    const uint64_t cw = c->comp_fit == LEAPQ_COMP_RANK1 ? 2 : 1;   // compensator vectors
     uint64_t off = 0;
     L->off_codes = off;
     off = round_up(off + H * kD * kD);
@@ -66,7 +72,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_comp_idx = off;
     off = round_up(off + H * C * 4);
     L->off_comp_vec = off;
-    off = round_up(off + H * C * kD * 4);
+    off = round_up(off + H * C * cw * kD * 4);
     L->off_rec_gamma = off;
     off = round_up(off + H * W * gw * 4);
     L->off_rec_k = off;
@@ -74,7 +80,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_rec_u = off;
     off = round_up(off + H * W * kD * ub);
     L->total_bytes = off;
-    L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * kD * 4;
+    L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * cw * kD * 4;
     L->record_bytes_per_head = W * (4 * gw + kD * kb + kD * ub);
 }
 
@@ -102,6 +108,7 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->key_bf16 = key_bf16(&layer->cfg);
     sv->kda = layer->cfg.decay == LEAPQ_DECAY_CHANNEL;
     sv->u_bf16 = layer->cfg.rec_dtype == LEAPQ_BF16;
+    sv->r1 = layer->cfg.comp_fit == LEAPQ_COMP_RANK1;
     return LEAPQ_OK;
 }
 
@@ -144,7 +151,9 @@ leapq::GateArgs plain_gate(const leapq_config &c) { return {nullptr, nullptr, 1.
 int32_t gate_of(const leapq_layer *layer, const leapq_gate *g, leapq::GateArgs *out)
 {
     if (!g || !g->A_log || !g->dt_bias) return LEAPQ_ERR_NULL;
-    if (layer->cfg.decay != LEAPQ_DECAY_SCALAR || layer->cfg.rec_dtype != LEAPQ_F32) return LEAPQ_ERR_RANGE;
+    if (layer->cfg.decay != LEAPQ_DECAY_SCALAR || layer->cfg.rec_dtype != LEAPQ_F32 ||
+        layer->cfg.comp_fit != LEAPQ_COMP_LINES)
+        return LEAPQ_ERR_RANGE;
     if (!aligned(g->A_log, 4) || !aligned(g->dt_bias, 4)) return LEAPQ_ERR_ALIGN;
     if (g->reserved[0] || g->reserved[1]) return LEAPQ_ERR_RANGE;
     if (!(g->norm_eps >= 0.0f) || g->norm_eps > 3.0e38f) return LEAPQ_ERR_RANGE;

@@ -73,20 +73,21 @@ __device__ __forceinline__ void copy_record(const HeadState &hs, int g, int l, f
     }
 }
 
-// LDS of one head in floats: records [n][stride] (keys K), lines [C][128],
-// rho [128], sigma [128], inputs (k, q, v as T), indices [8], then the
-// record decays [64] or, with CH, the token's decay vector [128]
-template <typename T, typename K, bool CH = false, typename U = float>
+// LDS of one head in floats: records [n][stride] (keys K), compensators
+// ([C][128] lines, or with R1 [C][2][128] rank-one pairs), rho [128], sigma
+// [128], inputs (k, q, v as T), indices [8], then the record decays [64] or,
+// with CH, the token's decay vector [128]
+template <typename T, typename K, bool CH = false, typename U = float, bool R1 = false>
 __host__ __device__ constexpr int head_lds_floats(int n, int C)
 {
-    return n * Rec<K, CH, U>::stride + C * 128 + 256 + InLds<T>::floats + 8 + (CH ? 128 : 64);
+    return n * Rec<K, CH, U>::stride + C * (R1 ? 256 : 128) + 256 + InLds<T>::floats + 8 + (CH ? 128 : 64);
 }
 // per-workgroup results of the dot jobs: coefficients [2][64], column-token
 // dots [2][8], k.q [1], then the gated alpha and beta [2] (+1 pad)
 constexpr int kDotFloats = 128 + 16 + 4;
 constexpr int kGateSlot = 145;
 
-template <typename T, typename K, bool CH = false, typename U = float>
+template <typename T, typename K, bool CH = false, typename U = float, bool R1 = false>
 struct HeadLds {
     float *rec, *cv, *srho, *ssig, *sin_, *sgam;
     int *sidx;
@@ -98,7 +99,7 @@ struct HeadLds {
     {
         rec = base;
         cv = rec + n * Rec<K, CH, U>::stride;
-        srho = cv + C * D;
+        srho = cv + C * D * (R1 ? 2 : 1);
         ssig = srho + D;
         sin_ = ssig + D;
         sidx = reinterpret_cast<int *>(sin_ + InLds<T>::floats);
@@ -120,17 +121,18 @@ __device__ __forceinline__ void wait_lds_copies()
 // Issues every global load of head h: every operand other than the codes
 // into the LDS buffer L by LDS-direct copies, then the thread's 64 codes into
 // qc as the wave's last kCodeLoads vector loads.
-template <typename T, typename K, bool CH = false, typename U = float>
+template <typename T, typename K, bool CH = false, typename U = float, bool R1 = false>
 __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
                                              const T *__restrict__ kin, const T *__restrict__ vin,
-                                             const MMap &a, const HeadLds<T, K, CH, U> &L, uint4 (&qc)[4],
+                                             const MMap &a, const HeadLds<T, K, CH, U, R1> &L, uint4 (&qc)[4],
                                              const float *__restrict__ alpha = nullptr)
 {
     const int C = sv.C, l = a.l, w = a.w;
     const HeadState hs = head_state(sv, h);
     for (int rr = w; rr < n; rr += 4) copy_record<K, CH, U>(hs, rr, l, L.rec + rr * Rec<K, CH, U>::stride);
-    for (int pair = 2 * w; pair < C; pair += 8)
-        if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
+    const int nvec = R1 ? 2 * C : C;  // 128-vectors of the compensators
+    for (int pair = 2 * w; pair < nvec; pair += 8)
+        if (pair + (l >> 5) < nvec) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), L.cv + pair * D);
     if (w == 0) {
         lds_copy16(l < 32 ? hs.rho + 4 * l : hs.sigma + 4 * (l - 32), L.srho);
     } else if (w == 1) {
@@ -198,9 +200,10 @@ __device__ __forceinline__ void gate_issue(const GateArgs &g, int h, const MMap 
 // dot (the record key is then the normalized k in fp32).  Expects the LDS copies landed and visible (wait_lds_copies() and a
 // barrier); the codes are waited for at their first use.  Contains one
 // lds_barrier (dot jobs -> residual read and tail).
-template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool CH = false, typename U = float>
+template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool CH = false, typename U = float,
+          bool R1 = false>
 __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a,
-                                               const HeadLds<T, K, CH, U> &L, float *dots, const uint4 (&qc)[4],
+                                               const HeadLds<T, K, CH, U, R1> &L, float *dots, const uint4 (&qc)[4],
                                                float a_h, float b_h, float *__restrict__ o, float q_scale = 1.0f,
                                                float eps = 0.0f)
 {
@@ -262,7 +265,8 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     //            (w_r . k), (w_r . q) with w_r = (gamma_t / gamma_r) (.) k_r;
     // job n: (k . q);
     // job n+1+jj: (line_jj . x), (line_jj . y) for column tokens, x = k and
-    //            y = q, or with CH x = gamma_t (.) k and y = gamma_t (.) q
+    //            y = q, or with CH x = gamma_t (.) k and y = gamma_t (.) q;
+    //            with R1 (a_jj . k), (a_jj . q) for every rank-one pair
     const int njobs = n + 1 + C;
     for (int job = w; job < njobs; job += 4) {
         if (job < n) {
@@ -291,8 +295,9 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
             if (l == 0) kqd[0] = d;
         } else {
             const int jj = job - n - 1;
-            if (sidx[jj] >= D) {
-                const float a0 = cv[jj * D + l], a1 = cv[jj * D + l + 64];
+            if (R1 || sidx[jj] >= D) {
+                const float *vj = cv + jj * D * (R1 ? 2 : 1);  // a line, or the pair's a
+                const float a0 = vj[l], a1 = vj[l + 64];
                 const float dk = wdot(a0, a1, CH ? gt0 * k0 : k0, CH ? gt1 * k1 : k1);
                 const float dq = wdot(a0, a1, CH ? gt0 * q0 : q0, CH ? gt1 * q1 : q1);
                 if (l == 0) {
@@ -345,6 +350,10 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     // ---- per-column tail: lane (vec, c)
     float b = sig_c * red;
     for (int jj = 0; jj < C; ++jj) {
+        if constexpr (R1) {  // (a_jj . x) b_jj[c]
+            b = fma_(cdot[vec * 8 + jj], cv[(2 * jj + 1) * D + c], b);
+            continue;
+        }
         const int id = sidx[jj];
         if (id < 0) continue;
         if (id < D) {

@@ -115,7 +115,7 @@ __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
     s.rho = sv.rho + (size_t)h * D;
     s.sigma = sv.sigma + (size_t)h * D;
     s.cidx = sv.cidx + (size_t)h * sv.C;
-    s.cvec = sv.cvec + (size_t)h * sv.C * D;
+    s.cvec = sv.cvec + (size_t)h * sv.C * D * (sv.r1 ? 2 : 1);
     s.rgam = sv.rgam + (size_t)h * sv.W * (sv.kda ? D : 1);
     s.rk = static_cast<char *>(sv.rk) + (size_t)h * sv.W * D * (sv.key_bf16 ? 2 : 4);
     s.ru = static_cast<char *>(sv.ru) + (size_t)h * sv.W * D * (sv.u_bf16 ? 2 : 4);

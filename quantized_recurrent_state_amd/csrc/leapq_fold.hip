@@ -63,12 +63,13 @@ struct FoldWork {
 
 // Copies boundary fields (lines, rho, sigma, indices) and the decays to LDS:
 // the n record decays, or with CH the last record's decay vector.
-template <bool CH, typename Stage>
+template <bool CH, typename Stage, bool R1 = false>
 __device__ __forceinline__ void stage_small(const MMap &a, const HeadState &hs, int C, int n, Stage &sm)
 {
     const int l = a.l, w = a.w;
-    for (int pair = 2 * w; pair < C; pair += 8)
-        if (pair + (l >> 5) < C) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), sm.lines + pair * D);
+    const int nvec = R1 ? 2 * C : C;  // 128-vectors of the compensators
+    for (int pair = 2 * w; pair < nvec; pair += 8)
+        if (pair + (l >> 5) < nvec) lds_copy16(hs.cvec + (pair + (l >> 5)) * D + 4 * (l & 31), sm.lines + pair * D);
     if (w == 0) {
         lds_copy16(l < 32 ? hs.rho + 4 * l : hs.sigma + 4 * (l - 32), sm.rho);
     } else if (w == 1) {
@@ -100,7 +101,9 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 // staged and visible.  Contains barriers when n > 16.  K: the key dtype.
 // CH: per-channel decay, gamma_n[r] read from gW (the last record's decay
 // vector), every scale and record coefficient taken per row.
-template <typename K, bool CH, typename U, typename Stage>
+// R1: the compensators are rank-one pairs [a | b] in sm.lines, applied as
+// matrix-instruction steps fma(gamma_n a[r], b[c], S) before the records.
+template <typename K, bool CH, typename U, typename Stage, bool R1 = false>
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
                                         bool lines, Stage &sm, float (&S)[4][16], const float *gW = nullptr)
 {
@@ -119,7 +122,7 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
 #pragma unroll
         for (int m = 0; m < 16; ++m) TS(S, p, m) = (code_f(cw[m >> 2], m & 3) * ap) * sg[m];
     }
-    if (lines && C > 0) {
+    if (!R1 && lines && C > 0) {
         // line of each of the thread's rows / columns (-1: none).  An entry
         // on a row line and a column line is +0 in the line extracted second
         // (it was zeroed by the first), so adding only one of the two gives
@@ -161,6 +164,20 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc[p >> 1][16 * (p & 1) + m] = S[p][m];
+    if constexpr (R1) {
+        if (lines) {
+            // A lane (w, jp) carries column w + 4 ((jp >> 2) & 1) + 8 (jp & 3) + 32 (jp >> 3)
+            const int ac = a.w + 4 * ((a.jp >> 2) & 1) + 8 * (a.jp & 3) + 32 * (a.jp >> 3);
+            const int kr = a.i + 32 * a.h;
+            for (int jj = 0; jj < C; ++jj) {
+                const float *av = sm.lines + jj * 2 * D, *bv = av + D;
+                const float b0 = gn * av[kr], b1 = gn * av[kr + 64];
+                const float au = bv[ac];
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b0, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(au, b1, acc[1], 0, 0, 0);
+            }
+        }
+    }
     for (int base = 0; base < n; base += 16) {
         const int cnt = n - base < 16 ? n - base : 16;
         if (base > 0) {
@@ -294,21 +311,136 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-// Steps after the rebuild, shared by init and fold.  Writes the head's new
-// boundary state (codes, rho, sigma, indices, lines).  CT >= 0: the number of
-// compensators as a compile-time constant (C == CT), unrolling the rounds.
+// Rank-one compensators by power sweeps (the rank-one fold option), in
+// order: the row of largest canonical energy (lowest index on ties; none,
+// with a zero pair and index -1, when no energy is positive); b = that row;
+// eight sweeps a = S b (canonical row dots), a = a * (1 / sqrt(T(a . a))),
+// b = S^T a (canonical column dots); the pair [a | b] is stored and S
+// deflated by fma(-a_r, b_c, S).  The row dots reduce like the row energies
+// (inside the thread, then lane bit 5, then across waves through LDS), the
+// column dots like the column energies; two barriers per sweep.
 template <int CT>
+__device__ __forceinline__ void fit_rank1(const MMap &a, float (&S)[4][16], const HeadState &hs, int C, FoldWork &sm)
+{
+    const int t = threadIdx.x, l = a.l;
+    constexpr int NR = CT >= 0 ? CT : 4;
+    const int nrounds = CT >= 0 ? CT : C;
+    float *bv = sm.colE[0];    // b, 128 values
+    float *rowP = sm.rowP[0];  // per-wave row partials [4][128]
+    auto combined = [&](int r) { return (rowP[r] + rowP[2 * D + r]) + (rowP[D + r] + rowP[3 * D + r]); };
+#pragma unroll
+    for (int jj = 0; jj < NR; ++jj) {
+        if (jj >= nrounds) break;
+        {
+            float rp[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
+            put_row_energies(a, rp, rowP);
+        }
+        lds_barrier();
+        const float e0 = combined(l), e1 = combined(l + 64);
+        const float M = wave_max(fmaxf(e0, e1));
+        int pick = -1;
+        if (M > 0.0f) {
+            const int cand = e0 == M ? l : e1 == M ? 64 + l : 1 << 20;
+            pick = __builtin_amdgcn_readfirstlane(wave_min(cand));
+        }
+        if (t == 0) hs.cidx[jj] = pick;
+        float *aout = hs.cvec + jj * 2 * D, *bout = aout + D;
+        if (pick < 0) {
+            aout[t] = 0.0f;  // a and b: 256 values
+            continue;
+        }
+        const int pr = pick >> 5;
+        if (a.i == (pick & 31)) {
+            // row pr of S by value selects (a branch per p becomes a runtime
+            // index into S)
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                bv[a.col(m)] = sel((pr & 2) != 0, sel((pr & 1) != 0, TS(S, 3, m), TS(S, 2, m)),
+                                   sel((pr & 1) != 0, TS(S, 1, m), TS(S, 0, m)));
+        }
+        lds_barrier();
+        float bc[16], ar[4], a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) bc[m] = bv[a.col(m)];
+        bool dead = false;
+        for (int s = 0; s < 8; ++s) {
+            float rd[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float x[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = fma_(TS(S, p, m), bc[m], TS(S, p, m + 8) * bc[m + 8]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[m] = x[m] + x[m + 4];
+                x[0] = x[0] + x[2];
+                x[1] = x[1] + x[3];
+                rd[p] = x[0] + x[1];
+            }
+            put_rows(a, xhalf32(rd[0], rd[2]), xhalf32(rd[1], rd[3]), rowP);
+            lds_barrier();
+#pragma unroll
+            for (int p = 0; p < 4; ++p) ar[p] = combined(a.row(p));
+            a0 = combined(l);
+            a1 = combined(l + 64);
+            const float na2 = wdot(a0, a1, a0, a1);
+            if (!(na2 > 0.0f)) {
+                dead = true;
+                break;
+            }
+            const float inv = 1.0f / sqrtf(na2);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) ar[p] = ar[p] * inv;
+            a0 = a0 * inv;
+            a1 = a1 * inv;
+            float cp[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                cp[m] = fma_(TS(S, 0, m), ar[0], TS(S, 2, m) * ar[2]) + fma_(TS(S, 1, m), ar[1], TS(S, 3, m) * ar[3]);
+            const float bcol = mcolsum16(cp, l);
+            if ((l & 1) == 0) bv[a.col(mcol_of(l))] = bcol;
+            lds_barrier();
+#pragma unroll
+            for (int m = 0; m < 16; ++m) bc[m] = bv[a.col(m)];
+        }
+        if (dead) {
+            aout[t] = 0.0f;
+            continue;
+        }
+        if (a.w == 0) {
+            aout[l] = a0;
+            aout[l + 64] = a1;
+        } else if (a.w == 1) {
+            bout[l] = bv[l];
+            bout[l + 64] = bv[l + 64];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) TS(S, p, m) = fma_(-ar[p], bc[m], TS(S, p, m));
+    }
+}
+
+// Steps after the rebuild, shared by init and fold.  Writes the head's new
+// boundary state (codes, rho, sigma, indices, compensators).  CT >= 0: the
+// number of compensators as a compile-time constant (C == CT), unrolling the
+// rounds.  R1: rank-one compensators by power sweeps in place of lines.
+template <int CT, bool R1 = false>
 __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16], const HeadState &hs, int C, int smoothing,
                                                float floor_, FoldWork &sm)
 {
     const int t = threadIdx.x, l = a.l;
-    // ---- compensator tokens: one greedy round per compensator (pick, store
-    // and zero the line, rescore the other axis).  Every wave takes the same
-    // pick from the energies in LDS, so a round needs one barrier: the
-    // rescored axis is written to the other of its two buffers, which no
-    // wave reads until that barrier.  The rounds are unrolled (C <= 8) and
-    // written out here, not called, so S stays in registers.
-    if (C > 0) {
+    // ---- compensator tokens.  Lines: one greedy round per compensator (pick,
+    // store and zero the line, rescore the other axis).  Every wave takes the
+    // same pick from the energies in LDS, so a round needs one barrier: the
+    // rescored axis is written to the other of its two buffers, which no wave
+    // reads until that barrier.  The rounds are unrolled (C <= 8) and written
+    // out here, not called, so S stays in registers.
+    if (R1 && C > 0) {
+        fit_rank1<CT>(a, S, hs, C, sm);
+        lds_barrier();
+    } else if (C > 0) {
         constexpr int NR = CT >= 0 ? CT : 8;
         const int nrounds = CT >= 0 ? CT : C;
         float rp[4];
@@ -458,7 +590,7 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
     }
 }
 
-template <int CT>
+template <int CT, bool R1>
 __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restrict__ S0, int smoothing,
                                               float floor_)
 {
@@ -472,10 +604,10 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int m = 0; m < 16; ++m) TS(S, p, m) = src[a.row(p) * D + a.col(m)];
-    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
+    quantize_state<CT, R1>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename K, int CT, bool CH, typename U>
+template <typename K, int CT, bool CH, typename U, bool R1>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
     __shared__ FoldStage<Rec<K, CH, U>::stride> st;
@@ -485,15 +617,15 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     const HeadState hs = head_state(sv, h);
     uint4 qc[4];
     load_codes(a, hs, qc);
-    stage_small<CH>(a, hs, sv.C, n, st);
+    stage_small<CH, decltype(st), R1>(a, hs, sv.C, n, st);
     stage_records<K, CH, U>(a, hs, 0, n < 16 ? n : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<K, CH, U>(a, hs, qc, sv.C, n, true, st, S, st.gW);
+    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n, true, st, S, st.gW);
     // no barrier: the quantization writes only LDS arrays the rebuild does
     // not read, and each thread rewrites only the codes it loaded
-    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
+    quantize_state<CT, R1>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
 // The last token of a full window and the fold, in one launch (W <= 16).
@@ -503,7 +635,7 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
 // empties the buffer), and the fold rebuilds from the same registers and LDS
 // instead of reading the boundary and the records again.  The results are
 // those of leapq_append followed by leapq_fold.
-template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, int CT>
+template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CT>
 __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
                                                      const T *__restrict__ kin, const T *__restrict__ vin,
                                                      const float *__restrict__ alpha,
@@ -519,9 +651,9 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     const int h = blockIdx.x;
     // with CH the token's decay vector is staged in gW (the fold then reads
     // gamma_n from the token's own record slot)
-    const HeadLds<T, K, CH, U> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
+    const HeadLds<T, K, CH, U, R1> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
     uint4 qc[4];
-    append_issue<T, K, CH, U>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    append_issue<T, K, CH, U, R1>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
     float a_h = CH ? 1.0f : sload(alpha, h);
     float b_h = sload(beta, h);
     if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
@@ -531,15 +663,15 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
         a_h = dots[kGateSlot];
         b_h = dots[kGateSlot + 1];
     }
-    append_compute<T, K, true, NORM, CH, U>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<K, CH, U>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
-    quantize_state<CT>(a, S, hs, sv.C, smoothing, floor_, wk);
+    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
+    quantize_state<CT, R1>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename K, bool CH, typename U>
+template <typename K, bool CH, typename U, bool R1>
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
     __shared__ FoldStage<Rec<K, CH, U>::stride> st;
@@ -549,12 +681,12 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
     const int nr = what == 2 ? n : 0;
     uint4 qc[4];
     load_codes(a, hs, qc);
-    stage_small<CH>(a, hs, sv.C, nr, st);
+    stage_small<CH, decltype(st), R1>(a, hs, sv.C, nr, st);
     stage_records<K, CH, U>(a, hs, 0, nr < 16 ? nr : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<K, CH, U>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
+    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
     float *dst = out + (size_t)h * D * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -567,25 +699,36 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
 hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
                        hipStream_t s)
 {
-    if (sv.C == 4)
-        hipLaunchKernelGGL(k_init<4>, dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
-    else
-        hipLaunchKernelGGL(k_init<-1>, dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    if (sv.r1) {
+        if (sv.C == 4)
+            hipLaunchKernelGGL((k_init<4, true>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+        else
+            hipLaunchKernelGGL((k_init<-1, true>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    } else if (sv.C == 4) {
+        hipLaunchKernelGGL((k_init<4, false>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    } else {
+        hipLaunchKernelGGL((k_init<-1, false>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    }
     return hipGetLastError();
 }
 
-template <typename K, bool CH, typename U = float>
+template <typename K, bool CH, typename U = float, bool R1 = false>
 static void launch_fold_t(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_fold<K, 4, CH, U>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, 4, CH, U, R1>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     else
-        hipLaunchKernelGGL((k_fold<K, -1, CH, U>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, -1, CH, U, R1>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
 }
 
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
-    if (sv.u_bf16) {
+    if (sv.r1) {
+        if (sv.key_bf16)
+            launch_fold_t<uint16_t, false, float, true>(sv, heads, n, smoothing, floor_, s);
+        else
+            launch_fold_t<float, false, float, true>(sv, heads, n, smoothing, floor_, s);
+    } else if (sv.u_bf16) {
         if (sv.key_bf16)
             launch_fold_t<uint16_t, false, uint16_t>(sv, heads, n, smoothing, floor_, s);
         else
@@ -603,17 +746,17 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
     return hipGetLastError();
 }
 
-template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float>
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false>
 static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, float *o, int smoothing, float floor_,
                                  const GateArgs &g, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, 4>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
-                           (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, 4>), dim3(heads), dim3(NT), 0, s, sv, n,
+                           (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
     else
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, -1>), dim3(heads), dim3(NT), 0, s, sv, n, (const T *)q,
-                           (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, -1>), dim3(heads), dim3(NT), 0, s, sv, n,
+                           (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
 }
 
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
@@ -623,7 +766,14 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
     // the (inputs, keys, gated, normalize) combinations of launch_append
     const bool kb = sv.key_bf16;
 #define LQ_AF(T, K, G, N) launch_append_fold_t<T, K, G, N>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
-    if (sv.u_bf16) {
+    if (sv.r1) {
+        if (!bf16)
+            launch_append_fold_t<float, float, false, false, false, float, true>(sv, heads, n, q, k, v, alpha, beta, o,
+                                                                               smoothing, floor_, g, s);
+        else
+            launch_append_fold_t<uint16_t, uint16_t, false, false, false, float, true>(
+                sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s);
+    } else if (sv.u_bf16) {
         if (!bf16)
             launch_append_fold_t<float, float, false, false, false, uint16_t>(sv, heads, n, q, k, v, alpha, beta, o,
                                                                             smoothing, floor_, g, s);
@@ -662,21 +812,28 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
 
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s)
 {
-    if (sv.u_bf16) {
+#define LQ_DQ(K, CH, U, R1) hipLaunchKernelGGL((k_dequant<K, CH, U, R1>), dim3(heads), dim3(NT), 0, s, sv, n, what, out)
+    if (sv.r1) {
         if (sv.key_bf16)
-            hipLaunchKernelGGL((k_dequant<uint16_t, false, uint16_t>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+            LQ_DQ(uint16_t, false, float, true);
         else
-            hipLaunchKernelGGL((k_dequant<float, false, uint16_t>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+            LQ_DQ(float, false, float, true);
+    } else if (sv.u_bf16) {
+        if (sv.key_bf16)
+            LQ_DQ(uint16_t, false, uint16_t, false);
+        else
+            LQ_DQ(float, false, uint16_t, false);
     } else if (sv.kda) {
         if (sv.key_bf16)
-            hipLaunchKernelGGL((k_dequant<uint16_t, true, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+            LQ_DQ(uint16_t, true, float, false);
         else
-            hipLaunchKernelGGL((k_dequant<float, true, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+            LQ_DQ(float, true, float, false);
     } else if (sv.key_bf16) {
-        hipLaunchKernelGGL((k_dequant<uint16_t, false, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+        LQ_DQ(uint16_t, false, float, false);
     } else {
-        hipLaunchKernelGGL((k_dequant<float, false, float>), dim3(heads), dim3(NT), 0, s, sv, n, what, out);
+        LQ_DQ(float, false, float, false);
     }
+#undef LQ_DQ
     return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ struct StateView {
     int key_bf16;  // record keys (and inputs) are bf16
     int kda;       // per-channel decay: alpha [heads][128], record decays [W][128]
     int u_bf16;    // record corrections stored in bf16
+    int r1;        // rank-one compensator pairs [C][2][128] in place of lines
 };
 
 // Gate arithmetic in front of the append (mode 0: alpha and beta are given;

@@ -29,6 +29,9 @@ LEAPQ_BF16 = 1
 LEAPQ_DECAY_SCALAR = 0
 LEAPQ_DECAY_CHANNEL = 1
 
+LEAPQ_COMP_LINES = 0
+LEAPQ_COMP_RANK1 = 1
+
 LEAPQ_DEQ_RESIDUAL = 0
 LEAPQ_DEQ_BOUNDARY = 1
 LEAPQ_DEQ_CURRENT = 2
@@ -43,7 +46,7 @@ class leapq_config(ctypes.Structure):
                 ("dv", ctypes.c_int32), ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
                 ("smoothing", ctypes.c_int32), ("sigma_floor", ctypes.c_float),
                 ("in_dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("decay", ctypes.c_int32),
-                ("rec_dtype", ctypes.c_int32)]
+                ("rec_dtype", ctypes.c_int32), ("comp_fit", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class leapq_gate(ctypes.Structure):
@@ -111,7 +114,7 @@ def _check(status, what):
 
 
 def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32",
-                qk_norm=False, decay="scalar", rec_dtype="f32"):
+                qk_norm=False, decay="scalar", rec_dtype="f32", comp_fit="lines"):
     c = leapq_config()
     c.batch, c.heads, c.dk, c.dv = int(batch), int(heads), D, D
     c.window, c.n_comp, c.smoothing = int(window), int(n_comp), int(bool(smoothing))
@@ -120,6 +123,7 @@ def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1
     c.qk_norm = int(bool(qk_norm))
     c.decay = LEAPQ_DECAY_CHANNEL if decay in ("channel", LEAPQ_DECAY_CHANNEL) else LEAPQ_DECAY_SCALAR
     c.rec_dtype = LEAPQ_BF16 if rec_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
+    c.comp_fit = LEAPQ_COMP_RANK1 if comp_fit in ("rank1", LEAPQ_COMP_RANK1) else LEAPQ_COMP_LINES
     return c
 
 
@@ -247,8 +251,10 @@ class Layer:
         return self._sec(self.layout.off_comp_idx, self.heads * C, torch.int32, (self.heads, C))
 
     def comp_vec(self):
+        """Compensators [heads, C, 128] (lines) or [heads, C, 256] (rank-one pairs [a | b])."""
         C = max(self.cfg.n_comp, 0)
-        return self._sec(self.layout.off_comp_vec, self.heads * C * D, torch.float32, (self.heads, C, D))
+        w = 2 * D if self.cfg.comp_fit == LEAPQ_COMP_RANK1 else D
+        return self._sec(self.layout.off_comp_vec, self.heads * C * w, torch.float32, (self.heads, C, w))
 
     def rec_gamma(self):
         """Record decays [heads, W] (scalar decay) or [heads, W, 128] (channel decay)."""

@@ -127,7 +127,8 @@ def _pool():
 
 
 def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="cuda", check_every_token=True,
-              fold_at=None, report=None, log=True, fused=False, gated=None, qk_norm=False, rec_u="f32"):
+              fold_at=None, report=None, log=True, fused=False, gated=None, qk_norm=False, rec_u="f32",
+              fit="lines"):
     """Runs `tokens` decode tokens of one layer on the GPU and, for the
     sampled heads, in the oracle; folds whenever the window is full (or at
     the token counts in fold_at).  With fused, the GPU takes each window's
@@ -135,14 +136,16 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     appends, then folds).  With gated = dict(q_scale=, eps=), the inputs are
     the raw projections of workloads.gated_token_inputs and the GPU runs the
     gated entry points (the oracle applies oracle.gated_inputs first); the
-    layer normalizes q and k when qk_norm.  Returns the Report."""
+    layer normalizes q and k when qk_norm.  rec_u selects the stored
+    correction's dtype and fit the compensator fit ("lines" or "rank1") on
+    both sides.  Returns (Report, Layer, oracle heads)."""
     rep = report or Report()
     dev = torch.device(device)
     H = wl.batch * wl.heads
     T = wl.tokens if tokens is None else tokens
     sample = list(range(H)) if sample is None else list(sample)
     cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype,
-                         qk_norm=qk_norm, decay=wl.decay, rec_dtype=rec_u)
+                         qk_norm=qk_norm, decay=wl.decay, rec_dtype=rec_u, comp_fit=fit)
     ash = (H, D) if wl.decay == "channel" else (H,)
     L = lq.Layer(cfg, dev)
     if gated is not None:
@@ -153,8 +156,8 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     S0 = workloads.initial_state(wl, layer, device=gen_device).reshape(H, D, D)
     lq.leapq_init_state(L, S0.to(dev))
     S0h = S0[sample].cpu().numpy()
-    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay, rec_u=rec_u)
-            for _ in sample]
+    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay, rec_u=rec_u,
+                        fit=fit) for _ in sample]
     with _pool() as pool:
         list(pool.map(lambda a: a[0].init(a[1]), zip(refs, S0h)))
         torch.cuda.synchronize(dev)

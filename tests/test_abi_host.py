@@ -319,3 +319,26 @@ def test_bf16_corrections_layout_and_checks():
         assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
     # the gated entry points keep fp32 corrections
     assert call_gated(fake_layer(cfg(rec_dtype="bf16")), gate_struct()) == lq.LEAPQ_ERR_RANGE
+
+
+# ---------------------------------------------------------------- rank-one compensators
+
+def test_rank1_layout_and_checks():
+    lines = layout(batch=2, heads=4, window=16, n_comp=4)
+    r1 = layout(batch=2, heads=4, window=16, n_comp=4, comp_fit="rank1")
+    # each compensator holds the pair (a, b): twice the vector bytes of a line
+    assert r1.off_rec_gamma - r1.off_comp_vec >= 2 * 4 * 4 * 256 * 4
+    assert r1.total_bytes - lines.total_bytes >= 2 * 4 * 4 * 128 * 4 - 256
+    assert r1.record_bytes_per_head == lines.record_bytes_per_head
+    out = lq.leapq_layout()
+    c = cfg()
+    c.comp_fit = 2
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE
+    for kw in (dict(n_comp=5), dict(decay="channel"), dict(rec_dtype="bf16")):
+        c = cfg(comp_fit="rank1", **kw)
+        assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
+    for C in (0, 1, 4):
+        c = cfg(comp_fit="rank1", n_comp=C)
+        assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_OK, C
+    # the gated entry points keep line compensators
+    assert call_gated(fake_layer(cfg(comp_fit="rank1")), gate_struct()) == lq.LEAPQ_ERR_RANGE
