@@ -44,6 +44,8 @@ def parse():
                    help="skip the per-channel decay (KDA) measurement at the same shape")
     p.add_argument("--no-bf16-records", action="store_true",
                    help="skip the measurement of the lossy bf16 record-corrections option")
+    p.add_argument("--no-rank1", action="store_true",
+                   help="skip the measurement of the rank-one compensator option")
     p.add_argument("--baseline-tokens", type=int, default=16)
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--separate", action="store_true",
@@ -262,57 +264,72 @@ def main():
         del glayers, gpool, gates
         torch.cuda.empty_cache()
 
-    # ---- the lossy option: record corrections kept in bf16, same inputs and
-    # schedule (a separate measurement, never the headline value)
-    bf16rec = None
-    if not args.no_bf16_records:
-        bcfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, rec_dtype="bf16")
-        blayers = []
+    # ---- layout options on the same inputs and schedule (separate
+    # measurements, never the headline value)
+    def time_option(vcfg, u_bytes=4, rank1=False):
+        vlayers = []
         for l in range(Lyr):
-            L = lq.Layer(bcfg, dev)
+            L = lq.Layer(vcfg, dev)
             S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
             lq.leapq_init_state(L, S0)
             del S0
-            blayers.append(L)
+            vlayers.append(L)
 
-        def bwindow(ev=None):
+        def vwindow(ev=None):
             for pos in range(W):
                 for l in range(Lyr):
                     q, k, v, a, b = pool[l][pos]
                     if ev is not None:
                         ev.append((pos, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
                         ev[-1][1].record(stream)
-                    if blayers[l].n_records == W - 1:
-                        lq.leapq_append_fold(blayers[l], q, k, v, a, b, outs[l], stream)
+                    if vlayers[l].n_records == W - 1:
+                        lq.leapq_append_fold(vlayers[l], q, k, v, a, b, outs[l], stream)
                     else:
-                        lq.leapq_append(blayers[l], q, k, v, a, b, outs[l], stream)
+                        lq.leapq_append(vlayers[l], q, k, v, a, b, outs[l], stream)
                     if ev is not None:
                         ev[-1][2].record(stream)
 
-        bwindow()
+        vwindow()
         torch.cuda.synchronize(dev)
-        bsteps = max(4, args.steps // 4)
+        vsteps = max(4, args.steps // 4)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(bsteps):
-            bwindow()
+        for _ in range(vsteps):
+            vwindow()
         e1.record(stream)
         torch.cuda.synchronize(dev)
-        b_ms = e0.elapsed_time(e1) / bsteps
-        bev = []
-        bwindow(bev)
+        v_ms = e0.elapsed_time(e1) / vsteps
+        vev = []
+        vwindow(vev)
         torch.cuda.synchronize(dev)
-        b_app = float(np.mean([1e3 * x.elapsed_time(y) for pos, x, y in bev if pos < W - 1]))
-        b_bytes = float(np.mean([metrics.append_bytes(n, C, in_bytes, u_bytes=2) for n in range(W - 1)])) * H
-        bf16rec = {"tokens_per_s": B * W / (b_ms / 1e3), "ms_per_step": b_ms, "steps": bsteps,
-                   "ratio_to_plain": (B * W / (b_ms / 1e3)) / tokens_per_s, "append_us": b_app,
-                   "append_fold_us": float(np.mean([1e3 * x.elapsed_time(y) for pos, x, y in bev if pos == W - 1])),
-                   "append_gbps_algorithmic": b_bytes / (b_app * 1e-6) / 1e9,
-                   "note": "lossy option: record corrections rounded to bf16 (see quality.py --rec-dtype bf16)"}
-        log(f"[bench] bf16 record corrections: {b_ms:.3f} ms per window, {bf16rec['tokens_per_s']:,.0f} tokens/s "
-            f"({bf16rec['ratio_to_plain']:.3f} of the plain path); append {b_app:.1f} us")
-        del blayers
+        del vlayers
         torch.cuda.empty_cache()
+        v_app = float(np.mean([1e3 * x.elapsed_time(y) for pos, x, y in vev if pos < W - 1]))
+        v_bytes = float(np.mean([metrics.append_bytes(n, C, in_bytes, u_bytes=u_bytes, rank1=rank1)
+                                 for n in range(W - 1)])) * H
+        return {"tokens_per_s": B * W / (v_ms / 1e3), "ms_per_step": v_ms, "steps": vsteps,
+                "ratio_to_plain": (B * W / (v_ms / 1e3)) / tokens_per_s, "append_us": v_app,
+                "append_fold_us": float(np.mean([1e3 * x.elapsed_time(y) for pos, x, y in vev if pos == W - 1])),
+                "append_gbps_algorithmic": v_bytes / (v_app * 1e-6) / 1e9}
+
+    bf16rec = None
+    if not args.no_bf16_records:
+        bf16rec = time_option(lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype,
+                                             rec_dtype="bf16"), u_bytes=2)
+        bf16rec["note"] = "lossy option: record corrections rounded to bf16 (see quality.py --rec-dtype bf16)"
+        log(f"[bench] bf16 record corrections: {bf16rec['ms_per_step']:.3f} ms per window, "
+            f"{bf16rec['tokens_per_s']:,.0f} tokens/s ({bf16rec['ratio_to_plain']:.3f} of the plain path); "
+            f"append {bf16rec['append_us']:.1f} us")
+
+    rank1 = None
+    if not args.no_rank1:
+        rank1 = time_option(lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype,
+                                           comp_fit="rank1"), rank1=True)
+        rank1["note"] = ("rank-one compensators fitted by power sweeps in the fold "
+                         "(see quality.py --comp-fit rank1)")
+        log(f"[bench] rank-one compensators: {rank1['ms_per_step']:.3f} ms per window, "
+            f"{rank1['tokens_per_s']:,.0f} tokens/s ({rank1['ratio_to_plain']:.3f} of the plain path); "
+            f"append {rank1['append_us']:.1f} us, last append + fold {rank1['append_fold_us']:.1f} us")
 
     # ---- per-channel decay (KDA): the same shape and schedule with alpha a
     # 128-vector per head and token, and the dense KDA baselines
@@ -478,6 +495,7 @@ def main():
         "gated": gated,
         "kda": kda,
         "bf16_record_corrections": bf16rec,
+        "rank1_compensators": rank1,
         "baselines": baselines,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),

@@ -5,6 +5,7 @@ for one head (no re-reads, no dense fp32 state):
 
   append, with n records already in the window (token n+1):
       read   codes 128*128 + rho, sigma 2*512 + compensators C*(4+512)
+             (C*(4+1024) for rank-one pairs a, b)
              + q, k, v 3*128*e_in + alpha, beta 8 + records n*(4+128*e_in+512)
       write  record 4+128*e_in+512 + output 512
   (a record holds gamma and u in fp32 and the key in the input dtype e_in,
@@ -24,9 +25,10 @@ share of window time is fold / (appends + fold).
 D = 128
 
 
-def boundary_bytes(C=4):
-    """Bytes of one head's boundary state: int8 codes, rho, sigma, C lines."""
-    return D * D + 2 * D * 4 + C * (4 + D * 4)
+def boundary_bytes(C=4, rank1=False):
+    """Bytes of one head's boundary state: int8 codes, rho, sigma, and C
+    compensators (an index and a line, or an index and a pair a, b)."""
+    return D * D + 2 * D * 4 + C * (4 + D * 4 * (2 if rank1 else 1))
 
 
 def record_bytes(in_bytes=2, channel=False, u_bytes=4):
@@ -35,17 +37,17 @@ def record_bytes(in_bytes=2, channel=False, u_bytes=4):
     return 4 * (D if channel else 1) + D * in_bytes + D * u_bytes
 
 
-def append_bytes(n, C=4, in_bytes=2, channel=False, u_bytes=4):
+def append_bytes(n, C=4, in_bytes=2, channel=False, u_bytes=4, rank1=False):
     """Algorithmic bytes of one head's append with n records present."""
     gates = 4 * (D if channel else 1) + 4
     rec = record_bytes(in_bytes, channel, u_bytes)
-    read = boundary_bytes(C) + 3 * D * in_bytes + gates + n * rec
+    read = boundary_bytes(C, rank1) + 3 * D * in_bytes + gates + n * rec
     write = rec + D * 4
     return read + write
 
 
-def fold_bytes(n, C=4, in_bytes=2, channel=False):
-    return 2 * boundary_bytes(C) + n * record_bytes(in_bytes, channel)
+def fold_bytes(n, C=4, in_bytes=2, channel=False, rank1=False):
+    return 2 * boundary_bytes(C, rank1) + n * record_bytes(in_bytes, channel)
 
 
 def init_bytes(C=4):

@@ -19,7 +19,8 @@ the GPU output and whether a fold followed; the parity tests use it to run
 CPU reference heads beside the GPU path.
 
   python -m quantized_recurrent_state_amd.quality [--workload long] [--layers 3]
-         [--tokens 4095] [--rec-dtype f32|bf16] [--out result.json]
+         [--tokens 4095] [--rec-dtype f32|bf16] [--comp-fit lines|rank1]
+         [--out result.json]
 """
 import argparse
 import json
@@ -43,14 +44,16 @@ def _summ(x):
             "heads": int(x.size)}
 
 
-def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, on_token=None, rec_dtype="f32"):
+def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, on_token=None, rec_dtype="f32",
+        comp_fit="lines"):
     wl = workloads.WORKLOADS[workload]
     dev = torch.device(device)
     B, Hh, W, C = wl.batch, wl.heads, wl.window, wl.n_comp
     H = B * Hh
     nlayers = wl.layers if layers is None else layers
     T = wl.tokens if tokens is None else tokens
-    cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, decay=wl.decay, rec_dtype=rec_dtype)
+    cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, decay=wl.decay, rec_dtype=rec_dtype,
+                         comp_fit=comp_fit)
     ash = (H, D) if wl.decay == "channel" else (H,)
     rel_q, rel_b, hard = [], [], []
     for layer in range(nlayers):
@@ -96,6 +99,7 @@ def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, o
     rq, rb, hd = np.concatenate(rel_q), np.concatenate(rel_b), np.concatenate(hard)
     out = {
         "workload": wl.name, "layers": nlayers, "tokens": T, "heads_per_layer": H, "record_corrections": rec_dtype,
+        "compensators": comp_fit,
         "metric": "per-head ||O - O_fp32||_F / ||O_fp32||_F over all tokens",
         "leapq": {"regular": _summ(rq[~hd]), "hard": _summ(rq[hd])},
         "bf16_per_token": {"regular": _summ(rb[~hd]), "hard": _summ(rb[hd])},
@@ -111,10 +115,12 @@ def main(argv=None):
     p.add_argument("--tokens", type=int, default=None)
     p.add_argument("--rec-dtype", default="f32", choices=("f32", "bf16"),
                    help="storage of the record corrections (bf16: the lossy lower-precision option)")
+    p.add_argument("--comp-fit", default="lines", choices=("lines", "rank1"),
+                   help="compensator fit: whole rows/columns, or rank-one pairs from power sweeps")
     p.add_argument("--out", default=None)
     a = p.parse_args(argv)
     res = run(a.workload, a.layers, a.tokens, log=lambda m: print(m, file=sys.stderr, flush=True),
-              rec_dtype=a.rec_dtype)
+              rec_dtype=a.rec_dtype, comp_fit=a.comp_fit)
     s = json.dumps(res, indent=1)
     print(s, flush=True)
     if a.out:
