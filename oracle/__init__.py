@@ -63,6 +63,10 @@ def _bind(L):
         "lqo_current_r1": (None, [i8p, f32p, f32p, ci, f32p, ci, f32p, f32p, f32p, f32p]),
         "lqo_append_r1": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p,
                                  f32p, f32p, f32p, cf, cf, f32p]),
+        "lqo_fit_block": (None, [f32p, ci, i32p, f32p, ci, ci]),
+        "lqo_quantize_block": (None, [f32p, ci, ci, cf, ci, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_init_block": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_fold_block": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
         "lqo_l2norm": (None, [f32p, cf, cf, f32p]),
         "lqo_dim": (ci, []),
     }
@@ -147,17 +151,20 @@ class Head:
         if rec_u not in ("f32", "bf16"):
             raise ValueError("rec_u must be 'f32' or 'bf16'")
         self.rec_u = rec_u
-        if fit not in ("lines", "rank1"):
-            raise ValueError("fit must be 'lines' or 'rank1'")
-        if fit == "rank1" and self.kda:
-            raise ValueError("rank-one compensators are defined for scalar decay")
+        if fit not in ("lines", "rank1", "block"):
+            raise ValueError("fit must be 'lines', 'rank1' or 'block'")
+        if fit != "lines" and self.kda:
+            raise ValueError("rank-one and block compensators are defined for scalar decay")
         self.fit = fit
-        self.r1 = fit == "rank1"
+        # rank-one and block fits store and read the same pairs [a | b]
+        self.r1 = fit in ("rank1", "block")
+        self.block = fit == "block"
         self.Q = np.zeros((D, D), np.int8)
         self.rho = np.zeros(D, np.float32)
         self.sigma = np.ones(D, np.float32)
         self.idx = np.full(max(self.C, 1), -1, np.int32)
-        # compensators: lines [C][128], or rank-one pairs [C][2 * 128] = [a | b]
+        # compensators: lines [C][128], or pairs [C][2 * 128] = [a | b] (rank-one
+        # and block fits)
         self.vec = np.zeros((max(self.C, 1), 2 * D if self.r1 else D), np.float32)
         self.gam = np.zeros((max(self.W, 1), D) if self.kda else max(self.W, 1), np.float32)
         self.rk = np.zeros((max(self.W, 1), D), np.float32)
@@ -176,7 +183,7 @@ class Head:
     def init(self, S0):
         S0 = f32(S0).reshape(D, D)
         fp = ctypes.c_float
-        fn = self.L.lqo_init_r1 if self.r1 else self.L.lqo_init
+        fn = self.L.lqo_init_block if self.block else self.L.lqo_init_r1 if self.r1 else self.L.lqo_init
         fn(_p(S0, fp), self.C, self.smoothing, self.floor, _p(self.Q, ctypes.c_int8),
            _p(self.rho, fp), _p(self.sigma, fp), _p(self.idx, ctypes.c_int32), _p(self.vec, fp))
         self.n = 0
@@ -205,7 +212,12 @@ class Head:
         return o, self.ru[self.n - 1].copy()
 
     def fold(self):
-        fn = self.L.lqo_fold_kda if self.kda else self.L.lqo_fold_r1 if self.r1 else self.L.lqo_fold
+        if self.kda:
+            fn = self.L.lqo_fold_kda
+        elif self.block:
+            fn = self.L.lqo_fold_block
+        else:
+            fn = self.L.lqo_fold_r1 if self.r1 else self.L.lqo_fold
         fn(*self._st(), *self._rec(), self.smoothing, self.floor)
         self.n = 0
         return self
@@ -236,6 +248,18 @@ class Head:
             setattr(h, name, getattr(self, name).copy())
         h.n = self.n
         return h
+
+
+def fit_block(R, C=4, idx=None, ab=None, warm=False, sweeps=2, L=None):
+    """The block fit alone on a copy of R: returns (deflated R, idx, ab).
+    With warm, the live pairs of (idx, ab) are the start."""
+    L = L or lib()
+    R = f32(R).reshape(D, D).copy()
+    idx = np.full(max(C, 1), -1, np.int32) if idx is None else np.array(idx, np.int32)
+    ab = np.zeros((max(C, 1), 2 * D), np.float32) if ab is None else np.array(ab, np.float32)
+    L.lqo_fit_block(_p(R, ctypes.c_float), int(C), _p(idx, ctypes.c_int32), _p(ab, ctypes.c_float), int(warm),
+                    int(sweeps))
+    return R, idx, ab
 
 
 def quantize(R, C=4, smoothing=True, sigma_floor=1e-6, L=None, fit="lines"):

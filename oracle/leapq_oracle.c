@@ -381,6 +381,133 @@ void lqo_fold_r1(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float
 }
 
 /* ------------------------------------------------------------------ */
+/* Block fit of the compensators (a fold option): [RN4] Redesign plans   */
+/* to fit the compensators together as one block, starting from the     */
+/* previous window's compensators.  Read as subspace (block power)      */
+/* iteration on the key side with modified Gram-Schmidt.  The pairs are */
+/* stored and read exactly as the rank-one pairs above ([a | b], the    */
+/* boundary is the residual plus sum_j a_j b_j^T); idx_j is j for a     */
+/* live pair and -1 for an unused one.                                   */
+/* ------------------------------------------------------------------ */
+
+#define LQO_BLOCK_SWEEPS 2       /* per fold, warm-started */
+#define LQO_BLOCK_SWEEPS_INIT 8  /* at init, from the longest rows */
+
+/* Modified Gram-Schmidt over the slots in order: each earlier live vector
+ * is projected out, y = fma(-T(a_i . y), a_i, y) per element; then a zero
+ * norm T(y . y) leaves the slot unused (y = 0), otherwise y is scaled by
+ * 1 / sqrt(T(y . y)). */
+static void block_mgs(float A[][D], int C, int *live)
+{
+    for (int j = 0; j < C; ++j) {
+        for (int i = 0; i < j; ++i) {
+            if (!live[i]) continue;
+            float d = lqo_t128_dot(A[i], A[j]);
+            for (int r = 0; r < D; ++r) A[j][r] = fmaf(-d, A[i][r], A[j][r]);
+        }
+        float n2 = lqo_t128_dot(A[j], A[j]);
+        live[j] = n2 > 0.0f;
+        if (!live[j]) {
+            for (int r = 0; r < D; ++r) A[j][r] = 0.0f;
+            continue;
+        }
+        float inv = 1.0f / sqrtf(n2);
+        for (int r = 0; r < D; ++r) A[j][r] = A[j][r] * inv;
+    }
+}
+
+/* z[c] = T(R[:, c] . a) for every column. */
+static void cols_dot(const float *R, const float *a, float *z)
+{
+    for (int c = 0; c < D; ++c) {
+        float col[D];
+        for (int r = 0; r < D; ++r) col[r] = R[r * D + c];
+        z[c] = lqo_t128_dot(col, a);
+    }
+}
+
+/* Fits C pairs to R and deflates R by them.
+ *   start: with warm, a live pair j (idx_j >= 0) starts from its stored a_j;
+ *          every other slot, in slot order, starts from the unit vector of
+ *          the next row by canonical energy (largest first, lowest index on
+ *          ties, rows of zero energy never), or from zero if none is left;
+ *          then A = MGS(start).
+ *   sweeps times: z_j = R^T a_j;  y_j[r] = T(R[r, :] . z_j);  A = MGS(Y).
+ *   b_j = R^T a_j;  idx_j = j (or -1 if unused);
+ *   R[r][c] = fma(-a_j[r], b_j[c], R[r][c]) for j in order. */
+void lqo_fit_block(float *R, int C, int32_t *idx, float *ab, int warm, int sweeps)
+{
+    float A[8][D], Z[D];
+    int live[8];
+    float e[D];
+    int used[D];
+    for (int r = 0; r < D; ++r) {
+        e[r] = lqo_t128_dot(R + r * D, R + r * D);
+        used[r] = 0;
+    }
+    for (int j = 0; j < C; ++j) {
+        if (warm && idx[j] >= 0) {
+            for (int r = 0; r < D; ++r) A[j][r] = ab[(size_t)j * 2 * D + r];
+            continue;
+        }
+        float best = 0.0f;
+        int pick = -1;
+        for (int r = 0; r < D; ++r)
+            if (!used[r] && e[r] > best) { best = e[r]; pick = r; }
+        for (int r = 0; r < D; ++r) A[j][r] = 0.0f;
+        if (pick >= 0) {
+            A[j][pick] = 1.0f;
+            used[pick] = 1;
+        }
+    }
+    block_mgs(A, C, live);
+    for (int s = 0; s < sweeps; ++s) {
+        for (int j = 0; j < C; ++j) {
+            cols_dot(R, A[j], Z);
+            for (int r = 0; r < D; ++r) A[j][r] = lqo_t128_dot(R + r * D, Z);
+        }
+        block_mgs(A, C, live);
+    }
+    for (int j = 0; j < C; ++j) {
+        float *a = ab + (size_t)j * 2 * D, *b = a + D;
+        for (int r = 0; r < D; ++r) a[r] = A[j][r];
+        cols_dot(R, A[j], b);
+        idx[j] = live[j] ? j : -1;
+    }
+    for (int j = 0; j < C; ++j) {
+        const float *a = ab + (size_t)j * 2 * D, *b = a + D;
+        for (int r = 0; r < D; ++r)
+            for (int c = 0; c < D; ++c) R[r * D + c] = fmaf(-a[r], b[c], R[r * D + c]);
+    }
+}
+
+/* Quantization with a block fit: the fit, then smoothing and rounding. */
+void lqo_quantize_block(float *R, int C, int smoothing, float sigma_floor, int warm,
+                        int8_t *Q, float *rho, float *sigma, int32_t *idx, float *ab)
+{
+    lqo_fit_block(R, C, idx, ab, warm, warm ? LQO_BLOCK_SWEEPS : LQO_BLOCK_SWEEPS_INIT);
+    smooth_and_round(R, smoothing, sigma_floor, Q, rho, sigma);
+}
+
+void lqo_init_block(const float *S0, int C, int smoothing, float sigma_floor,
+                    int8_t *Q, float *rho, float *sigma, int32_t *idx, float *ab)
+{
+    float R[D * D];
+    memcpy(R, S0, sizeof R);
+    lqo_quantize_block(R, C, smoothing, sigma_floor, 0, Q, rho, sigma, idx, ab);
+}
+
+/* Fold with a block fit: the current state (as with rank-one pairs), then
+ * the fit warm-started from the window's own pairs. */
+void lqo_fold_block(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *ab,
+                    int n, const float *gam, const float *rk, const float *ru, int smoothing, float sigma_floor)
+{
+    float R[D * D];
+    lqo_current_r1(Q, rho, sigma, C, ab, n, gam, rk, ru, R);
+    lqo_quantize_block(R, C, smoothing, sigma_floor, 1, Q, rho, sigma, idx, ab);
+}
+
+/* ------------------------------------------------------------------ */
 /* Append: one decode token against the fixed boundary plus the records */
 /* ------------------------------------------------------------------ */
 

@@ -673,6 +673,136 @@ def pin_rank1_zero_state(L):
     assert list(h.idx[:4]) == [-1] * 4 and not np.any(h.vec) and not np.any(h.Q)
 
 
+def _mgs64(Y):
+    """Modified Gram-Schmidt in float64 over the rows of Y (slot order)."""
+    A = np.array(Y, np.float64)
+    for j in range(A.shape[0]):
+        for i in range(j):
+            A[j] -= (A[i] @ A[j]) * A[i]
+        A[j] /= np.linalg.norm(A[j])
+    return A
+
+
+def pin_block_start_rows(L):
+    """Block fit, cold start with no sweep: the slots start from the unit
+    vectors of the rows in decreasing canonical energy, so the pairs are
+    exactly those rows (a = e_r, b = R[r, :]), deflation zeroes exactly
+    those rows and leaves the rest bitwise unchanged, and rows of zero
+    energy are never a start."""
+    rng = np.random.default_rng(61)
+    R = rng.normal(0, 1, (D, D)).astype(np.float32)
+    R[[5, 90, 17]] *= np.float32(8.0)
+    R[[33, 34]] = 0.0
+    Rd, idx, ab = oracle.fit_block(R, C=4, sweeps=0, L=L)
+    energy = (R.astype(np.float64) ** 2).sum(1)
+    order = list(np.argsort(-energy, kind="stable")[:4])
+    assert list(idx[:4]) == [0, 1, 2, 3]
+    for j, r in enumerate(order):
+        e = np.zeros(D, np.float32)
+        e[r] = 1.0
+        assert np.array_equal(ab[j, :D], e) and np.array_equal(ab[j, D:], R[r]), j
+    keep = np.ones(D, bool)
+    keep[order] = False
+    assert not np.any(Rd[order]) and np.array_equal(Rd[keep], R[keep])
+    # a state with two nonzero rows: the other two slots stay unused
+    Z = np.zeros((D, D), np.float32)
+    Z[3], Z[70] = rng.normal(size=D), 2 * rng.normal(size=D)
+    _, idx2, ab2 = oracle.fit_block(Z, C=4, sweeps=0, L=L)
+    assert list(idx2[:4]) == [0, 1, -1, -1] and not np.any(ab2[2:])
+    assert ab2[0, 70] == 1.0 and ab2[1, 3] == 1.0
+
+
+def pin_block_fit_svd(L):
+    """With many sweeps the block fit converges to the leading singular
+    subspace: the pairs' sum equals the best rank-4 approximation (SVD,
+    Eckart-Young) to 1e-4 relative, a is orthonormal to 1e-5, and the
+    deflated matrix is the SVD tail."""
+    rng = np.random.default_rng(62)
+    U, _ = np.linalg.qr(rng.normal(size=(D, D)))
+    V, _ = np.linalg.qr(rng.normal(size=(D, D)))
+    s = np.concatenate([[40.0, 25.0, 15.0, 9.0], 1.0 / (1 + np.arange(D - 4))])
+    R = ((U * s) @ V.T).astype(np.float32)
+    Rd, idx, ab = oracle.fit_block(R, C=4, sweeps=60, L=L)
+    A, B = ab[:4, :D].astype(np.float64), ab[:4, D:].astype(np.float64)
+    assert list(idx[:4]) == [0, 1, 2, 3]
+    assert np.abs(A @ A.T - np.eye(4)).max() < 1e-5
+    u, sv, vt = np.linalg.svd(R.astype(np.float64))
+    best = (u[:, :4] * sv[:4]) @ vt[:4]
+    assert rel(A.T @ B, best) < 1e-4, rel(A.T @ B, best)
+    assert rel(Rd, R.astype(np.float64) - best) < 1e-3
+
+
+def pin_block_fit_steps(L):
+    """Two warm-started sweeps equal float64 subspace iteration with
+    modified Gram-Schmidt from the stored a's (z = R^T a, y = R z, then
+    orthonormalize), followed by b = R^T a, to 1e-5."""
+    rng = np.random.default_rng(63)
+    R = (rng.normal(size=(D, D)) + 4 * np.outer(rng.normal(size=D), rng.normal(size=D))).astype(np.float32)
+    start = _mgs64(rng.normal(size=(4, D))).astype(np.float32)
+    ab0 = np.zeros((4, 2 * D), np.float32)
+    ab0[:, :D] = start
+    _, idx, ab = oracle.fit_block(R, C=4, idx=[0, 1, 2, 3], ab=ab0, warm=True, sweeps=2, L=L)
+    R64 = R.astype(np.float64)
+    A = _mgs64(start)
+    for _ in range(2):
+        A = _mgs64((R64 @ (R64.T @ A.T)).T)
+    B = (R64.T @ A.T).T
+    assert rel(ab[:4, :D], A) < 1e-5 and rel(ab[:4, D:], B) < 1e-5, (rel(ab[:4, :D], A), rel(ab[:4, D:], B))
+    # a cold start from the same matrix differs (the start is the longest rows)
+    _, _, abc = oracle.fit_block(R, C=4, sweeps=2, L=L)
+    assert not np.array_equal(abc, ab)
+
+
+def pin_block_warm_fixed_point(L):
+    """A state that is exactly rank 4 in the span of the stored a's is
+    captured by one warm sweep: the fitted a's span the stored ones (their
+    4 x 4 matrix of cosines is orthogonal) and the deflated state is zero to
+    1e-5 of its scale."""
+    rng = np.random.default_rng(64)
+    A0 = _mgs64(rng.normal(size=(4, D)))
+    Vb = rng.normal(size=(4, D)) * np.array([[30.0], [12.0], [5.0], [2.0]])
+    R = (A0.T @ Vb).astype(np.float32)
+    ab0 = np.zeros((4, 2 * D), np.float32)
+    ab0[:, :D] = A0.astype(np.float32)
+    Rd, idx, ab = oracle.fit_block(R, C=4, idx=[0, 1, 2, 3], ab=ab0, warm=True, sweeps=1, L=L)
+    P = ab[:4, :D].astype(np.float64) @ A0.T  # cosines between fitted and stored bases
+    assert np.abs(P @ P.T - np.eye(4)).max() < 1e-5
+    assert np.abs(Rd).max() < 1e-5 * np.abs(R).max()
+
+
+def pin_block_zero_state(L):
+    """An all-zero state: no start row, unused pairs, zero codes."""
+    h = oracle.quantize(np.zeros((D, D), np.float32), C=4, L=L, fit="block")
+    assert list(h.idx[:4]) == [-1] * 4 and not np.any(h.vec) and not np.any(h.Q)
+
+
+def pin_block_window_and_fold(L):
+    """With block pairs a window equals the float64 dense recurrence from
+    its boundary to 1e-5 (the read is the rank-one read); the fold equals
+    the block fit of the current state warm-started from the window's own
+    pairs, followed by smoothing and rounding; the buffer is then empty."""
+    S0, toks = tiny_inputs(seed=65, tokens=16, init="gauss")
+    h = oracle.Head(C=4, W=16, L=L, fit="block").init(S0[0])
+    assert list(h.idx[:4]) == [0, 1, 2, 3]
+    S = h.dequant(1).astype(np.float64)
+    for (q, k, v, a, b) in toks:
+        o, _ = h.append(q, k, v, a, b)
+        _, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            float(a), float(b))
+        assert rel(o, o64) < 1e-5
+    cur = h.dequant(2)
+    assert rel(cur, S) < 1e-5
+    Rd, idx, ab = oracle.fit_block(cur, C=4, idx=h.idx, ab=h.vec, warm=True, sweeps=2, L=L)
+    cold = oracle.quantize(cur, C=4, L=L, fit="block")
+    h.fold()
+    assert h.n == 0 and np.array_equal(h.vec, ab) and np.array_equal(h.idx, idx)
+    assert not np.array_equal(h.vec, cold.vec)
+    res = h.dequant(0).astype(np.float64)
+    step = np.outer(h.rho, h.sigma).astype(np.float64)
+    assert np.all(np.abs(res - Rd) <= 0.5 * step * (1 + 1e-5) + 1e-6 * np.abs(Rd).max())
+    assert np.array_equal(h.dequant(2), h.dequant(1))
+
+
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
@@ -681,4 +811,6 @@ ALL = [
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
     pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step, pin_bf16_records,
     pin_rank1_fit, pin_rank1_window_and_fold, pin_rank1_zero_state,
+    pin_block_start_rows, pin_block_fit_svd, pin_block_fit_steps, pin_block_warm_fixed_point,
+    pin_block_zero_state, pin_block_window_and_fold,
 ]

@@ -65,10 +65,20 @@ MUTANTS = [
     ("r1_sweep_rows_for_columns", "                for (int r = 0; r < D; ++r) col[r] = R[r * D + c];\n                b[c] = lqo_t128_dot(col, a);",
      "                for (int r = 0; r < D; ++r) col[r] = R[c * D + r];\n                b[c] = lqo_t128_dot(col, a);"),
     ("r1_not_normalized", "for (int r = 0; r < D; ++r) a[r] = a[r] * inv;", ";"),
-    ("r1_no_deflation", "for (int c = 0; c < D; ++c) R[r * D + c] = fmaf(-a[r], b[c], R[r * D + c]);", ";"),
+    ("r1_no_deflation", "        }\n        for (int r = 0; r < D; ++r)\n            for (int c = 0; c < D; ++c) R[r * D + c] = fmaf(-a[r], b[c], R[r * D + c]);",
+     "        }\n"),
     ("r1_read_with_b", "float d = lqo_t128_dot(a, x);", "float d = lqo_t128_dot(b, x);"),
     ("r1_rebuild_unscaled", "float w = g * a[r];", "float w = a[r];"),
     ("r1_start_last_max", "if (e > best) { best = e; pick = r; }", "if (e >= best) { best = e; pick = r; }"),
+    ("blk_no_projection", "for (int r = 0; r < D; ++r) A[j][r] = fmaf(-d, A[i][r], A[j][r]);", "(void)d;"),
+    ("blk_not_normalized", "for (int r = 0; r < D; ++r) A[j][r] = A[j][r] * inv;", "(void)inv;"),
+    ("blk_fold_cold", "lqo_quantize_block(R, C, smoothing, sigma_floor, 1, Q,", "lqo_quantize_block(R, C, smoothing, sigma_floor, 0, Q,"),
+    ("blk_sweep_transposed", "for (int r = 0; r < D; ++r) A[j][r] = lqo_t128_dot(R + r * D, Z);", "cols_dot(R, Z, A[j]);"),
+    ("blk_no_deflation", "*b = a + D;\n        for (int r = 0; r < D; ++r)\n            for (int c = 0; c < D; ++c) R[r * D + c] = fmaf(-a[r], b[c], R[r * D + c]);",
+     "*b = a + D;\n        (void)a; (void)b;"),
+    ("blk_start_last_max", "if (!used[r] && e[r] > best)", "if (!used[r] && e[r] >= best)"),
+    ("blk_start_reused_row", "            used[pick] = 1;\n", ""),
+    ("blk_unused_marked_live", "idx[j] = live[j] ? j : -1;", "idx[j] = j;"),
     ("kda_step_column_decay", "S[r * D + c] = alpha[r] * S[r * D + c];", "S[r * D + c] = alpha[c] * S[r * D + c];"),
 ]
 
