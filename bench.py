@@ -46,6 +46,8 @@ def parse():
                    help="skip the measurement of the lossy bf16 record-corrections option")
     p.add_argument("--no-rank1", action="store_true",
                    help="skip the measurement of the rank-one compensator option")
+    p.add_argument("--no-block", action="store_true",
+                   help="skip the measurement of the block compensator fit option")
     p.add_argument("--baseline-tokens", type=int, default=16)
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--separate", action="store_true",
@@ -331,6 +333,16 @@ def main():
             f"{rank1['tokens_per_s']:,.0f} tokens/s ({rank1['ratio_to_plain']:.3f} of the plain path); "
             f"append {rank1['append_us']:.1f} us, last append + fold {rank1['append_fold_us']:.1f} us")
 
+    block = None
+    if not args.no_block:
+        block = time_option(lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype,
+                                           comp_fit="block"), rank1=True)
+        block["note"] = ("compensator pairs fitted as a block, warm-started from the window's own pairs "
+                         "(see quality.py --comp-fit block)")
+        log(f"[bench] block compensator fit: {block['ms_per_step']:.3f} ms per window, "
+            f"{block['tokens_per_s']:,.0f} tokens/s ({block['ratio_to_plain']:.3f} of the plain path); "
+            f"append {block['append_us']:.1f} us, last append + fold {block['append_fold_us']:.1f} us")
+
     # ---- per-channel decay (KDA): the same shape and schedule with alpha a
     # 128-vector per head and token, and the dense KDA baselines
     kda = None
@@ -496,6 +508,7 @@ def main():
         "kda": kda,
         "bf16_record_corrections": bf16rec,
         "rank1_compensators": rank1,
+        "block_compensators": block,
         "baselines": baselines,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),

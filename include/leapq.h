@@ -66,12 +66,17 @@ extern "C" {
 #define LEAPQ_DECAY_CHANNEL 1
 
 /* compensator fit at init and fold: greedy extraction of whole rows or
- * columns, or rank-one pairs (a_j, b_j) by power sweeps from the longest row
+ * columns; rank-one pairs (a_j, b_j) by power sweeps from the longest row
  * ("Recurrent-state quantization for linear attention: a first GPU kernel",
  * Where the time goes: four compensators, eight sweeps each; "LeapQuant"
- * 3.3: compensators as rank-one updates) */
+ * 3.3: compensators as rank-one updates); or the same pairs fitted together
+ * as a block, warm-started from the window's own pairs (the same page,
+ * Redesign): subspace iteration with modified Gram-Schmidt, 2 sweeps per
+ * fold and 8 at init, where the start is the unit vectors of the rows of
+ * largest energy */
 #define LEAPQ_COMP_LINES 0
 #define LEAPQ_COMP_RANK1 1
+#define LEAPQ_COMP_BLOCK 2
 
 /* what leapq_dequant writes */
 #define LEAPQ_DEQ_RESIDUAL 0 /* (code * rho_r) * sigma_c, compensator lines left at zero */
@@ -94,9 +99,10 @@ typedef struct leapq_config {
                             bf16, rounded to nearest even on store (a lossy lower-precision option; the
                             token that makes a record reads out with its fp32 u); LEAPQ_BF16 requires
                             scalar decay and qk_norm = 0 and is not taken by the gated entry points */
-    int32_t comp_fit;    /* LEAPQ_COMP_LINES (whole rows or columns) or LEAPQ_COMP_RANK1 (rank-one pairs
-                            fitted by power sweeps; requires n_comp <= 4, scalar decay, rec_dtype
-                            LEAPQ_F32, and is not taken by the gated entry points) */
+    int32_t comp_fit;    /* LEAPQ_COMP_LINES (whole rows or columns), LEAPQ_COMP_RANK1 (rank-one pairs
+                            fitted by power sweeps) or LEAPQ_COMP_BLOCK (the pairs fitted as a block);
+                            the pair fits require n_comp <= 4, scalar decay, rec_dtype LEAPQ_F32, and
+                            are not taken by the gated entry points */
     int32_t reserved[3]; /* must be zero */
 } leapq_config;
 
@@ -113,9 +119,11 @@ typedef struct leapq_config {
  *   comp_idx  int32 [heads][C]         -1 unused, 0..127 row r, 128+c column c
  *   comp_vec  fp32  [heads][C][128]    the line's values (over c for a row,
  *                                      over r for a column), natural order;
- *                   [heads][C][2][128] with LEAPQ_COMP_RANK1: a_j (unit
- *                                      norm, over rows) then b_j (over
- *                                      columns); comp_idx holds the start row
+ *                   [heads][C][2][128] with LEAPQ_COMP_RANK1 or _BLOCK:
+ *                                      a_j (unit norm, over rows) then b_j
+ *                                      (over columns); comp_idx holds the
+ *                                      start row (rank-one) or j (block),
+ *                                      -1 for an unused pair
  *   rec_gamma fp32  [heads][W]         cumulative decay since the window start
  *                   ([heads][W][128] per key row with LEAPQ_DECAY_CHANNEL)
  *   rec_k     e     [heads][W][128]    record keys in key-row order, in the

@@ -42,8 +42,9 @@ int32_t check_method_config(const leapq_config *c)
     if (c->decay == LEAPQ_DECAY_CHANNEL && c->qk_norm) return LEAPQ_ERR_RANGE;
     if (c->rec_dtype != LEAPQ_F32 && c->rec_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
     if (c->rec_dtype == LEAPQ_BF16 && (c->decay != LEAPQ_DECAY_SCALAR || c->qk_norm)) return LEAPQ_ERR_RANGE;
-    if (c->comp_fit != LEAPQ_COMP_LINES && c->comp_fit != LEAPQ_COMP_RANK1) return LEAPQ_ERR_RANGE;
-    if (c->comp_fit == LEAPQ_COMP_RANK1 &&
+    if (c->comp_fit != LEAPQ_COMP_LINES && c->comp_fit != LEAPQ_COMP_RANK1 && c->comp_fit != LEAPQ_COMP_BLOCK)
+        return LEAPQ_ERR_RANGE;
+    if (c->comp_fit != LEAPQ_COMP_LINES &&
         (c->n_comp > 4 || c->decay != LEAPQ_DECAY_SCALAR || c->rec_dtype != LEAPQ_F32))
         return LEAPQ_ERR_RANGE;
     if (c->reserved[0] || c->reserved[1] || c->reserved[2]) return LEAPQ_ERR_RANGE;
@@ -61,7 +62,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     const uint64_t kb = key_bf16(c) ? 2 : 4;  // record key element
     const uint64_t gw = c->decay == LEAPQ_DECAY_CHANNEL ? kD : 1;  // record decay values
     const uint64_t ub = c->rec_dtype == LEAPQ_BF16 ? 2 : 4;        // record correction element
-    const uint64_t cw = c->comp_fit == LEAPQ_COMP_RANK1 ? 2 : 1;   // compensator vectors
+    const uint64_t cw = c->comp_fit != LEAPQ_COMP_LINES ? 2 : 1;   // compensator vectors (pairs: a, b)
     uint64_t off = 0;
     L->off_codes = off;
     off = round_up(off + H * kD * kD);
@@ -108,7 +109,8 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->key_bf16 = key_bf16(&layer->cfg);
     sv->kda = layer->cfg.decay == LEAPQ_DECAY_CHANNEL;
     sv->u_bf16 = layer->cfg.rec_dtype == LEAPQ_BF16;
-    sv->r1 = layer->cfg.comp_fit == LEAPQ_COMP_RANK1;
+    sv->r1 = layer->cfg.comp_fit != LEAPQ_COMP_LINES;
+    sv->blk = layer->cfg.comp_fit == LEAPQ_COMP_BLOCK;
     return LEAPQ_OK;
 }
 

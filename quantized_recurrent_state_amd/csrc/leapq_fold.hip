@@ -59,7 +59,21 @@ struct FoldWork {
     float part[4 * 128];     // cross-wave row maxima
     float rowg[4][128];      // per wave: 127 / M_r per row (0 for zero rows)
     float sinv[128];         // 1 / sigma_c
+    float spare[128];        // pads the area to the block fit's arrays
 };
+// The block fit's arrays, laid over FoldWork (the fit ends before the
+// smoothing uses it).  z holds a slot's column dots in the thread-contiguous
+// order zpos(c): thread (w, h) reads its 16 columns w + 4h + 8m as four
+// 16-byte loads.
+struct BlockWork {
+    float P[4][128][4];  // per slot and row: the four waves' row-dot partials
+    float z[4][128];     // per slot: column dots (z, finally b)
+};
+static_assert(sizeof(BlockWork) <= sizeof(FoldWork), "block fit arrays exceed the fold's work area");
+__device__ __forceinline__ int zpos(int c) { return (2 * (c & 3) + ((c >> 2) & 1)) * 16 + (c >> 3); }
+
+constexpr int kBlockSweeps = 2;      // per fold, warm-started
+constexpr int kBlockSweepsInit = 8;  // at init, from the longest rows
 
 // Copies boundary fields (lines, rho, sigma, indices) and the decays to LDS:
 // the n record decays, or with CH the last record's decay vector.
@@ -422,13 +436,197 @@ __device__ __forceinline__ void fit_rank1(const MMap &a, float (&S)[4][16], cons
     }
 }
 
+// Canonical 128-term dot of two vectors held in the row layout (rows
+// i + 32p of the thread, p = 0..3, the same in both lane halves and in every
+// wave): levels 0 (p, p + 2) and 32 (p = 0, 1) inside the thread, then
+// levels 16, 8, 4, 2, 1 as butterflies on lane bit 4 (permlane16 swap), lane
+// bit 3 (row_ror:8), lane ^ 7 (row_half_mirror: row ^ 4 through the xor in
+// i), lane bits 1 and 0.  Every lane ends with the value.
+__device__ __forceinline__ float rdot(const float (&x)[4], const float (&y)[4])
+{
+    float s = fma_(x[0], y[0], x[2] * y[2]) + fma_(x[1], y[1], x[3] * y[3]);
+    s = xhalf16(s, s);
+    s = s + dpp<DPP_ROR8>(s);
+    s = s + dpp<DPP_HMIR>(s);
+    s = s + dpp<DPP_XOR2>(s);
+    return s + dpp<DPP_XOR1>(s);
+}
+
+// Block fit of the compensators (the block fold option): subspace iteration
+// on the key side, fitting the pairs together.  Start: with WARM, a slot
+// whose stored index is live starts from its stored a (prev, staged in LDS);
+// every other slot, in slot order, from the unit vector of the next row by
+// canonical energy (largest first, lowest index on ties, zero-energy rows
+// never), else from zero.  Then A = MGS(start); per sweep z_j = S^T a_j
+// (canonical column dots), y_j = S z_j (canonical row dots), A = MGS(Y);
+// finally b_j = S^T a_j, index j (or -1 for an unused slot), and S deflated
+// by fma(-a_j[r], b_j[c], S) in slot order.  MGS projects each earlier live
+// slot out with fma(-T(a_i . y), a_i, y), then scales by 1 / sqrt(T(y . y))
+// or leaves the slot unused (zero) when that norm is not positive.  A lives
+// in the row layout (4 values per slot and thread), so its dots are rdot;
+// two barriers per sweep.
+template <int CT, bool WARM>
+__device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], const HeadState &hs, int C,
+                                          const float *prev, const int *prev_idx, int sweeps, FoldWork &fw)
+{
+    constexpr int NR = CT >= 0 ? CT : 4;
+    const int nslot = CT >= 0 ? CT : C;
+    BlockWork &bw = *reinterpret_cast<BlockWork *>(&fw);
+    const int t = threadIdx.x, l = a.l;
+    const int zb = (2 * a.w + a.h) * 16;
+    float A[NR][4];
+    bool live[NR];
+    bool warm[NR];
+    bool any_cold = false;
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        warm[j] = WARM && j < nslot && prev_idx[j] >= 0;
+        any_cold = any_cold || (j < nslot && !warm[j]);
+    }
+    // ---- start vectors
+    float e0 = -1.0f, e1 = -1.0f;
+    if (any_cold) {
+        float rp[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
+        put_row_energies(a, rp, fw.rowP[0]);
+        lds_barrier();
+        const float *rowP = fw.rowP[0];
+        e0 = (rowP[l] + rowP[2 * D + l]) + (rowP[D + l] + rowP[3 * D + l]);
+        e1 = (rowP[l + 64] + rowP[2 * D + l + 64]) + (rowP[D + l + 64] + rowP[3 * D + l + 64]);
+    }
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        if (j >= nslot) break;
+        if (warm[j]) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) A[j][p] = prev[2 * j * D + a.row(p)];
+        } else {
+            const float M = wave_max(fmaxf(e0, e1));
+            int pick = -1;
+            if (M > 0.0f) {
+                const int cand = e0 == M ? l : e1 == M ? 64 + l : 1 << 20;
+                pick = __builtin_amdgcn_readfirstlane(wave_min(cand));
+                e0 = pick == l ? -1.0f : e0;
+                e1 = pick == l + 64 ? -1.0f : e1;
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p) A[j][p] = a.row(p) == pick ? 1.0f : 0.0f;
+        }
+    }
+    auto mgs = [&]() {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            if (j >= nslot) break;
+#pragma unroll
+            for (int i = 0; i < j; ++i) {
+                const float d = rdot(A[i], A[j]);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) A[j][p] = live[i] ? fma_(-d, A[i][p], A[j][p]) : A[j][p];
+            }
+            const float n2 = rdot(A[j], A[j]);
+            live[j] = n2 > 0.0f;
+            const float inv = 1.0f / sqrtf(live[j] ? n2 : 1.0f);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) A[j][p] = live[j] ? A[j][p] * inv : 0.0f;
+        }
+    };
+    mgs();
+    for (int s = 0;; ++s) {
+        // z_j = S^T a_j over the wave's own columns
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            if (j >= nslot) break;
+            float cp[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                cp[m] = fma_(TS(S, 0, m), A[j][0], TS(S, 2, m) * A[j][2]) +
+                        fma_(TS(S, 1, m), A[j][1], TS(S, 3, m) * A[j][3]);
+            const float z = mcolsum16(cp, l);
+            if ((l & 1) == 0) bw.z[j][zb + mcol_of(l)] = z;
+        }
+        lds_barrier();
+        if (s == sweeps) break;
+        // y_j = S z_j: rows inside the thread, lane bit 5, then across waves
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            if (j >= nslot) break;
+            float zc[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4 *>(&bw.z[j][zb + 4 * q]);
+                zc[4 * q] = v.x;
+                zc[4 * q + 1] = v.y;
+                zc[4 * q + 2] = v.z;
+                zc[4 * q + 3] = v.w;
+            }
+            float rd[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                float x[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = fma_(TS(S, p, m), zc[m], TS(S, p, m + 8) * zc[m + 8]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[m] = x[m] + x[m + 4];
+                x[0] = x[0] + x[2];
+                x[1] = x[1] + x[3];
+                rd[p] = x[0] + x[1];
+            }
+            const int r = a.i + 64 * a.h;
+            bw.P[j][r][a.w] = xhalf32(rd[0], rd[2]);
+            bw.P[j][r + 32][a.w] = xhalf32(rd[1], rd[3]);
+        }
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            if (j >= nslot) break;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float4 v = *reinterpret_cast<const float4 *>(&bw.P[j][a.row(p)][0]);
+                A[j][p] = (v.x + v.z) + (v.y + v.w);
+            }
+        }
+        mgs();
+    }
+    // store the pairs, then deflate
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        if (j >= nslot) break;
+        float *aout = hs.cvec + j * 2 * D, *bout = aout + D;
+        if (t == 0) hs.cidx[j] = live[j] ? j : -1;
+        if (a.w == 0 && a.h == 0) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) aout[a.row(p)] = A[j][p];
+        } else if (a.w == 1) {
+            bout[l] = bw.z[j][zpos(l)];
+            bout[l + 64] = bw.z[j][zpos(l + 64)];
+        }
+        float bc[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(&bw.z[j][zb + 4 * q]);
+            bc[4 * q] = v.x;
+            bc[4 * q + 1] = v.y;
+            bc[4 * q + 2] = v.z;
+            bc[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) TS(S, p, m) = fma_(-A[j][p], bc[m], TS(S, p, m));
+    }
+}
+
 // Steps after the rebuild, shared by init and fold.  Writes the head's new
 // boundary state (codes, rho, sigma, indices, compensators).  CT >= 0: the
 // number of compensators as a compile-time constant (C == CT), unrolling the
-// rounds.  R1: rank-one compensators by power sweeps in place of lines.
-template <int CT, bool R1 = false>
+// rounds.  R1: compensator pairs in place of lines, fitted by power sweeps,
+// or with BLK by the block fit (WARM: from the pairs staged in prev and
+// prev_idx, the window's own).
+template <int CT, bool R1 = false, bool BLK = false, bool WARM = false>
 __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16], const HeadState &hs, int C, int smoothing,
-                                               float floor_, FoldWork &sm)
+                                               float floor_, FoldWork &sm, const float *prev = nullptr,
+                                               const int *prev_idx = nullptr)
 {
     const int t = threadIdx.x, l = a.l;
     // ---- compensator tokens.  Lines: one greedy round per compensator (pick,
@@ -437,7 +635,10 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
     // rescored axis is written to the other of its two buffers, which no wave
     // reads until that barrier.  The rounds are unrolled (C <= 8) and written
     // out here, not called, so S stays in registers.
-    if (R1 && C > 0) {
+    if (BLK && C > 0) {
+        fit_block<CT, WARM>(a, S, hs, C, prev, prev_idx, WARM ? kBlockSweeps : kBlockSweepsInit, sm);
+        lds_barrier();
+    } else if (R1 && C > 0) {
         fit_rank1<CT>(a, S, hs, C, sm);
         lds_barrier();
     } else if (C > 0) {
@@ -590,7 +791,7 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
     }
 }
 
-template <int CT, bool R1>
+template <int CT, bool R1, bool BLK = false>
 __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restrict__ S0, int smoothing,
                                               float floor_)
 {
@@ -604,10 +805,10 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int m = 0; m < 16; ++m) TS(S, p, m) = src[a.row(p) * D + a.col(m)];
-    quantize_state<CT, R1>(a, S, hs, sv.C, smoothing, floor_, wk);
+    quantize_state<CT, R1, BLK>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename K, int CT, bool CH, typename U, bool R1>
+template <typename K, int CT, bool CH, typename U, bool R1, bool BLK = false>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
     __shared__ FoldStage<Rec<K, CH, U>::stride> st;
@@ -625,7 +826,7 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n, true, st, S, st.gW);
     // no barrier: the quantization writes only LDS arrays the rebuild does
     // not read, and each thread rewrites only the codes it loaded
-    quantize_state<CT, R1>(a, S, hs, sv.C, smoothing, floor_, wk);
+    quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
 // The last token of a full window and the fold, in one launch (W <= 16).
@@ -635,7 +836,7 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
 // empties the buffer), and the fold rebuilds from the same registers and LDS
 // instead of reading the boundary and the records again.  The results are
 // those of leapq_append followed by leapq_fold.
-template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CT>
+template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CT, bool BLK = false>
 __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
                                                      const T *__restrict__ kin, const T *__restrict__ vin,
                                                      const float *__restrict__ alpha,
@@ -668,7 +869,7 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     const HeadState hs = head_state(sv, h);
     float S[4][16];
     rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
-    quantize_state<CT, R1>(a, S, hs, sv.C, smoothing, floor_, wk);
+    quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
 template <typename K, bool CH, typename U, bool R1>
@@ -699,7 +900,12 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
 hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
                        hipStream_t s)
 {
-    if (sv.r1) {
+    if (sv.blk) {
+        if (sv.C == 4)
+            hipLaunchKernelGGL((k_init<4, true, true>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+        else
+            hipLaunchKernelGGL((k_init<-1, true, true>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    } else if (sv.r1) {
         if (sv.C == 4)
             hipLaunchKernelGGL((k_init<4, true>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
         else
@@ -712,18 +918,23 @@ hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoo
     return hipGetLastError();
 }
 
-template <typename K, bool CH, typename U = float, bool R1 = false>
+template <typename K, bool CH, typename U = float, bool R1 = false, bool BLK = false>
 static void launch_fold_t(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_fold<K, 4, CH, U, R1>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, 4, CH, U, R1, BLK>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
     else
-        hipLaunchKernelGGL((k_fold<K, -1, CH, U, R1>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, -1, CH, U, R1, BLK>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
 }
 
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
-    if (sv.r1) {
+    if (sv.blk) {
+        if (sv.key_bf16)
+            launch_fold_t<uint16_t, false, float, true, true>(sv, heads, n, smoothing, floor_, s);
+        else
+            launch_fold_t<float, false, float, true, true>(sv, heads, n, smoothing, floor_, s);
+    } else if (sv.r1) {
         if (sv.key_bf16)
             launch_fold_t<uint16_t, false, float, true>(sv, heads, n, smoothing, floor_, s);
         else
@@ -746,17 +957,18 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
     return hipGetLastError();
 }
 
-template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false>
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false,
+          bool BLK = false>
 static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, float *o, int smoothing, float floor_,
                                  const GateArgs &g, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, 4>), dim3(heads), dim3(NT), 0, s, sv, n,
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, 4, BLK>), dim3(heads), dim3(NT), 0, s, sv, n,
                            (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
     else
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, -1>), dim3(heads), dim3(NT), 0, s, sv, n,
-                           (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, -1, BLK>), dim3(heads), dim3(NT), 0, s, sv,
+                           n, (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
 }
 
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
@@ -766,7 +978,14 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
     // the (inputs, keys, gated, normalize) combinations of launch_append
     const bool kb = sv.key_bf16;
 #define LQ_AF(T, K, G, N) launch_append_fold_t<T, K, G, N>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
-    if (sv.r1) {
+    if (sv.blk) {
+        if (!bf16)
+            launch_append_fold_t<float, float, false, false, false, float, true, true>(sv, heads, n, q, k, v, alpha,
+                                                                                     beta, o, smoothing, floor_, g, s);
+        else
+            launch_append_fold_t<uint16_t, uint16_t, false, false, false, float, true, true>(
+                sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s);
+    } else if (sv.r1) {
         if (!bf16)
             launch_append_fold_t<float, float, false, false, false, float, true>(sv, heads, n, q, k, v, alpha, beta, o,
                                                                                smoothing, floor_, g, s);

@@ -22,7 +22,8 @@ struct StateView {
     int key_bf16;  // record keys (and inputs) are bf16
     int kda;       // per-channel decay: alpha [heads][128], record decays [W][128]
     int u_bf16;    // record corrections stored in bf16
-    int r1;        // rank-one compensator pairs [C][2][128] in place of lines
+    int r1;        // compensator pairs [C][2][128] (a, b) in place of lines
+    int blk;       // the pairs are fitted as a block (with r1)
 };
 
 // Gate arithmetic in front of the append (mode 0: alpha and beta are given;

@@ -31,6 +31,7 @@ LEAPQ_DECAY_CHANNEL = 1
 
 LEAPQ_COMP_LINES = 0
 LEAPQ_COMP_RANK1 = 1
+LEAPQ_COMP_BLOCK = 2
 
 LEAPQ_DEQ_RESIDUAL = 0
 LEAPQ_DEQ_BOUNDARY = 1
@@ -123,7 +124,8 @@ def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1
     c.qk_norm = int(bool(qk_norm))
     c.decay = LEAPQ_DECAY_CHANNEL if decay in ("channel", LEAPQ_DECAY_CHANNEL) else LEAPQ_DECAY_SCALAR
     c.rec_dtype = LEAPQ_BF16 if rec_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
-    c.comp_fit = LEAPQ_COMP_RANK1 if comp_fit in ("rank1", LEAPQ_COMP_RANK1) else LEAPQ_COMP_LINES
+    fits = {"lines": LEAPQ_COMP_LINES, "rank1": LEAPQ_COMP_RANK1, "block": LEAPQ_COMP_BLOCK}
+    c.comp_fit = fits.get(comp_fit, comp_fit)
     return c
 
 
@@ -253,7 +255,7 @@ class Layer:
     def comp_vec(self):
         """Compensators [heads, C, 128] (lines) or [heads, C, 256] (rank-one pairs [a | b])."""
         C = max(self.cfg.n_comp, 0)
-        w = 2 * D if self.cfg.comp_fit == LEAPQ_COMP_RANK1 else D
+        w = 2 * D if self.cfg.comp_fit != LEAPQ_COMP_LINES else D
         return self._sec(self.layout.off_comp_vec, self.heads * C * w, torch.float32, (self.heads, C, w))
 
     def rec_gamma(self):

@@ -19,7 +19,7 @@ the GPU output and whether a fold followed; the parity tests use it to run
 CPU reference heads beside the GPU path.
 
   python -m quantized_recurrent_state_amd.quality [--workload long] [--layers 3]
-         [--tokens 4095] [--rec-dtype f32|bf16] [--comp-fit lines|rank1]
+         [--tokens 4095] [--rec-dtype f32|bf16] [--comp-fit lines|rank1|block]
          [--out result.json]
 """
 import argparse
@@ -115,8 +115,9 @@ def main(argv=None):
     p.add_argument("--tokens", type=int, default=None)
     p.add_argument("--rec-dtype", default="f32", choices=("f32", "bf16"),
                    help="storage of the record corrections (bf16: the lossy lower-precision option)")
-    p.add_argument("--comp-fit", default="lines", choices=("lines", "rank1"),
-                   help="compensator fit: whole rows/columns, or rank-one pairs from power sweeps")
+    p.add_argument("--comp-fit", default="lines", choices=("lines", "rank1", "block"),
+                   help="compensator fit: whole rows/columns, rank-one pairs from power sweeps, or pairs "
+                        "fitted as a block warm-started from the previous window")
     p.add_argument("--out", default=None)
     a = p.parse_args(argv)
     res = run(a.workload, a.layers, a.tokens, log=lambda m: print(m, file=sys.stderr, flush=True),

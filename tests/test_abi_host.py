@@ -332,7 +332,7 @@ def test_rank1_layout_and_checks():
     assert r1.record_bytes_per_head == lines.record_bytes_per_head
     out = lq.leapq_layout()
     c = cfg()
-    c.comp_fit = 2
+    c.comp_fit = -1
     assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE
     for kw in (dict(n_comp=5), dict(decay="channel"), dict(rec_dtype="bf16")):
         c = cfg(comp_fit="rank1", **kw)
@@ -342,3 +342,19 @@ def test_rank1_layout_and_checks():
         assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_OK, C
     # the gated entry points keep line compensators
     assert call_gated(fake_layer(cfg(comp_fit="rank1")), gate_struct()) == lq.LEAPQ_ERR_RANGE
+
+
+def test_block_fit_layout_and_checks():
+    r1 = layout(batch=2, heads=4, window=16, n_comp=4, comp_fit="rank1")
+    blk = layout(batch=2, heads=4, window=16, n_comp=4, comp_fit="block")
+    # the block fit stores the same pairs as the rank-one fit
+    for f in ("total_bytes", "off_comp_vec", "off_rec_gamma", "boundary_bytes_per_head"):
+        assert getattr(blk, f) == getattr(r1, f), f
+    out = lq.leapq_layout()
+    c = cfg()
+    c.comp_fit = 3
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE
+    for kw in (dict(n_comp=5), dict(decay="channel"), dict(rec_dtype="bf16")):
+        c = cfg(comp_fit="block", **kw)
+        assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
+    assert call_gated(fake_layer(cfg(comp_fit="block")), gate_struct()) == lq.LEAPQ_ERR_RANGE

@@ -1,0 +1,93 @@
+"""GPU parity of the block compensator fit (comp_fit = block) through the C
+ABI.
+
+The C pairs (a, b) are fitted together by subspace iteration with modified
+Gram-Schmidt: 8 sweeps from the longest rows at init, 2 per fold starting from
+the window's own pairs.  The pairs are stored and read as with the rank-one
+fit.  Runs are free-running against the oracle's fit="block" heads with the bar
+of tests/gpu_harness.py, bitwise on every fp32 value.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_recurrent_state_amd import leapq as lq
+from quantized_recurrent_state_amd import workloads
+from tests.gpu_harness import D, progress, run_layer
+
+pytestmark = pytest.mark.gpu
+
+WL = workloads.WORKLOADS
+
+
+def _wl(base, **kw):
+    return dataclasses.replace(WL[base], **kw)
+
+
+def _finish(rep):
+    progress(f"    summary: {rep.summary()}")
+    rep.check()
+    assert sum(rep.nonbit.values()) == 0, rep.nonbit
+
+
+@pytest.mark.parametrize("name,wl,tokens,fused,fold_at", [
+    ("f32", _wl("tiny", seed=100), 64, False, None),
+    ("bf16_fused", _wl("tiny", in_dtype="bf16", seed=101), 48, True, None),
+    ("W20_two_launches", _wl("tiny", window=20, seed=102), 40, True, None),
+    ("W1", _wl("tiny", window=1, seed=103), 6, False, None),
+    ("C1_nosmooth", _wl("tiny", n_comp=1, smoothing=False, seed=104), 20, True, None),
+    ("C0", _wl("tiny", n_comp=0, seed=105), 20, True, None),
+    ("partial_window", _wl("tiny", seed=106), 23, False, {5, 6, 17}),
+    ("ragged_heads_writes", _wl("tiny", batch=3, heads=5, init="writes", seed=107), 18, True, None),
+    ("hard", _wl("tiny", init="hard", batch=1, heads=32, seed=4), 33, True, None),
+])
+def test_block_against_oracle(name, wl, tokens, fused, fold_at):
+    progress(f"  case {name}: {wl}")
+    rep, L, _ = run_layer(wl, tokens=tokens, fused=fused, fold_at=fold_at, fit="block")
+    if wl.n_comp:
+        assert tuple(L.comp_vec().shape) == (wl.batch * wl.heads, wl.n_comp, 2 * D)
+    _finish(rep)
+
+
+def test_block_dequant_views():
+    wl = _wl("tiny", seed=108, init="writes")
+    H = wl.batch * wl.heads
+    rep, L, refs = run_layer(wl, tokens=23, fit="block")
+    out = torch.empty(H, D, D, device="cuda")
+    for what, name in ((lq.LEAPQ_DEQ_RESIDUAL, "dequant0"), (lq.LEAPQ_DEQ_BOUNDARY, "dequant1"),
+                       (lq.LEAPQ_DEQ_CURRENT, "dequant2")):
+        lq.leapq_dequant(L, what, out)
+        got = out.cpu().numpy()
+        for h in range(H):
+            rep.fp(name, got[h], refs[h].dequant(what))
+    _finish(rep)
+
+
+def test_block_zero_state_and_empty_fold():
+    """A zero state has no row with energy: every pair is unused (index -1,
+    zero a; b is the column dots of zero), and the codes are all zero."""
+    H = 4
+    cfg = lq.make_config(1, H, comp_fit="block")
+    L = lq.Layer(cfg)
+    lq.leapq_init_state(L, torch.zeros(H, D, D, device="cuda"))
+    lq.leapq_fold(L)
+    torch.cuda.synchronize()
+    ref = oracle.Head(fit="block").init(np.zeros((D, D), np.float32)).fold()
+    assert list(ref.idx) == [-1] * 4 and not np.any(ref.vec)
+    for h in range(H):
+        assert np.array_equal(L.codes()[h].cpu().numpy(), ref.Q)
+        assert np.array_equal(L.rho()[h].cpu().numpy(), ref.rho)
+        assert np.array_equal(L.sigma()[h].cpu().numpy(), ref.sigma)
+        assert list(L.comp_idx()[h].cpu().numpy()) == [-1] * 4
+        assert np.array_equal(L.comp_vec()[h].cpu().numpy().view(np.uint32), ref.vec.view(np.uint32))
+
+
+def test_block_full_size_b512_sampled():
+    wl = WL["b512"]
+    sample = list(range(7, 16384, 256))
+    rep, _, _ = run_layer(wl, tokens=32, sample=sample, gen_device="cuda", check_every_token=False, fused=True,
+                          fit="block")
+    _finish(rep)
