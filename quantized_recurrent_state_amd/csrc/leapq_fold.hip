@@ -53,7 +53,7 @@ struct FoldStage {
     float gam[64];   // record decays (scalar decay)
     float gW[128];   // the last record's decay vector (per-channel decay)
 };
-struct FoldWork {
+struct alignas(16) FoldWork {
     float colE[2][128];      // column energies (two buffers, see extraction)
     float rowP[2][4 * 128];  // per-wave row-energy partials (two buffers)
     float part[4 * 128];     // cross-wave row maxima
@@ -65,7 +65,7 @@ struct FoldWork {
 // smoothing uses it).  z holds a slot's column dots in the thread-contiguous
 // order zpos(c): thread (w, h) reads its 16 columns w + 4h + 8m as four
 // 16-byte loads.
-struct BlockWork {
+struct alignas(16) BlockWork {
     float P[4][128][4];  // per slot and row: the four waves' row-dot partials
     float z[4][128];     // per slot: column dots (z, finally b)
 };
@@ -531,9 +531,8 @@ __device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], cons
             for (int p = 0; p < 4; ++p) A[j][p] = live[j] ? A[j][p] * inv : 0.0f;
         }
     };
-    mgs();
-    for (int s = 0;; ++s) {
-        // z_j = S^T a_j over the wave's own columns
+    // z_j = S^T a_j over the wave's own columns (canonical column dots)
+    auto col_dots = [&]() {
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
             if (j >= nslot) break;
@@ -544,9 +543,13 @@ __device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], cons
                         fma_(TS(S, 1, m), A[j][1], TS(S, 3, m) * A[j][3]);
             const float z = mcolsum16(cp, l);
             if ((l & 1) == 0) bw.z[j][zb + mcol_of(l)] = z;
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    mgs();
+    for (int s = 0; s < sweeps; ++s) {
+        col_dots();
         lds_barrier();
-        if (s == sweeps) break;
         // y_j = S z_j: rows inside the thread, lane bit 5, then across waves
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
@@ -575,6 +578,7 @@ __device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], cons
             const int r = a.i + 64 * a.h;
             bw.P[j][r][a.w] = xhalf32(rd[0], rd[2]);
             bw.P[j][r + 32][a.w] = xhalf32(rd[1], rd[3]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
 #pragma unroll
@@ -585,9 +589,12 @@ __device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], cons
                 const float4 v = *reinterpret_cast<const float4 *>(&bw.P[j][a.row(p)][0]);
                 A[j][p] = (v.x + v.z) + (v.y + v.w);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         mgs();
     }
+    col_dots();  // b_j = S^T a_j
+    lds_barrier();
     // store the pairs, then deflate
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
@@ -614,6 +621,7 @@ __device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], cons
         for (int p = 0; p < 4; ++p)
 #pragma unroll
             for (int m = 0; m < 16; ++m) TS(S, p, m) = fma_(-A[j][p], bc[m], TS(S, p, m));
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
