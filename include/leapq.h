@@ -234,6 +234,31 @@ int32_t leapq_append_gated(leapq_layer *layer, const leapq_gate *gate, const voi
 int32_t leapq_append_fold_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
                                 const void *v, const float *a, const float *b, float *o, void *stream);
 
+/* One decode token with a window phase per request (staggered phases:
+ * requests that joined at different times fold at different tokens; a
+ * window still holds W tokens of each request, "Recurrent-state quantization
+ * for linear attention: a first GPU kernel", Why rounding the state is
+ * difficult; What we built).  n_in [batch] int32 (device) holds each
+ * request's record count n: with n = window - 1 its heads append and fold in
+ * this launch (as leapq_append_fold), with 0 <= n < window - 1 they append
+ * (as leapq_append), and with any other n (negative: the request takes no
+ * token this step) its heads' state and output rows are left untouched.
+ * n_out [batch] int32 (device) or NULL receives each request's next count:
+ * 0 after a fold, n + 1 after an append, n otherwise; it must not overlap
+ * n_in (LEAPQ_ERR_RANGE).  gate NULL: alpha, beta are given as for
+ * leapq_append; otherwise a, b are the raw projections and the gate
+ * arithmetic of leapq_append_gated applies.  Requires window <= 16
+ * (LEAPQ_ERR_RANGE).  The token arguments, layout and per-head results are
+ * those of the entry points named above, bit for bit.  layer->n_records is
+ * neither read nor changed: a layer driven by leapq_step keeps its phases in
+ * the caller's array and must not be mixed with the single-phase calls
+ * (leapq_append, leapq_append_fold, leapq_fold, and leapq_dequant of the
+ * current state) unless every request has the phase n_records.  All blocks
+ * are resourced for the fold (4 per compute unit). */
+int32_t leapq_step(leapq_layer *layer, const leapq_gate *gate, const int32_t *n_in, int32_t *n_out,
+                   const void *q, const void *k, const void *v, const float *alpha, const float *beta, float *o,
+                   void *stream);
+
 /* Closes the window ("Recurrent-state quantization for linear attention: a
  * first GPU kernel", What we built: rebuild, select compensators, rescale,
  * round, empty the buffer; "LeapQuant" B.3): rebuilds the current state from

@@ -217,6 +217,29 @@ int32_t append_fold_impl(leapq_layer *layer, const leapq_gate *gate, const void 
     return st;
 }
 
+int32_t step_impl(leapq_layer *layer, const leapq_gate *gate, const int32_t *n_in, int32_t *n_out, const void *q,
+                  const void *k, const void *v, const float *alpha, const float *beta, float *o, void *stream)
+{
+    leapq::StateView sv;
+    int32_t st = view_of(layer, &sv);
+    if (st != LEAPQ_OK) return st;
+    leapq::GateArgs g = plain_gate(layer->cfg);
+    if (gate && (st = gate_of(layer, gate, &g)) != LEAPQ_OK) return st;
+    if ((st = check_token(q, k, v, alpha, beta, o, sv.kda)) != LEAPQ_OK) return st;
+    if (!n_in) return LEAPQ_ERR_NULL;
+    if (!aligned(n_in, 4) || (n_out && !aligned(n_out, 4))) return LEAPQ_ERR_ALIGN;
+    if (layer->cfg.window > 16) return LEAPQ_ERR_RANGE;
+    // every head of a request reads n_in while block 0 of the request writes n_out
+    if (n_out) {
+        const char *a0 = (const char *)n_in, *b0 = (const char *)n_out;
+        const size_t bytes = sizeof(int32_t) * (size_t)layer->cfg.batch;
+        if (a0 < b0 + bytes && b0 < a0 + bytes) return LEAPQ_ERR_RANGE;
+    }
+    return hip_status(leapq::launch_step(sv, heads_of(&layer->cfg), layer->cfg.heads, n_in, n_out,
+                                         layer->cfg.in_dtype == LEAPQ_BF16, q, k, v, alpha, beta, o,
+                                         layer->cfg.smoothing, layer->cfg.sigma_floor, g, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +268,12 @@ int32_t leapq_append_fold_gated(leapq_layer *layer, const leapq_gate *gate, cons
 {
     if (!gate) return LEAPQ_ERR_NULL;
     return append_fold_impl(layer, gate, q, k, v, a, b, o, stream);
+}
+
+int32_t leapq_step(leapq_layer *layer, const leapq_gate *gate, const int32_t *n_in, int32_t *n_out, const void *q,
+                   const void *k, const void *v, const float *alpha, const float *beta, float *o, void *stream)
+{
+    return step_impl(layer, gate, n_in, n_out, q, k, v, alpha, beta, o, stream);
 }
 
 int32_t leapq_fold(leapq_layer *layer, void *stream)

@@ -338,6 +338,11 @@ __device__ __forceinline__ float sload(const float *p, int i)
     typedef const __attribute__((address_space(4))) float *cptr;
     return ((cptr)(uintptr_t)p)[i];
 }
+__device__ __forceinline__ int sloadi(const int *p, int i)
+{
+    typedef const __attribute__((address_space(4))) int *cptr;
+    return ((cptr)(uintptr_t)p)[i];
+}
 
 __device__ __forceinline__ float rdl(float x, int lane)
 {

@@ -880,6 +880,59 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
+// One decode token with a window phase per request (W <= 16).  The heads of
+// request b (blocks b * heads_per_req ..) hold n = n_in[b] records: with
+// n = W - 1 the head appends and folds in this launch (the steps of
+// k_append_fold), with 0 <= n < W - 1 it appends (the steps of k_append,
+// staged as in k_append_fold), and any other n takes no token: the head's
+// state and output are left as they are.  Block 0 of each request writes the
+// request's next count to n_out (when given): 0 after a fold, n + 1 after an
+// append, n unchanged otherwise.  n is uniform per block, so the branches
+// cost nothing, but every block is resourced for the fold.
+template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CT, bool BLK>
+__global__ __launch_bounds__(NT) void k_step(StateView sv, int heads_per_req, const int *__restrict__ n_in,
+                                              int *__restrict__ n_out, const T *__restrict__ qin,
+                                              const T *__restrict__ kin, const T *__restrict__ vin,
+                                              const float *__restrict__ alpha, const float *__restrict__ beta,
+                                              float *__restrict__ o, int smoothing, float floor_, GateArgs g)
+{
+    using R = Rec<K, CH, U>;
+    __shared__ FoldStage<R::stride> st;
+    __shared__ float sin_[InLds<T>::floats];
+    __shared__ float dots[kDotFloats];
+    __shared__ FoldWork wk;
+    const MMap a = mmap();
+    const int h = blockIdx.x;
+    const int req = h / heads_per_req;
+    const int n = sloadi(n_in, req);
+    const bool take = n >= 0 && n < sv.W;
+    const bool last = n == sv.W - 1;
+    if (n_out && h == req * heads_per_req && threadIdx.x == 0) n_out[req] = !take ? n : last ? 0 : n + 1;
+    if (!take) return;
+    const HeadLds<T, K, CH, U, R1> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
+    uint4 qc[4];
+    append_issue<T, K, CH, U, R1>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    float a_h = CH ? 1.0f : sload(alpha, h);
+    float b_h = sload(beta, h);
+    if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
+    wait_lds_copies();
+    lds_barrier();
+    if constexpr (GATED) {
+        a_h = dots[kGateSlot];
+        b_h = dots[kGateSlot + 1];
+    }
+    if (!last) {
+        append_compute<T, K, false, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+        return;
+    }
+    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    lds_barrier();  // record n is in LDS for every wave
+    const HeadState hs = head_state(sv, h);
+    float S[4][16];
+    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
+    quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
+}
+
 template <typename K, bool CH, typename U, bool R1>
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
@@ -1034,6 +1087,73 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
         LQ_AF(uint16_t, float, true, false);
     }
 #undef LQ_AF
+    return hipGetLastError();
+}
+
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false,
+          bool BLK = false>
+static void launch_step_t(const StateView &sv, int heads, int heads_per_req, const int *n_in, int *n_out,
+                          const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                          float *o, int smoothing, float floor_, const GateArgs &g, hipStream_t s)
+{
+    if (sv.C == 4)
+        hipLaunchKernelGGL((k_step<T, K, GATED, NORM, CH, U, R1, 4, BLK>), dim3(heads), dim3(NT), 0, s, sv,
+                           heads_per_req, n_in, n_out, (const T *)q, (const T *)k, (const T *)v, alpha, beta, o,
+                           smoothing, floor_, g);
+    else
+        hipLaunchKernelGGL((k_step<T, K, GATED, NORM, CH, U, R1, -1, BLK>), dim3(heads), dim3(NT), 0, s, sv,
+                           heads_per_req, n_in, n_out, (const T *)q, (const T *)k, (const T *)v, alpha, beta, o,
+                           smoothing, floor_, g);
+}
+
+hipError_t launch_step(const StateView &sv, int heads, int heads_per_req, const int *n_in, int *n_out, int bf16,
+                       const void *q, const void *k, const void *v, const float *alpha, const float *beta, float *o,
+                       int smoothing, float floor_, const GateArgs &g, hipStream_t s)
+{
+    // the variants of launch_append_fold
+    const bool kb = sv.key_bf16;
+#define LQ_ST(...) \
+    launch_step_t<__VA_ARGS__>(sv, heads, heads_per_req, n_in, n_out, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
+    if (sv.blk) {
+        if (!bf16)
+            LQ_ST(float, float, false, false, false, float, true, true);
+        else
+            LQ_ST(uint16_t, uint16_t, false, false, false, float, true, true);
+    } else if (sv.r1) {
+        if (!bf16)
+            LQ_ST(float, float, false, false, false, float, true);
+        else
+            LQ_ST(uint16_t, uint16_t, false, false, false, float, true);
+    } else if (sv.u_bf16) {
+        if (!bf16)
+            LQ_ST(float, float, false, false, false, uint16_t);
+        else
+            LQ_ST(uint16_t, uint16_t, false, false, false, uint16_t);
+    } else if (sv.kda) {
+        if (!bf16)
+            LQ_ST(float, float, false, false, true);
+        else
+            LQ_ST(uint16_t, uint16_t, false, false, true);
+    } else if (!g.gated) {
+        if (!bf16)
+            LQ_ST(float, float, false, false);
+        else if (kb)
+            LQ_ST(uint16_t, uint16_t, false, false);
+        else
+            LQ_ST(uint16_t, float, false, false);
+    } else if (!bf16) {
+        if (g.normalize)
+            LQ_ST(float, float, true, true);
+        else
+            LQ_ST(float, float, true, false);
+    } else if (kb) {
+        LQ_ST(uint16_t, uint16_t, true, false);
+    } else if (g.normalize) {
+        LQ_ST(uint16_t, float, true, true);
+    } else {
+        LQ_ST(uint16_t, float, true, false);
+    }
+#undef LQ_ST
     return hipGetLastError();
 }
 

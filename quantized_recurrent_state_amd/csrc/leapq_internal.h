@@ -51,6 +51,9 @@ hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const 
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
                               const void *v, const float *alpha, const float *beta, float *o, int smoothing,
                               float floor_, const GateArgs &g, hipStream_t s);
+hipError_t launch_step(const StateView &sv, int heads, int heads_per_req, const int *n_in, int *n_out, int bf16,
+                       const void *q, const void *k, const void *v, const float *alpha, const float *beta, float *o,
+                       int smoothing, float floor_, const GateArgs &g, hipStream_t s);
 hipError_t launch_gdn_decode(int heads, int state_bf16, int in_bf16, int kda, void *S, const void *q, const void *k,
                              const void *v, const float *alpha, const float *beta, float *o, hipStream_t s);
 

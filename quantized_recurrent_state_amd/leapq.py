@@ -38,8 +38,8 @@ LEAPQ_DEQ_BOUNDARY = 1
 LEAPQ_DEQ_CURRENT = 2
 
 SYMBOLS = ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold", "leapq_append_gated",
-           "leapq_append_fold_gated", "leapq_fold", "leapq_dequant", "leapq_gdn_decode", "leapq_status_str",
-           "leapq_version")
+           "leapq_append_fold_gated", "leapq_step", "leapq_fold", "leapq_dequant", "leapq_gdn_decode",
+           "leapq_status_str", "leapq_version")
 
 
 class leapq_config(ctypes.Structure):
@@ -91,11 +91,13 @@ def lib():
         for f in ("leapq_append_gated", "leapq_append_fold_gated"):
             getattr(L, f).argtypes = [ctypes.POINTER(leapq_layer), ctypes.POINTER(leapq_gate), vp, vp, vp, vp, vp,
                                       vp, vp]
+        L.leapq_step.argtypes = [ctypes.POINTER(leapq_layer), ctypes.POINTER(leapq_gate), vp, vp, vp, vp, vp, vp,
+                                 vp, vp, vp]
         L.leapq_fold.argtypes = [ctypes.POINTER(leapq_layer), vp]
         L.leapq_dequant.argtypes = [ctypes.POINTER(leapq_layer), i32, vp, vp]
         L.leapq_gdn_decode.argtypes = [ctypes.POINTER(leapq_config), i32, vp, vp, vp, vp, vp, vp, vp, vp]
         for f in ("leapq_query_layout", "leapq_init_state", "leapq_append", "leapq_append_fold",
-                  "leapq_append_gated", "leapq_append_fold_gated", "leapq_fold", "leapq_dequant",
+                  "leapq_append_gated", "leapq_append_fold_gated", "leapq_step", "leapq_fold", "leapq_dequant",
                   "leapq_gdn_decode", "leapq_version"):
             getattr(L, f).restype = i32
         L.leapq_status_str.argtypes = [i32]
@@ -337,6 +339,26 @@ def leapq_append_fold_gated(layer, gate, q, k, v, a, b, o, stream=None):
     """leapq_append_fold with the gate arithmetic."""
     _check(lib().leapq_append_fold_gated(*_gated_args(layer, gate, q, k, v, a, b, o),
                                          _stream(stream, layer.device)), "leapq_append_fold_gated")
+
+
+def leapq_step(layer, n_in, n_out, q, k, v, alpha, beta, o, gate=None, stream=None):
+    """One token with a window phase per request: n_in, n_out int32 [batch]
+    (n_out may be None); with a gate, alpha and beta are the raw a, b."""
+    H, dt, dev = layer.heads, layer.in_dtype, layer.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(t, name, dt, (H, D), dev)
+    _dev_tensor(alpha, "alpha", torch.float32, (H,) if gate is not None else _alpha_shape(layer.cfg), dev)
+    _dev_tensor(beta, "beta", torch.float32, (H,), dev)
+    _dev_tensor(o, "o", torch.float32, (H, D), dev)
+    _dev_tensor(n_in, "n_in", torch.int32, (layer.cfg.batch,), dev)
+    if n_out is not None:
+        _dev_tensor(n_out, "n_out", torch.int32, (layer.cfg.batch,), dev)
+    if gate is not None:
+        for name, t in (("A_log", gate.A_log), ("dt_bias", gate.dt_bias)):
+            _dev_tensor(t, name, torch.float32, (layer.cfg.heads,), dev)
+    _check(lib().leapq_step(ctypes.byref(layer.c), ctypes.byref(gate.c) if gate is not None else None, _ptr(n_in),
+                            _ptr(n_out) if n_out is not None else None, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                            _ptr(beta), _ptr(o), _stream(stream, dev)), "leapq_step")
 
 
 def leapq_fold(layer, stream=None):

@@ -206,3 +206,117 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
                              f"worst {max(rep.worst.values()):.2e}, non-bitwise {sum(rep.nonbit.values())}, "
                              f"codes bad {rep.code_bad}, idx bad {rep.idx_bad}")
     return rep, L, refs
+
+
+def run_staggered(wl, tokens, starts, skip=None, layer=0, sample=None, gen_device="cpu", device="cuda", gated=None,
+                  qk_norm=False, rec_u="f32", fit="lines", check_state=True, log=True):
+    """Drives one layer through leapq_step with a window phase per request.
+    Request b takes its first token at step starts[b] (it takes none before),
+    and none at the steps t with skip(t, b) true; the host keeps each
+    request's record count and hands it to the step as n_in (-1 for a
+    request that takes no token).  The sampled heads run in oracle heads that
+    append and fold on their own requests' schedule.  Checked each step: the
+    outputs of the active sampled heads, that output rows of requests that
+    took no token are untouched (a NaN fill survives), n_out against the
+    host's counts, and (check_state) the sampled heads' boundary state and
+    their own n records.  Returns (Report, Layer, oracle heads, counts)."""
+    rep = Report()
+    dev = torch.device(device)
+    B, Hh = wl.batch, wl.heads
+    H = B * Hh
+    sample = list(range(H)) if sample is None else list(sample)
+    cfg = lq.make_config(B, Hh, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype, qk_norm=qk_norm,
+                         decay=wl.decay, rec_dtype=rec_u, comp_fit=fit)
+    ash = (H, D) if wl.decay == "channel" else (H,)
+    L = lq.Layer(cfg, dev)
+    gate = None
+    if gated is not None:
+        A_log, dt_bias = workloads.gate_params(wl, layer)
+        gate = lq.Gate(A_log.to(dev), dt_bias.to(dev), gated["q_scale"], gated["eps"])
+        pA, pdt = A_log.numpy(), dt_bias.numpy()
+    S0 = workloads.initial_state(wl, layer, device=gen_device).reshape(H, D, D)
+    lq.leapq_init_state(L, S0.to(dev))
+    refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay, rec_u=rec_u, fit=fit)
+            for _ in sample]
+    S0h = S0[sample].cpu().numpy()
+    counts = np.zeros(B, np.int64)
+    sidx = torch.as_tensor(sample)
+    o = torch.empty(H, D, dtype=torch.float32, device=dev)
+    n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    with _pool() as pool:
+        list(pool.map(lambda a: a[0].init(a[1]), zip(refs, S0h)))
+        for t in range(tokens):
+            active = np.array([t >= starts[b] and not (skip is not None and skip(t, b)) for b in range(B)])
+            n_in = torch.as_tensor(np.where(active, counts, -1).astype(np.int32), device=dev)
+            gen = workloads.gated_token_inputs if gated is not None else workloads.token_inputs
+            q, k, v, a, b = gen(wl, layer, t, device=gen_device)
+            qd, kd, vd = (x.reshape(H, D).to(dev) for x in (q, k, v))
+            ad = a.reshape((H,) if gated is not None else ash).to(dev)
+            bd = b.reshape(H).to(dev)
+            o.fill_(float("nan"))
+            lq.leapq_step(L, n_in, n_out, qd, kd, vd, ad, bd, o, gate=gate)
+            W = wl.window
+            expect = np.where(active, np.where(counts == W - 1, 0, counts + 1), -1)
+            got_n = n_out.cpu().numpy()
+            assert np.array_equal(got_n, expect), (t, got_n, expect)
+            og = o.cpu().numpy()
+            act_rows = np.repeat(active, Hh)
+            assert np.all(np.isnan(og[~act_rows])), f"step {t}: output rows of idle requests were written"
+            assert not np.any(np.isnan(og[act_rows])), f"step {t}: missing outputs"
+            qh = workloads.widen(q.reshape(H, D)[sidx]).cpu().numpy()
+            kh = workloads.widen(k.reshape(H, D)[sidx]).cpu().numpy()
+            vh = workloads.widen(v.reshape(H, D)[sidx]).cpu().numpy()
+            ah = a.reshape((H,) if gated is not None else ash)[sidx].cpu().numpy()
+            bh = b.reshape(H)[sidx].cpu().numpy()
+
+            def step(s):
+                h = sample[s]
+                if not active[h // Hh]:
+                    return None
+                if gated is not None:
+                    j = h % Hh
+                    args = oracle.gated_inputs(qh[s], kh[s], vh[s], ah[s], bh[s], pA[j], pdt[j], gated["q_scale"],
+                                               gated["eps"], qk_norm)
+                else:
+                    args = (qh[s], kh[s], vh[s], ah[s], bh[s])
+                out = refs[s].append(*args)[0]
+                if refs[s].n == W:
+                    refs[s].fold()
+                return out
+
+            outs = list(pool.map(step, range(len(sample))))
+            for s, h in enumerate(sample):
+                if outs[s] is not None:
+                    rep.fp("o", og[h], outs[s])
+            counts = np.where(active, np.where(counts == W - 1, 0, counts + 1), counts)
+            if check_state:
+                torch.cuda.synchronize(dev)
+                _compare_staggered(L, refs, sample, counts[np.asarray(sample) // Hh], rep)
+            if log and (t + 1) % 16 == 0:
+                progress(f"  [{wl.name} staggered] step {t + 1}/{tokens}: worst {max(rep.worst.values()):.2e}, "
+                         f"non-bitwise {sum(rep.nonbit.values())}, codes bad {rep.code_bad}, idx bad {rep.idx_bad}")
+    return rep, L, refs, counts
+
+
+def _compare_staggered(L, heads_ref, sample, n_of, rep):
+    """Boundary state and each head's own n records against the oracle."""
+    idx = torch.as_tensor(sample, device=L.device)
+    codes = L.codes()[idx].cpu().numpy()
+    rho, sig = L.rho()[idx].cpu().numpy(), L.sigma()[idx].cpu().numpy()
+    C = L.cfg.n_comp
+    cidx = L.comp_idx()[idx].cpu().numpy() if C else None
+    cvec = L.comp_vec()[idx].cpu().numpy() if C else None
+    rg, rk, ru = (f()[idx].cpu().numpy() for f in (L.rec_gamma, L.rec_k, L.rec_u))
+    for s, h in enumerate(heads_ref):
+        n = int(n_of[s])
+        assert h.n == n, (s, h.n, n)
+        rep.codes(codes[s], h.Q, None)
+        rep.fp("rho", rho[s], h.rho)
+        rep.fp("sigma", sig[s], h.sigma)
+        if C:
+            rep.idx_bad += int(np.sum(cidx[s] != h.idx[:C]))
+            rep.fp("comp_vec", cvec[s], h.vec[:C])
+        if n:
+            rep.fp("rec_gamma", rg[s, :n], h.gam[:n])
+            rep.fp("rec_k", rk[s, :n], h.rk[:n])
+            rep.fp("rec_u", ru[s, :n], h.ru[:n])

@@ -358,3 +358,30 @@ def test_block_fit_layout_and_checks():
         c = cfg(comp_fit="block", **kw)
         assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
     assert call_gated(fake_layer(cfg(comp_fit="block")), gate_struct()) == lq.LEAPQ_ERR_RANGE
+
+
+# ---------------------------------------------------------------- per-request phases
+
+def call_step(L, n_in=FAKE, n_out=FAKE + 4096, gate=None, a=FAKE):
+    vp = ctypes.c_void_p
+    gp = ctypes.byref(gate) if gate is not None else None
+    return lq.lib().leapq_step(ctypes.byref(L), gp, vp(n_in), vp(n_out) if n_out else None, vp(FAKE), vp(FAKE),
+                               vp(FAKE), vp(a), vp(FAKE), vp(FAKE), None)
+
+
+def test_step_checks():
+    c = cfg()  # batch 2
+    assert call_step(fake_layer(c), n_in=0) == lq.LEAPQ_ERR_NULL
+    assert call_step(fake_layer(c), n_in=FAKE + 2) == lq.LEAPQ_ERR_ALIGN
+    assert call_step(fake_layer(c), n_out=FAKE + 4096 + 2) == lq.LEAPQ_ERR_ALIGN
+    # n_out must not overlap n_in (batch 2: 8 bytes)
+    assert call_step(fake_layer(c), n_out=FAKE) == lq.LEAPQ_ERR_RANGE
+    assert call_step(fake_layer(c), n_out=FAKE + 4) == lq.LEAPQ_ERR_RANGE
+    assert call_step(fake_layer(cfg(window=17))) == lq.LEAPQ_ERR_RANGE
+    assert call_step(fake_layer(c), a=FAKE + 2) == lq.LEAPQ_ERR_ALIGN
+    g = gate_struct()
+    g.reserved[1] = 1
+    assert call_step(fake_layer(cfg(qk_norm=True)), gate=g) == lq.LEAPQ_ERR_RANGE
+    # the layer's host count is neither checked nor changed
+    L = fake_layer(c, n=16)
+    assert call_step(L, n_in=0) == lq.LEAPQ_ERR_NULL and L.n_records == 16
