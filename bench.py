@@ -48,6 +48,8 @@ def parse():
                    help="skip the measurement of the rank-one compensator option")
     p.add_argument("--no-block", action="store_true",
                    help="skip the measurement of the block compensator fit option")
+    p.add_argument("--no-staggered", action="store_true",
+                   help="skip the measurement of per-request window phases (leapq_step)")
     p.add_argument("--baseline-tokens", type=int, default=16)
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--separate", action="store_true",
@@ -343,6 +345,76 @@ def main():
             f"{block['tokens_per_s']:,.0f} tokens/s ({block['ratio_to_plain']:.3f} of the plain path); "
             f"append {block['append_us']:.1f} us, last append + fold {block['append_fold_us']:.1f} us")
 
+    # ---- per-request window phases: request b is b % W tokens into its
+    # window, so every step folds about 1/W of the requests (leapq_step, one
+    # launch per layer and token); same inputs and work per window as the
+    # lockstep schedule, with the fold spread over the window's tokens
+    staggered = None
+    if not args.no_staggered and W <= 16:
+        slayers = []
+        for l in range(Lyr):
+            L = lq.Layer(cfg, dev)
+            S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
+            lq.leapq_init_state(L, S0)
+            del S0
+            slayers.append(L)
+        ph = np.arange(B) % W
+        # spread the phases: request b takes no token in the first W - ph[b] steps
+        spread = [torch.as_tensor(np.where(t >= W - ph, t - (W - ph), -1).astype(np.int32), device=dev)
+                  for t in range(W)]
+        n_cur = torch.as_tensor(ph.astype(np.int32), device=dev)
+        n_nxt = torch.empty_like(n_cur)
+
+        def sstep(pos, n_in, n_out, ev=None):
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record(stream)
+            for l in range(Lyr):
+                q, k, v, a, b = pool[l][pos]
+                lq.leapq_step(slayers[l], n_in, n_out, q, k, v, a, b, outs[l], stream=stream)
+            if ev is not None:
+                ev.append(torch.cuda.Event(enable_timing=True))
+                ev[-1].record(stream)
+
+        for t in range(W):
+            sstep(t, spread[t], n_nxt)
+        torch.cuda.synchronize(dev)
+        # requests at phase 0 took no token (their n_out echoes -1)
+        assert torch.equal(torch.where(n_cur > 0, n_nxt, n_cur), n_cur), "phase spread"
+
+        def swindow(ev=None):
+            nonlocal n_cur, n_nxt
+            for pos in range(W):
+                sstep(pos, n_cur, n_nxt, ev)
+                n_cur, n_nxt = n_nxt, n_cur
+
+        swindow()
+        torch.cuda.synchronize(dev)
+        ssteps = max(4, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(ssteps):
+            swindow()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        s_ms = e0.elapsed_time(e1) / ssteps
+        sev = []
+        for _ in range(2):
+            swindow(sev)
+        torch.cuda.synchronize(dev)
+        tok_ms = [x.elapsed_time(y) for x, y in zip(sev[0::2], sev[1::2])]
+        lock_tok = [Lyr * app_us[p] / 1e3 for p in range(W - 1)] + [Lyr * fused_us / 1e3]
+        staggered = {"tokens_per_s": B * W / (s_ms / 1e3), "ms_per_step": s_ms, "steps": ssteps,
+                     "ratio_to_lockstep": (B * W / (s_ms / 1e3)) / tokens_per_s,
+                     "token_ms_min": min(tok_ms), "token_ms_max": max(tok_ms),
+                     "lockstep_token_ms_min": min(lock_tok), "lockstep_token_ms_max": max(lock_tok),
+                     "phases": "request b at b % W tokens into its window"}
+        log(f"[bench] per-request phases (leapq_step): {s_ms:.3f} ms per window, {staggered['tokens_per_s']:,.0f} "
+            f"tokens/s ({staggered['ratio_to_lockstep']:.3f} of lockstep); one token through {Lyr} layers takes "
+            f"{min(tok_ms):.3f}..{max(tok_ms):.3f} ms against {min(lock_tok):.3f}..{max(lock_tok):.3f} ms in lockstep")
+        del slayers
+        torch.cuda.empty_cache()
+
     # ---- per-channel decay (KDA): the same shape and schedule with alpha a
     # 128-vector per head and token, and the dense KDA baselines
     kda = None
@@ -509,6 +581,7 @@ def main():
         "bf16_record_corrections": bf16rec,
         "rank1_compensators": rank1,
         "block_compensators": block,
+        "staggered_phases": staggered,
         "baselines": baselines,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),
