@@ -101,3 +101,44 @@ def test_step_in_phase_equals_append_calls():
     for f in ("rec_gamma", "rec_k", "rec_u"):
         assert torch.equal(getattr(La, f)()[:, :n], getattr(Ls, f)()[:, :n]), f
     progress(f"  in phase: {wl.window + 3} tokens, outputs, boundary state and {n} records equal")
+
+
+def test_step_out_of_range_phases_take_no_token():
+    """Counts outside [0, W) (negative, W, far above) take no token: those
+    requests' output rows and state bytes stay as they were, n_out echoes the
+    count, and the other requests step normally; with n_out = NULL the step
+    writes no counts."""
+    wl = _wl("tiny", batch=4, heads=2, seed=119)
+    H, dev = wl.batch * wl.heads, torch.device("cuda")
+    cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype)
+    L, R = lq.Layer(cfg, dev), lq.Layer(cfg, dev)
+    S0 = workloads.initial_state(wl, 0, device=dev).reshape(H, D, D)
+    lq.leapq_init_state(L, S0)
+    lq.leapq_init_state(R, S0)
+    q, k, v, a, b = (x.reshape(H, -1).squeeze(-1).to(dev) for x in workloads.token_inputs(wl, 0, 0))
+    before = L.state.clone()
+    o = torch.full((H, D), float("nan"), device=dev)
+    n_in = torch.tensor([-5, 0, 16, 1000], dtype=torch.int32, device=dev)
+    n_out = torch.full((wl.batch,), 7, dtype=torch.int32, device=dev)
+    lq.leapq_step(L, n_in, n_out, q, k, v, a, b, o)
+    ref = torch.empty(H, D, device=dev)
+    lq.leapq_append(R, q, k, v, a, b, ref)  # every request at n = 0
+    torch.cuda.synchronize()
+    assert n_out.tolist() == [-5, 1, 16, 1000]
+    rows = torch.arange(H, device=dev) // wl.heads
+    idle = rows != 1
+    assert torch.all(torch.isnan(o[idle])) and torch.equal(o[~idle].view(torch.int32), ref[~idle].view(torch.int32))
+    # an append leaves the boundary alone; request 1's record 0 equals the
+    # append's, and the idle requests' record bytes are those from before
+    for f in ("codes", "rho", "sigma", "comp_idx", "comp_vec"):
+        assert torch.equal(getattr(L, f)(), getattr(R, f)()), f
+    B0 = lq.Layer(cfg, dev)
+    B0.state.copy_(before)
+    hidle = idle.nonzero().flatten()
+    for f in ("rec_gamma", "rec_k", "rec_u"):
+        got, ref_f, old = getattr(L, f)(), getattr(R, f)(), getattr(B0, f)()
+        assert torch.equal(got[~idle][:, 0], ref_f[~idle][:, 0]), f
+        assert torch.equal(got[hidle].view(torch.int32), old[hidle].view(torch.int32)), f
+    lq.leapq_step(L, torch.zeros(wl.batch, dtype=torch.int32, device=dev), None, q, k, v, a, b, o)
+    torch.cuda.synchronize()
+    assert not torch.any(torch.isnan(o))
