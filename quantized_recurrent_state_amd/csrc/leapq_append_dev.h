@@ -159,7 +159,7 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
     // the code loads stay behind every copy (wait_lds_copies counts on it)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(w, l, p));
+    for (int p = 0; p < 4; ++p) qc[p] = ld_stream(hs.codes + code_off(w, l, p));
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -379,19 +379,27 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     if (vec == 0) {
         // the record's correction (rounded to nearest even with bf16 U); this
         // token's own output below uses the fp32 u
-        if constexpr (std::is_same<U, float>::value)
-            reinterpret_cast<float *>(ru)[uc] = u;
-        else
+        if constexpr (std::is_same<U, float>::value) {
+            if constexpr (REC_LDS)
+                reinterpret_cast<float *>(ru)[uc] = u;
+            else
+                st_stream(reinterpret_cast<float *>(ru) + uc, u);
+        } else
             reinterpret_cast<uint16_t *>(ru)[uc] = f32_to_bf16_rne(u);
     } else {
-        o[(size_t)h * D + c] = fma_(kqd[0], u_from_k, acc);
+        st_stream(o + (size_t)h * D + c, fma_(kqd[0], u_from_k, acc));
     }
     if (w == 0) {
         if constexpr (std::is_same<K, T>::value && !NORM) {
             // the key is the token's k as staged (the first kbytes of the inputs)
             const uint32_t *kw = reinterpret_cast<const uint32_t *>(sin_);
-            rk[l] = kw[l];
-            if (R::kf > 64) rk[l + 64] = kw[l + 64];
+            if constexpr (REC_LDS) {
+                rk[l] = kw[l];
+                if (R::kf > 64) rk[l + 64] = kw[l + 64];
+            } else {
+                st_stream(rk + l, kw[l]);
+                if (R::kf > 64) st_stream(rk + l + 64, kw[l + 64]);
+            }
         } else {
             static_assert(std::is_same<K, float>::value, "normalized or widened keys are fp32");
             rk[l] = __float_as_uint(k0);

@@ -321,6 +321,25 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_s_barrier();
 }
 
+// ---------------------------------------------------------------- streaming access
+// Loads and stores of data that no later access of the same launch reuses
+// (the codes an append reads, the output and the record it writes), with the
+// non-temporal cache hint.
+__device__ __forceinline__ uint4 ld_stream(const int8_t *p)
+{
+    // four dword loads that combine into one 16-byte load (a vector-typed
+    // load here costs the append some 20 VGPRs)
+    const unsigned int *q = reinterpret_cast<const unsigned int *>(p);
+    uint4 r;
+    r.x = __builtin_nontemporal_load(q);
+    r.y = __builtin_nontemporal_load(q + 1);
+    r.z = __builtin_nontemporal_load(q + 2);
+    r.w = __builtin_nontemporal_load(q + 3);
+    return r;
+}
+__device__ __forceinline__ void st_stream(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_stream(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
 // ---------------------------------------------------------------- LDS-direct copies
 __device__ __forceinline__ void lds_copy16(const void *g, float *lds)
 {
