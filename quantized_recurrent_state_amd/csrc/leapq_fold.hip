@@ -315,6 +315,96 @@ __device__ __forceinline__ int pick_all(const MMap &a, const float *colE, const 
     return __builtin_amdgcn_readfirstlane(wave_min(cand));
 }
 
+// Zeroing an extracted line in the register tile.  The line's position in
+// the tile is wave-uniform (a row pick is block p = pick / 32 in the lanes
+// with i = pick % 32; a column pick is entry m = c / 8 of the four blocks in
+// lane half h of wave c % 4), but the tile is indexed statically.  Each asm
+// block below tests one candidate position with a scalar compare and skips
+// its lane-masked selects unless it is the one, so a round issues 16 (row)
+// or 4 (column) vector instructions instead of one select per entry.  The
+// test lives inside the asm: a C++ branch on the position made the compiler
+// keep a copy of the tile on each side.
+template <int P>
+__device__ __forceinline__ void zero_row_if(float (&x)[16], int pr, uint64_t lanes)
+{
+    asm volatile("s_cmp_eq_u32 %[pr], %[pp]\n\t"
+                 "s_cbranch_scc0 1f\n\t"
+                 "v_cndmask_b32_e64 %0, %0, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %1, %1, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %2, %2, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %3, %3, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %4, %4, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %5, %5, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %6, %6, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %7, %7, 0, %[ln]\n"
+                 "1:"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+                 : [pr] "s"(pr), [pp] "n"(P), [ln] "s"(lanes)
+                 : "scc");
+    asm volatile("s_cmp_eq_u32 %[pr], %[pp]\n\t"
+                 "s_cbranch_scc0 1f\n\t"
+                 "v_cndmask_b32_e64 %0, %0, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %1, %1, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %2, %2, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %3, %3, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %4, %4, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %5, %5, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %6, %6, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %7, %7, 0, %[ln]\n"
+                 "1:"
+                 : "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]),
+                   "+v"(x[15])
+                 : [pr] "s"(pr), [pp] "n"(P), [ln] "s"(lanes)
+                 : "scc");
+}
+
+template <int M>
+__device__ __forceinline__ void zero_col_if(float (&S)[4][16], int mm, uint64_t lanes)
+{
+    asm volatile("s_cmp_eq_u32 %[mm], %[m]\n\t"
+                 "s_cbranch_scc0 1f\n\t"
+                 "v_cndmask_b32_e64 %0, %0, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %1, %1, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %2, %2, 0, %[ln]\n\t"
+                 "v_cndmask_b32_e64 %3, %3, 0, %[ln]\n"
+                 "1:"
+                 : "+v"(S[0][M]), "+v"(S[1][M]), "+v"(S[2][M]), "+v"(S[3][M])
+                 : [mm] "s"(mm), [m] "n"(M), [ln] "s"(lanes)
+                 : "scc");
+}
+
+// Zeroes the picked line (pick: -1 none, 0..127 row, 128..255 column) in S.
+__device__ __forceinline__ void zero_line(const MMap &a, float (&S)[4][16], int pick)
+{
+    const bool isrow = pick >= 0 && pick < D, iscol = pick >= D;
+    const int cc = pick - D;
+    // -1 matches no block; the owning lanes as a lane mask
+    const int pr = __builtin_amdgcn_readfirstlane(isrow ? pick >> 5 : -1);
+    const int mm = __builtin_amdgcn_readfirstlane(iscol && a.w == (cc & 3) ? cc >> 3 : -1);
+    const uint64_t rl = __builtin_amdgcn_ballot_w64(a.i == (pick & 31));
+    const uint64_t cl = __builtin_amdgcn_ballot_w64(a.h == ((cc >> 2) & 1));
+    zero_row_if<0>(S[0], pr, rl);
+    zero_row_if<1>(S[1], pr, rl);
+    zero_row_if<2>(S[2], pr, rl);
+    zero_row_if<3>(S[3], pr, rl);
+    zero_col_if<0>(S, mm, cl);
+    zero_col_if<1>(S, mm, cl);
+    zero_col_if<2>(S, mm, cl);
+    zero_col_if<3>(S, mm, cl);
+    zero_col_if<4>(S, mm, cl);
+    zero_col_if<5>(S, mm, cl);
+    zero_col_if<6>(S, mm, cl);
+    zero_col_if<7>(S, mm, cl);
+    zero_col_if<8>(S, mm, cl);
+    zero_col_if<9>(S, mm, cl);
+    zero_col_if<10>(S, mm, cl);
+    zero_col_if<11>(S, mm, cl);
+    zero_col_if<12>(S, mm, cl);
+    zero_col_if<13>(S, mm, cl);
+    zero_col_if<14>(S, mm, cl);
+    zero_col_if<15>(S, mm, cl);
+}
+
 // Low byte of rint(y) for |y| < 2^22: adding 1.5 * 2^23 rounds y to an
 // integer (to nearest even) in the low mantissa bits.
 __device__ __forceinline__ uint32_t rint_bits(float y) { return __float_as_uint(y + 12582912.0f); }
@@ -703,16 +793,9 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
                     vec[a.row(p)] = sel((mm & 1) != 0, x2[1], x2[0]);
                 }
             }
+            zero_line(a, S, pick);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const bool zr = own_r && p == pr;
-#pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    const bool zc = own_c && m == mm;
-                    TS(S, p, m) = (zr || zc) ? 0.0f : TS(S, p, m);
-                }
-                rp[p] = zr ? 0.0f : rp[p];
-            }
+            for (int p = 0; p < 4; ++p) rp[p] = (own_r && p == pr) ? 0.0f : rp[p];
             if (jj + 1 < nrounds && pick >= 0) {
                 if (isrow) {
                     // column energies from S (picked lines already zeroed)
