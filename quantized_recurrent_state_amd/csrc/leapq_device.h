@@ -235,6 +235,28 @@ __device__ __forceinline__ float wave_max(float x)
     x = fmaxf(x, dpp<DPP_XOR2>(x));
     return fmaxf(x, dpp<DPP_XOR1>(x));
 }
+__device__ __forceinline__ int xmax32i(int x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int xmax16i(int x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    return max((int)r[0], (int)r[1]);
+}
+// Largest int of the wave, in every lane.  On bit patterns of floats it is
+// the float maximum when no value is NaN or -0 and every negative one is the
+// same (non-negative floats order like their bits).
+__device__ __forceinline__ int wave_max_i(int x)
+{
+    x = xmax32i(x);
+    x = xmax16i(x);
+    x = max(x, dppi<DPP_ROR8>(x));
+    x = max(x, dppi<DPP_ROR4>(x));
+    x = max(x, dppi<DPP_XOR2>(x));
+    return max(x, dppi<DPP_XOR1>(x));
+}
 __device__ __forceinline__ int wave_min(int x)
 {
     x = xmin32i(x);

@@ -290,29 +290,31 @@ __device__ __forceinline__ void put_row_energies(const MMap &a, const float (&rp
 // largest energy, lowest candidate on ties, the candidates in pk[0..npk)
 // (earlier picks) excluded; -1 when no energy is positive.  Every wave
 // computes it from LDS; the row energy is the canonical sum of the four
-// waves' partials (w, w ^ 2 first, then the two pairs).
+// waves' partials (w, w ^ 2 first, then the two pairs).  Energies are sums
+// of squares (+0 or positive, never -0), so they are compared as their bit
+// patterns, with -1 for an excluded candidate; the pick is wave-uniform.
 template <int NP>
 __device__ __forceinline__ int pick_all(const MMap &a, const float *colE, const float *rowP, const int (&pk)[NP],
                                         int npk)
 {
     const int l = a.l;
-    float e[4];
+    int e[4];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int r = l + 64 * k;
-        e[k] = (rowP[r] + rowP[2 * D + r]) + (rowP[D + r] + rowP[3 * D + r]);
-        e[2 + k] = colE[r];
+        e[k] = __float_as_int((rowP[r] + rowP[2 * D + r]) + (rowP[D + r] + rowP[3 * D + r]));
+        e[2 + k] = __float_as_int(colE[r]);
     }
 #pragma unroll
     for (int j = 0; j < NP; ++j)
         if (j < npk) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) e[k] = (pk[j] == 64 * k + l) ? -1.0f : e[k];
+            for (int k = 0; k < 4; ++k) e[k] = (pk[j] == 64 * k + l) ? -1 : e[k];
         }
-    const float M = wave_max(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])));
-    if (!(M > 0.0f)) return -1;
+    const int M = __builtin_amdgcn_readfirstlane(wave_max_i(max(max(e[0], e[1]), max(e[2], e[3]))));
     const int cand = e[0] == M ? l : e[1] == M ? 64 + l : e[2] == M ? 128 + l : e[3] == M ? 192 + l : 1 << 20;
-    return __builtin_amdgcn_readfirstlane(wave_min(cand));
+    const int pick = __builtin_amdgcn_readfirstlane(wave_min(cand));
+    return M > 0 ? pick : -1;
 }
 
 // Zeroing an extracted line in the register tile.  The line's position in
@@ -770,28 +772,27 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
             const bool own_r = isrow && a.i == (pick & 31);
             const bool own_c = iscol && a.w == (cc & 3) && a.h == ((cc >> 2) & 1);
             if (pick < 0 && t < D) vec[t] = 0.0f;
+            // the line's stores from its own registers, one uniform branch
+            // per candidate block; the empty asm statements differ per
+            // branch, so the compiler cannot merge the branches' stores into
+            // one store of a selected (copied) block
             if (own_r) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
                     if (p == pr) {
 #pragma unroll
                         for (int m = 0; m < 16; ++m) vec[a.col(m)] = TS(S, p, m);
+                        asm volatile("; row line block %0" ::"n"(p) : "memory");
                     }
             }
             if (own_c) {
-                // S[p][mm] by a select tree on the bits of mm (value selects;
-                // a branch per m would turn into a runtime index into S)
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    float x8[8], x4[4], x2[2];
+                for (int m = 0; m < 16; ++m)
+                    if (m == mm) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) x8[e] = sel((mm & 8) != 0, TS(S, p, e + 8), TS(S, p, e));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x4[e] = sel((mm & 4) != 0, x8[e + 4], x8[e]);
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) x2[e] = sel((mm & 2) != 0, x4[e + 2], x4[e]);
-                    vec[a.row(p)] = sel((mm & 1) != 0, x2[1], x2[0]);
-                }
+                        for (int p = 0; p < 4; ++p) vec[a.row(p)] = TS(S, p, m);
+                        asm volatile("; column line entry %0" ::"n"(m) : "memory");
+                    }
             }
             zero_line(a, S, pick);
 #pragma unroll
