@@ -238,7 +238,9 @@ static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t 
     }
 
     /* Symmetric per-row int8 with round half to even ([LQ] abstract: 8-bit
-     * state; [RN4] Why rounding: rounded once per window). */
+     * state; [RN4] Why rounding: rounded once per window).  A code is the
+     * integer nearest to the exact product x * g, ties to even: one rounding
+     * (the float64 product of two floats is exact). */
     for (int r = 0; r < D; ++r) {
         float x[D];
         float M = 0.0f;
@@ -254,7 +256,7 @@ static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t 
         rho[r] = M / 127.0f;
         float g = 127.0f / M;
         for (int c = 0; c < D; ++c) {
-            float y = rintf(x[c] * g);
+            float y = (float)rint((double)x[c] * (double)g);
             if (y > 127.0f) y = 127.0f;
             if (y < -127.0f) y = -127.0f;
             Q[r * D + c] = (int8_t)y;

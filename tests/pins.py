@@ -110,6 +110,21 @@ def pin_round_half_even(L):
     assert not h.Q[others].any() and not h.rho[others].any()
 
 
+def pin_round_exact_product_once(L):
+    """A code is the nearest integer to the exact product x * (127 / M), with
+    one rounding: the fixture's entry lies a sliver above a .5 boundary, where
+    rounding the fp32 product first lands on the tie and goes to the even code."""
+    case = golden("arith_fixtures.json")["round_exact_product_once"]
+    R = np.zeros((D, D), np.float32)
+    R[40] = sparse_vec(case["row"])
+    h = oracle.Head(C=0, smoothing=False, L=L).init(R)
+    want = np.zeros(D, np.int8)
+    for i, c in case["expected_codes"].items():
+        want[int(i)] = c
+    assert np.array_equal(h.Q[40], want), h.Q[40][:4]
+    assert h.rho[40] == np.float32(case["expected_rho"])
+
+
 def pin_pick_ties(L):
     g = golden("arith_fixtures.json")
     R = np.zeros((D, D), np.float32)
@@ -804,7 +819,7 @@ def pin_block_window_and_fold(L):
 
 
 ALL = [
-    pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_pick_ties,
+    pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_round_exact_product_once, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
     pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,

@@ -40,8 +40,9 @@ MUTANTS = [
     ("smooth_no_floor", "if (s < sigma_floor) s = sigma_floor;", ";"),
     ("smooth_no_sqrt", "s = sqrtf(m);", "s = m;"),
     ("quant_128", "rho[r] = M / 127.0f;", "rho[r] = M / 128.0f;"),
-    ("quant_round_away", "rintf(x[c] * g)", "roundf(x[c] * g)"),
-    ("quant_truncate", "rintf(x[c] * g)", "truncf(x[c] * g)"),
+    ("quant_round_away", "rint((double)x[c] * (double)g)", "round((double)x[c] * (double)g)"),
+    ("quant_truncate", "rint((double)x[c] * (double)g)", "trunc((double)x[c] * (double)g)"),
+    ("quant_double_rounding", "(float)rint((double)x[c] * (double)g)", "rintf(x[c] * g)"),
     ("quant_no_tiny_guard", "if (!(M >= LQO_TINY)) {", "if (!(M > 0.0f)) {"),
     ("step_no_decay", "    for (int e = 0; e < D * D; ++e) S[e] = alpha * S[e];\n    float u[D];",
      "    float u[D];"),
