@@ -276,19 +276,14 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
                 a0 = (gt0 / kj[R::goff + l]) * a0;
                 a1 = (gt1 / kj[R::goff + l + 64]) * a1;
             }
-            const float dk = wdot(a0, a1, k0, k1);
-            const float dq = wdot(a0, a1, q0, q1);
+            // lanes 0..31: the key dot, lanes 32..63: the query dot; lanes 0
+            // and 32 store them at coef[job] and coef[64 + job]
+            const float d = wdot2(a0, a1, k0, k1, q0, q1);
             if constexpr (CH) {
-                if (l == 0) {
-                    coef[job] = dk;
-                    coef[64 + job] = dq;
-                }
+                if ((l & 31) == 0) coef[job + 2 * l] = d;
             } else {
                 const float ci = rdl(ci_l, job);
-                if (l == 0) {
-                    coef[job] = ci * dk;
-                    coef[64 + job] = ci * dq;
-                }
+                if ((l & 31) == 0) coef[job + 2 * l] = ci * d;
             }
         } else if (job == n) {
             const float d = wdot(k0, k1, q0, q1);
@@ -298,12 +293,9 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
             if (R1 || sidx[jj] >= D) {
                 const float *vj = cv + jj * D * (R1 ? 2 : 1);  // a line, or the pair's a
                 const float a0 = vj[l], a1 = vj[l + 64];
-                const float dk = wdot(a0, a1, CH ? gt0 * k0 : k0, CH ? gt1 * k1 : k1);
-                const float dq = wdot(a0, a1, CH ? gt0 * q0 : q0, CH ? gt1 * q1 : q1);
-                if (l == 0) {
-                    cdot[jj] = dk;
-                    cdot[8 + jj] = dq;
-                }
+                const float d = wdot2(a0, a1, CH ? gt0 * k0 : k0, CH ? gt1 * k1 : k1, CH ? gt0 * q0 : q0,
+                                      CH ? gt1 * q1 : q1);
+                if ((l & 31) == 0) cdot[jj + (l >> 2)] = d;  // lane 32: cdot[8 + jj]
             }
         }
     }

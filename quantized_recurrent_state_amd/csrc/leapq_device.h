@@ -225,6 +225,20 @@ __device__ __forceinline__ float wdot(float a0, float a1, float b0, float b1)
     return s;
 }
 
+// The canonical dots (a . x) and (a . y) in one butterfly: level 32
+// exchanges halves, so lanes 0..31 end with a . x and lanes 32..63 with
+// a . y, each bitwise equal to wdot.
+__device__ __forceinline__ float wdot2(float a0, float a1, float x0, float x1, float y0, float y1)
+{
+    float s = xhalf32(fma_(a0, x0, a1 * x1), fma_(a0, y0, a1 * y1));
+    s = xhalf16(s, s);
+    s = s + dpp<DPP_ROR8>(s);
+    s = s + dpp<DPP_ROR4>(s);
+    s = s + dpp<DPP_XOR2>(s);
+    s = s + dpp<DPP_XOR1>(s);
+    return s;
+}
+
 // wave-wide max / min (order-free); every lane ends with the result
 __device__ __forceinline__ float wave_max(float x)
 {

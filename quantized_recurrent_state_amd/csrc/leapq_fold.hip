@@ -407,9 +407,10 @@ __device__ __forceinline__ void zero_line(const MMap &a, float (&S)[4][16], int 
     zero_col_if<15>(S, mm, cl);
 }
 
-// Low byte of rint(y) for |y| < 2^22: adding 1.5 * 2^23 rounds y to an
-// integer (to nearest even) in the low mantissa bits.
-__device__ __forceinline__ uint32_t rint_bits(float y) { return __float_as_uint(y + 12582912.0f); }
+// Low byte of the integer nearest to the exact product x * g (ties to even)
+// for |x * g| < 2^22: the fused add of 1.5 * 2^23 rounds the product once,
+// to an integer in the low mantissa bits.
+__device__ __forceinline__ uint32_t rint_bits(float x, float g) { return __float_as_uint(fma_(x, g, 12582912.0f)); }
 __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3)
 {
     const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
@@ -876,7 +877,7 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
         const float g = sm.rowg[a.w][a.row(p)];
         uint32_t b[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) b[m] = rint_bits(TS(S, p, m) * g);
+        for (int m = 0; m < 16; ++m) b[m] = rint_bits(TS(S, p, m), g);
         *reinterpret_cast<uint4 *>(hs.codes + code_off(a.w, a.l, p)) =
             make_uint4(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]),
                        pack4(b[8], b[9], b[10], b[11]), pack4(b[12], b[13], b[14], b[15]));
