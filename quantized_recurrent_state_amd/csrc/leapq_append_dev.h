@@ -205,7 +205,7 @@ template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool 
 __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a,
                                                const HeadLds<T, K, CH, U, R1> &L, float *dots, const uint4 (&qc)[4],
                                                float a_h, float b_h, float *__restrict__ o, float q_scale = 1.0f,
-                                               float eps = 0.0f)
+                                               float eps = 0.0f, float *wout = nullptr)
 {
     using R = Rec<K, CH, U>;
     const int C = sv.C, l = a.l, w = a.w;
@@ -279,11 +279,13 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
             // lanes 0..31: the key dot, lanes 32..63: the query dot; lanes 0
             // and 32 store them at coef[job] and coef[64 + job]
             const float d = wdot2(a0, a1, k0, k1, q0, q1);
-            if constexpr (CH) {
-                if ((l & 31) == 0) coef[job + 2 * l] = d;
-            } else {
-                const float ci = rdl(ci_l, job);
-                if ((l & 31) == 0) coef[job + 2 * l] = ci * d;
+            const float ci = CH ? 1.0f : rdl(ci_l, job);
+            if ((l & 31) == 0) coef[job + 2 * l] = CH ? d : ci * d;
+            if constexpr (REC_LDS) {
+                // the record's weighted key c_i k_i (with CH the weighted
+                // key itself) for the fold's rebuild of this head
+                wout[job * D + l] = CH ? a0 : ci * a0;
+                wout[job * D + l + 64] = CH ? a1 : ci * a1;
             }
         } else if (job == n) {
             const float d = wdot(k0, k1, q0, q1);
@@ -382,6 +384,12 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
         st_stream(o + (size_t)h * D + c, fma_(kqd[0], u_from_k, acc));
     }
     if (w == 0) {
+        if constexpr (REC_LDS) {
+            // this token's own record enters the rebuild with coefficient
+            // gamma_t / gamma_t = 1
+            wout[n * D + l] = k0;
+            wout[n * D + l + 64] = k1;
+        }
         if constexpr (std::is_same<K, T>::value && !NORM) {
             // the key is the token's k as staged (the first kbytes of the inputs)
             const uint32_t *kw = reinterpret_cast<const uint32_t *>(sin_);

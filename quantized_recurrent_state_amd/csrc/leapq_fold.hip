@@ -70,6 +70,7 @@ struct alignas(16) BlockWork {
     float z[4][128];     // per slot: column dots (z, finally b)
 };
 static_assert(sizeof(BlockWork) <= sizeof(FoldWork), "block fit arrays exceed the fold's work area");
+static_assert(sizeof(FoldWork) >= 16 * 128 * sizeof(float), "the weighted keys of 16 records exceed the work area");
 __device__ __forceinline__ int zpos(int c) { return (2 * (c & 3) + ((c >> 2) & 1)) * 16 + (c >> 3); }
 
 constexpr int kBlockSweeps = 2;      // per fold, warm-started
@@ -117,9 +118,13 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 // vector), every scale and record coefficient taken per row.
 // R1: the compensators are rank-one pairs [a | b] in sm.lines, applied as
 // matrix-instruction steps fma(gamma_n a[r], b[c], S) before the records.
-template <typename K, bool CH, typename U, typename Stage, bool R1 = false>
+// wpre (n <= 16): the records' weighted keys c_i k_i (with CH, the per-row
+// weighted keys) as [n][128] fp32 in LDS, formed by the append that shares
+// the launch; the matrix steps then read their key operands from it.
+template <typename K, bool CH, typename U, typename Stage, bool R1 = false, bool WPRE = false>
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
-                                        bool lines, Stage &sm, float (&S)[4][16], const float *gW = nullptr)
+                                        bool lines, Stage &sm, float (&S)[4][16], const float *gW = nullptr,
+                                        const float *wpre = nullptr)
 {
     using R = Rec<K, CH, U>;
     const float gn = CH ? 1.0f : (n > 0 ? sm.gam[n - 1] : 1.0f);
@@ -211,7 +216,10 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
             for (int u = 0; u < 4; ++u) {
                 const float *rr = sm.rec + (r + u) * R::stride;
                 float b0, b1;
-                if constexpr (CH) {
+                if constexpr (WPRE) {
+                    b0 = wpre[(r + u) * D + kr0];
+                    b1 = wpre[(r + u) * D + kr0 + 64];
+                } else if constexpr (CH) {
                     b0 = (gw0 / rr[R::goff + kr0]) * R::key(rr, kr0);
                     b1 = (gw1 / rr[R::goff + kr0 + 64]) * R::key(rr, kr0 + 64);
                 } else {
@@ -227,7 +235,10 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
         for (; r < cnt; ++r) {
             const float *rr = sm.rec + r * R::stride;
             float b0, b1;
-            if constexpr (CH) {
+            if constexpr (WPRE) {
+                b0 = wpre[r * D + kr0];
+                b1 = wpre[r * D + kr0 + 64];
+            } else if constexpr (CH) {
                 b0 = (gw0 / rr[R::goff + kr0]) * R::key(rr, kr0);
                 b1 = (gw1 / rr[R::goff + kr0 + 64]) * R::key(rr, kr0 + 64);
             } else {
@@ -957,11 +968,16 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
         a_h = dots[kGateSlot];
         b_h = dots[kGateSlot + 1];
     }
-    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    // the records' weighted keys go to the work area, unused until the
+    // rebuild has read them (barrier below)
+    float *wkeys = reinterpret_cast<float *>(&wk);
+    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps, wkeys);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
+    rebuild<K, CH, U, decltype(st), R1, true>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff,
+                                                wkeys);
+    lds_barrier();  // every wave is done with the weighted keys
     quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
@@ -1010,11 +1026,16 @@ __global__ __launch_bounds__(NT) void k_step(StateView sv, int heads_per_req, co
         append_compute<T, K, false, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
         return;
     }
-    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    // the records' weighted keys go to the work area, unused until the
+    // rebuild has read them (barrier below)
+    float *wkeys = reinterpret_cast<float *>(&wk);
+    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps, wkeys);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff);
+    rebuild<K, CH, U, decltype(st), R1, true>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff,
+                                                wkeys);
+    lds_barrier();  // every wave is done with the weighted keys
     quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
