@@ -101,6 +101,35 @@ def test_zero_state_and_empty_fold():
     assert L.n_records == 0
 
 
+def test_code_rounds_exact_product_once():
+    """The hand-derived fixture row (an entry a sliver above a .5 tie after
+    scaling) quantized on the GPU: code 65 as the oracle and the fixture say,
+    where rounding the fp32 product first would give 64.  Placed in a
+    different row and head each time, without smoothing and compensators."""
+    import json
+    import os
+    case = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "arith_fixtures.json")))[
+        "round_exact_product_once"]
+    H = 4
+    cfg = lq.make_config(1, H, n_comp=0, smoothing=False)
+    L = lq.Layer(cfg)
+    S0 = np.zeros((H, D, D), np.float32)
+    rows = [40, 3, 77, 127]
+    for h, r in enumerate(rows):
+        for i, x in case["row"].items():
+            S0[h, r, (int(i) + 9 * h) % D] = np.float32(x)
+    lq.leapq_init_state(L, torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    Q = L.codes().cpu().numpy()
+    rho = L.rho().cpu().numpy()
+    for h, r in enumerate(rows):
+        ref = oracle.Head(C=0, smoothing=False).init(S0[h])
+        assert np.array_equal(Q[h], ref.Q) and np.array_equal(rho[h], ref.rho)
+        for i, c in case["expected_codes"].items():
+            assert int(Q[h, r, (int(i) + 9 * h) % D]) == c
+        assert rho[h, r] == np.float32(case["expected_rho"])
+
+
 def test_dequant_all_views():
     wl = _wl("tiny", seed=32, init="writes")
     H = wl.batch * wl.heads
