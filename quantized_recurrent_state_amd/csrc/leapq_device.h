@@ -377,13 +377,15 @@ __device__ __forceinline__ void st_stream(float *p, float v) { __builtin_nontemp
 __device__ __forceinline__ void st_stream(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 // ---------------------------------------------------------------- LDS-direct copies
+// Non-temporal (cache policy nt): a launch reads every copied operand once.
+constexpr int kCopyPolicyNT = 2;
 __device__ __forceinline__ void lds_copy16(const void *g, float *lds)
 {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, kCopyPolicyNT);
 }
 __device__ __forceinline__ void lds_copy4(const void *g, void *lds)
 {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 4, 0, kCopyPolicyNT);
 }
 // A read-only fp32 value at a wave-uniform index, as a scalar load (constant
 // address space): waited for by lgkmcnt, so it does not wait behind the
