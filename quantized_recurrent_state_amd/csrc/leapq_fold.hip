@@ -323,8 +323,12 @@ __device__ __forceinline__ int pick_all(const MMap &a, const float *colE, const 
             for (int k = 0; k < 4; ++k) e[k] = (pk[j] == 64 * k + l) ? -1 : e[k];
         }
     const int M = __builtin_amdgcn_readfirstlane(wave_max_i(max(max(e[0], e[1]), max(e[2], e[3]))));
-    const int cand = e[0] == M ? l : e[1] == M ? 64 + l : e[2] == M ? 128 + l : e[3] == M ? 192 + l : 1 << 20;
-    const int pick = __builtin_amdgcn_readfirstlane(wave_min(cand));
+    // the lowest candidate holding M: candidate 64 k + l is e[k] of lane l,
+    // so the first k whose lane mask is not empty, then its lowest lane
+    const uint64_t b0 = __builtin_amdgcn_ballot_w64(e[0] == M), b1 = __builtin_amdgcn_ballot_w64(e[1] == M);
+    const uint64_t b2 = __builtin_amdgcn_ballot_w64(e[2] == M), b3 = __builtin_amdgcn_ballot_w64(e[3] == M);
+    const int pick = b0 ? __builtin_ctzll(b0) : b1 ? 64 + __builtin_ctzll(b1) : b2 ? 128 + __builtin_ctzll(b2)
+                                                                              : 192 + __builtin_ctzll(b3);
     return M > 0 ? pick : -1;
 }
 
