@@ -772,10 +772,43 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
         for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
         put_row_energies(a, rp, sm.rowP[0]);
         lds_barrier();
+        // Rescoring is lazy.  Removing a line only lowers the other axis's
+        // energies (every square and every add of the canonical tree is
+        // monotone), so after a row pick the stale column energies bound the
+        // true ones from above, and likewise for rows after a column pick.
+        // A pick made with stale energies on the other axis is therefore the
+        // greedy pick whenever it falls on the fresh axis (a row beats every
+        // column it ties, a column must beat the rows strictly); only a pick
+        // on a stale axis rescores that axis (one barrier) and picks again.
+        // At most one axis is stale at a time: a pick is only taken on a
+        // fresh axis.
+        bool staleR = false, staleC = false;
+        bool dirty = false;  // this wave's row partials miss a zeroed column of its own
 #pragma unroll
         for (int jj = 0; jj < NR; ++jj) {
             if (jj >= nrounds) break;
-            const int pick = pick_all(a, sm.colE[cb], sm.rowP[rb], pk, jj);
+            int pick = pick_all(a, sm.colE[cb], sm.rowP[rb], pk, jj);
+            if ((pick >= 0 && pick < D && staleR) || (pick >= D && staleC)) {
+                if (pick >= D) {
+                    // column energies from S (picked lines already zeroed)
+                    float cp[16];
+                    col_partials(S, cp);
+                    put_cols(a, cp, sm.colE[cb ^ 1]);
+                    cb ^= 1;
+                    staleC = false;
+                } else {
+                    if (dirty) {
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
+                    }
+                    dirty = false;
+                    put_row_energies(a, rp, sm.rowP[rb ^ 1]);
+                    rb ^= 1;
+                    staleR = false;
+                }
+                lds_barrier();
+                pick = pick_all(a, sm.colE[cb], sm.rowP[rb], pk, jj);
+            }
             pk[jj] = pick;
             float *vec = hs.cvec + jj * D;
             if (t == 0) hs.cidx[jj] = pick;
@@ -813,23 +846,9 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
             zero_line(a, S, pick);
 #pragma unroll
             for (int p = 0; p < 4; ++p) rp[p] = (own_r && p == pr) ? 0.0f : rp[p];
-            if (jj + 1 < nrounds && pick >= 0) {
-                if (isrow) {
-                    // column energies from S (picked lines already zeroed)
-                    float cp[16];
-                    col_partials(S, cp);
-                    put_cols(a, cp, sm.colE[cb ^ 1]);
-                    cb ^= 1;
-                } else {
-                    if (a.w == (cc & 3)) {
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) rp[p] = row_partial(S, p);
-                    }
-                    put_row_energies(a, rp, sm.rowP[rb ^ 1]);
-                    rb ^= 1;
-                }
-                lds_barrier();
-            }
+            staleC = staleC || isrow;
+            staleR = staleR || iscol;
+            dirty = dirty || (iscol && a.w == (cc & 3));
         }
     }
     // ---- residual smoothing
