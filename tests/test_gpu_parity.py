@@ -130,6 +130,33 @@ def test_code_rounds_exact_product_once():
         assert rho[h, r] == np.float32(case["expected_rho"])
 
 
+def test_symmetric_states_tie_rows_and_columns():
+    """Symmetric states: row i and column i hold the same entries in the same
+    canonical order, so every row energy ties its column's.  The greedy pick
+    takes the row (rows first), and the next pick meets the stale energies of
+    the columns at their maximum, which must be rescored before picking again.
+    Codes, scales, indices and lines bitwise against the oracle."""
+    H = 8
+    rng = np.random.default_rng(41)
+    S0 = np.empty((H, D, D), np.float32)
+    for h in range(H):
+        A = rng.standard_normal((D, D)).astype(np.float32) * np.float32(0.02)
+        for r in rng.choice(D, size=1 + h % 3, replace=False):
+            A[r, :] *= np.float32(30.0 + 10.0 * h)
+        S0[h] = np.triu(A) + np.triu(A, 1).T  # exactly symmetric
+    cfg = lq.make_config(1, H)
+    L = lq.Layer(cfg)
+    lq.leapq_init_state(L, torch.from_numpy(S0).cuda())
+    torch.cuda.synchronize()
+    Q, rho, sig = L.codes().cpu().numpy(), L.rho().cpu().numpy(), L.sigma().cpu().numpy()
+    idx, vec = L.comp_idx().cpu().numpy(), L.comp_vec().cpu().numpy()
+    for h in range(H):
+        ref = oracle.Head().init(S0[h])
+        assert list(idx[h]) == list(ref.idx), (h, list(idx[h]), list(ref.idx))
+        assert np.array_equal(vec[h].view(np.uint32), ref.vec.view(np.uint32))
+        assert np.array_equal(Q[h], ref.Q) and np.array_equal(rho[h], ref.rho) and np.array_equal(sig[h], ref.sigma)
+
+
 def test_dequant_all_views():
     wl = _wl("tiny", seed=32, init="writes")
     H = wl.batch * wl.heads
