@@ -335,62 +335,11 @@ __device__ __forceinline__ int pick_all(const MMap &a, const float *colE, const 
 // Zeroing an extracted line in the register tile.  The line's position in
 // the tile is wave-uniform (a row pick is block p = pick / 32 in the lanes
 // with i = pick % 32; a column pick is entry m = c / 8 of the four blocks in
-// lane half h of wave c % 4), but the tile is indexed statically.  Each asm
-// block below tests one candidate position with a scalar compare and skips
-// its lane-masked selects unless it is the one, so a round issues 16 (row)
-// or 4 (column) vector instructions instead of one select per entry.  The
-// test lives inside the asm: a C++ branch on the position made the compiler
-// keep a copy of the tile on each side.
-template <int P>
-__device__ __forceinline__ void zero_row_if(float (&x)[16], int pr, uint64_t lanes)
-{
-    asm volatile("s_cmp_eq_u32 %[pr], %[pp]\n\t"
-                 "s_cbranch_scc0 1f\n\t"
-                 "v_cndmask_b32_e64 %0, %0, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %1, %1, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %2, %2, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %3, %3, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %4, %4, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %5, %5, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %6, %6, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %7, %7, 0, %[ln]\n"
-                 "1:"
-                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
-                 : [pr] "s"(pr), [pp] "n"(P), [ln] "s"(lanes)
-                 : "scc");
-    asm volatile("s_cmp_eq_u32 %[pr], %[pp]\n\t"
-                 "s_cbranch_scc0 1f\n\t"
-                 "v_cndmask_b32_e64 %0, %0, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %1, %1, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %2, %2, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %3, %3, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %4, %4, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %5, %5, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %6, %6, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %7, %7, 0, %[ln]\n"
-                 "1:"
-                 : "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]),
-                   "+v"(x[15])
-                 : [pr] "s"(pr), [pp] "n"(P), [ln] "s"(lanes)
-                 : "scc");
-}
-
-template <int M>
-__device__ __forceinline__ void zero_col_if(float (&S)[4][16], int mm, uint64_t lanes)
-{
-    asm volatile("s_cmp_eq_u32 %[mm], %[m]\n\t"
-                 "s_cbranch_scc0 1f\n\t"
-                 "v_cndmask_b32_e64 %0, %0, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %1, %1, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %2, %2, 0, %[ln]\n\t"
-                 "v_cndmask_b32_e64 %3, %3, 0, %[ln]\n"
-                 "1:"
-                 : "+v"(S[0][M]), "+v"(S[1][M]), "+v"(S[2][M]), "+v"(S[3][M])
-                 : [mm] "s"(mm), [m] "n"(M), [ln] "s"(lanes)
-                 : "scc");
-}
-
-// Zeroes the picked line (pick: -1 none, 0..127 row, 128..255 column) in S.
+// lane half h of wave c % 4), but the tile is indexed statically.  One asm
+// block walks a scalar branch tree on the block (p: 2 bits, m: 4 bits; -1
+// skips) down to 16 (row) or 4 (column) lane-masked selects, in place of one
+// select per entry (64).  The tree lives inside the asm: a C++ branch on the
+// block made the compiler keep a copy of the tile on each side.
 __device__ __forceinline__ void zero_line(const MMap &a, float (&S)[4][16], int pick)
 {
     const bool isrow = pick >= 0 && pick < D, iscol = pick >= D;
@@ -400,26 +349,73 @@ __device__ __forceinline__ void zero_line(const MMap &a, float (&S)[4][16], int 
     const int mm = __builtin_amdgcn_readfirstlane(iscol && a.w == (cc & 3) ? cc >> 3 : -1);
     const uint64_t rl = __builtin_amdgcn_ballot_w64(a.i == (pick & 31));
     const uint64_t cl = __builtin_amdgcn_ballot_w64(a.h == ((cc >> 2) & 1));
-    zero_row_if<0>(S[0], pr, rl);
-    zero_row_if<1>(S[1], pr, rl);
-    zero_row_if<2>(S[2], pr, rl);
-    zero_row_if<3>(S[3], pr, rl);
-    zero_col_if<0>(S, mm, cl);
-    zero_col_if<1>(S, mm, cl);
-    zero_col_if<2>(S, mm, cl);
-    zero_col_if<3>(S, mm, cl);
-    zero_col_if<4>(S, mm, cl);
-    zero_col_if<5>(S, mm, cl);
-    zero_col_if<6>(S, mm, cl);
-    zero_col_if<7>(S, mm, cl);
-    zero_col_if<8>(S, mm, cl);
-    zero_col_if<9>(S, mm, cl);
-    zero_col_if<10>(S, mm, cl);
-    zero_col_if<11>(S, mm, cl);
-    zero_col_if<12>(S, mm, cl);
-    zero_col_if<13>(S, mm, cl);
-    zero_col_if<14>(S, mm, cl);
-    zero_col_if<15>(S, mm, cl);
+    asm volatile("s_cmp_lt_i32 %[pr], 0\n\ts_cbranch_scc1 10f\n\ts_bitcmp1_b32 %[pr], 1\n\ts_cbranch_scc1 11f\n\t"
+                 "s_bitcmp1_b32 %[pr], 0\n\ts_cbranch_scc1 12f\n\tv_cndmask_b32_e64 %0, %0, 0, %[rl]\n\tv_cndmask_b32_e64 %1, %1, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %2, %2, 0, %[rl]\n\tv_cndmask_b32_e64 %3, %3, 0, %[rl]\n\tv_cndmask_b32_e64 %4, %4, 0, %[rl]\n\tv_cndmask_b32_e64 %5, %5, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %6, %6, 0, %[rl]\n\tv_cndmask_b32_e64 %7, %7, 0, %[rl]\n\tv_cndmask_b32_e64 %8, %8, 0, %[rl]\n\tv_cndmask_b32_e64 %9, %9, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %10, %10, 0, %[rl]\n\tv_cndmask_b32_e64 %11, %11, 0, %[rl]\n\tv_cndmask_b32_e64 %12, %12, 0, %[rl]\n\tv_cndmask_b32_e64 %13, %13, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %14, %14, 0, %[rl]\n\tv_cndmask_b32_e64 %15, %15, 0, %[rl]\n\ts_branch 10f\n\t12:\n\t"
+                 "v_cndmask_b32_e64 %16, %16, 0, %[rl]\n\tv_cndmask_b32_e64 %17, %17, 0, %[rl]\n\tv_cndmask_b32_e64 %18, %18, 0, %[rl]\n\tv_cndmask_b32_e64 %19, %19, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %20, %20, 0, %[rl]\n\tv_cndmask_b32_e64 %21, %21, 0, %[rl]\n\tv_cndmask_b32_e64 %22, %22, 0, %[rl]\n\tv_cndmask_b32_e64 %23, %23, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %24, %24, 0, %[rl]\n\tv_cndmask_b32_e64 %25, %25, 0, %[rl]\n\tv_cndmask_b32_e64 %26, %26, 0, %[rl]\n\tv_cndmask_b32_e64 %27, %27, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %28, %28, 0, %[rl]\n\tv_cndmask_b32_e64 %29, %29, 0, %[rl]\n\tv_cndmask_b32_e64 %30, %30, 0, %[rl]\n\tv_cndmask_b32_e64 %31, %31, 0, %[rl]\n\t"
+                 "s_branch 10f\n\t11:\n\ts_bitcmp1_b32 %[pr], 0\n\ts_cbranch_scc1 13f\n\t"
+                 "v_cndmask_b32_e64 %32, %32, 0, %[rl]\n\tv_cndmask_b32_e64 %33, %33, 0, %[rl]\n\tv_cndmask_b32_e64 %34, %34, 0, %[rl]\n\tv_cndmask_b32_e64 %35, %35, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %36, %36, 0, %[rl]\n\tv_cndmask_b32_e64 %37, %37, 0, %[rl]\n\tv_cndmask_b32_e64 %38, %38, 0, %[rl]\n\tv_cndmask_b32_e64 %39, %39, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %40, %40, 0, %[rl]\n\tv_cndmask_b32_e64 %41, %41, 0, %[rl]\n\tv_cndmask_b32_e64 %42, %42, 0, %[rl]\n\tv_cndmask_b32_e64 %43, %43, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %44, %44, 0, %[rl]\n\tv_cndmask_b32_e64 %45, %45, 0, %[rl]\n\tv_cndmask_b32_e64 %46, %46, 0, %[rl]\n\tv_cndmask_b32_e64 %47, %47, 0, %[rl]\n\t"
+                 "s_branch 10f\n\t13:\n\tv_cndmask_b32_e64 %48, %48, 0, %[rl]\n\tv_cndmask_b32_e64 %49, %49, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %50, %50, 0, %[rl]\n\tv_cndmask_b32_e64 %51, %51, 0, %[rl]\n\tv_cndmask_b32_e64 %52, %52, 0, %[rl]\n\tv_cndmask_b32_e64 %53, %53, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %54, %54, 0, %[rl]\n\tv_cndmask_b32_e64 %55, %55, 0, %[rl]\n\tv_cndmask_b32_e64 %56, %56, 0, %[rl]\n\tv_cndmask_b32_e64 %57, %57, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %58, %58, 0, %[rl]\n\tv_cndmask_b32_e64 %59, %59, 0, %[rl]\n\tv_cndmask_b32_e64 %60, %60, 0, %[rl]\n\tv_cndmask_b32_e64 %61, %61, 0, %[rl]\n\t"
+                 "v_cndmask_b32_e64 %62, %62, 0, %[rl]\n\tv_cndmask_b32_e64 %63, %63, 0, %[rl]\n\t10:\n\ts_cmp_lt_i32 %[mm], 0\n\t"
+                 "s_cbranch_scc1 14f\n\ts_bitcmp1_b32 %[mm], 3\n\ts_cbranch_scc1 15f\n\ts_bitcmp1_b32 %[mm], 2\n\t"
+                 "s_cbranch_scc1 16f\n\ts_bitcmp1_b32 %[mm], 1\n\ts_cbranch_scc1 17f\n\ts_bitcmp1_b32 %[mm], 0\n\t"
+                 "s_cbranch_scc1 18f\n\tv_cndmask_b32_e64 %0, %0, 0, %[cl]\n\tv_cndmask_b32_e64 %16, %16, 0, %[cl]\n\tv_cndmask_b32_e64 %32, %32, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %48, %48, 0, %[cl]\n\ts_branch 14f\n\t18:\n\tv_cndmask_b32_e64 %1, %1, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %17, %17, 0, %[cl]\n\tv_cndmask_b32_e64 %33, %33, 0, %[cl]\n\tv_cndmask_b32_e64 %49, %49, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "17:\n\ts_bitcmp1_b32 %[mm], 0\n\ts_cbranch_scc1 19f\n\tv_cndmask_b32_e64 %2, %2, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %18, %18, 0, %[cl]\n\tv_cndmask_b32_e64 %34, %34, 0, %[cl]\n\tv_cndmask_b32_e64 %50, %50, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "19:\n\tv_cndmask_b32_e64 %3, %3, 0, %[cl]\n\tv_cndmask_b32_e64 %19, %19, 0, %[cl]\n\tv_cndmask_b32_e64 %35, %35, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %51, %51, 0, %[cl]\n\ts_branch 14f\n\t16:\n\ts_bitcmp1_b32 %[mm], 1\n\t"
+                 "s_cbranch_scc1 20f\n\ts_bitcmp1_b32 %[mm], 0\n\ts_cbranch_scc1 21f\n\tv_cndmask_b32_e64 %4, %4, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %20, %20, 0, %[cl]\n\tv_cndmask_b32_e64 %36, %36, 0, %[cl]\n\tv_cndmask_b32_e64 %52, %52, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "21:\n\tv_cndmask_b32_e64 %5, %5, 0, %[cl]\n\tv_cndmask_b32_e64 %21, %21, 0, %[cl]\n\tv_cndmask_b32_e64 %37, %37, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %53, %53, 0, %[cl]\n\ts_branch 14f\n\t20:\n\ts_bitcmp1_b32 %[mm], 0\n\t"
+                 "s_cbranch_scc1 22f\n\tv_cndmask_b32_e64 %6, %6, 0, %[cl]\n\tv_cndmask_b32_e64 %22, %22, 0, %[cl]\n\tv_cndmask_b32_e64 %38, %38, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %54, %54, 0, %[cl]\n\ts_branch 14f\n\t22:\n\tv_cndmask_b32_e64 %7, %7, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %23, %23, 0, %[cl]\n\tv_cndmask_b32_e64 %39, %39, 0, %[cl]\n\tv_cndmask_b32_e64 %55, %55, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "15:\n\ts_bitcmp1_b32 %[mm], 2\n\ts_cbranch_scc1 23f\n\ts_bitcmp1_b32 %[mm], 1\n\t"
+                 "s_cbranch_scc1 24f\n\ts_bitcmp1_b32 %[mm], 0\n\ts_cbranch_scc1 25f\n\tv_cndmask_b32_e64 %8, %8, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %24, %24, 0, %[cl]\n\tv_cndmask_b32_e64 %40, %40, 0, %[cl]\n\tv_cndmask_b32_e64 %56, %56, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "25:\n\tv_cndmask_b32_e64 %9, %9, 0, %[cl]\n\tv_cndmask_b32_e64 %25, %25, 0, %[cl]\n\tv_cndmask_b32_e64 %41, %41, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %57, %57, 0, %[cl]\n\ts_branch 14f\n\t24:\n\ts_bitcmp1_b32 %[mm], 0\n\t"
+                 "s_cbranch_scc1 26f\n\tv_cndmask_b32_e64 %10, %10, 0, %[cl]\n\tv_cndmask_b32_e64 %26, %26, 0, %[cl]\n\tv_cndmask_b32_e64 %42, %42, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %58, %58, 0, %[cl]\n\ts_branch 14f\n\t26:\n\tv_cndmask_b32_e64 %11, %11, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %27, %27, 0, %[cl]\n\tv_cndmask_b32_e64 %43, %43, 0, %[cl]\n\tv_cndmask_b32_e64 %59, %59, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "23:\n\ts_bitcmp1_b32 %[mm], 1\n\ts_cbranch_scc1 27f\n\ts_bitcmp1_b32 %[mm], 0\n\t"
+                 "s_cbranch_scc1 28f\n\tv_cndmask_b32_e64 %12, %12, 0, %[cl]\n\tv_cndmask_b32_e64 %28, %28, 0, %[cl]\n\tv_cndmask_b32_e64 %44, %44, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %60, %60, 0, %[cl]\n\ts_branch 14f\n\t28:\n\tv_cndmask_b32_e64 %13, %13, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %29, %29, 0, %[cl]\n\tv_cndmask_b32_e64 %45, %45, 0, %[cl]\n\tv_cndmask_b32_e64 %61, %61, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "27:\n\ts_bitcmp1_b32 %[mm], 0\n\ts_cbranch_scc1 29f\n\tv_cndmask_b32_e64 %14, %14, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %30, %30, 0, %[cl]\n\tv_cndmask_b32_e64 %46, %46, 0, %[cl]\n\tv_cndmask_b32_e64 %62, %62, 0, %[cl]\n\ts_branch 14f\n\t"
+                 "29:\n\tv_cndmask_b32_e64 %15, %15, 0, %[cl]\n\tv_cndmask_b32_e64 %31, %31, 0, %[cl]\n\tv_cndmask_b32_e64 %47, %47, 0, %[cl]\n\t"
+                 "v_cndmask_b32_e64 %63, %63, 0, %[cl]\n\ts_branch 14f\n\t14:\n\t"
+                 : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[0][2]), "+v"(S[0][3]), "+v"(S[0][4]), "+v"(S[0][5]),
+                   "+v"(S[0][6]), "+v"(S[0][7]), "+v"(S[0][8]), "+v"(S[0][9]), "+v"(S[0][10]),
+                   "+v"(S[0][11]), "+v"(S[0][12]), "+v"(S[0][13]), "+v"(S[0][14]), "+v"(S[0][15]),
+                   "+v"(S[1][0]), "+v"(S[1][1]), "+v"(S[1][2]), "+v"(S[1][3]), "+v"(S[1][4]),
+                   "+v"(S[1][5]), "+v"(S[1][6]), "+v"(S[1][7]), "+v"(S[1][8]), "+v"(S[1][9]),
+                   "+v"(S[1][10]), "+v"(S[1][11]), "+v"(S[1][12]), "+v"(S[1][13]), "+v"(S[1][14]),
+                   "+v"(S[1][15]), "+v"(S[2][0]), "+v"(S[2][1]), "+v"(S[2][2]), "+v"(S[2][3]),
+                   "+v"(S[2][4]), "+v"(S[2][5]), "+v"(S[2][6]), "+v"(S[2][7]), "+v"(S[2][8]),
+                   "+v"(S[2][9]), "+v"(S[2][10]), "+v"(S[2][11]), "+v"(S[2][12]), "+v"(S[2][13]),
+                   "+v"(S[2][14]), "+v"(S[2][15]), "+v"(S[3][0]), "+v"(S[3][1]), "+v"(S[3][2]),
+                   "+v"(S[3][3]), "+v"(S[3][4]), "+v"(S[3][5]), "+v"(S[3][6]), "+v"(S[3][7]),
+                   "+v"(S[3][8]), "+v"(S[3][9]), "+v"(S[3][10]), "+v"(S[3][11]), "+v"(S[3][12]),
+                   "+v"(S[3][13]), "+v"(S[3][14]), "+v"(S[3][15])
+                 : [pr] "s"(pr), [mm] "s"(mm), [rl] "s"(rl), [cl] "s"(cl)
+                 : "scc");
 }
 
 // Low byte of the integer nearest to the exact product x * g (ties to even)
