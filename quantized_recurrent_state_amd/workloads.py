@@ -2,8 +2,10 @@
 
 This module draws the inputs that both the GPU library and the CPU oracle
 consume: initial fp32 states and per-token q, k, v, alpha, beta.  It holds
-none of the decode path's arithmetic (no recurrence, no quantization); every
-tensor it returns is an input.  The shapes follow a Qwen3.5-9B-like hybrid
+none of the quantized path's arithmetic (no windowed read, no record, no
+fold, no quantization); its one piece of arithmetic is the dense prefill
+that builds the initial states (below).  Every tensor it returns is an
+input.  The shapes follow a Qwen3.5-9B-like hybrid
 model: 24 GDN layers of 32 heads with a 128 x 128 state each ("Recurrent-state
 quantization for linear attention: a first GPU kernel", Background).  The
 recorded traces that page replays are not available, so these seeded
@@ -18,16 +20,23 @@ distributions stand in for them:
 Initial states:
   "gauss":   N(0, 0.02^2) entries with 2 random rows and 2 random columns
              scaled x50 (outlier rows and columns, LeapQuant 1 Introduction).
-  "writes":  a stand-in for a prefilled state: the sum of 64 rank-one writes
-             k_m v_m^T (k_m unit-norm Gaussian, v_m Gaussian) with geometric
-             weights 0.95^(63-m), then 1..4 distinct lines per head, each a
-             row or a column with probability 1/2, scaled by U[20, 100].
-             (The rank-one writes use no delta-rule correction: the generator
-             carries none of the path's arithmetic.)
-  "hard":    "writes" for heads < 24; heads 24..31 draw alpha from
-             z ~ N(-6.9, 0.25) (alpha ~ 0.999) and, in place of the lines
-             above, scale 2 rows and 2 columns x200 (a hard, slowly decaying
-             late layer).
+  "prefill": the state a prompt leaves behind: 512 prefill tokens, drawn
+             like the decode tokens but from a stream of their own, run
+             through the dense fp32 recurrence from S = 0 (rows decayed by
+             alpha, r = S^T k, u = beta (v - r), S += k u^T; with per-channel
+             decay alpha scales each key row), then 1..4 distinct lines per
+             head, each a row or a column with probability 1/2, scaled by
+             U[20, 100].
+  "hard":    "prefill" for heads < 24; heads 24..31 draw alpha from
+             z ~ N(-6.9, 0.25) (alpha ~ 0.999), in the prefill as in decode,
+             and, in place of the lines above, scale 2 rows and 2 columns
+             x200 (a hard, slowly decaying late layer).
+
+The prefill is the model's plain token step (the Gated DeltaNet recurrence of
+"Recurrent-state quantization for linear attention: a first GPU kernel",
+Background), written here with batched torch operations so that it can run on
+either device; it is part of the input recipe, not of the quantized path, and
+both sides of every comparison receive the tensor it produces.
 
 Gated inputs (the raw projections that the gate arithmetic of the gated
 entry points consumes) follow the Gated DeltaNet layer's parameterization:
@@ -82,7 +91,7 @@ class Workload:
     window: int = 16
     n_comp: int = 4
     in_dtype: str = "f32"          # "f32" or "bf16" for q, k, v
-    init: str = "writes"           # "gauss", "writes" or "hard"
+    init: str = "prefill"          # "gauss", "prefill" or "hard"
     seed: int = 0
     smoothing: bool = True
     sigma_floor: float = 1e-6
@@ -117,7 +126,9 @@ WORKLOADS = {
 }
 
 # stream ids
-_S_INIT, _S_TOK, _S_HARD, _S_GTOK, _S_GPAR = 1, 2, 3, 4, 5
+_S_INIT, _S_TOK, _S_HARD, _S_GTOK, _S_GPAR, _S_PRE = 1, 2, 3, 4, 5, 6
+
+PREFILL_TOKENS = 512
 
 
 def _normal(shape, g, device, mean=0.0, std=1.0):
@@ -146,12 +157,7 @@ def initial_state(wl, layer, device="cpu", return_lines=False):
         mult_c = torch.ones((B, H, D), device=device).scatter_(2, cols, 50.0)
         S = (S * mult_r.unsqueeze(-1) * mult_c.unsqueeze(-2)).contiguous()
         return (S, (rows, cols)) if return_lines else S
-    M = 64
-    kk = _normal((B, H, D, M), g, device)
-    kk = kk / kk.norm(dim=2, keepdim=True)
-    vv = _normal((B, H, M, D), g, device)
-    w = 0.95 ** torch.arange(M - 1, -1, -1, device=device, dtype=torch.float32)
-    S = torch.matmul(kk * w, vv.contiguous())
+    S = prefill_state(wl, layer, device).reshape(B, H, D, D)
     # per-head outlier lines: count U{1..4}, axis with p = 1/2, scale U[20, 100]
     count = torch.randint(1, 5, (B, H), generator=g, device=device)
     axis = torch.randint(0, 2, (B, H, 4), generator=g, device=device)
@@ -178,15 +184,16 @@ def initial_state(wl, layer, device="cpu", return_lines=False):
     return (S, (line, axis == 0, active)) if return_lines else S
 
 
-def token_inputs(wl, layer, token, device="cpu"):
+def token_inputs(wl, layer, token, device="cpu", stream=_S_TOK):
     """Inputs of one decode token for one layer.
 
     Returns q, k, v as [batch, heads, 128] in the workload's input dtype and
     alpha, beta as fp32 [batch, heads]; with per-channel decay alpha is
     [batch, heads, 128], drawn per channel from the same distribution.
+    `stream` separates the decode tokens from the prefill tokens.
     """
     B, H = wl.batch, wl.heads
-    g = _gen(device, wl.seed, _S_TOK, layer, token)
+    g = _gen(device, wl.seed, stream, layer, token)
     q = _normal((B, H, D), g, device)
     k = _normal((B, H, D), g, device)
     v = _normal((B, H, D), g, device)
@@ -205,6 +212,23 @@ def token_inputs(wl, layer, token, device="cpu"):
     dt = wl.torch_dtype()
     return (q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous(),
             alpha.contiguous(), beta.contiguous())
+
+
+def prefill_state(wl, layer, device="cpu", tokens=PREFILL_TOKENS):
+    """fp32 state [batch * heads, 128, 128] after `tokens` prefill tokens of
+    the dense recurrence from zero, in token order.  The tokens come from
+    token_inputs on the prefill stream (bf16 q/k/v widened exactly)."""
+    N = wl.batch * wl.heads
+    S = torch.zeros((N, D, D), dtype=torch.float32, device=device)
+    for t in range(tokens):
+        _, k, v, alpha, beta = token_inputs(wl, layer, t, device=device, stream=_S_PRE)
+        k = k.reshape(N, D).to(torch.float32).contiguous()
+        v = v.reshape(N, D).to(torch.float32)
+        S.mul_(alpha.reshape((N, D, 1) if wl.decay == "channel" else (N, 1, 1)))
+        r = torch.bmm(k.unsqueeze(1), S).squeeze(1)
+        u = beta.reshape(N, 1) * (v - r)
+        S.baddbmm_(k.unsqueeze(2), u.unsqueeze(1))
+    return S
 
 
 def gate_params(wl, layer, device="cpu"):

@@ -320,3 +320,79 @@ def _compare_staggered(L, heads_ref, sample, n_of, rep):
             rep.fp("rec_gamma", rg[s, :n], h.gam[:n])
             rep.fp("rec_k", rk[s, :n], h.rk[:n])
             rep.fp("rec_u", ru[s, :n], h.ru[:n])
+
+
+
+class Twin:
+    """One layer of batch 1 x H heads on the GPU beside H oracle heads, both
+    started from an explicit initial state S0 (fp32 [H,128,128]) and stepped
+    with explicit tokens (q, k, v [H,128], alpha [H], beta [H] as numpy fp32,
+    bf16-valued when in_dtype is bf16).  Every step compares what it
+    changed against the oracle into `rep`."""
+
+    def __init__(self, S0, C=4, W=16, smoothing=True, sigma_floor=1e-6, in_dtype="f32", rep=None, device="cuda"):
+        self.rep = rep or Report()
+        self.dev = torch.device(device)
+        S0 = np.ascontiguousarray(S0, np.float32)
+        self.H, self.W = S0.shape[0], W
+        self.cfg = lq.make_config(1, self.H, W, C, smoothing, sigma_floor, in_dtype)
+        self.L = lq.Layer(self.cfg, self.dev)
+        lq.leapq_init_state(self.L, torch.from_numpy(S0).to(self.dev))
+        self.refs = [oracle.Head(C, W, smoothing, sigma_floor).init(S0[h]) for h in range(self.H)]
+        self.tdt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+        self.o = torch.empty(self.H, D, dtype=torch.float32, device=self.dev)
+        self.compare()
+
+    def compare(self):
+        torch.cuda.synchronize(self.dev)
+        compare_state(self.L, self.refs, list(range(self.H)), self.rep)
+
+    def _dev(self, x, dtype):
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(self.dev).to(dtype).contiguous()
+
+    def append(self, tok, fused=False):
+        """One token; with fused it must be the window's last, and the GPU
+        takes it and the fold in one leapq_append_fold call."""
+        q, k, v, a, b = tok
+        qd, kd, vd = (self._dev(x, self.tdt) for x in (q, k, v))
+        ad, bd = self._dev(a, torch.float32), self._dev(b, torch.float32)
+        if fused:
+            assert self.L.n_records == self.W - 1
+            lq.leapq_append_fold(self.L, qd, kd, vd, ad, bd, self.o)
+        else:
+            lq.leapq_append(self.L, qd, kd, vd, ad, bd, self.o)
+        outs = [self.refs[h].append(q[h], k[h], v[h], a[h], b[h])[0] for h in range(self.H)]
+        self.rep.fp("o", self.o.cpu().numpy(), np.stack(outs))
+        if fused:
+            for r in self.refs:
+                r.fold()
+        self.compare()
+
+    def current(self):
+        """(GPU, oracle) current states, dequant view 2 [H,128,128]."""
+        cur = torch.empty(self.H, D, D, dtype=torch.float32, device=self.dev)
+        lq.leapq_dequant(self.L, lq.LEAPQ_DEQ_CURRENT, cur)
+        return cur.cpu().numpy(), np.stack([r.dequant(2) for r in self.refs])
+
+    def fold(self, check_current=True):
+        if check_current:
+            got, ref = self.current()
+            self.rep.fp("current", got, ref)
+        lq.leapq_fold(self.L)
+        for r in self.refs:
+            r.fold()
+        self.compare()
+
+
+def run_custom(S0, toks, fused=False, check_current=True, **kw):
+    """Twin run through a list of tokens, folding whenever the window is
+    full (fused: the last token and its fold in one call; otherwise a
+    separate fold, after comparing the full current state when
+    check_current).  Returns the Twin."""
+    tw = Twin(S0, **kw)
+    for tok in toks:
+        last = fused and tw.L.n_records == tw.W - 1
+        tw.append(tok, fused=last)
+        if not last and tw.L.n_records == tw.W:
+            tw.fold(check_current)
+    return tw

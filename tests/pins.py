@@ -221,6 +221,19 @@ def pin_planted_outliers(L):
         assert set(int(i) for i in head.idx) == want, (h_, head.idx, want)
 
 
+def pin_planted_prefill_lines(L):
+    """The prefilled initial states (512 dense tokens from zero) carry 1..4
+    injected lines x20..100 per head; with C = 4 each injected line is among
+    the compensators picked at init (planted ground truth)."""
+    wl = workloads.Workload("pin", 1, 1, 8, 16, seed=1)
+    S0, (line, is_row, active) = workloads.initial_state(wl, 0, return_lines=True)
+    for h_ in range(8):
+        want = {int(line[0, h_, j]) + (0 if bool(is_row[0, h_, j]) else D)
+                for j in range(4) if bool(active[0, h_, j])}
+        head = oracle.Head(C=4, L=L).init(S0.numpy()[0, h_])
+        assert want <= set(int(i) for i in head.idx), (h_, head.idx, want)
+
+
 def pin_greedy_bruteforce(L):
     """Every greedy pick is the float64 argmax of the line energies of the
     matrix left after the earlier picks, unless the top two are within 1e-6."""
@@ -299,7 +312,7 @@ def pin_window_vs_dense_f64(L):
     """Within a window the windowed path equals the dense recurrence started
     from the dequantized boundary (exact in real arithmetic): o, u and the
     rebuilt state agree to 1e-5 relative."""
-    for seed, init in ((0, "gauss"), (1, "writes"), (4, "hard")):
+    for seed, init in ((0, "gauss"), (1, "prefill"), (4, "hard")):
         S0, toks = tiny_inputs(seed=seed, tokens=16, heads=1, init=init)
         for C, sm in ((4, True), (0, False), (2, True)):
             _, eo, eu, es = _window(L, S0[0], toks, C=C, smoothing=sm)
@@ -324,7 +337,7 @@ def pin_beta_zero(L):
 def pin_overwrite_identity(L):
     """beta = 1 and q = k with |k| = 1 read back exactly what was written:
     o = (alpha S)^T k + (k.k)(v - (alpha S)^T k) = v."""
-    S0, toks = tiny_inputs(seed=6, tokens=16, init="writes")
+    S0, toks = tiny_inputs(seed=6, tokens=16, init="prefill")
     h = oracle.Head(C=4, L=L).init(S0[0])
     for (_, k, v, a, _) in toks:
         k64 = k.astype(np.float64)
@@ -337,7 +350,7 @@ def pin_fold_invariants(L):
     """After a fold the buffer is empty and the current state equals the
     boundary; the fold's new boundary is within the quantization bound of the
     state rebuilt before it."""
-    S0, toks = tiny_inputs(seed=8, tokens=16, init="writes")
+    S0, toks = tiny_inputs(seed=8, tokens=16, init="prefill")
     h = oracle.Head(C=4, L=L).init(S0[0])
     for (q, k, v, a, b) in toks:
         h.append(q, k, v, a, b)
@@ -354,7 +367,7 @@ def pin_xor_equivariance(L):
     """Relabelling key rows (with k and q) or value columns (with v) by
     i -> i XOR m, 0 < m < 64, is an automorphism of the canonical trees, so
     every output and every state field is permuted exactly."""
-    S0, toks = tiny_inputs(seed=9, tokens=16, init="writes")
+    S0, toks = tiny_inputs(seed=9, tokens=16, init="prefill")
     S = S0[0]
     for m in (1, 22, 63):
         p = np.arange(D) ^ m
@@ -406,7 +419,7 @@ def pin_dense_steps(L):
     """The fp32 and fp64 dense steps match the float64 numpy recurrence, and
     the bf16 step equals the fp32 step on the widened state followed by
     torch's round-to-nearest-even bf16 conversion."""
-    S0, toks = tiny_inputs(seed=12, tokens=8, init="writes")
+    S0, toks = tiny_inputs(seed=12, tokens=8, init="prefill")
     S32 = S0[0].copy()
     S64 = S0[0].astype(np.float64)
     Sn = S0[0].astype(np.float64)
@@ -431,7 +444,7 @@ def pin_dense_steps(L):
 def pin_window_one(L):
     """W=1 quantizes after every token: each fold's input state equals the
     dense step from the previous boundary."""
-    S0, toks = tiny_inputs(seed=13, tokens=4, init="writes")
+    S0, toks = tiny_inputs(seed=13, tokens=4, init="prefill")
     h = oracle.Head(C=4, W=1, L=L).init(S0[0])
     for (q, k, v, a, b) in toks:
         S = h.dequant(1).astype(np.float64)
@@ -821,6 +834,7 @@ def pin_block_window_and_fold(L):
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_round_exact_product_once, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
+    pin_planted_prefill_lines,
     pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,

@@ -34,7 +34,7 @@ def _finish(rep):
     ("f32", _wl("tiny", seed=80), 64, False),
     ("bf16_fused", _wl("tiny", in_dtype="bf16", seed=81), 48, True),
     ("W20_two_launches", _wl("tiny", window=20, seed=82), 40, True),
-    ("W64", _wl("tiny", window=64, seed=83, init="writes"), 64, False),
+    ("W64", _wl("tiny", window=64, seed=83, init="prefill"), 64, False),
     ("C8", _wl("tiny", n_comp=8, seed=84), 32, True),
     ("ragged_heads", _wl("tiny", batch=3, heads=5, seed=85), 32, True),
 ])
@@ -47,7 +47,7 @@ def test_bf16_records_against_oracle(name, wl, tokens, fused):
 
 
 def test_bf16_records_dequant_current():
-    wl = _wl("tiny", seed=86, init="writes")
+    wl = _wl("tiny", seed=86, init="prefill")
     H = wl.batch * wl.heads
     rep, L, refs = run_layer(wl, tokens=23, rec_u="bf16")
     out = torch.empty(H, D, D, device="cuda")

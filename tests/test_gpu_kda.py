@@ -40,7 +40,7 @@ def _finish(rep):
     ("bf16", _wl("tiny_kda", in_dtype="bf16", seed=62), 37, False),
     ("W1", _wl("tiny_kda", window=1, seed=63), 6, False),
     ("W20_two_launches", _wl("tiny_kda", window=20, seed=64), 40, True),
-    ("W64", _wl("tiny_kda", window=64, seed=65, init="writes"), 64, False),
+    ("W64", _wl("tiny_kda", window=64, seed=65, init="prefill"), 64, False),
     ("C0_nosmooth", _wl("tiny_kda", n_comp=0, smoothing=False, seed=66), 32, True),
     ("C8", _wl("tiny_kda", n_comp=8, seed=67), 32, False),
     ("ragged_heads", _wl("tiny_kda", batch=3, heads=5, seed=68), 32, True),
@@ -53,7 +53,7 @@ def test_kda_against_oracle(name, wl, tokens, fused):
 
 
 def test_kda_dequant_views():
-    wl = _wl("tiny_kda", seed=69, init="writes")
+    wl = _wl("tiny_kda", seed=69, init="prefill")
     H = wl.batch * wl.heads
     rep, L, refs = run_layer(wl, tokens=21)  # one fold, then 5 records
     assert L.n_records == 5
@@ -68,7 +68,7 @@ def test_kda_dequant_views():
 
 def test_kda_dense_baseline():
     """Dense fp32-state KDA decode against the oracle's dense step, 8 tokens."""
-    wl = _wl("tiny_kda", batch=2, heads=16, init="writes", seed=70)
+    wl = _wl("tiny_kda", batch=2, heads=16, init="prefill", seed=70)
     H = wl.batch * wl.heads
     cfg = lq.make_config(wl.batch, wl.heads, decay="channel")
     S0 = workloads.initial_state(wl, 0).reshape(H, D, D)

@@ -58,10 +58,11 @@ def test_window_tiny_bf16_inputs():
 
 
 def test_window_b32_sampled():
-    """Batch 32 x 32 heads (1024 heads, several tiles and XCD rounds), 64
-    sampled heads through 64 tokens (4 folds)."""
+    """Batch 32 x 32 heads (1024 heads, several tiles and XCD rounds) from the
+    prefilled, outlier-injected initial state: 64 sampled heads through all
+    256 tokens (16 folds)."""
     sample = list(range(0, 1024, 16))
-    rep, _, _ = run_layer(WL["b32"], tokens=64, sample=sample, check_every_token=False)
+    rep, _, _ = run_layer(WL["b32"], sample=sample, gen_device="cuda", check_every_token=False)
     _finish(rep)
 
 
@@ -74,7 +75,7 @@ def test_window_b32_sampled():
     ("W64", dict(window=64), 70, None),
     ("partial_window", dict(), 23, {5, 6, 17}),
     ("ragged_heads", dict(batch=3, heads=5), 18, None),
-    ("one_head", dict(batch=1, heads=1, init="writes"), 17, None),
+    ("one_head", dict(batch=1, heads=1, init="prefill"), 17, None),
     ("hard", dict(init="hard", batch=1, heads=32, seed=4), 33, None),
 ])
 def test_edge_cases(name, kw, tokens, fold_at):
@@ -158,7 +159,7 @@ def test_symmetric_states_tie_rows_and_columns():
 
 
 def test_dequant_all_views():
-    wl = _wl("tiny", seed=32, init="writes")
+    wl = _wl("tiny", seed=32, init="prefill")
     H = wl.batch * wl.heads
     rep, L, refs = run_layer(wl, tokens=21)  # one fold, then 5 records
     assert L.n_records == 5
@@ -175,7 +176,7 @@ def test_dequant_all_views():
                                                   (torch.bfloat16, "f32"), (torch.bfloat16, "bf16")])
 def test_gdn_baselines(state_dtype, in_dtype):
     """Dense per-token decode against the oracle's dense step, 8 tokens."""
-    wl = _wl("tiny", batch=2, heads=16, init="writes", in_dtype=in_dtype, seed=33)
+    wl = _wl("tiny", batch=2, heads=16, init="prefill", in_dtype=in_dtype, seed=33)
     H = wl.batch * wl.heads
     cfg = lq.make_config(wl.batch, wl.heads, in_dtype=in_dtype)
     S0 = workloads.initial_state(wl, 0).reshape(H, D, D)

@@ -41,7 +41,7 @@ def _finish(rep):
     ("C1_nosmooth", _wl("tiny", n_comp=1, smoothing=False, seed=94), 20, True, None),
     ("C0", _wl("tiny", n_comp=0, seed=95), 20, True, None),
     ("partial_window", _wl("tiny", seed=96), 23, False, {5, 6, 17}),
-    ("ragged_heads_writes", _wl("tiny", batch=3, heads=5, init="writes", seed=97), 18, True, None),
+    ("ragged_heads_prefill", _wl("tiny", batch=3, heads=5, init="prefill", seed=97), 18, True, None),
     ("hard", _wl("tiny", init="hard", batch=1, heads=32, seed=4), 33, True, None),
 ])
 def test_rank1_against_oracle(name, wl, tokens, fused, fold_at):
@@ -53,7 +53,7 @@ def test_rank1_against_oracle(name, wl, tokens, fused, fold_at):
 
 
 def test_rank1_dequant_views():
-    wl = _wl("tiny", seed=98, init="writes")
+    wl = _wl("tiny", seed=98, init="prefill")
     H = wl.batch * wl.heads
     rep, L, refs = run_layer(wl, tokens=23, fit="rank1")
     out = torch.empty(H, D, D, device="cuda")
