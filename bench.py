@@ -24,6 +24,12 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s and HBM GB/s (% of peak), append+fold, 24Lx32H, batch 512"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_b512_traffic.json")
+VALU_FILE = os.path.join(ROOT, "profiles", "append_fold_b512_valu.json")
+# plain (unpacked) fp32 VALU issue rate: 256 CUs x 4 SIMDs x 16 lanes per
+# cycle x 2.4 GHz, in lane-operations per second
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+N_SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
 
 
 def log(msg):
@@ -62,6 +68,11 @@ def kernel_sha():
     return sha()
 
 
+def fold_sha():
+    from quantized_recurrent_state_amd.profiling import FOLD_SOURCES, kernel_sha as sha
+    return sha(FOLD_SOURCES)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -86,14 +97,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     log(f"[bench] {wl.name}: {wl.notes}; {Lyr} layers x {H} heads; device {torch.cuda.get_device_name(0)}")
 
-    # ---- state and inputs, resident before timing
+    # ---- state and inputs, resident before timing.  The initial states (512
+    # prefill tokens of the dense fp32 recurrence per layer, then the outlier
+    # lines) are built once and shared by every section below.
+    t_pre = time.perf_counter()
+    S0s = []
+    for l in range(Lyr):
+        S0s.append(workloads.initial_state(wl, l, device=dev).reshape(H, D, D))
+        torch.cuda.synchronize(dev)
+        log(f"[bench] initial state of layer {l + 1}/{Lyr} built "
+            f"({workloads.PREFILL_TOKENS} prefill tokens, {time.perf_counter() - t_pre:.1f} s so far)")
     cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype)
     layers = []
     for l in range(Lyr):
         L = lq.Layer(cfg, dev)
-        S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
-        lq.leapq_init_state(L, S0)
-        del S0
+        lq.leapq_init_state(L, S0s[l])
         layers.append(L)
     pool = []
     for l in range(Lyr):
@@ -202,6 +220,30 @@ def main():
         f"({fold_gbps:.0f} GB/s), last append + fold in one launch {fused_us:.1f} us; fold share "
         f"{100 * share:.1f}% ({100 * share_sep:.1f}% with a separate fold), whole path {path_gbps:.0f} GB/s")
 
+    # the fused launch (the window's last append and the fold) against the
+    # plain VALU issue rate: VALU instructions x 64 lanes per launch from the
+    # recorded counters (while the kernels' sources are unchanged) over the
+    # launch time measured here; matrix-core busy time beside it
+    fold_roofline = {"bound": "alu", "kernel": "leapq append_fold (fused last append + fold)",
+                     "achieved_gbps_algorithmic": fold_gbps, "peak": VALU_PEAK_LANE_OPS / 1e12,
+                     "unit": "T lane-ops/s", "achieved": None, "frac": None}
+    if os.path.exists(VALU_FILE) and fused_us:
+        with open(VALU_FILE) as f:
+            vc = json.load(f)
+        if vc.get("kernel_sha") == fold_sha() and vc.get("workload") == wl.name:
+            lane_ops = vc["insts_valu_per_launch"] * 64
+            fold_roofline.update({
+                "achieved": lane_ops / (fused_us * 1e-6) / 1e12,
+                "frac": lane_ops / (fused_us * 1e-6) / VALU_PEAK_LANE_OPS,
+                "valu_lane_ops_per_launch": lane_ops,
+                "mfma_busy_frac": vc["mfma_busy_cycles_per_launch"] / (N_SIMDS * fused_us * 1e-6 * CLOCK_HZ),
+                "mfma_valu_coexec_cycles_per_launch": vc.get("mfma_coexec_cycles_per_launch"),
+                "counters": os.path.relpath(VALU_FILE, ROOT)})
+
+    copy_gbps = copy_ceiling(torch, stream)
+    log(f"[bench] streaming ceiling (1 GiB elementwise y = -x, 4 B read + 4 B written per element): "
+        f"{copy_gbps:.0f} GB/s ({100 * copy_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -217,9 +259,7 @@ def main():
         glayers, gpool, gates = [], [], []
         for l in range(Lyr):
             L = lq.Layer(gcfg, dev)
-            S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
-            lq.leapq_init_state(L, S0)
-            del S0
+            lq.leapq_init_state(L, S0s[l])
             glayers.append(L)
             gates.append(lq.Gate(*workloads.gate_params(wl, l, device=dev)))
             toks = []
@@ -274,9 +314,7 @@ def main():
         vlayers = []
         for l in range(Lyr):
             L = lq.Layer(vcfg, dev)
-            S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
-            lq.leapq_init_state(L, S0)
-            del S0
+            lq.leapq_init_state(L, S0s[l])
             vlayers.append(L)
 
         def vwindow(ev=None):
@@ -354,9 +392,7 @@ def main():
         slayers = []
         for l in range(Lyr):
             L = lq.Layer(cfg, dev)
-            S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
-            lq.leapq_init_state(L, S0)
-            del S0
+            lq.leapq_init_state(L, S0s[l])
             slayers.append(L)
         ph = np.arange(B) % W
         # spread the phases: request b takes no token in the first W - ph[b] steps
@@ -422,12 +458,11 @@ def main():
     if not args.no_kda and kname in workloads.WORKLOADS:
         kwl = workloads.WORKLOADS[kname]
         kcfg = lq.make_config(B, Hh, W, C, kwl.smoothing, kwl.sigma_floor, kwl.in_dtype, decay="channel")
-        klayers, kpool = [], []
+        klayers, kpool, kS0s = [], [], []
         for l in range(Lyr):
+            kS0s.append(workloads.initial_state(kwl, l, device=dev).reshape(H, D, D))
             L = lq.Layer(kcfg, dev)
-            S0 = workloads.initial_state(kwl, l, device=dev).reshape(H, D, D)
-            lq.leapq_init_state(L, S0)
-            del S0
+            lq.leapq_init_state(L, kS0s[l])
             klayers.append(L)
             toks = []
             for pos in range(W):
@@ -477,11 +512,7 @@ def main():
             f"{kda['append_fold_us']:.1f} us")
         if not args.no_baselines:
             for name, sdt, sbytes in (("fp32_state", torch.float32, 4), ("bf16_state", torch.bfloat16, 2)):
-                states = []
-                for l in range(Lyr):
-                    S0 = workloads.initial_state(kwl, l, device=dev).reshape(H, D, D)
-                    states.append(S0.to(sdt).contiguous())
-                    del S0
+                states = [kS0s[l].to(sdt, copy=True).contiguous() for l in range(Lyr)]
                 for pos in range(2):
                     for l in range(Lyr):
                         q, k, v, a, b = kpool[l][pos]
@@ -503,7 +534,7 @@ def main():
                 kda[f"speedup_vs_{name}"] = kda["tokens_per_s"] / kda[name]["tokens_per_s"]
                 log(f"[bench] kda baseline {name}: {ms_tok:.3f} ms/token, {B / (ms_tok * 1e-3):,.0f} tokens/s")
                 del states
-        del kpool
+        del kpool, kS0s
         torch.cuda.empty_cache()
 
     # ---- baselines at the same shape: dense fp32-state and bf16-state decode
@@ -511,11 +542,8 @@ def main():
     if not args.no_baselines:
         baselines = {}
         for name, sdt, sbytes in (("fp32_state", torch.float32, 4), ("bf16_state", torch.bfloat16, 2)):
-            states = []
-            for l in range(Lyr):
-                S0 = workloads.initial_state(wl, l, device=dev).reshape(H, D, D)
-                states.append(S0.to(sdt).contiguous())
-                del S0
+            # the dense decode updates its state in place: a copy of each S0
+            states = [S0s[l].to(sdt, copy=True).contiguous() for l in range(Lyr)]
             for pos in range(2):  # warmup
                 for l in range(Lyr):
                     q, k, v, a, b = pool[l][pos]
@@ -542,7 +570,7 @@ def main():
     # ---- CPU baseline: the oracle on one layer's heads for one window
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, pool, args.cpu_threads)
+        cpu = cpu_baseline(wl, pool, S0s[0].cpu().numpy(), args.cpu_threads)
 
     result = {
         "metric": METRIC,
@@ -574,8 +602,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "leapq append", "achieved": append_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": append_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
-                     "bytes_per_launch_algorithmic": app_bytes_avg},
-        "fold_roofline": {"bound": "alu", "achieved_gbps_algorithmic": fold_gbps},
+                     "bytes_per_launch_algorithmic": app_bytes_avg,
+                     "copy_ceiling_gbps": copy_gbps, "frac_of_copy_ceiling": append_gbps / copy_gbps},
+        "fold_roofline": fold_roofline,
         "gated": gated,
         "kda": kda,
         "bf16_record_corrections": bf16rec,
@@ -592,21 +621,48 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, pool, threads):
+def copy_ceiling(torch, stream, mib=1024, reps=8):
+    """GB/s of a plain elementwise kernel over `mib` MiB of fp32 (one read and
+    one write per element), events on the launch stream: the streaming rate
+    this GPU sustains in practice, beside the 8 TB/s of the data sheet."""
+    n = mib * 2**20 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x, y
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, pool, S0, threads):
     """The oracle (unmodified, single-threaded per head; heads spread over a
     thread pool) on layer 0's heads for one whole window, scaled to the
     workload's tokens/s."""
     import concurrent.futures as cf
 
     import numpy as np
-    import torch
 
     import oracle
-    from quantized_recurrent_state_amd import workloads
 
-    D = 128
     H = wl.batch * wl.heads
-    S0 = workloads.initial_state(wl, 0, device="cuda").reshape(H, D, D).cpu().numpy()
     toks = [tuple(x.float().cpu().numpy() for x in pool[0][pos]) for pos in range(wl.window)]
     heads = list(range(H))
 
@@ -632,8 +688,9 @@ def cpu_baseline(wl, pool, threads):
     log(f"[bench] cpu baseline: {dt:.2f} s for one layer-window -> {tok_s:.1f} tokens/s")
     return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"layer 0 only ({H} heads), one window (16 appends + fold per head), "
-                      f"{dt:.2f} s wall; scaled by {scale} layers",
-            "host_cpus": os.cpu_count()}
+                      f"{dt:.2f} s wall; scaled by {scale} layers (a bounded sample: the full "
+                      f"{scale}-layer window would hold the run for about {dt * scale / 60:.0f} minutes)",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 if __name__ == "__main__":

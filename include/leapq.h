@@ -32,6 +32,10 @@
  *   - Tensors are dense, row-major, contiguous; "heads" below means
  *     batch * heads, and head h's data starts at h * (per-head size).
  *   - A leapq_layer must not be used from two streams at once.
+ *   - Inputs and states must be finite.  With a NaN or an infinity in S0,
+ *     q, k, v, alpha, beta or the gate arguments the results are unspecified
+ *     (no error is reported); in particular the compensator picks, which
+ *     compare line energies, need not follow the tie rule.
  */
 #ifndef LEAPQ_H
 #define LEAPQ_H
@@ -106,8 +110,10 @@ typedef struct leapq_config {
     int32_t reserved[3]; /* must be zero */
 } leapq_config;
 
-/* Byte layout of one layer's state buffer.  Sections are "structure of
- * arrays" over heads; each section starts on a 256-byte boundary and head h's
+/* Byte layout of one layer's state buffer ("LeapQuant" 4.3: the boundary
+ * state with its scales and compensators costs about 1.19 bytes per state
+ * element, against 4 for fp32).  Sections are "structure of arrays" over
+ * heads; each section starts on a 256-byte boundary and head h's
  * slice starts at off_X + h * (per-head size of X).  With
  * iperm(x) = x ^ (x & 4 ? 3 : 0) for x < 32:
  *   codes     int8  [heads][16384]     the code of (key row r, value column c)
@@ -159,7 +165,14 @@ typedef struct leapq_layer {
     int32_t reserved;
 } leapq_layer;
 
-/* Fills *out with the layout for cfg.  Host only; touches no device. */
+/* Fills *out with the layout for cfg ("LeapQuant" 4.3: int8 codes with
+ * per-row and per-column scales and fp32 compensators, 19,472 bytes per
+ * 128 x 128 head at C = 4, the 1.19 bytes per element it reports; plus the
+ * window's records, "Recurrent-state quantization for linear attention: a
+ * first GPU kernel", Why rounding the state is difficult: recent updates
+ * kept in higher precision).  Host only; touches no device.  Returns
+ * LEAPQ_ERR_NULL for a NULL argument and the configuration statuses above
+ * for an invalid cfg. */
 int32_t leapq_query_layout(const leapq_config *cfg, leapq_layout *out);
 
 /* Quantizes the caller's fp32 states S0 [heads][128][128] (device) into the
@@ -218,7 +231,9 @@ typedef struct leapq_gate {
     int32_t reserved[2];  /* must be zero */
 } leapq_gate;
 
-/* leapq_append with the gate arithmetic fused in front: a, b [heads] fp32
+/* leapq_append with the gate arithmetic fused in front ("Recurrent-state
+ * quantization for linear attention: a first GPU kernel", Results: the
+ * kernel timed with gate arithmetic): a, b [heads] fp32
  * (device) are the raw decay and step-size projections of this token, and q,
  * k are the raw projections (normalized in the kernel when qk_norm = 1).
  * Everything else, including the record written and the output, is as for
@@ -230,7 +245,10 @@ typedef struct leapq_gate {
 int32_t leapq_append_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
                            const void *v, const float *a, const float *b, float *o, void *stream);
 
-/* leapq_append_fold with the gate arithmetic of leapq_append_gated. */
+/* leapq_append_fold with the gate arithmetic of leapq_append_gated
+ * ("Recurrent-state quantization for linear attention: a first GPU kernel",
+ * Results: gate arithmetic; What we built: the append, then the fold).
+ * Arguments, requirements and statuses as for the two calls it joins. */
 int32_t leapq_append_fold_gated(leapq_layer *layer, const leapq_gate *gate, const void *q, const void *k,
                                 const void *v, const float *a, const float *b, float *o, void *stream);
 
@@ -269,11 +287,20 @@ int32_t leapq_fold(leapq_layer *layer, void *stream);
 
 /* Writes an fp32 [heads][128][128] view of the layer's state to S_out
  * (device): what = LEAPQ_DEQ_RESIDUAL, LEAPQ_DEQ_BOUNDARY or LEAPQ_DEQ_CURRENT
- * (see above).  Reads the state only. */
+ * (see above; "LeapQuant" B.3: the residual is rescaled in original
+ * coordinates and the compensators added in full precision; B.2: the state
+ * after n records of the window is the decayed boundary plus the records'
+ * rank-one terms).  Reads the state only; what outside {0, 1, 2} gives
+ * LEAPQ_ERR_RANGE.  The current view runs the fold's own rebuild. */
 int32_t leapq_dequant(const leapq_layer *layer, int32_t what, float *S_out, void *stream);
 
 /* Unquantized per-token GDN decode on a dense state, in place (the fp32-state
- * and bf16-state baselines).  S [heads][128][128] in state_dtype (device,
+ * and bf16-state baselines: "Recurrent-state quantization for linear
+ * attention: a first GPU kernel", Background: per token the state is decayed,
+ * read with the key, corrected and written back as a rank-one update, and the
+ * output read, and Results: the kernels timed with an fp32 state;
+ * "LeapQuant" 3.1 and App. A: the delta-rule recurrence with a scalar or
+ * diagonal decay).  S [heads][128][128] in state_dtype (device,
  * natural row-major layout); q, k, v in cfg->in_dtype; alpha, beta fp32;
  * o fp32.  Per token: S = alpha S (row r scaled by alpha[r] with cfg->decay
  * = LEAPQ_DECAY_CHANNEL, alpha then [heads][128]); u = beta (v - S^T k);
@@ -284,10 +311,12 @@ int32_t leapq_gdn_decode(const leapq_config *cfg, int32_t state_dtype, void *S, 
                          const void *k, const void *v, const float *alpha, const float *beta,
                          float *o, void *stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (a utility with no passage behind
+ * it; unknown codes give "unknown status"). */
 const char *leapq_status_str(int32_t status);
 
-/* Library version: major * 10000 + minor * 100 + patch. */
+/* Library version: major * 10000 + minor * 100 + patch (a utility with no
+ * passage behind it). */
 int32_t leapq_version(void);
 
 #ifdef __cplusplus

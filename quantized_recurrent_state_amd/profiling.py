@@ -16,6 +16,11 @@ Reductions (CPU only, read the CSV files rocprofv3 wrote):
       --kernel 'k_append<' --fetch F.csv --write W.csv \
       --copy-fetch CF.csv --copy-write CW.csv --copy-mib 1024 --workload b512 --out X.json
   python3 -m quantized_recurrent_state_amd.profiling stats --csv kernel_stats.csv
+  python3 -m quantized_recurrent_state_amd.profiling valu --kernel k_append_fold \
+      --csv SQ.csv [--csv SQ2.csv] --workload b512 --out X.json
+      VALU instructions, waves and matrix-core busy cycles per launch from
+      SQ_INSTS_VALU, SQ_WAVES, SQ_VALU_MFMA_BUSY_CYCLES (and, when present,
+      SQ_VALU_MFMA_COEXEC_CYCLES, SQ_INSTS_MFMA) counter runs
 """
 import argparse
 import csv
@@ -30,6 +35,8 @@ ROOT = os.path.dirname(PKG)
 
 # the sources of the append kernel: its traffic figure holds while they are unchanged
 APPEND_SOURCES = ("leapq_append.hip", "leapq_append_dev.h", "leapq_device.h")
+# the sources of the fold kernels (the fused last append + fold includes the append's)
+FOLD_SOURCES = ("leapq_fold.hip", "leapq_append_dev.h", "leapq_device.h")
 
 
 def kernel_sha(srcs=APPEND_SOURCES):
@@ -136,6 +143,28 @@ def traffic(args):
     print(json.dumps(out, indent=1))
 
 
+def valu(args):
+    """Per-launch VALU instructions, waves and matrix-core cycles of `kernel`."""
+    want = {"SQ_INSTS_VALU": "insts_valu_per_launch", "SQ_WAVES": "waves_per_launch",
+            "SQ_VALU_MFMA_BUSY_CYCLES": "mfma_busy_cycles_per_launch",
+            "SQ_VALU_MFMA_COEXEC_CYCLES": "mfma_coexec_cycles_per_launch",
+            "SQ_INSTS_MFMA": "insts_mfma_per_launch", "SQ_ACTIVE_INST_VALU": "active_inst_valu_per_launch"}
+    out = {"kernel": args.kernel, "kernel_sha": kernel_sha(FOLD_SOURCES), "workload": args.workload}
+    for path in args.csv:
+        names = {r.get("Counter_Name") for r in _rows(path) if args.kernel in r.get("Kernel_Name", "")}
+        for c in sorted(names & set(want)):
+            if want[c] not in out:
+                out[want[c]], n = counter_per_dispatch(path, args.kernel, c)
+                out.setdefault("dispatches", n)
+    for k in ("insts_valu_per_launch", "waves_per_launch", "mfma_busy_cycles_per_launch"):
+        if k not in out:
+            raise SystemExit(f"missing counter for {k}")
+    out["insts_valu_per_wave"] = out["insts_valu_per_launch"] / out["waves_per_launch"]
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def stats(args):
     """Kernel-trace stats CSV -> a short table (name, calls, mean us, total ms)."""
     rows = _rows(args.csv)
@@ -169,6 +198,11 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     s = sub.add_parser("stats")
     s.add_argument("--csv", required=True)
+    v = sub.add_parser("valu")
+    v.add_argument("--kernel", default="k_append_fold")
+    v.add_argument("--csv", action="append", required=True)
+    v.add_argument("--workload", default="b512")
+    v.add_argument("--out", required=True)
     a = p.parse_args(argv)
     if a.cmd == "run":
         run_layer(a.workload, a.windows, a.fused)
@@ -176,6 +210,8 @@ def main(argv=None):
         run_copy(a.mib, a.reps)
     elif a.cmd == "traffic":
         traffic(a)
+    elif a.cmd == "valu":
+        valu(a)
     else:
         stats(a)
 

@@ -15,6 +15,7 @@ from tests.pins import golden
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = 0x7F0000000000  # a 256-byte-aligned address that is never dereferenced
+HEADER = os.path.join(ROOT, "include", "leapq.h")
 
 
 def header_functions():
@@ -29,6 +30,31 @@ def test_header_symbols_exported():
     L = lq.lib()
     for n in names:
         assert hasattr(L, n), n
+
+
+PAGE_TITLES = ("Recurrent-state quantization for linear attention", "LeapQuant")
+
+
+def test_declarations_cite_pages():
+    """Every entry point of include/leapq.h is preceded by a comment that
+    names the page defining its operation, except the two utilities
+    (status strings and the version), whose comments say they have none."""
+    import re
+    text = open(HEADER).read()
+    decls = list(re.finditer(r"\n(?:int32_t|const char \*)\s*(leapq_\w+)\(", text))
+    assert {m.group(1) for m in decls} == set(lq.SYMBOLS)
+    for m in decls:
+        before = text[:m.start() + 1]
+        start = before.rfind("/*")
+        end = before.rfind("*/")
+        assert 0 <= start < end, m.group(1)
+        between = before[end + 2:]
+        assert not between.strip(), f"{m.group(1)}: no comment right above the declaration"
+        comment = " ".join(re.sub(r"\n\s*\*", " ", before[start:end]).split())
+        if m.group(1) in ("leapq_status_str", "leapq_version"):
+            assert "no passage" in comment, m.group(1)
+        else:
+            assert any(t in comment for t in PAGE_TITLES), f"{m.group(1)} cites no page: {comment[:120]}"
 
 
 def test_version_and_status_strings():
