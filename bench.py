@@ -528,9 +528,9 @@ def main():
                 e1.record(stream)
                 torch.cuda.synchronize(dev)
                 ms_tok = e0.elapsed_time(e1) / T
+                kgb = metrics.gdn_step_bytes(sbytes, in_bytes, channel=True) * H * Lyr / (ms_tok * 1e-3) / 1e9
                 kda[name] = {"tokens_per_s": B / (ms_tok * 1e-3), "ms_per_token": ms_tok,
-                             "hbm_gbps_algorithmic": metrics.gdn_step_bytes(sbytes, in_bytes, channel=True) * H * Lyr
-                             / (ms_tok * 1e-3) / 1e9}
+                             "hbm_gbps_algorithmic": kgb, "frac": kgb / HBM_PEAK_GBPS}
                 kda[f"speedup_vs_{name}"] = kda["tokens_per_s"] / kda[name]["tokens_per_s"]
                 log(f"[bench] kda baseline {name}: {ms_tok:.3f} ms/token, {B / (ms_tok * 1e-3):,.0f} tokens/s")
                 del states
@@ -561,7 +561,8 @@ def main():
             ms_tok = e0.elapsed_time(e1) / T
             gb = metrics.gdn_step_bytes(sbytes, in_bytes) * H * Lyr / (ms_tok * 1e-3) / 1e9
             baselines[name] = {"tokens_per_s": B / (ms_tok * 1e-3), "ms_per_token": ms_tok,
-                               "hbm_gbps_algorithmic": gb}
+                               "hbm_gbps_algorithmic": gb, "frac": gb / HBM_PEAK_GBPS,
+                               "frac_of_copy_ceiling": gb / copy_gbps}
             log(f"[bench] baseline {name}: {ms_tok:.3f} ms/token, {B / (ms_tok * 1e-3):,.0f} tokens/s, "
                 f"{gb:.0f} GB/s")
             del states

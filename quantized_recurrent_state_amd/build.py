@@ -8,9 +8,11 @@ Flags that matter for the numbers:
   (no fast-math, no denormal flush; '/' and sqrtf stay correctly rounded,
    which is hipcc's default for HIP)
 """
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -23,7 +25,7 @@ SOURCES = [os.path.join(CSRC, f) for f in
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math",
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,16 +34,25 @@ FLAGS = [
 ]
 
 
-def build(out=LIB, extra=(), verbose=False):
-    """Compile every HIP source into `out`; returns the path."""
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
-        print(" ".join(cmd))
+        print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libleapq")
+
+
+def build(out=LIB, extra=(), verbose=False):
+    """Compile every HIP source (one hipcc process each, in parallel) and
+    link them into `out`; returns the path."""
+    tmp = out + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="leapq_build_") as d:
+        objs = [os.path.join(d, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[HIPCC, *FLAGS, *extra, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

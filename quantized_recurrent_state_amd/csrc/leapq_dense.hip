@@ -7,56 +7,27 @@
 // Diag(alpha) per key row for per-channel decay (CH), and b_t = beta):
 //   S = D_t S;  r = S^T k;  u = beta (v - r);  S = S + k u^T;  o = S^T q
 // with S[r][c] indexed (key row, value column).  A bf16 state is widened,
-// updated in fp32 and rounded to nearest even on store.  The reads are
-// canonical-tree dot products over the rows; the update is one fma per
-// entry.  A bf16 state is stored with the hardware round-to-nearest-even
-// conversion.
+// updated in fp32 and rounded to nearest even on store (the hardware's
+// packed conversion).  The update is one fma per entry; the reads are sums
+// over the rows in the order of the thread map below (these baselines are
+// checked against the dense fp32 step to a tolerance, not bit for bit).
 //
-// Thread map: rows i + 32p as in leapq_device.h, but the 16 columns of a
-// thread are contiguous (16 j + m) to match the natural state layout.
+// Thread map: the head's state is read and written as 16-byte pieces, piece
+// d * 256 + t by thread t (d = 0 .. 64 / VEC - 1), so every load and store
+// instruction of a wave covers 1 KB of contiguous memory.  A piece holds VEC
+// = 4 (fp32) or 8 (bf16) consecutive columns of one row: thread t owns the
+// columns VEC (t % LPR) .. + VEC - 1 (LPR = 128 / VEC pieces per row) of the
+// rows t / LPR + (256 / LPR) d.  Column sums run over the thread's rows,
+// then across the lanes that share the column group (lane bits >= log2 LPR),
+// then across the four waves through LDS.  The state is streamed with the
+// non-temporal hint: each launch reads and writes every byte once.
 #include "leapq_device.h"
 
 namespace leapq {
 namespace {
 using namespace dev;
 
-template <typename TS>
-__device__ __forceinline__ void load_row16(const TS *p, float (&x)[16]);
-template <>
-__device__ __forceinline__ void load_row16<float>(const float *p, float (&x)[16])
-{
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float4 v = reinterpret_cast<const float4 *>(p)[d];
-        x[4 * d] = v.x;
-        x[4 * d + 1] = v.y;
-        x[4 * d + 2] = v.z;
-        x[4 * d + 3] = v.w;
-    }
-}
-template <>
-__device__ __forceinline__ void load_row16<uint16_t>(const uint16_t *p, float (&x)[16])
-{
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        const uint4 v = reinterpret_cast<const uint4 *>(p)[d];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            x[8 * d + 2 * b] = bf16_to_f32((uint16_t)(w4[b] & 0xffffu));
-            x[8 * d + 2 * b + 1] = bf16_to_f32((uint16_t)(w4[b] >> 16));
-        }
-    }
-}
-template <typename TS>
-__device__ __forceinline__ void store_row16(TS *p, const float (&x)[16]);
-template <>
-__device__ __forceinline__ void store_row16<float>(float *p, const float (&x)[16])
-{
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-        reinterpret_cast<float4 *>(p)[d] = make_float4(x[4 * d], x[4 * d + 1], x[4 * d + 2], x[4 * d + 3]);
-}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -68,16 +39,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <>
-__device__ __forceinline__ void store_row16<uint16_t>(uint16_t *p, const float (&x)[16])
+template <typename TS>
+struct Piece {
+    static constexpr int VEC = 16 / (int)sizeof(TS);  // elements per 16-byte piece
+    static constexpr int LPR = D / VEC;                // pieces per row
+    static constexpr int RPT = 64 / VEC;               // pieces (rows) per thread
+    static constexpr int RS = NT / LPR;                // row stride between a thread's pieces
+};
+
+__device__ __forceinline__ void unpack(u32x4 x, float (&f)[4])
 {
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        uint32_t w4[4];
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(x[e]);
+}
+__device__ __forceinline__ void unpack(u32x4 x, float (&f)[8])
+{
 #pragma unroll
-        for (int b = 0; b < 4; ++b) w4[b] = pack_bf16x2(x[8 * d + 2 * b], x[8 * d + 2 * b + 1]);
-        reinterpret_cast<uint4 *>(p)[d] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(x[e] << 16);
+        f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
     }
+}
+__device__ __forceinline__ u32x4 pack(const float (&f)[4])
+{
+    u32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __float_as_uint(f[e]);
+    return x;
+}
+__device__ __forceinline__ u32x4 pack(const float (&f)[8])
+{
+    u32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+    return x;
+}
+
+// Sum of x over the lanes of the wave that share lane % LPR.
+template <int LPR>
+__device__ __forceinline__ float lanesum(float x)
+{
+#pragma unroll
+    for (int s = LPR; s < 64; s <<= 1) x += __shfl_xor(x, s);
+    return x;
 }
 
 template <typename TS, typename TI, bool CH>
@@ -86,54 +90,79 @@ __global__ __launch_bounds__(NT) void k_gdn_decode(TS *__restrict__ Sg, const TI
                                                     const float *__restrict__ alpha,
                                                     const float *__restrict__ beta, float *__restrict__ o)
 {
-    __shared__ float uc[D];
-    const AMap a = amap();
-    const int l = a.l;
+    using P = Piece<TS>;
+    constexpr int VEC = P::VEC, LPR = P::LPR, RPT = P::RPT, RS = P::RS;
+    __shared__ float red[2][4][D];  // per-wave column partials of S^T k and S^T q
+    __shared__ float kq[3][D];      // k, q and (per-channel decay) alpha of the head
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int cg = t % LPR, g = t / LPR;
     const int h = blockIdx.x;
-    TS *Sh = Sg + (size_t)h * D * D;
-    const TI *qh = qin + (size_t)h * D, *kh = kin + (size_t)h * D;
-    float S[4][16], kr[4], qr[4], al[4];
+    u32x4 *Sh = reinterpret_cast<u32x4 *>(Sg + (size_t)h * D * D);
+    u32x4 raw[RPT];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        al[p] = CH ? alpha[(size_t)h * D + a.row(p)] : alpha[h];
-        kr[p] = ld_in<TI>(kh, a.row(p));
-        qr[p] = ld_in<TI>(qh, a.row(p));
-        load_row16<TS>(Sh + a.row(p) * D + 16 * a.j, S[p]);
+    for (int d = 0; d < RPT; ++d) raw[d] = __builtin_nontemporal_load(Sh + d * NT + t);
+    const TI *qh = qin + (size_t)h * D, *kh = kin + (size_t)h * D, *vh = vin + (size_t)h * D;
+    if (t < D) {
+        kq[0][t] = ld_in<TI>(kh, t);
+        kq[1][t] = ld_in<TI>(qh, t);
+        if (CH) kq[2][t] = alpha[(size_t)h * D + t];
     }
-    const int c = 16 * a.j + colm_of(l);
-    const float vc = ld_in<TI>(vin + (size_t)h * D, c);
+    float vc[VEC];
+#pragma unroll
+    for (int m = 0; m < VEC; ++m) vc[m] = ld_in<TI>(vh, cg * VEC + m);
     const float bt = beta[h];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int m = 0; m < 16; ++m) S[p][m] = al[p] * S[p][m];
-    float v[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m)
-        v[m] = fma_(S[0][m], kr[0], S[2][m] * kr[2]) + fma_(S[1][m], kr[1], S[3][m] * kr[3]);
-    const float rc = colsum16(v, l);
-    if ((l & 1) == 0) uc[c] = bt * (vc - rc);
+    const float a0 = CH ? 0.0f : alpha[h];
     __syncthreads();
-    float u[16];
+    float S[RPT][VEC], pr[VEC];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float4 uu = reinterpret_cast<const float4 *>(uc + 16 * a.j)[d];
-        u[4 * d] = uu.x;
-        u[4 * d + 1] = uu.y;
-        u[4 * d + 2] = uu.z;
-        u[4 * d + 3] = uu.w;
+    for (int m = 0; m < VEC; ++m) pr[m] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < RPT; ++d) {
+        unpack(raw[d], S[d]);
+        const float al = CH ? kq[2][d * RS + g] : a0;
+        const float kr = kq[0][d * RS + g];
+#pragma unroll
+        for (int m = 0; m < VEC; ++m) {
+            S[d][m] = al * S[d][m];
+            pr[m] = fma_(S[d][m], kr, pr[m]);
+        }
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int m = 0; m < VEC; ++m) pr[m] = lanesum<LPR>(pr[m]);
+    if (l < LPR)
 #pragma unroll
-        for (int m = 0; m < 16; ++m) S[p][m] = fma_(kr[p], u[m], S[p][m]);
+        for (int m = 0; m < VEC; ++m) red[0][w][cg * VEC + m] = pr[m];
+    __syncthreads();
+    float u[VEC], po[VEC];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        v[m] = fma_(S[0][m], qr[0], S[2][m] * qr[2]) + fma_(S[1][m], qr[1], S[3][m] * qr[3]);
-    const float oc = colsum16(v, l);
-    if ((l & 1) == 0) o[(size_t)h * D + c] = oc;
+    for (int m = 0; m < VEC; ++m) {
+        const int c = cg * VEC + m;
+        const float rc = (red[0][0][c] + red[0][1][c]) + (red[0][2][c] + red[0][3][c]);
+        u[m] = bt * (vc[m] - rc);
+        po[m] = 0.0f;
+    }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) store_row16<TS>(Sh + a.row(p) * D + 16 * a.j, S[p]);
+    for (int d = 0; d < RPT; ++d) {
+        const float kr = kq[0][d * RS + g], qr = kq[1][d * RS + g];
+#pragma unroll
+        for (int m = 0; m < VEC; ++m) {
+            S[d][m] = fma_(kr, u[m], S[d][m]);
+            po[m] = fma_(S[d][m], qr, po[m]);
+        }
+        __builtin_nontemporal_store(pack(S[d]), Sh + d * NT + t);
+    }
+#pragma unroll
+    for (int m = 0; m < VEC; ++m) po[m] = lanesum<LPR>(po[m]);
+    if (l < LPR)
+#pragma unroll
+        for (int m = 0; m < VEC; ++m) red[1][w][cg * VEC + m] = po[m];
+    __syncthreads();
+    if (t < LPR)
+#pragma unroll
+        for (int m = 0; m < VEC; ++m) {
+            const int c = cg * VEC + m;
+            o[(size_t)h * D + c] = (red[1][0][c] + red[1][1][c]) + (red[1][2][c] + red[1][3][c]);
+        }
 }
 
 }  // namespace

@@ -208,7 +208,12 @@ def test_gdn_baselines(state_dtype, in_dtype):
     if state_dtype == torch.float32:
         assert eo < 1e-5 and es < 1e-5
     else:
-        assert eo < 1e-3 and es < 1e-2
+        # The baseline sums S^T k and S^T q in another order than the
+        # oracle's sequential chain, so an fp32 value may land on the other
+        # side of a bf16 rounding boundary: a stored entry then differs by
+        # one bf16 unit (2^-8 relative), and later tokens carry it on.  The
+        # bar allows a few such units.
+        assert eo < 1e-2 and es < 1e-2
 
 
 def test_full_size_b512_layer_sampled():
