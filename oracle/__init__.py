@@ -43,6 +43,8 @@ def _bind(L):
         "lqo_current": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, f32p]),
         "lqo_quantize": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
         "lqo_init": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_quantize_keyrow": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_boundary_keyrow": (None, [i8p, f32p, f32p, ci, i32p, f32p, f32p]),
         "lqo_fold": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
         "lqo_append": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p,
                               f32p, f32p, f32p, cf, cf, f32p]),
@@ -129,6 +131,33 @@ def gated_inputs(q, k, v, a, b, A_log, dt_bias, q_scale=1.0, eps=1e-6, normalize
         q = l2norm(q, eps, q_scale, L)
         k = l2norm(k, eps, 1.0, L)
     return f32(q), f32(k), f32(v), alpha, beta
+
+
+def quantize_axis(S, C=4, smoothing=True, sigma_floor=1e-6, axis="value", L=None):
+    """Quantizes one fp32 state [128][128] as init does and returns
+    (Q, rho, sigma, idx, vec, B) with B the boundary state.  axis="value"
+    is the path's smoothing (sigma per value column, rho per key row);
+    axis="key" is the study of the other axis (sigma per key row, rho per
+    value column)."""
+    L = L or lib()
+    R = f32(S).reshape(D, D).copy()
+    Q = np.zeros((D, D), np.int8)
+    rho, sig = np.zeros(D, np.float32), np.zeros(D, np.float32)
+    idx, vec = np.full(max(C, 1), -1, np.int32), np.zeros((max(C, 1), D), np.float32)
+    B = np.zeros((D, D), np.float32)
+    fp, ip = ctypes.c_float, ctypes.c_int8
+    args = (_p(Q, ip), _p(rho, fp), _p(sig, fp))
+    if axis == "value":
+        L.lqo_quantize(_p(R, fp), C, int(smoothing), float(sigma_floor), *args, _p(idx, ctypes.c_int32),
+                       _p(vec, fp))
+        L.lqo_boundary(*args, C, _p(idx, ctypes.c_int32), _p(vec, fp), _p(B, fp))
+    elif axis == "key":
+        L.lqo_quantize_keyrow(_p(R, fp), C, int(smoothing), float(sigma_floor), *args, _p(idx, ctypes.c_int32),
+                              _p(vec, fp))
+        L.lqo_boundary_keyrow(*args, C, _p(idx, ctypes.c_int32), _p(vec, fp), _p(B, fp))
+    else:
+        raise ValueError("axis must be 'value' or 'key'")
+    return Q, rho, sig, idx[:C], vec[:C], B
 
 
 class Head:

@@ -178,8 +178,8 @@ void lqo_current(const int8_t *Q, const float *rho, const float *sigma, int C,
 /* R is consumed (extracted lines are zeroed in place). */
 static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t *Q, float *rho, float *sigma);
 
-void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
-                  int8_t *Q, float *rho, float *sigma, int32_t *idx, float *vec)
+/* Greedy extraction of C compensator lines from R (zeroed in place). */
+static void extract_lines(float *R, int C, int32_t *idx, float *vec)
 {
     /* Compensator tokens ([LQ] 3.3; [RN4] Why rounding): greedy extraction
      * of whole rows or columns, largest energy first.  Energy of a line is
@@ -214,6 +214,12 @@ void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
             for (int r = 0; r < D; ++r) { v[r] = R[r * D + c]; R[r * D + c] = 0.0f; }
         }
     }
+}
+
+void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
+                  int8_t *Q, float *rho, float *sigma, int32_t *idx, float *vec)
+{
+    extract_lines(R, C, idx, vec);
     smooth_and_round(R, smoothing, sigma_floor, Q, rho, sigma);
 }
 
@@ -262,6 +268,72 @@ static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t 
             Q[r * D + c] = (int8_t)y;
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* The other smoothing axis (a study, CPU only).  "LeapQuant" 3.4      */
+/* describes smoothing as a rescaling of the key rows whose inverse     */
+/* restores the key coordinates; the path built here smooths per value  */
+/* column with int8 scales per key row.  This variant exchanges the two */
+/* axes: per key row, the square root of the row's mean absolute value  */
+/* (floored) divides the row; the int8 scales are then per value column */
+/* (absmax / 127, one rounding of the exact product, ties to even).     */
+/* The compensators are extracted as in lqo_quantize.  On S it equals   */
+/* lqo_quantize on the transpose of S, transposed (when no row ties a   */
+/* column), which pins it.                                              */
+/* ------------------------------------------------------------------ */
+static void smooth_and_round_keyrow(float *R, int smoothing, float sigma_floor, int8_t *Q, float *rho_col,
+                                    float *sigma_row)
+{
+    float inv_row[D];
+    for (int r = 0; r < D; ++r) {
+        float sr = 1.0f;
+        if (smoothing) {
+            float a[D];
+            for (int c = 0; c < D; ++c) a[c] = fabsf(R[r * D + c]);
+            sr = sqrtf(lqo_t128_sum(a) * (1.0f / 128.0f));
+            if (sr < sigma_floor) sr = sigma_floor;
+        }
+        sigma_row[r] = sr;
+        inv_row[r] = 1.0f / sr;
+    }
+    for (int c = 0; c < D; ++c) {
+        float y[D];
+        float Mc = 0.0f;
+        for (int r = 0; r < D; ++r) {
+            y[r] = R[r * D + c] * inv_row[r];
+            if (fabsf(y[r]) > Mc) Mc = fabsf(y[r]);
+        }
+        if (!(Mc >= LQO_TINY)) {
+            rho_col[c] = 0.0f;
+            for (int r = 0; r < D; ++r) Q[r * D + c] = 0;
+            continue;
+        }
+        rho_col[c] = Mc / 127.0f;
+        float gc = 127.0f / Mc;
+        for (int r = 0; r < D; ++r) {
+            double z = rint((double)y[r] * (double)gc);
+            if (z > 127.0) z = 127.0;
+            if (z < -127.0) z = -127.0;
+            Q[r * D + c] = (int8_t)z;
+        }
+    }
+}
+
+void lqo_quantize_keyrow(float *R, int C, int smoothing, float sigma_floor,
+                         int8_t *Q, float *rho_col, float *sigma_row, int32_t *idx, float *vec)
+{
+    extract_lines(R, C, idx, vec);
+    smooth_and_round_keyrow(R, smoothing, sigma_floor, Q, rho_col, sigma_row);
+}
+
+/* Boundary of the key-row variant: (code * rho_c) * sigma_r plus the lines. */
+void lqo_boundary_keyrow(const int8_t *Q, const float *rho_col, const float *sigma_row, int C,
+                         const int32_t *idx, const float *vec, float *out)
+{
+    for (int r = 0; r < D; ++r)
+        for (int c = 0; c < D; ++c) out[r * D + c] = ((float)Q[r * D + c] * rho_col[c]) * sigma_row[r];
+    add_lines(out, C, idx, vec, 1.0f);
 }
 
 /* Initial quantization of a caller's fp32 state: the fold without records. */

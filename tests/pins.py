@@ -234,6 +234,30 @@ def pin_planted_prefill_lines(L):
         assert want <= set(int(i) for i in head.idx), (h_, head.idx, want)
 
 
+def pin_keyrow_smoothing_is_transpose(L):
+    """The other smoothing axis (smoothing per key row, int8 scales per value
+    column; a CPU study only) applied to S equals the path's quantizer
+    applied to the transpose of S, transposed, bit for bit: codes, scales,
+    boundary state, lines, and each row pick of one is the same-numbered
+    column pick of the other.  Random states with outlier lines (no exact
+    row/column energy ties), with and without smoothing, C = 0 and 4."""
+    rng = np.random.default_rng(17)
+    for trial in range(4):
+        S = (rng.standard_normal((D, D)) * 10.0 ** rng.uniform(-2, 1, (D, 1))).astype(np.float32)
+        S[rng.integers(0, D, 2)] *= np.float32(20.0)
+        S[:, rng.integers(0, D, 2)] *= np.float32(15.0)
+        C, sm = (4, True) if trial < 2 else ((0, True) if trial == 2 else (4, False))
+        Qa, ra, sa, ia, va, Ba = oracle.quantize_axis(S, C, sm, 1e-6, axis="key", L=L)
+        Qb, rb, sb, ib, vb, Bb = oracle.quantize_axis(np.ascontiguousarray(S.T), C, sm, 1e-6, axis="value", L=L)
+        assert np.array_equal(Qa, Qb.T)
+        assert np.array_equal(ra.view(np.uint32), rb.view(np.uint32))
+        assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+        assert np.array_equal(Ba.view(np.uint32), np.ascontiguousarray(Bb.T).view(np.uint32))
+        swap = [(-1 if i < 0 else (i + D if i < D else i - D)) for i in ib]
+        assert list(ia) == swap, (list(ia), swap)
+        assert np.array_equal(va.view(np.uint32), vb.view(np.uint32))
+
+
 def pin_greedy_bruteforce(L):
     """Every greedy pick is the float64 argmax of the line energies of the
     matrix left after the earlier picks, unless the top two are within 1e-6."""
@@ -834,7 +858,7 @@ def pin_block_window_and_fold(L):
 ALL = [
     pin_t128_fixtures, pin_t128_exact_integers, pin_round_half_even, pin_round_exact_product_once, pin_pick_ties,
     pin_textbook_int8, pin_smoothing_closed_form, pin_scaling_exact, pin_planted_outliers,
-    pin_planted_prefill_lines,
+    pin_planted_prefill_lines, pin_keyrow_smoothing_is_transpose,
     pin_greedy_bruteforce, pin_reconstruction_bound, pin_window_vs_dense_f64, pin_beta_zero,
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,

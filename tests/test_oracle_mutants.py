@@ -80,6 +80,11 @@ MUTANTS = [
     ("blk_start_last_max", "if (!used[r] && e[r] > best)", "if (!used[r] && e[r] >= best)"),
     ("blk_start_reused_row", "            used[pick] = 1;\n", ""),
     ("blk_unused_marked_live", "idx[j] = live[j] ? j : -1;", "idx[j] = j;"),
+    ("keyrow_smooth_columns", "for (int c = 0; c < D; ++c) a[c] = fabsf(R[r * D + c]);",
+     "for (int c = 0; c < D; ++c) a[c] = fabsf(R[c * D + r]);"),
+    ("keyrow_no_sqrt", "sr = sqrtf(lqo_t128_sum(a) * (1.0f / 128.0f));", "sr = lqo_t128_sum(a) * (1.0f / 128.0f);"),
+    ("keyrow_boundary_axes", "((float)Q[r * D + c] * rho_col[c]) * sigma_row[r];",
+     "((float)Q[r * D + c] * rho_col[r]) * sigma_row[c];"),
     ("kda_step_column_decay", "S[r * D + c] = alpha[r] * S[r * D + c];", "S[r * D + c] = alpha[c] * S[r * D + c];"),
 ]
 
