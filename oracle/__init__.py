@@ -58,6 +58,9 @@ def _bind(L):
         "lqo_gdn_step_bf16": (None, [u16p, f32p, f32p, f32p, cf, cf, f32p, f32p]),
         "lqo_f32_to_bf16": (ctypes.c_uint16, [cf]),
         "lqo_round_bf16": (None, [f32p, ci]),
+        "lqo_f32_to_e4m3": (ctypes.c_uint8, [cf]),
+        "lqo_e4m3_to_f32": (cf, [ctypes.c_uint8]),
+        "lqo_round_fp8_record": (None, [f32p]),
         "lqo_gate": (None, [cf, cf, cf, cf, f32p, f32p]),
         "lqo_quantize_r1": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
         "lqo_init_r1": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
@@ -177,8 +180,8 @@ class Head:
             raise ValueError("decay must be 'scalar' or 'channel'")
         self.decay = decay
         self.kda = decay == "channel"
-        if rec_u not in ("f32", "bf16"):
-            raise ValueError("rec_u must be 'f32' or 'bf16'")
+        if rec_u not in ("f32", "bf16", "fp8"):
+            raise ValueError("rec_u must be 'f32', 'bf16' or 'fp8'")
         self.rec_u = rec_u
         if fit not in ("lines", "rank1", "block"):
             raise ValueError("fit must be 'lines', 'rank1' or 'block'")
@@ -238,6 +241,10 @@ class Head:
             # the record keeps u rounded to bf16; this token's output used
             # the fp32 u (lqo_append above)
             self.L.lqo_round_bf16(_p(self.ru[self.n - 1], fp), D)
+        elif self.rec_u == "fp8":
+            # the record keeps u as fp8 with a power-of-two scale per group
+            # of 32 value columns; this token's output used the fp32 u
+            self.L.lqo_round_fp8_record(_p(self.ru[self.n - 1], fp))
         return o, self.ru[self.n - 1].copy()
 
     def fold(self):

@@ -934,6 +934,61 @@ void lqo_round_bf16(float *x, int n)
     for (int e = 0; e < n; ++e) x[e] = bf16_to_f32(lqo_f32_to_bf16(x[e]));
 }
 
+/* ------------------------------------------------------------------ */
+/* fp8 record corrections (an option; [RN4] Why rounding the state is   */
+/* difficult keeps the records in higher precision, [LQ] 4.4 notes that */
+/* record traffic grows with the window: a narrower record trades the   */
+/* two).  Format: OCP 8-bit floating point E4M3 (sign, 4 exponent bits  */
+/* with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals  */
+/* m * 2^-9; the largest finite value is 1.75 * 2^8 = 448; no infinity). */
+/* A record's 128 corrections form 4 groups, value columns c with c % 4 */
+/* = j; group j is stored as E4M3 codes of u_c / s_j, where s_j is the  */
+/* smallest power of two not below 2^-126 with max_c |u_c| <= 448 s_j,  */
+/* rounded to nearest, ties to even.  The stored correction is         */
+/* decode(code) * s_j (exact).                                          */
+/* ------------------------------------------------------------------ */
+
+/* The E4M3 code of x, |x| <= 448, rounded to nearest, ties to even. */
+uint8_t lqo_f32_to_e4m3(float x)
+{
+    double a = fabs((double)x);
+    unsigned sign = signbit(x) ? 0x80u : 0u;
+    unsigned mag;
+    if (a >= 0x1p-6) {
+        int e;
+        frexp(a, &e);                      /* a = f 2^e, f in [0.5, 1) */
+        int E = e - 1;                     /* a = q 2^E, q in [1, 2) */
+        double q = ldexp(a, -E);
+        /* a mantissa that rounds up to 8 carries into the exponent field */
+        mag = (unsigned)((E + 7) * 8) + (unsigned)rint((q - 1.0) * 8.0);
+    } else {
+        mag = (unsigned)rint(a * 512.0);   /* subnormal: a multiple of 2^-9 (8 carries to 2^-6) */
+    }
+    return (uint8_t)(sign | mag);
+}
+
+float lqo_e4m3_to_f32(uint8_t c)
+{
+    int E = (c >> 3) & 15, m = c & 7;
+    double v = E == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), E - 10);
+    return (float)((c & 0x80) ? -v : v);
+}
+
+/* In place: a record correction u[128] (value-column order) replaced by
+ * its stored fp8 value. */
+void lqo_round_fp8_record(float *u)
+{
+    for (int j = 0; j < 4; ++j) {
+        float M = 0.0f;
+        for (int c = j; c < D; c += 4)
+            if (fabsf(u[c]) > M) M = fabsf(u[c]);
+        double s = 0x1p-126;
+        while ((double)M > 448.0 * s) s *= 2.0;
+        float sf = (float)s, inv = 1.0f / sf;
+        for (int c = j; c < D; c += 4) u[c] = lqo_e4m3_to_f32(lqo_f32_to_e4m3(u[c] * inv)) * sf;
+    }
+}
+
 /* Per-token bf16 state ([RN4] Why rounding: a bf16 state rounded at every
  * token; [LQ] 4.2/4.4 per-step baselines): widen, take the fp32 step, keep
  * the output of the fp32 state, store the state rounded to bf16. */

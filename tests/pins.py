@@ -665,6 +665,75 @@ def pin_bf16_records(L):
     assert rel(hb.dequant(2), S) < 5e-3
 
 
+def _torch_e4m3(x):
+    """torch's float8_e4m3fn rounding of fp32 values, as (codes uint8, values fp32)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy(), t.float().numpy()
+
+
+def pin_fp8_codec(L):
+    """The oracle's E4M3 codec against torch's float8_e4m3fn: the value of
+    every code (NaN codes aside, -0 included), and the code of every
+    representable value, of every midpoint between neighbours (ties go to
+    the even code) and of the floats next to those midpoints, of random
+    values over every binade up to 448, and of fp32 subnormals."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([L.lqo_e4m3_to_f32(int(c)) for c in codes], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    pos = np.unique(want[want > 0]).astype(np.float64)
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    rng = np.random.default_rng(23)
+    rnd = (rng.uniform(1, 2, 4000) * 2.0 ** rng.integers(-12, 8, 4000)).astype(np.float32)
+    sub = (rng.integers(1, 1 << 23, 200) * 2.0 ** -149).astype(np.float32)
+    x = np.concatenate([pos.astype(np.float32), mids, near, rnd, sub, [np.float32(448.0), np.float32(0.0)]])
+    x = np.concatenate([x, -x])
+    wc, _ = _torch_e4m3(x)
+    gc = np.array([L.lqo_f32_to_e4m3(float(v)) for v in x], np.uint8)
+    bad = np.flatnonzero(gc != wc)
+    assert bad.size == 0, (x[bad[:5]], gc[bad[:5]], wc[bad[:5]])
+
+
+def pin_fp8_records(L):
+    """Records whose corrections are kept in fp8: the token that makes a
+    record reads out with its fp32 u; the stored u of each group of 32
+    value columns (c % 4 = j) is torch's E4M3 rounding of u / s times s, with
+    s a power of two that puts the group's largest magnitude in (224, 448]
+    (or 2^-126 for a group that small); a window stays within fp8 rounding
+    of the float64 dense recurrence."""
+    S0, toks = tiny_inputs(seed=43, tokens=16, init="gauss")
+    hf = oracle.Head(C=4, W=16, L=L).init(S0[0])
+    h8 = oracle.Head(C=4, W=16, L=L, rec_u="fp8").init(S0[0])
+    S = h8.dequant(1).astype(np.float64)
+    worst = 0.0
+    for t, (q, k, v, a, b) in enumerate(toks):
+        of, uf = hf.append(q, k, v, a, b)
+        o8, u8 = h8.append(q, k, v, a, b)
+        if t == 0:
+            assert np.array_equal(of, o8)
+        # the record as h8 made it: its fp32 u is that of a twin of h8 with
+        # fp32 records up to this token
+        twin = h8.copy()
+        twin.n -= 1
+        twin.rec_u = "f32"
+        _, u32 = twin.append(q, k, v, a, b)
+        for j in range(4):
+            g = u32[j::4]
+            M = float(np.max(np.abs(g)))
+            e = int(np.floor(np.log2(M / 224.0)))
+            sc = [2.0 ** (e + d) for d in (-1, 0, 1) if 224.0 * 2.0 ** (e + d) < M <= 448.0 * 2.0 ** (e + d)]
+            assert len(sc) == 1, (M, e)
+            sc = np.float32(sc[0])
+            _, want = _torch_e4m3(g / sc)
+            assert np.array_equal(u8[j::4], (want * sc).astype(np.float32)), (t, j)
+        _, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                            float(a), float(b))
+        worst = max(worst, rel(o8, o64))
+    assert worst < 0.05, worst
+    assert rel(h8.dequant(2), S) < 0.05
+
+
 def pin_rank1_fit(L):
     """Rank-one compensators by power sweeps: the start is the fp64 argmax
     row energy; after 8 sweeps a and b equal float64 power iteration from
@@ -863,6 +932,7 @@ ALL = [
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
     pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step, pin_bf16_records,
+    pin_fp8_codec, pin_fp8_records,
     pin_rank1_fit, pin_rank1_window_and_fold, pin_rank1_zero_state,
     pin_block_start_rows, pin_block_fit_svd, pin_block_fit_steps, pin_block_warm_fixed_point,
     pin_block_zero_state, pin_block_window_and_fold,

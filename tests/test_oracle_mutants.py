@@ -85,6 +85,12 @@ MUTANTS = [
     ("keyrow_no_sqrt", "sr = sqrtf(lqo_t128_sum(a) * (1.0f / 128.0f));", "sr = lqo_t128_sum(a) * (1.0f / 128.0f);"),
     ("keyrow_boundary_axes", "((float)Q[r * D + c] * rho_col[c]) * sigma_row[r];",
      "((float)Q[r * D + c] * rho_col[r]) * sigma_row[c];"),
+    ("fp8_truncate", "(unsigned)rint((q - 1.0) * 8.0)", "(unsigned)floor((q - 1.0) * 8.0)"),
+    ("fp8_subnormal_exponent", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("fp8_no_scale", "float sf = (float)s, inv = 1.0f / sf;", "float sf = 1.0f, inv = 1.0f;"),
+    ("fp8_contiguous_groups", "for (int c = j; c < D; c += 4)\n            if (fabsf(u[c]) > M)",
+     "for (int c = 32 * j; c < 32 * j + 32; ++c)\n            if (fabsf(u[c]) > M)"),
+    ("fp8_record_unrounded", "u[c] = lqo_e4m3_to_f32(lqo_f32_to_e4m3(u[c] * inv)) * sf;", "u[c] = u[c];"),
     ("kda_step_column_decay", "S[r * D + c] = alpha[r] * S[r * D + c];", "S[r * D + c] = alpha[c] * S[r * D + c];"),
 ]
 
