@@ -50,6 +50,8 @@ def parse():
                    help="skip the per-channel decay (KDA) measurement at the same shape")
     p.add_argument("--no-bf16-records", action="store_true",
                    help="skip the measurement of the lossy bf16 record-corrections option")
+    p.add_argument("--no-fp8-records", action="store_true",
+                   help="skip the measurement of the lossy fp8 record-corrections option")
     p.add_argument("--no-rank1", action="store_true",
                    help="skip the measurement of the rank-one compensator option")
     p.add_argument("--no-block", action="store_true",
@@ -363,6 +365,16 @@ def main():
             f"{bf16rec['tokens_per_s']:,.0f} tokens/s ({bf16rec['ratio_to_plain']:.3f} of the plain path); "
             f"append {bf16rec['append_us']:.1f} us")
 
+    fp8rec = None
+    if not args.no_fp8_records:
+        fp8rec = time_option(lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype,
+                                            rec_dtype="fp8"), u_bytes=144 / 128)
+        fp8rec["note"] = ("lossy option: record corrections as E4M3 with a power-of-two scale per 32 value columns "
+                          "(see quality.py --rec-dtype fp8)")
+        log(f"[bench] fp8 record corrections: {fp8rec['ms_per_step']:.3f} ms per window, "
+            f"{fp8rec['tokens_per_s']:,.0f} tokens/s ({fp8rec['ratio_to_plain']:.3f} of the plain path); "
+            f"append {fp8rec['append_us']:.1f} us")
+
     rank1 = None
     if not args.no_rank1:
         rank1 = time_option(lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype,
@@ -609,6 +621,7 @@ def main():
         "gated": gated,
         "kda": kda,
         "bf16_record_corrections": bf16rec,
+        "fp8_record_corrections": fp8rec,
         "rank1_compensators": rank1,
         "block_compensators": block,
         "staggered_phases": staggered,

@@ -56,12 +56,16 @@ extern "C" {
                                       [0, window], reserved fields not zero */
 #define LEAPQ_ERR_ALIGN (-4)       /* state not 256-byte aligned, or a tensor not 16-byte aligned */
 #define LEAPQ_ERR_WINDOW_FULL (-5) /* append with n_records == window: fold first */
-#define LEAPQ_ERR_DTYPE (-6)       /* in_dtype / state_dtype not LEAPQ_F32 or LEAPQ_BF16 */
+#define LEAPQ_ERR_DTYPE (-6)       /* in_dtype / state_dtype not LEAPQ_F32 or LEAPQ_BF16, rec_dtype not
+                                      LEAPQ_F32, LEAPQ_BF16 or LEAPQ_FP8 */
 #define LEAPQ_ERR_HIP (-7)         /* the HIP launch failed */
 
 /* element types of q, k, v (in_dtype) and of the dense baseline state */
 #define LEAPQ_F32 0
 #define LEAPQ_BF16 1
+/* record corrections only (rec_dtype): OCP FP8 E4M3 codes with one
+ * power-of-two scale per group of 32 value columns */
+#define LEAPQ_FP8 2
 
 /* decay of the recurrence ("LeapQuant" App. A: D_t = Diag(alpha_t)): one
  * scalar per head and token (Gated DeltaNet), or one value per key channel
@@ -99,10 +103,16 @@ typedef struct leapq_config {
     int32_t qk_norm;     /* 1: the gated appends L2-normalize q and k (record keys are then fp32); 0 or 1 */
     int32_t decay;       /* LEAPQ_DECAY_SCALAR (GDN: alpha per head) or LEAPQ_DECAY_CHANNEL (KDA: alpha
                             per head and key channel); channel decay excludes qk_norm */
-    int32_t rec_dtype;   /* LEAPQ_F32 (the method's records) or LEAPQ_BF16: record corrections u kept in
-                            bf16, rounded to nearest even on store (a lossy lower-precision option; the
-                            token that makes a record reads out with its fp32 u); LEAPQ_BF16 requires
-                            scalar decay and qk_norm = 0 and is not taken by the gated entry points */
+    int32_t rec_dtype;   /* LEAPQ_F32 (the method's records), LEAPQ_BF16: record corrections u kept in
+                            bf16, rounded to nearest even on store, or LEAPQ_FP8: u kept as E4M3 (sign,
+                            4 exponent bits, bias 7, 3 mantissa bits, largest 448) of u_c / s_j, where
+                            group j holds the value columns c with c % 4 = j and s_j is the smallest
+                            power of two >= 2^-126 with max_c |u_c| <= 448 s_j, rounded to nearest, ties
+                            to even (lossy lower-precision options, "Recurrent-state quantization for
+                            linear attention: a first GPU kernel", Why rounding the state is difficult:
+                            records kept in higher precision, traded here for bytes; the token that makes
+                            a record reads out with its fp32 u); both require scalar decay and
+                            qk_norm = 0 and are not taken by the gated entry points */
     int32_t comp_fit;    /* LEAPQ_COMP_LINES (whole rows or columns), LEAPQ_COMP_RANK1 (rank-one pairs
                             fitted by power sweeps) or LEAPQ_COMP_BLOCK (the pairs fitted as a block);
                             the pair fits require n_comp <= 4, scalar decay, rec_dtype LEAPQ_F32, and
@@ -139,14 +149,19 @@ typedef struct leapq_config {
  *                                      when qk_norm = 1
  *   rec_u     fp32 or bf16 (rec_dtype) [heads][W][128]  record corrections; value column c is
  *                                      stored at 32 (c % 4) + 8 (c / 32)
- *                                      + 4 ((c / 4) % 2) + (c / 8) % 4
+ *                                      + 4 ((c / 4) % 2) + (c / 8) % 4;
+ *             with LEAPQ_FP8 [heads][W][144 bytes]: the 128 E4M3 codes
+ *                                      in that order, then the 4 fp32 scales
+ *                                      (scale j serves positions 32 j .. 32 j
+ *                                      + 31, the columns with c % 4 = j)
  * These orders are the thread map of the kernels (each thread's 64 codes are
  * four 16-byte loads, each wave's loads 1 KB contiguous; the record keys and
  * corrections are the A operand order of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
- * 1.19 bytes per state element); record_bytes_per_head = W * (4 g + 128 e + 128 f)
+ * 1.19 bytes per state element); record_bytes_per_head = W * (4 g + 128 e + f)
  * with e = 2 for bf16 inputs and qk_norm = 0, else 4, g = 1 (scalar decay)
- * or 128 (channel decay), and f = 4, or 2 with rec_dtype = LEAPQ_BF16. */
+ * or 128 (channel decay), and f = 512, 256 with rec_dtype = LEAPQ_BF16, or
+ * 144 with LEAPQ_FP8. */
 typedef struct leapq_layout {
     uint64_t total_bytes;
     uint64_t off_codes, off_row_scale, off_col_scale, off_comp_idx, off_comp_vec;

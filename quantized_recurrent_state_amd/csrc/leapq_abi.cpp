@@ -40,8 +40,9 @@ int32_t check_method_config(const leapq_config *c)
     if (!(c->sigma_floor > 0.0f) || c->sigma_floor > 3.0e38f) return LEAPQ_ERR_RANGE;
     if (c->qk_norm != 0 && c->qk_norm != 1) return LEAPQ_ERR_RANGE;
     if (c->decay == LEAPQ_DECAY_CHANNEL && c->qk_norm) return LEAPQ_ERR_RANGE;
-    if (c->rec_dtype != LEAPQ_F32 && c->rec_dtype != LEAPQ_BF16) return LEAPQ_ERR_DTYPE;
-    if (c->rec_dtype == LEAPQ_BF16 && (c->decay != LEAPQ_DECAY_SCALAR || c->qk_norm)) return LEAPQ_ERR_RANGE;
+    if (c->rec_dtype != LEAPQ_F32 && c->rec_dtype != LEAPQ_BF16 && c->rec_dtype != LEAPQ_FP8)
+        return LEAPQ_ERR_DTYPE;
+    if (c->rec_dtype != LEAPQ_F32 && (c->decay != LEAPQ_DECAY_SCALAR || c->qk_norm)) return LEAPQ_ERR_RANGE;
     if (c->comp_fit != LEAPQ_COMP_LINES && c->comp_fit != LEAPQ_COMP_RANK1 && c->comp_fit != LEAPQ_COMP_BLOCK)
         return LEAPQ_ERR_RANGE;
     if (c->comp_fit != LEAPQ_COMP_LINES &&
@@ -61,7 +62,8 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     const uint64_t C = (uint64_t)c->n_comp, W = (uint64_t)c->window;
     const uint64_t kb = key_bf16(c) ? 2 : 4;  // record key element
     const uint64_t gw = c->decay == LEAPQ_DECAY_CHANNEL ? kD : 1;  // record decay values
-    const uint64_t ub = c->rec_dtype == LEAPQ_BF16 ? 2 : 4;        // record correction element
+    // one record's corrections: 128 fp32 or bf16 values, or 128 fp8 codes and 4 fp32 scales
+    const uint64_t ub = c->rec_dtype == LEAPQ_BF16 ? 2 * kD : c->rec_dtype == LEAPQ_FP8 ? kD + 16 : 4 * kD;
     const uint64_t cw = c->comp_fit != LEAPQ_COMP_LINES ? 2 : 1;   // compensator vectors (pairs: a, b)
     uint64_t off = 0;
     L->off_codes = off;
@@ -79,10 +81,10 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_rec_k = off;
     off = round_up(off + H * W * kD * kb);
     L->off_rec_u = off;
-    off = round_up(off + H * W * kD * ub);
+    off = round_up(off + H * W * ub);
     L->total_bytes = off;
     L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * cw * kD * 4;
-    L->record_bytes_per_head = W * (4 * gw + kD * kb + kD * ub);
+    L->record_bytes_per_head = W * (4 * gw + kD * kb + ub);
 }
 
 int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
@@ -109,6 +111,8 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->key_bf16 = key_bf16(&layer->cfg);
     sv->kda = layer->cfg.decay == LEAPQ_DECAY_CHANNEL;
     sv->u_bf16 = layer->cfg.rec_dtype == LEAPQ_BF16;
+    sv->u_fp8 = layer->cfg.rec_dtype == LEAPQ_FP8;
+    sv->u_rec_bytes = layer->cfg.rec_dtype == LEAPQ_BF16 ? 2 * kD : layer->cfg.rec_dtype == LEAPQ_FP8 ? kD + 16 : 4 * kD;
     sv->r1 = layer->cfg.comp_fit != LEAPQ_COMP_LINES;
     sv->blk = layer->cfg.comp_fit == LEAPQ_COMP_BLOCK;
     return LEAPQ_OK;

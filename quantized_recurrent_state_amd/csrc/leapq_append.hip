@@ -88,6 +88,12 @@ hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const 
         else
             launch_append_t<uint16_t, uint16_t, false, false, false, uint16_t>(sv, heads, n, q, k, v, alpha, beta, o,
                                                                              g, s);
+    } else if (sv.u_fp8) {  // lossy fp8 corrections: as bf16 ones
+        if (!bf16)
+            launch_append_t<float, float, false, false, false, Fp8>(sv, heads, n, q, k, v, alpha, beta, o, g, s);
+        else
+            launch_append_t<uint16_t, uint16_t, false, false, false, Fp8>(sv, heads, n, q, k, v, alpha, beta, o, g,
+                                                                        s);
     } else if (sv.kda) {
         if (!bf16)
             launch_append_t<float, float, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o, g, s);

@@ -27,18 +27,40 @@ struct InLds<uint16_t> {
     }
 };
 
+// Record corrections kept as fp8 (an option): a record's 128 corrections in
+// stored order are 128 E4M3 codes, then 4 fp32 scales, scale j serving
+// stored positions 32 j .. 32 j + 31 (value columns c with c % 4 = j, the
+// columns of wave j); the value is decode(code) * scale, exact.
+struct Fp8 {};
+template <>
+struct InLds<Fp8> {
+    __device__ static float get(const float *base, int vecno, int e)
+    {
+        (void)vecno;
+        return e4m3_to_f32(reinterpret_cast<const uint8_t *>(base)[e]) * base[32 + (e >> 5)];
+    }
+};
+template <typename U>
+struct UBytes {
+    static constexpr int value = D * (int)sizeof(U);
+};
+template <>
+struct UBytes<Fp8> {
+    static constexpr int value = D + 16;
+};
+
 // A record as stored and as staged in LDS: the key in dtype T (row order;
 // the input dtype stores the token's k exactly unless the append normalizes
 // it, which needs fp32), then the correction (fp32, stored order); keys take
 // kbytes, a staged record stride floats.
 // With per-channel decay (CH) a record also holds its cumulative decay as a
 // 128-vector; the staged record is then [decay | correction | key].  U: the
-// correction's storage dtype (fp32, or bf16 as a lossy option).
+// correction's storage (fp32, or bf16 or fp8 as lossy options).
 template <typename T, bool CH = false, typename U = float>
 struct Rec {
     static constexpr int kbytes = D * (int)sizeof(T);
     static constexpr int kf = kbytes / 4;
-    static constexpr int ubytes = D * (int)sizeof(U);
+    static constexpr int ubytes = UBytes<U>::value;
     static constexpr int uf = ubytes / 4;
     static constexpr int goff = 0;                   // CH: the decay vector
     static constexpr int uoff = CH ? D : kf;         // the correction
@@ -364,6 +386,10 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     for (int r = 0; r < n; ++r) acc = fma_(coef[vec * 64 + r], R::u(rec + r * R::stride, uc), acc);
     // k lanes form u; q lanes receive it from lane l-16 and finish o
     const float u = b_h * (v_c - acc);
+    // fp8 records: the scale of this wave's 32 corrections from their
+    // largest magnitude (q lanes contribute 0)
+    float s8 = 1.0f;
+    if constexpr (std::is_same<U, Fp8>::value) s8 = fp8_scale(wave_max(vec == 0 ? fabsf(u) : 0.0f));
     auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(u), false, false);
     const float u_from_k = __uint_as_float(sw[0]);
     // the record goes to HBM, or (REC_LDS) into slot n of the staged records
@@ -371,15 +397,21 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
     uint32_t *rk = REC_LDS ? reinterpret_cast<uint32_t *>(L.rec + n * R::stride + R::koff)
                            : reinterpret_cast<uint32_t *>(hs.rk + n * R::kbytes);
     if (vec == 0) {
-        // the record's correction (rounded to nearest even with bf16 U); this
-        // token's own output below uses the fp32 u
+        // the record's correction (rounded to nearest even with bf16 or fp8
+        // U); this token's own output below uses the fp32 u
         if constexpr (std::is_same<U, float>::value) {
             if constexpr (REC_LDS)
                 reinterpret_cast<float *>(ru)[uc] = u;
             else
                 st_stream(reinterpret_cast<float *>(ru) + uc, u);
-        } else
+        } else if constexpr (std::is_same<U, Fp8>::value) {
+            // u / s is exact (s is a power of two, 1 / s = 2^-e)
+            const float inv = __uint_as_float((254u - (__float_as_uint(s8) >> 23)) << 23);
+            reinterpret_cast<uint8_t *>(ru)[uc] = (uint8_t)f32_to_e4m3(u * inv);
+            if (l == 0) reinterpret_cast<float *>(ru + D)[w] = s8;
+        } else {
             reinterpret_cast<uint16_t *>(ru)[uc] = f32_to_bf16_rne(u);
+        }
     } else {
         st_stream(o + (size_t)h * D + c, fma_(kqd[0], u_from_k, acc));
     }

@@ -105,7 +105,7 @@ struct HeadState {
     float *cvec;
     float *rgam;
     char *rk;  // keys in the input dtype, row order
-    char *ru;  // corrections (fp32 or bf16), stored order
+    char *ru;  // corrections (fp32, bf16, or fp8 codes then 4 scales), stored order
 };
 
 __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
@@ -118,12 +118,49 @@ __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
     s.cvec = sv.cvec + (size_t)h * sv.C * D * (sv.r1 ? 2 : 1);
     s.rgam = sv.rgam + (size_t)h * sv.W * (sv.kda ? D : 1);
     s.rk = static_cast<char *>(sv.rk) + (size_t)h * sv.W * D * (sv.key_bf16 ? 2 : 4);
-    s.ru = static_cast<char *>(sv.ru) + (size_t)h * sv.W * D * (sv.u_bf16 ? 2 : 4);
+    s.ru = static_cast<char *>(sv.ru) + (size_t)h * sv.W * sv.u_rec_bytes;
     return s;
 }
 
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// OCP 8-bit floating point E4M3 (sign, 4 exponent bits with bias 7, 3
+// mantissa bits; exponent field 0 holds the subnormals m * 2^-9; largest
+// finite value 448; no infinity).  The code of x, |x| <= 448, rounded to
+// nearest, ties to even, in integer steps: a normal value keeps its top 3
+// mantissa bits plus a carry (which may carry into the exponent field); a
+// value below 2^-6 becomes rint(|x| * 2^9), exact before the rounding.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x)
+{
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const int e = (int)((b >> 23) & 0xffu) - 127;
+    uint32_t mag;
+    if (e >= -6) {
+        const uint32_t f = b & 0x7fffffu, rem = f & 0xfffffu, m = f >> 20;
+        mag = ((uint32_t)(e + 7) << 3) + m + ((rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ? 1u : 0u);
+    } else {
+        mag = (uint32_t)__builtin_rintf(__uint_as_float(b & 0x7fffffffu) * 512.0f);
+    }
+    return sign | mag;
+}
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c)
+{
+    const uint32_t E = (c >> 3) & 15u, m = c & 7u;
+    const float v = E == 0 ? (float)m * 0x1p-9f : __uint_as_float(((E + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+// The smallest power of two s >= 2^-126 with M <= 448 s (M >= 0 finite):
+// M = 1.f * 2^(E - 127) needs s = 2^(E - 135), or 2^(E - 134) when 1.f > 1.75.
+__device__ __forceinline__ float fp8_scale(float M)
+{
+    const uint32_t b = __float_as_uint(M);
+    const int E = (int)(b >> 23);
+    int e = E - 135 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+    e = (E == 0 || e < -126) ? -126 : e;
+    return __uint_as_float((uint32_t)(e + 127) << 23);
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {

@@ -1130,6 +1130,11 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
             launch_fold_t<uint16_t, false, uint16_t>(sv, heads, n, smoothing, floor_, s);
         else
             launch_fold_t<float, false, uint16_t>(sv, heads, n, smoothing, floor_, s);
+    } else if (sv.u_fp8) {
+        if (sv.key_bf16)
+            launch_fold_t<uint16_t, false, Fp8>(sv, heads, n, smoothing, floor_, s);
+        else
+            launch_fold_t<float, false, Fp8>(sv, heads, n, smoothing, floor_, s);
     } else if (sv.kda) {
         if (sv.key_bf16)
             launch_fold_t<uint16_t, true>(sv, heads, n, smoothing, floor_, s);
@@ -1185,6 +1190,13 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
         else
             launch_append_fold_t<uint16_t, uint16_t, false, false, false, uint16_t>(
                 sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s);
+    } else if (sv.u_fp8) {
+        if (!bf16)
+            launch_append_fold_t<float, float, false, false, false, Fp8>(sv, heads, n, q, k, v, alpha, beta, o,
+                                                                       smoothing, floor_, g, s);
+        else
+            launch_append_fold_t<uint16_t, uint16_t, false, false, false, Fp8>(sv, heads, n, q, k, v, alpha, beta,
+                                                                             o, smoothing, floor_, g, s);
     } else if (sv.kda) {
         if (!bf16)
             launch_append_fold_t<float, float, false, false, true>(sv, heads, n, q, k, v, alpha, beta, o, smoothing,
@@ -1254,6 +1266,11 @@ hipError_t launch_step(const StateView &sv, int heads, int heads_per_req, const 
             LQ_ST(float, float, false, false, false, uint16_t);
         else
             LQ_ST(uint16_t, uint16_t, false, false, false, uint16_t);
+    } else if (sv.u_fp8) {
+        if (!bf16)
+            LQ_ST(float, float, false, false, false, Fp8);
+        else
+            LQ_ST(uint16_t, uint16_t, false, false, false, Fp8);
     } else if (sv.kda) {
         if (!bf16)
             LQ_ST(float, float, false, false, true);
@@ -1295,6 +1312,11 @@ hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float
             LQ_DQ(uint16_t, false, uint16_t, false);
         else
             LQ_DQ(float, false, uint16_t, false);
+    } else if (sv.u_fp8) {
+        if (sv.key_bf16)
+            LQ_DQ(uint16_t, false, Fp8, false);
+        else
+            LQ_DQ(float, false, Fp8, false);
     } else if (sv.kda) {
         if (sv.key_bf16)
             LQ_DQ(uint16_t, true, float, false);

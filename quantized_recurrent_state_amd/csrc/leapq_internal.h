@@ -16,12 +16,14 @@ struct StateView {
     float *cvec;
     float *rgam;
     void *rk;  // record keys in the input dtype (fp32 or bf16)
-    void *ru;  // record corrections (fp32, or bf16 with u_bf16)
+    void *ru;  // record corrections (fp32, bf16 with u_bf16, fp8 codes and scales with u_fp8)
     int C;  // compensator lines per head
     int W;  // record slots per head
     int key_bf16;  // record keys (and inputs) are bf16
     int kda;       // per-channel decay: alpha [heads][128], record decays [W][128]
     int u_bf16;    // record corrections stored in bf16
+    int u_fp8;     // record corrections stored as E4M3 codes with 4 power-of-two scales
+    int u_rec_bytes;  // bytes of one record's corrections: 512 (fp32), 256 (bf16), 144 (fp8)
     int r1;        // compensator pairs [C][2][128] (a, b) in place of lines
     int blk;       // the pairs are fitted as a block (with r1)
 };

@@ -25,6 +25,7 @@ LEAPQ_ERR_HIP = -7
 
 LEAPQ_F32 = 0
 LEAPQ_BF16 = 1
+LEAPQ_FP8 = 2  # record corrections only
 
 LEAPQ_DECAY_SCALAR = 0
 LEAPQ_DECAY_CHANNEL = 1
@@ -125,7 +126,8 @@ def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1
     c.in_dtype = LEAPQ_BF16 if in_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
     c.qk_norm = int(bool(qk_norm))
     c.decay = LEAPQ_DECAY_CHANNEL if decay in ("channel", LEAPQ_DECAY_CHANNEL) else LEAPQ_DECAY_SCALAR
-    c.rec_dtype = LEAPQ_BF16 if rec_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else LEAPQ_F32
+    c.rec_dtype = (LEAPQ_BF16 if rec_dtype in ("bf16", torch.bfloat16, LEAPQ_BF16) else
+                   LEAPQ_FP8 if rec_dtype in ("fp8", LEAPQ_FP8) else LEAPQ_F32)
     fits = {"lines": LEAPQ_COMP_LINES, "rank1": LEAPQ_COMP_RANK1, "block": LEAPQ_COMP_BLOCK}
     c.comp_fit = fits.get(comp_fit, comp_fit)
     return c
@@ -273,8 +275,12 @@ class Layer:
         return self._sec(self.layout.off_rec_k, self.heads * W * D, self.key_dtype, (self.heads, W, D))
 
     def rec_u_physical(self):
-        """Record corrections [heads, W, 128] as stored (fp32, or bf16 with rec_dtype bf16)."""
+        """Record corrections [heads, W, 128] as stored (fp32, or bf16 with rec_dtype bf16); with
+        rec_dtype fp8 the tuple (E4M3 codes uint8 [heads, W, 128], scales fp32 [heads, W, 4])."""
         W = self.cfg.window
+        if self.cfg.rec_dtype == LEAPQ_FP8:
+            raw = self._sec(self.layout.off_rec_u, self.heads * W * (D + 16), torch.uint8, (self.heads, W, D + 16))
+            return raw[:, :, :D], raw[:, :, D:].contiguous().view(torch.float32)
         dt = torch.bfloat16 if self.cfg.rec_dtype == LEAPQ_BF16 else torch.float32
         return self._sec(self.layout.off_rec_u, self.heads * W * D, dt, (self.heads, W, D))
 
@@ -283,8 +289,13 @@ class Layer:
         return self.rec_k_physical().float()
 
     def rec_u(self):
-        """Record corrections [heads, W, 128] in logical value-column order."""
+        """Record corrections [heads, W, 128] in logical value-column order, as fp32 (fp8 codes are
+        decoded with torch's float8_e4m3fn and multiplied by their group's scale)."""
         c = torch.arange(D, device=self.device)
+        if self.cfg.rec_dtype == LEAPQ_FP8:
+            codes, scales = self.rec_u_physical()
+            vals = codes.contiguous().view(torch.float8_e4m3fn).float() * scales.repeat_interleave(32, dim=2)
+            return vals[:, :, corr_pos(c)]
         return self.rec_u_physical()[:, :, corr_pos(c)].float()
 
 

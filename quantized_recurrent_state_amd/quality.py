@@ -19,7 +19,7 @@ the GPU output and whether a fold followed; the parity tests use it to run
 CPU reference heads beside the GPU path.
 
   python -m quantized_recurrent_state_amd.quality [--workload long] [--layers 3]
-         [--tokens 4095] [--rec-dtype f32|bf16] [--comp-fit lines|rank1|block]
+         [--tokens 4095] [--rec-dtype f32|bf16|fp8] [--comp-fit lines|rank1|block]
          [--out result.json]
 """
 import argparse
@@ -113,8 +113,8 @@ def main(argv=None):
     p.add_argument("--workload", default="long")
     p.add_argument("--layers", type=int, default=None)
     p.add_argument("--tokens", type=int, default=None)
-    p.add_argument("--rec-dtype", default="f32", choices=("f32", "bf16"),
-                   help="storage of the record corrections (bf16: the lossy lower-precision option)")
+    p.add_argument("--rec-dtype", default="f32", choices=("f32", "bf16", "fp8"),
+                   help="storage of the record corrections (bf16, fp8: the lossy lower-precision options)")
     p.add_argument("--comp-fit", default="lines", choices=("lines", "rank1", "block"),
                    help="compensator fit: whole rows/columns, rank-one pairs from power sweeps, or pairs "
                         "fitted as a block warm-started from the previous window")

@@ -61,6 +61,9 @@ void lqo_gdn_step_bf16(uint16_t *, const float *, const float *, const float *, 
 void lqo_kda_step_f32(float *, const float *, const float *, const float *, const float *, float, float *, float *);
 uint16_t lqo_f32_to_bf16(float);
 void lqo_round_bf16(float *, int);
+uint8_t lqo_f32_to_e4m3(float);
+float lqo_e4m3_to_f32(uint8_t);
+void lqo_round_fp8_record(float *);
 float lqo_t128_sum(const float *);
 float lqo_t128_dot(const float *, const float *);
 }
@@ -237,6 +240,8 @@ static void part_abi()
             abi_layer(c);
             c.decay = LEAPQ_DECAY_SCALAR;
             c.rec_dtype = LEAPQ_BF16;
+            abi_layer(c);
+            c.rec_dtype = LEAPQ_FP8;
             abi_layer(c);
         }
     // invalid configurations
@@ -420,6 +425,12 @@ static void part_oracle()
         lqo_gdn_step_bf16(Sb.data(), x.data(), y.data(), x.data(), 0.9f, 0.5f, u.data(), o.data());
         CHECK(lqo_f32_to_bf16(1.0f) == 0x3f80 && lqo_f32_to_bf16(-0.0f) == 0x8000);
         lqo_round_bf16(x.data(), D);
+        for (int c = 0; c < 256; ++c)
+            if ((c & 0x7f) != 0x7f) CHECK(lqo_f32_to_e4m3(lqo_e4m3_to_f32((uint8_t)c)) == (uint8_t)c);
+        std::vector<float> rec(D);
+        for (int i = 0; i < D; ++i) rec[i] = ldexpf(gauss(), (i % 7) * 9 - 30);
+        lqo_round_fp8_record(rec.data());
+        CHECK(finite(rec.data(), D));
         const float sx = lqo_t128_sum(x.data()), dxy = lqo_t128_dot(x.data(), y.data());
         CHECK(isfinite(sx) && isfinite(dxy));
     }

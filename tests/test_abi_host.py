@@ -347,6 +347,25 @@ def test_bf16_corrections_layout_and_checks():
     assert call_gated(fake_layer(cfg(rec_dtype="bf16")), gate_struct()) == lq.LEAPQ_ERR_RANGE
 
 
+def test_fp8_corrections_layout_and_checks():
+    for dt, e in (("bf16", 2), ("f32", 4)):
+        L = layout(batch=2, heads=4, window=16, n_comp=4, in_dtype=dt, rec_dtype="fp8")
+        assert L.total_bytes - L.off_rec_u >= 2 * 4 * 16 * 144
+        assert L.record_bytes_per_head == 16 * (4 + 128 * e + 144), dt
+        assert L.off_rec_u % 256 == 0
+    out = lq.leapq_layout()
+    for kw in (dict(decay="channel"), dict(qk_norm=True), dict(comp_fit="rank1"), dict(comp_fit="block")):
+        c = cfg(rec_dtype="fp8", **kw)
+        assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
+    c = cfg()
+    c.rec_dtype = 3
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_DTYPE
+    c = cfg()
+    c.in_dtype = lq.LEAPQ_FP8  # fp8 is a record format, not an input dtype
+    assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_DTYPE
+    assert call_gated(fake_layer(cfg(rec_dtype="fp8")), gate_struct()) == lq.LEAPQ_ERR_RANGE
+
+
 # ---------------------------------------------------------------- rank-one compensators
 
 def test_rank1_layout_and_checks():

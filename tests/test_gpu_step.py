@@ -45,6 +45,7 @@ def _skip_some(t, b):
     ("gated_f32", _wl("tiny", batch=3, heads=2, seed=113), 36, [2, 0, 6], dict(gated=GATE)),
     ("kda", _wl("tiny_kda", batch=3, heads=2, seed=114), 40, [0, 4, 10], {}),
     ("bf16_records", _wl("tiny", batch=3, heads=2, in_dtype="bf16", seed=115), 40, [0, 6, 2], dict(rec_u="bf16")),
+    ("fp8_records", _wl("tiny", batch=3, heads=2, in_dtype="bf16", seed=118), 40, [0, 6, 2], dict(rec_u="fp8")),
     ("rank1", _wl("tiny", batch=3, heads=2, seed=116, init="prefill"), 36, [0, 8, 3], dict(fit="rank1")),
     ("block", _wl("tiny", batch=3, heads=2, seed=117, init="prefill"), 36, [0, 8, 3], dict(fit="block")),
     ("C0_W1", _wl("tiny", batch=2, heads=2, window=1, n_comp=0, smoothing=False, seed=118), 8, [0, 2], {}),
