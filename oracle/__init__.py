@@ -43,6 +43,8 @@ def _bind(L):
         "lqo_current": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, f32p]),
         "lqo_quantize": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
         "lqo_init": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_init_bits": (None, [f32p, ci, ci, cf, ci, i8p, f32p, f32p, i32p, f32p]),
+        "lqo_fold_bits": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf, ci]),
         "lqo_quantize_keyrow": (None, [f32p, ci, ci, cf, i8p, f32p, f32p, i32p, f32p]),
         "lqo_boundary_keyrow": (None, [i8p, f32p, f32p, ci, i32p, f32p, f32p]),
         "lqo_fold": (None, [i8p, f32p, f32p, ci, i32p, f32p, ci, f32p, f32p, f32p, ci, cf]),
@@ -173,8 +175,13 @@ class Head:
     """
 
     def __init__(self, C=4, W=16, smoothing=True, sigma_floor=1e-6, L=None, decay="scalar", rec_u="f32",
-                 fit="lines"):
+                 fit="lines", bits=8):
         self.L = L or lib()
+        if bits not in (8, 6, 4):
+            raise ValueError("bits must be 8, 6 or 4")
+        if bits != 8 and (decay != "scalar" or fit != "lines"):
+            raise ValueError("6- and 4-bit states are defined for scalar decay and line compensators")
+        self.bits = int(bits)
         self.C, self.W, self.smoothing, self.floor = int(C), int(W), int(smoothing), float(sigma_floor)
         if decay not in ("scalar", "channel"):
             raise ValueError("decay must be 'scalar' or 'channel'")
@@ -215,6 +222,11 @@ class Head:
     def init(self, S0):
         S0 = f32(S0).reshape(D, D)
         fp = ctypes.c_float
+        if self.bits != 8:
+            self.L.lqo_init_bits(_p(S0, fp), self.C, self.smoothing, self.floor, self.bits, _p(self.Q, ctypes.c_int8),
+                                 _p(self.rho, fp), _p(self.sigma, fp), _p(self.idx, ctypes.c_int32), _p(self.vec, fp))
+            self.n = 0
+            return self
         fn = self.L.lqo_init_block if self.block else self.L.lqo_init_r1 if self.r1 else self.L.lqo_init
         fn(_p(S0, fp), self.C, self.smoothing, self.floor, _p(self.Q, ctypes.c_int8),
            _p(self.rho, fp), _p(self.sigma, fp), _p(self.idx, ctypes.c_int32), _p(self.vec, fp))
@@ -248,6 +260,10 @@ class Head:
         return o, self.ru[self.n - 1].copy()
 
     def fold(self):
+        if self.bits != 8:
+            self.L.lqo_fold_bits(*self._st(), *self._rec(), self.smoothing, self.floor, self.bits)
+            self.n = 0
+            return self
         if self.kda:
             fn = self.L.lqo_fold_kda
         elif self.block:
@@ -279,7 +295,7 @@ class Head:
         return out
 
     def copy(self):
-        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay, self.rec_u, self.fit)
+        h = Head(self.C, self.W, self.smoothing, self.floor, self.L, self.decay, self.rec_u, self.fit, self.bits)
         for name in ("Q", "rho", "sigma", "idx", "vec", "gam", "rk", "ru"):
             setattr(h, name, getattr(self, name).copy())
         h.n = self.n

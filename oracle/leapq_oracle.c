@@ -225,7 +225,18 @@ void lqo_quantize(float *R, int C, int smoothing, float sigma_floor,
 
 /* Smoothing and per-row int8 of the residual R (what remains after the
  * compensators), shared by both compensator fits. */
+/* lv: the largest code; 127 for the int8 state, 31 or 7 for the 6- and
+ * 4-bit options (symmetric codes -lv .. lv, scale absmax / lv). */
+static void smooth_and_round_lv(float *R, int smoothing, float sigma_floor, float lv, int8_t *Q, float *rho,
+                                float *sigma);
+
 static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t *Q, float *rho, float *sigma)
+{
+    smooth_and_round_lv(R, smoothing, sigma_floor, 127.0f, Q, rho, sigma);
+}
+
+static void smooth_and_round_lv(float *R, int smoothing, float sigma_floor, float lv, int8_t *Q, float *rho,
+                                float *sigma)
 {
     /* Residual smoothing ([LQ] 3.4): per value column, the square root of
      * the mean absolute value over the key rows, with a positive floor. */
@@ -243,7 +254,7 @@ static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t 
         inv_sigma[c] = 1.0f / s;
     }
 
-    /* Symmetric per-row int8 with round half to even ([LQ] abstract: 8-bit
+    /* Symmetric per-row codes (int8: lv = 127) with round half to even ([LQ] abstract: 8-bit
      * state; [RN4] Why rounding: rounded once per window).  A code is the
      * integer nearest to the exact product x * g, ties to even: one rounding
      * (the float64 product of two floats is exact). */
@@ -259,12 +270,12 @@ static void smooth_and_round(float *R, int smoothing, float sigma_floor, int8_t 
             for (int c = 0; c < D; ++c) Q[r * D + c] = 0;
             continue;
         }
-        rho[r] = M / 127.0f;
-        float g = 127.0f / M;
+        rho[r] = M / lv;
+        float g = lv / M;
         for (int c = 0; c < D; ++c) {
             float y = (float)rint((double)x[c] * (double)g);
-            if (y > 127.0f) y = 127.0f;
-            if (y < -127.0f) y = -127.0f;
+            if (y > lv) y = lv;
+            if (y < -lv) y = -lv;
             Q[r * D + c] = (int8_t)y;
         }
     }
@@ -355,6 +366,34 @@ void lqo_fold(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *v
     float R[D * D];
     lqo_current(Q, rho, sigma, C, idx, vec, n, gam, rk, ru, R);
     lqo_quantize(R, C, smoothing, sigma_floor, Q, rho, sigma, idx, vec);
+}
+
+/* ------------------------------------------------------------------ */
+/* 6- and 4-bit residual states (an option; [LQ] 4.2 reports LeapQuant  */
+/* at 6 and 4 bits beside 8): the same fold with symmetric codes of     */
+/* -31 .. 31 or -7 .. 7 (scale absmax / 31 or / 7).  bits = 8 is the    */
+/* int8 state.  The codes keep their logical int8 array here; only the  */
+/* GPU layout packs them.                                               */
+/* ------------------------------------------------------------------ */
+static float levels_of(int bits) { return bits == 4 ? 7.0f : bits == 6 ? 31.0f : 127.0f; }
+
+void lqo_init_bits(const float *S0, int C, int smoothing, float sigma_floor, int bits,
+                   int8_t *Q, float *rho, float *sigma, int32_t *idx, float *vec)
+{
+    float R[D * D];
+    memcpy(R, S0, sizeof R);
+    extract_lines(R, C, idx, vec);
+    smooth_and_round_lv(R, smoothing, sigma_floor, levels_of(bits), Q, rho, sigma);
+}
+
+void lqo_fold_bits(int8_t *Q, float *rho, float *sigma, int C, int32_t *idx, float *vec,
+                   int n, const float *gam, const float *rk, const float *ru,
+                   int smoothing, float sigma_floor, int bits)
+{
+    float R[D * D];
+    lqo_current(Q, rho, sigma, C, idx, vec, n, gam, rk, ru, R);
+    extract_lines(R, C, idx, vec);
+    smooth_and_round_lv(R, smoothing, sigma_floor, levels_of(bits), Q, rho, sigma);
 }
 
 /* ------------------------------------------------------------------ */

@@ -159,6 +159,57 @@ def pin_textbook_int8(L):
         assert int(diff.sum()) <= 2
 
 
+def pin_low_bit_textbook(L):
+    """6- and 4-bit states with C = 0 and no smoothing are per-row symmetric
+    absmax codes with 31 or 7 levels: scale = max|x| / L, code =
+    round-half-even(x L / max), computed here in float64; every live row
+    reaches +-L, no code exceeds L, and a code may differ only within 1e-5
+    of a .5 boundary."""
+    rng = np.random.default_rng(7)
+    for bits, lv in ((6, 31.0), (4, 7.0)):
+        for trial in range(3):
+            R = (rng.standard_normal((D, D)) * (10.0 ** rng.integers(-3, 3, (D, 1)))).astype(np.float32)
+            h = oracle.Head(C=0, smoothing=False, L=L, bits=bits).init(R)
+            M = np.abs(R.astype(np.float64)).max(axis=1)
+            assert np.allclose(h.rho, M / lv, rtol=2e-7, atol=0)
+            y = R.astype(np.float64) * (lv / M)[:, None]
+            want = np.rint(y)
+            diff = h.Q.astype(np.float64) != want
+            near = np.abs(np.abs(y - np.trunc(y)) - 0.5) < 1e-5
+            assert not np.any(diff & ~near), (bits, np.argwhere(diff & ~near)[:5])
+            assert np.abs(h.Q).max() == lv and np.all(np.abs(h.Q).max(axis=1) == lv)
+
+
+def pin_low_bit_planted(L):
+    """6- and 4-bit states pick the planted outlier lines of the tiny case
+    as their compensators, as the int8 state does."""
+    wl = workloads.Workload("pin", 1, 1, 4, 16, init="gauss", seed=0)
+    G, lines = workloads.initial_state(wl, 0, return_lines=True)
+    for bits in (6, 4):
+        for h_ in range(4):
+            want = set(int(r) for r in lines[0][0, h_]) | set(D + int(c) for c in lines[1][0, h_])
+            got = oracle.Head(C=4, L=L, bits=bits).init(G.numpy()[0, h_]).idx
+            assert set(int(i) for i in got) == want
+
+
+def pin_low_bit_window(L):
+    """A window from a 4-bit boundary equals the float64 dense recurrence
+    from that boundary (outputs and rebuilt state to 1e-5); the fold then
+    equals a fresh 4-bit quantization of the rebuilt state."""
+    S0, toks = tiny_inputs(seed=45, tokens=16, init="prefill")
+    h = oracle.Head(C=4, W=16, L=L, bits=4).init(S0[0])
+    S = h.dequant(1).astype(np.float64)
+    for (q, k, v, a, b) in toks:
+        o, _ = h.append(q, k, v, a, b)
+        _, o64 = np_gdn_f64(S, q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), float(a), float(b))
+        assert rel(o, o64) < 1e-5
+    cur = h.dequant(2)
+    assert rel(cur, S) < 1e-5
+    h.fold()
+    want = oracle.Head(C=4, W=16, L=L, bits=4).init(cur)
+    assert np.array_equal(h.Q, want.Q) and np.array_equal(h.rho, want.rho) and np.array_equal(h.idx, want.idx)
+
+
 def pin_smoothing_closed_form(L):
     """Column c holds +-s_c (alternating signs) with s_c a power of 4, so the mean
     absolute value over the key rows is s_c and sigma_c = sqrt(s_c) exactly;
@@ -292,12 +343,13 @@ def pin_greedy_bruteforce(L):
 def pin_reconstruction_bound(L):
     """After quantization every entry is within half a step rho_r*sigma_c of
     the input (plus a few fp32 roundings), and extracted lines come back
-    exactly.  Error budget: |code*rho*sigma - R| <= rho*sigma*(0.5 + 1200*2^-24)."""
+    exactly; for the int8 state and the 6- and 4-bit options.  Error budget:
+    |code*rho*sigma - R| <= rho*sigma*(0.5 + 1200*2^-24)."""
     S0, _ = tiny_inputs(seed=2, tokens=1, heads=2)
-    for sm in (True, False):
+    for sm, bits in ((True, 8), (False, 8), (True, 6), (False, 4), (True, 4)):
         for h_ in range(2):
             R = S0[h_]
-            h = oracle.Head(C=4, smoothing=sm, L=L).init(R)
+            h = oracle.Head(C=4, smoothing=sm, L=L, bits=bits).init(R)
             res = h.dequant(0).astype(np.float64)
             B = h.dequant(1)
             step = h.rho.astype(np.float64)[:, None] * h.sigma.astype(np.float64)[None, :]
@@ -932,7 +984,7 @@ ALL = [
     pin_overwrite_identity, pin_fold_invariants, pin_xor_equivariance, pin_zero_state,
     pin_tiny_rows, pin_dense_steps, pin_window_one, pin_gate_closed_forms, pin_l2norm, pin_gated_window,
     pin_kda_window_vs_dense_f64, pin_kda_uniform_is_gdn, pin_kda_dense_step, pin_bf16_records,
-    pin_fp8_codec, pin_fp8_records,
+    pin_fp8_codec, pin_fp8_records, pin_low_bit_textbook, pin_low_bit_planted, pin_low_bit_window,
     pin_rank1_fit, pin_rank1_window_and_fold, pin_rank1_zero_state,
     pin_block_start_rows, pin_block_fit_svd, pin_block_fit_steps, pin_block_warm_fixed_point,
     pin_block_zero_state, pin_block_window_and_fold,

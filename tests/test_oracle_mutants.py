@@ -39,7 +39,9 @@ MUTANTS = [
     ("smooth_mean_64", "* 0.0078125f", "* 0.015625f"),
     ("smooth_no_floor", "if (s < sigma_floor) s = sigma_floor;", ";"),
     ("smooth_no_sqrt", "s = sqrtf(m);", "s = m;"),
-    ("quant_128", "rho[r] = M / 127.0f;", "rho[r] = M / 128.0f;"),
+    ("quant_128", "rho[r] = M / lv;", "rho[r] = M / (lv + 1.0f);"),
+    ("bits_levels_swapped", "return bits == 4 ? 7.0f : bits == 6 ? 31.0f : 127.0f;",
+     "return bits == 4 ? 15.0f : bits == 6 ? 63.0f : 127.0f;"),
     ("quant_round_away", "rint((double)x[c] * (double)g)", "round((double)x[c] * (double)g)"),
     ("quant_truncate", "rint((double)x[c] * (double)g)", "trunc((double)x[c] * (double)g)"),
     ("quant_double_rounding", "(float)rint((double)x[c] * (double)g)", "rintf(x[c] * g)"),
