@@ -52,6 +52,8 @@ def parse():
                    help="skip the measurement of the lossy bf16 record-corrections option")
     p.add_argument("--no-fp8-records", action="store_true",
                    help="skip the measurement of the lossy fp8 record-corrections option")
+    p.add_argument("--no-low-bits", action="store_true",
+                   help="skip the measurement of the 6- and 4-bit residual-state options")
     p.add_argument("--no-rank1", action="store_true",
                    help="skip the measurement of the rank-one compensator option")
     p.add_argument("--no-block", action="store_true",
@@ -312,7 +314,7 @@ def main():
 
     # ---- layout options on the same inputs and schedule (separate
     # measurements, never the headline value)
-    def time_option(vcfg, u_bytes=4, rank1=False):
+    def time_option(vcfg, u_bytes=4, rank1=False, bits=8):
         vlayers = []
         for l in range(Lyr):
             L = lq.Layer(vcfg, dev)
@@ -349,7 +351,7 @@ def main():
         del vlayers
         torch.cuda.empty_cache()
         v_app = float(np.mean([1e3 * x.elapsed_time(y) for pos, x, y in vev if pos < W - 1]))
-        v_bytes = float(np.mean([metrics.append_bytes(n, C, in_bytes, u_bytes=u_bytes, rank1=rank1)
+        v_bytes = float(np.mean([metrics.append_bytes(n, C, in_bytes, u_bytes=u_bytes, rank1=rank1, bits=bits)
                                  for n in range(W - 1)])) * H
         return {"tokens_per_s": B * W / (v_ms / 1e3), "ms_per_step": v_ms, "steps": vsteps,
                 "ratio_to_plain": (B * W / (v_ms / 1e3)) / tokens_per_s, "append_us": v_app,
@@ -374,6 +376,19 @@ def main():
         log(f"[bench] fp8 record corrections: {fp8rec['ms_per_step']:.3f} ms per window, "
             f"{fp8rec['tokens_per_s']:,.0f} tokens/s ({fp8rec['ratio_to_plain']:.3f} of the plain path); "
             f"append {fp8rec['append_us']:.1f} us")
+
+    low_bits = {}
+    if not args.no_low_bits:
+        for bits in (6, 4):
+            r = time_option(lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, state_bits=bits),
+                            bits=bits)
+            r["note"] = (f"residual codes of {bits} bits (symmetric, {31 if bits == 6 else 7} levels), packed "
+                         f"(see quality.py --state-bits {bits})")
+            low_bits[f"{bits}_bit_state"] = r
+            log(f"[bench] {bits}-bit residual state: {r['ms_per_step']:.3f} ms per window, "
+                f"{r['tokens_per_s']:,.0f} tokens/s ({r['ratio_to_plain']:.3f} of the plain path); append "
+                f"{r['append_us']:.1f} us ({r['append_gbps_algorithmic']:.0f} GB/s), last append + fold "
+                f"{r['append_fold_us']:.1f} us")
 
     rank1 = None
     if not args.no_rank1:
@@ -622,6 +637,7 @@ def main():
         "kda": kda,
         "bf16_record_corrections": bf16rec,
         "fp8_record_corrections": fp8rec,
+        "low_bit_states": low_bits or None,
         "rank1_compensators": rank1,
         "block_compensators": block,
         "staggered_phases": staggered,

@@ -53,7 +53,8 @@ extern "C" {
 #define LEAPQ_ERR_RANGE (-3)       /* batch/heads < 1, window not in [1,64], n_comp not in [0,8],
                                       smoothing or qk_norm not 0/1, sigma_floor not > 0, what not
                                       in {0,1,2}, heads*batch too large, n_records out of
-                                      [0, window], reserved fields not zero */
+                                      [0, window], state_bits not 0/8/6/4, an option combined
+                                      with one it excludes, reserved fields not zero */
 #define LEAPQ_ERR_ALIGN (-4)       /* state not 256-byte aligned, or a tensor not 16-byte aligned */
 #define LEAPQ_ERR_WINDOW_FULL (-5) /* append with n_records == window: fold first */
 #define LEAPQ_ERR_DTYPE (-6)       /* in_dtype / state_dtype not LEAPQ_F32 or LEAPQ_BF16, rec_dtype not
@@ -117,7 +118,12 @@ typedef struct leapq_config {
                             fitted by power sweeps) or LEAPQ_COMP_BLOCK (the pairs fitted as a block);
                             the pair fits require n_comp <= 4, scalar decay, rec_dtype LEAPQ_F32, and
                             are not taken by the gated entry points */
-    int32_t reserved[3]; /* must be zero */
+    int32_t state_bits;  /* bits per residual code: 0 or 8 (int8, the method's state), 6 or 4 (symmetric
+                            codes -31..31 or -7..7 with scale absmax / 31 or / 7, "LeapQuant" 4.2: the
+                            method at 6 and 4 bits); 6 and 4 require scalar decay, line compensators,
+                            rec_dtype LEAPQ_F32 and qk_norm = 0, and are not taken by the gated entry
+                            points or leapq_step */
+    int32_t reserved[2]; /* must be zero */
 } leapq_config;
 
 /* Byte layout of one layer's state buffer ("LeapQuant" 4.3: the boundary
@@ -129,7 +135,17 @@ typedef struct leapq_config {
  *   codes     int8  [heads][16384]     the code of (key row r, value column c)
  *                                      is byte 4096 (c % 4) + 1024 (r / 32)
  *                                      + 16 (iperm(r % 32) + 32 ((c / 4) % 2))
- *                                      + c / 8 of the head's block
+ *                                      + c / 8 of the head's block;
+ *             state_bits 4: [heads][8192], with w = c % 4, p = r / 32,
+ *                                      l = iperm(r % 32) + 32 ((c / 4) % 2),
+ *                                      m = c / 8: the nibble of byte 2048 w
+ *                                      + 1024 (p / 2) + 16 l + 8 (p % 2)
+ *                                      + 4 (m / 8) + m % 4, low nibble for
+ *                                      m % 8 < 4, else high (two's complement);
+ *             state_bits 6: [heads][12288], bits 0-3 as for 4 bits in the
+ *                                      first 8192 bytes, bits 4-5 at bit
+ *                                      2 (m / 4) of byte 8192 + 1024 w + 16 l
+ *                                      + 4 p + m % 4
  *   row_scale fp32  [heads][128]       rho_r
  *   col_scale fp32  [heads][128]       sigma_c
  *   comp_idx  int32 [heads][C]         -1 unused, 0..127 row r, 128+c column c
@@ -158,7 +174,7 @@ typedef struct leapq_config {
  * four 16-byte loads, each wave's loads 1 KB contiguous; the record keys and
  * corrections are the A operand order of the fold's matrix instructions).
  * boundary_bytes_per_head = 16384 + 512 + 512 + 4C + 512C (19,472 at C = 4:
- * 1.19 bytes per state element); record_bytes_per_head = W * (4 g + 128 e + f)
+ * 1.19 bytes per state element; 12,288 or 8,192 code bytes at 6 or 4 bits); record_bytes_per_head = W * (4 g + 128 e + f)
  * with e = 2 for bf16 inputs and qk_norm = 0, else 4, g = 1 (scalar decay)
  * or 128 (channel decay), and f = 512, 256 with rec_dtype = LEAPQ_BF16, or
  * 144 with LEAPQ_FP8. */

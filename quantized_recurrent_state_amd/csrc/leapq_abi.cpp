@@ -48,13 +48,24 @@ int32_t check_method_config(const leapq_config *c)
     if (c->comp_fit != LEAPQ_COMP_LINES &&
         (c->n_comp > 4 || c->decay != LEAPQ_DECAY_SCALAR || c->rec_dtype != LEAPQ_F32))
         return LEAPQ_ERR_RANGE;
-    if (c->reserved[0] || c->reserved[1] || c->reserved[2]) return LEAPQ_ERR_RANGE;
+    if (c->state_bits != 0 && c->state_bits != 8 && c->state_bits != 6 && c->state_bits != 4) return LEAPQ_ERR_RANGE;
+    if (c->state_bits == 6 || c->state_bits == 4) {
+        // the 6- and 4-bit options: scalar decay, line compensators, fp32 records, no normalizing appends
+        if (c->decay != LEAPQ_DECAY_SCALAR || c->comp_fit != LEAPQ_COMP_LINES || c->rec_dtype != LEAPQ_F32 ||
+            c->qk_norm)
+            return LEAPQ_ERR_RANGE;
+    }
+    if (c->reserved[0] || c->reserved[1]) return LEAPQ_ERR_RANGE;
     return LEAPQ_OK;
 }
 
 // Record keys are stored in the input dtype, which holds the token's k
 // exactly, unless the layer's gated appends normalize k (then fp32).
 bool key_bf16(const leapq_config *c) { return c->in_dtype == LEAPQ_BF16 && !c->qk_norm; }
+
+// bits per residual code (8 when the field is 0) and bytes of a head's codes
+int code_bits(const leapq_config *c) { return c->state_bits == 6 || c->state_bits == 4 ? c->state_bits : 8; }
+uint64_t code_bytes(const leapq_config *c) { return (uint64_t)kD * kD * code_bits(c) / 8; }
 
 void compute_layout(const leapq_config *c, leapq_layout *L)
 {
@@ -67,7 +78,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     const uint64_t cw = c->comp_fit != LEAPQ_COMP_LINES ? 2 : 1;   // compensator vectors (pairs: a, b)
     uint64_t off = 0;
     L->off_codes = off;
-    off = round_up(off + H * kD * kD);
+    off = round_up(off + H * code_bytes(c));
     L->off_row_scale = off;
     off = round_up(off + H * kD * 4);
     L->off_col_scale = off;
@@ -83,7 +94,7 @@ void compute_layout(const leapq_config *c, leapq_layout *L)
     L->off_rec_u = off;
     off = round_up(off + H * W * ub);
     L->total_bytes = off;
-    L->boundary_bytes_per_head = (uint64_t)kD * kD + 2 * kD * 4 + C * 4 + C * cw * kD * 4;
+    L->boundary_bytes_per_head = code_bytes(c) + 2 * kD * 4 + C * 4 + C * cw * kD * 4;
     L->record_bytes_per_head = W * (4 * gw + kD * kb + ub);
 }
 
@@ -115,6 +126,8 @@ int32_t view_of(const leapq_layer *layer, leapq::StateView *sv)
     sv->u_rec_bytes = layer->cfg.rec_dtype == LEAPQ_BF16 ? 2 * kD : layer->cfg.rec_dtype == LEAPQ_FP8 ? kD + 16 : 4 * kD;
     sv->r1 = layer->cfg.comp_fit != LEAPQ_COMP_LINES;
     sv->blk = layer->cfg.comp_fit == LEAPQ_COMP_BLOCK;
+    sv->cbits = code_bits(&layer->cfg);
+    sv->code_bytes = (int)code_bytes(&layer->cfg);
     return LEAPQ_OK;
 }
 
@@ -158,7 +171,7 @@ int32_t gate_of(const leapq_layer *layer, const leapq_gate *g, leapq::GateArgs *
 {
     if (!g || !g->A_log || !g->dt_bias) return LEAPQ_ERR_NULL;
     if (layer->cfg.decay != LEAPQ_DECAY_SCALAR || layer->cfg.rec_dtype != LEAPQ_F32 ||
-        layer->cfg.comp_fit != LEAPQ_COMP_LINES)
+        layer->cfg.comp_fit != LEAPQ_COMP_LINES || code_bits(&layer->cfg) != 8)
         return LEAPQ_ERR_RANGE;
     if (!aligned(g->A_log, 4) || !aligned(g->dt_bias, 4)) return LEAPQ_ERR_ALIGN;
     if (g->reserved[0] || g->reserved[1]) return LEAPQ_ERR_RANGE;
@@ -232,7 +245,7 @@ int32_t step_impl(leapq_layer *layer, const leapq_gate *gate, const int32_t *n_i
     if ((st = check_token(q, k, v, alpha, beta, o, sv.kda)) != LEAPQ_OK) return st;
     if (!n_in) return LEAPQ_ERR_NULL;
     if (!aligned(n_in, 4) || (n_out && !aligned(n_out, 4))) return LEAPQ_ERR_ALIGN;
-    if (layer->cfg.window > 16) return LEAPQ_ERR_RANGE;
+    if (layer->cfg.window > 16 || code_bits(&layer->cfg) != 8) return LEAPQ_ERR_RANGE;
     // every head of a request reads n_in while block 0 of the request writes n_out
     if (n_out) {
         const char *a0 = (const char *)n_in, *b0 = (const char *)n_out;

@@ -31,7 +31,7 @@ namespace leapq {
 namespace {
 using namespace dev;
 
-template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1>
+template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CB = 8>
 __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__restrict__ qin,
                                                 const T *__restrict__ kin, const T *__restrict__ vin,
                                                 const float *__restrict__ alpha, const float *__restrict__ beta,
@@ -43,28 +43,29 @@ __global__ __launch_bounds__(NT) void k_append(StateView sv, int n, const T *__r
     const HeadLds<T, K, CH, U, R1> L(dsm, n, sv.C);
     float *dots = dsm + head_lds_floats<T, K, CH, U, R1>(n, sv.C);
     uint4 qc[4];
-    append_issue<T, K, CH, U, R1>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    append_issue<T, K, CH, U, R1, CB>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
     float a_h = CH ? 1.0f : sload(alpha, h);  // with CH the decay vector is staged in LDS
     float b_h = sload(beta, h);
     if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
-    wait_lds_copies();
+    wait_lds_copies<CodeFmt<CB>::loads>();
     lds_barrier();
     if constexpr (GATED) {
         a_h = dots[kGateSlot];
         b_h = dots[kGateSlot + 1];
     }
-    append_compute<T, K, false, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
+    append_compute<T, K, false, NORM, CH, U, R1, CB>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps);
 }
 
 }  // namespace
 
-template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false>
+template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false,
+          int CB = 8>
 static void launch_append_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, float *o, const GateArgs &g, hipStream_t s)
 {
     const size_t lds = sizeof(float) * (head_lds_floats<T, K, CH, U, R1>(n, sv.C) + kDotFloats);
-    hipLaunchKernelGGL((k_append<T, K, GATED, NORM, CH, U, R1>), dim3(heads), dim3(NT), lds, s, sv, n, (const T *)q,
-                       (const T *)k, (const T *)v, alpha, beta, o, g);
+    hipLaunchKernelGGL((k_append<T, K, GATED, NORM, CH, U, R1, CB>), dim3(heads), dim3(NT), lds, s, sv, n,
+                       (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, g);
 }
 
 hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
@@ -75,7 +76,23 @@ hipError_t launch_append(const StateView &sv, int heads, int n, int bf16, const 
     // whose keys are fp32 because its gated appends normalize k; per-channel
     // decay comes with keys in the input dtype and no gates
     const bool kb = sv.key_bf16;
-    if (sv.r1) {  // rank-one compensators: scalar decay, fp32 corrections, keys in the input dtype, no gates
+    if (sv.cbits != 8) {  // 6- or 4-bit codes: scalar decay, lines, fp32 corrections, keys in the input dtype, no gates
+        if (sv.cbits == 6) {
+            if (!bf16)
+                launch_append_t<float, float, false, false, false, float, false, 6>(sv, heads, n, q, k, v, alpha, beta,
+                                                                                 o, g, s);
+            else
+                launch_append_t<uint16_t, uint16_t, false, false, false, float, false, 6>(sv, heads, n, q, k, v, alpha,
+                                                                                       beta, o, g, s);
+        } else {
+            if (!bf16)
+                launch_append_t<float, float, false, false, false, float, false, 4>(sv, heads, n, q, k, v, alpha, beta,
+                                                                                 o, g, s);
+            else
+                launch_append_t<uint16_t, uint16_t, false, false, false, float, false, 4>(sv, heads, n, q, k, v, alpha,
+                                                                                       beta, o, g, s);
+        }
+    } else if (sv.r1) {  // rank-one compensators: scalar decay, fp32 corrections, keys in the input dtype, no gates
         if (!bf16)
             launch_append_t<float, float, false, false, false, float, true>(sv, heads, n, q, k, v, alpha, beta, o, g,
                                                                           s);

@@ -129,21 +129,22 @@ struct HeadLds {
     }
 };
 
-// Wait until at most kCodeLoads vector loads of this wave are outstanding:
+// Wait until at most NL vector loads of this wave are outstanding:
 // with the codes issued last, every LDS-direct copy of append_issue() has
 // landed (vector loads complete in issue order) while the codes may still be
 // in flight.  Other waves' copies need a barrier after this.
-constexpr int kCodeLoads = 4;
+// NL = CodeFmt<CB>::loads (4 for the int8 state, 3 or 2 for 6 or 4 bits).
+template <int NL = 4>
 __device__ __forceinline__ void wait_lds_copies()
 {
-    // vmcnt(4) (bits 3:0 and 15:14), expcnt(7), lgkmcnt(15): not waited
-    __builtin_amdgcn_s_waitcnt((kCodeLoads & 15) | ((kCodeLoads >> 4) << 14) | 0x70 | 0xF00);
+    // vmcnt(NL) (bits 3:0 and 15:14), expcnt(7), lgkmcnt(15): not waited
+    __builtin_amdgcn_s_waitcnt((NL & 15) | ((NL >> 4) << 14) | 0x70 | 0xF00);
 }
 
 // Issues every global load of head h: every operand other than the codes
 // into the LDS buffer L by LDS-direct copies, then the thread's 64 codes into
-// qc as the wave's last kCodeLoads vector loads.
-template <typename T, typename K, bool CH = false, typename U = float, bool R1 = false>
+// qc as the wave's last CodeFmt<CB>::loads vector loads.
+template <typename T, typename K, bool CH = false, typename U = float, bool R1 = false, int CB = 8>
 __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, const T *__restrict__ qin,
                                              const T *__restrict__ kin, const T *__restrict__ vin,
                                              const MMap &a, const HeadLds<T, K, CH, U, R1> &L, uint4 (&qc)[4],
@@ -181,7 +182,7 @@ __device__ __forceinline__ void append_issue(const StateView &sv, int n, int h, 
     // the code loads stay behind every copy (wait_lds_copies counts on it)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = ld_stream(hs.codes + code_off(w, l, p));
+    for (int j = 0; j < CodeFmt<CB>::loads; ++j) qc[j] = ld_stream(hs.codes + code_piece_off<CB>(w, l, j));
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -223,7 +224,7 @@ __device__ __forceinline__ void gate_issue(const GateArgs &g, int h, const MMap 
 // barrier); the codes are waited for at their first use.  Contains one
 // lds_barrier (dot jobs -> residual read and tail).
 template <typename T, typename K, bool REC_LDS = false, bool NORM = false, bool CH = false, typename U = float,
-          bool R1 = false>
+          bool R1 = false, int CB = 8>
 __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h, const MMap &a,
                                                const HeadLds<T, K, CH, U, R1> &L, float *dots, const uint4 (&qc)[4],
                                                float a_h, float b_h, float *__restrict__ o, float q_scale = 1.0f,
@@ -339,8 +340,8 @@ __device__ __forceinline__ void append_compute(const StateView &sv, int n, int h
             wk[p] = kr[p] * rh[p];
             wq[p] = qr[p] * rh[p];
         }
-        const uint32_t cw[4][4] = {{qc[0].x, qc[0].y, qc[0].z, qc[0].w}, {qc[1].x, qc[1].y, qc[1].z, qc[1].w},
-                                   {qc[2].x, qc[2].y, qc[2].z, qc[2].w}, {qc[3].x, qc[3].y, qc[3].z, qc[3].w}};
+        uint32_t cw[4][4];
+        unpack_codes<CB>(qc, cw);
         float a16[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {

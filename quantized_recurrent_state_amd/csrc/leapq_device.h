@@ -91,6 +91,105 @@ __device__ __forceinline__ AMap amap()
 // the bytes code_off(w, l, p) + m, m = 0..15 (column w + 4h + 8m), so each
 // 16-byte load of a wave reads 1 KB contiguous.
 __host__ __device__ __forceinline__ int code_off(int w, int l, int p) { return w * 4096 + p * 1024 + l * 16; }
+
+// Codes of the 6- and 4-bit options (state_bits).  CB = 4: 8192 bytes per
+// head of nibbles; thread (w, l)'s rows p = 2j and 2j + 1 (j = 0, 1) sit in
+// the 16 bytes at 2048 w + 1024 j + 16 l, two words per row, word t holding
+// codes 8t .. 8t + 3 (columns w + 4h + 8m, m = code index) in the low
+// nibbles of its bytes and codes 8t + 4 .. 8t + 7 in the high nibbles.
+// CB = 6: the same low nibbles (bits 0-3 of each code), then 4096 bytes of
+// bits 4-5: the word of row p at 8192 + 1024 w + 16 l + 4 p holds those of
+// code 4k + b at bits 8b + 2k.  Every load and store of a wave covers 1 KB.
+template <int CB>
+struct CodeFmt;
+template <>
+struct CodeFmt<8> {
+    static constexpr int loads = 4, bytes = D * D;
+    static constexpr float levels = 127.0f;
+};
+template <>
+struct CodeFmt<6> {
+    static constexpr int loads = 3, bytes = D * D * 3 / 4;
+    static constexpr float levels = 31.0f;
+};
+template <>
+struct CodeFmt<4> {
+    static constexpr int loads = 2, bytes = D * D / 2;
+    static constexpr float levels = 7.0f;
+};
+// byte offset of the thread's j-th 16-byte piece of codes
+template <int CB>
+__host__ __device__ __forceinline__ int code_piece_off(int w, int l, int j)
+{
+    if constexpr (CB == 8)
+        return code_off(w, l, j);
+    else
+        return j < 2 ? w * 2048 + j * 1024 + l * 16 : 8192 + w * 1024 + l * 16;
+}
+// 4 packed nibbles / 6-bit values (one per byte) sign-extended to int8 bytes
+__device__ __forceinline__ uint32_t sext4x4(uint32_t x) { return x | ((x & 0x08080808u) * 0x1Eu); }
+__device__ __forceinline__ uint32_t sext6x4(uint32_t x) { return x | ((x & 0x20202020u) * 0x06u); }
+__device__ __forceinline__ uint32_t u4comp(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// The thread's stored pieces (raw[j], j < CodeFmt<CB>::loads) as int8 code
+// bytes: cw[p][k] holds the codes 4k .. 4k + 3 of row block p.
+template <int CB>
+__device__ __forceinline__ void unpack_codes(const uint4 (&raw)[4], uint32_t (&cw)[4][4])
+{
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if constexpr (CB == 8) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) cw[p][k] = u4comp(raw[p], k);
+        } else {
+            const uint32_t P0 = u4comp(raw[p >> 1], 2 * (p & 1)), P1 = u4comp(raw[p >> 1], 2 * (p & 1) + 1);
+            const uint32_t lo[4] = {P0 & 0x0F0F0F0Fu, (P0 >> 4) & 0x0F0F0F0Fu, P1 & 0x0F0F0F0Fu,
+                                    (P1 >> 4) & 0x0F0F0F0Fu};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (CB == 4) {
+                    cw[p][k] = sext4x4(lo[k]);
+                } else {
+                    const uint32_t H = u4comp(raw[2], p);
+                    cw[p][k] = sext6x4(lo[k] | (((H >> (2 * k)) & 0x03030303u) << 4));
+                }
+            }
+        }
+    }
+}
+
+// Stores the thread's codes, given as int8 bytes B[p][k] (codes 4k .. 4k +
+// 3 of row block p), in the layout of CodeFmt<CB>.
+template <int CB>
+__device__ __forceinline__ void store_codes(int8_t *codes, int w, int l, const uint32_t (&B)[4][4])
+{
+    if constexpr (CB == 8) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<uint4 *>(codes + code_off(w, l, p)) = make_uint4(B[p][0], B[p][1], B[p][2], B[p][3]);
+    } else {
+        uint32_t P[4][2];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            P[p][0] = (B[p][0] & 0x0F0F0F0Fu) | ((B[p][1] & 0x0F0F0F0Fu) << 4);
+            P[p][1] = (B[p][2] & 0x0F0F0F0Fu) | ((B[p][3] & 0x0F0F0F0Fu) << 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<uint4 *>(codes + code_piece_off<CB>(w, l, j)) =
+                make_uint4(P[2 * j][0], P[2 * j][1], P[2 * j + 1][0], P[2 * j + 1][1]);
+        if constexpr (CB == 6) {
+            uint32_t H[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                H[p] = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) H[p] |= ((B[p][k] >> 4) & 0x03030303u) << (2 * k);
+            }
+            *reinterpret_cast<uint4 *>(codes + code_piece_off<CB>(w, l, 2)) = make_uint4(H[0], H[1], H[2], H[3]);
+        }
+    }
+}
 // Record corrections: column c at upos(c), the A operand order (lane a of
 // wave w reads 32 w + (a & 31)).
 __host__ __device__ __forceinline__ int upos(int c)
@@ -111,7 +210,7 @@ struct HeadState {
 __device__ __forceinline__ HeadState head_state(const StateView &sv, int h)
 {
     HeadState s;
-    s.codes = sv.codes + (size_t)h * D * D;
+    s.codes = sv.codes + (size_t)h * sv.code_bytes;
     s.rho = sv.rho + (size_t)h * D;
     s.sigma = sv.sigma + (size_t)h * D;
     s.cidx = sv.cidx + (size_t)h * sv.C;

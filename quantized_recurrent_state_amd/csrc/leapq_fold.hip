@@ -105,10 +105,12 @@ __device__ __forceinline__ void stage_records(const MMap &a, const HeadState &hs
         copy_record<K, CH, U>(hs, base + rr, a.l, sm.rec + rr * Rec<K, CH, U>::stride);
 }
 
+template <int CB = 8>
 __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, uint4 (&qc)[4])
 {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) qc[p] = *reinterpret_cast<const uint4 *>(hs.codes + code_off(a.w, a.l, p));
+    for (int j = 0; j < CodeFmt<CB>::loads; ++j)
+        qc[j] = *reinterpret_cast<const uint4 *>(hs.codes + code_piece_off<CB>(a.w, a.l, j));
 }
 
 // Current state in the tile.  qc: the thread's 4 code chunks.  Expects
@@ -121,7 +123,7 @@ __device__ __forceinline__ void load_codes(const MMap &a, const HeadState &hs, u
 // wpre (n <= 16): the records' weighted keys c_i k_i (with CH, the per-row
 // weighted keys) as [n][128] fp32 in LDS, formed by the append that shares
 // the launch; the matrix steps then read their key operands from it.
-template <typename K, bool CH, typename U, typename Stage, bool R1 = false, bool WPRE = false>
+template <typename K, bool CH, typename U, typename Stage, bool R1 = false, bool WPRE = false, int CB = 8>
 __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, const uint4 (&qc)[4], int C, int n,
                                         bool lines, Stage &sm, float (&S)[4][16], const float *gW = nullptr,
                                         const float *wpre = nullptr)
@@ -134,12 +136,13 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
     float sg[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) sg[m] = sm.sig[a.col(m)];
+    uint32_t cw[4][4];
+    unpack_codes<CB>(qc, cw);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const float ap = gr[p] * sm.rho[a.row(p)];
-        const uint32_t cw[4] = {qc[p].x, qc[p].y, qc[p].z, qc[p].w};
 #pragma unroll
-        for (int m = 0; m < 16; ++m) TS(S, p, m) = (code_f(cw[m >> 2], m & 3) * ap) * sg[m];
+        for (int m = 0; m < 16; ++m) TS(S, p, m) = (code_f(cw[p][m >> 2], m & 3) * ap) * sg[m];
     }
     if (!R1 && lines && C > 0) {
         // line of each of the thread's rows / columns (-1: none).  An entry
@@ -735,7 +738,7 @@ __device__ __forceinline__ void fit_block(const MMap &a, float (&S)[4][16], cons
 // rounds.  R1: compensator pairs in place of lines, fitted by power sweeps,
 // or with BLK by the block fit (WARM: from the pairs staged in prev and
 // prev_idx, the window's own).
-template <int CT, bool R1 = false, bool BLK = false, bool WARM = false>
+template <int CT, bool R1 = false, bool BLK = false, bool WARM = false, int CB = 8>
 __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16], const HeadState &hs, int C, int smoothing,
                                                float floor_, FoldWork &sm, const float *prev = nullptr,
                                                const int *prev_idx = nullptr)
@@ -868,7 +871,7 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
     // the wave reads back only its own columns: LDS order within the wave
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_wave_barrier();
-    // ---- per-row symmetric int8, round half to even
+    // ---- per-row symmetric codes (int8, or 6 / 4 bits), round half to even
     {
         float inv[16];
 #pragma unroll
@@ -896,25 +899,26 @@ __device__ __forceinline__ void quantize_state(const MMap &a, float (&S)[4][16],
             const int r = l + 64 * k;
             const float M = fmaxf(fmaxf(sm.part[r], sm.part[D + r]), fmaxf(sm.part[2 * D + r], sm.part[3 * D + r]));
             const bool live = M >= 0x1p-120f;
-            if (a.w == 0) hs.rho[r] = live ? M / 127.0f : 0.0f;
-            rg[r] = live ? 127.0f / M : 0.0f;
+            if (a.w == 0) hs.rho[r] = live ? M / CodeFmt<CB>::levels : 0.0f;
+            rg[r] = live ? CodeFmt<CB>::levels / M : 0.0f;
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
     }
+    uint32_t B[4][4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const float g = sm.rowg[a.w][a.row(p)];
         uint32_t b[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) b[m] = rint_bits(TS(S, p, m), g);
-        *reinterpret_cast<uint4 *>(hs.codes + code_off(a.w, a.l, p)) =
-            make_uint4(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]),
-                       pack4(b[8], b[9], b[10], b[11]), pack4(b[12], b[13], b[14], b[15]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) B[p][k] = pack4(b[4 * k], b[4 * k + 1], b[4 * k + 2], b[4 * k + 3]);
     }
+    store_codes<CB>(hs.codes, a.w, a.l, B);
 }
 
-template <int CT, bool R1, bool BLK = false>
+template <int CT, bool R1, bool BLK = false, int CB = 8>
 __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restrict__ S0, int smoothing,
                                               float floor_)
 {
@@ -928,10 +932,10 @@ __global__ __launch_bounds__(NT) void k_init(StateView sv, const float *__restri
     for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int m = 0; m < 16; ++m) TS(S, p, m) = src[a.row(p) * D + a.col(m)];
-    quantize_state<CT, R1, BLK>(a, S, hs, sv.C, smoothing, floor_, wk);
+    quantize_state<CT, R1, BLK, false, CB>(a, S, hs, sv.C, smoothing, floor_, wk);
 }
 
-template <typename K, int CT, bool CH, typename U, bool R1, bool BLK = false>
+template <typename K, int CT, bool CH, typename U, bool R1, bool BLK = false, int CB = 8>
 __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing, float floor_)
 {
     __shared__ FoldStage<Rec<K, CH, U>::stride> st;
@@ -940,16 +944,16 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
     const int h = blockIdx.x;
     const HeadState hs = head_state(sv, h);
     uint4 qc[4];
-    load_codes(a, hs, qc);
+    load_codes<CB>(a, hs, qc);
     stage_small<CH, decltype(st), R1>(a, hs, sv.C, n, st);
     stage_records<K, CH, U>(a, hs, 0, n < 16 ? n : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, n, true, st, S, st.gW);
+    rebuild<K, CH, U, decltype(st), R1, false, CB>(a, hs, qc, sv.C, n, true, st, S, st.gW);
     // no barrier: the quantization writes only LDS arrays the rebuild does
     // not read, and each thread rewrites only the codes it loaded
-    quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
+    quantize_state<CT, R1, BLK, true, CB>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
 // The last token of a full window and the fold, in one launch (W <= 16).
@@ -959,7 +963,8 @@ __global__ __launch_bounds__(NT) void k_fold(StateView sv, int n, int smoothing,
 // empties the buffer), and the fold rebuilds from the same registers and LDS
 // instead of reading the boundary and the records again.  The results are
 // those of leapq_append followed by leapq_fold.
-template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CT, bool BLK = false>
+template <typename T, typename K, bool GATED, bool NORM, bool CH, typename U, bool R1, int CT, bool BLK = false,
+          int CB = 8>
 __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T *__restrict__ qin,
                                                      const T *__restrict__ kin, const T *__restrict__ vin,
                                                      const float *__restrict__ alpha,
@@ -977,11 +982,11 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     // gamma_n from the token's own record slot)
     const HeadLds<T, K, CH, U, R1> L(st.rec, st.lines, st.rho, sin_, st.idx, CH ? st.gW : st.gam);
     uint4 qc[4];
-    append_issue<T, K, CH, U, R1>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
+    append_issue<T, K, CH, U, R1, CB>(sv, n, h, qin, kin, vin, a, L, qc, alpha);
     float a_h = CH ? 1.0f : sload(alpha, h);
     float b_h = sload(beta, h);
     if constexpr (GATED) gate_issue(g, h, a, a_h, b_h, dots);
-    wait_lds_copies();
+    wait_lds_copies<CodeFmt<CB>::loads>();
     lds_barrier();
     if constexpr (GATED) {
         a_h = dots[kGateSlot];
@@ -990,14 +995,14 @@ __global__ __launch_bounds__(NT) void k_append_fold(StateView sv, int n, const T
     // the records' weighted keys go to the work area, unused until the
     // rebuild has read them (barrier below)
     float *wkeys = reinterpret_cast<float *>(&wk);
-    append_compute<T, K, true, NORM, CH, U, R1>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps, wkeys);
+    append_compute<T, K, true, NORM, CH, U, R1, CB>(sv, n, h, a, L, dots, qc, a_h, b_h, o, g.q_scale, g.eps, wkeys);
     lds_barrier();  // record n is in LDS for every wave
     const HeadState hs = head_state(sv, h);
     float S[4][16];
-    rebuild<K, CH, U, decltype(st), R1, true>(a, hs, qc, sv.C, n + 1, true, st, S, st.rec + n * R::stride + R::goff,
-                                                wkeys);
+    rebuild<K, CH, U, decltype(st), R1, true, CB>(a, hs, qc, sv.C, n + 1, true, st, S,
+                                                    st.rec + n * R::stride + R::goff, wkeys);
     lds_barrier();  // every wave is done with the weighted keys
-    quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
+    quantize_state<CT, R1, BLK, true, CB>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
 // One decode token with a window phase per request (W <= 16).  The heads of
@@ -1058,7 +1063,7 @@ __global__ __launch_bounds__(NT) void k_step(StateView sv, int heads_per_req, co
     quantize_state<CT, R1, BLK, true>(a, S, hs, sv.C, smoothing, floor_, wk, st.lines, st.idx);
 }
 
-template <typename K, bool CH, typename U, bool R1>
+template <typename K, bool CH, typename U, bool R1, int CB = 8>
 __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, float *__restrict__ out)
 {
     __shared__ FoldStage<Rec<K, CH, U>::stride> st;
@@ -1067,13 +1072,13 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
     const HeadState hs = head_state(sv, h);
     const int nr = what == 2 ? n : 0;
     uint4 qc[4];
-    load_codes(a, hs, qc);
+    load_codes<CB>(a, hs, qc);
     stage_small<CH, decltype(st), R1>(a, hs, sv.C, nr, st);
     stage_records<K, CH, U>(a, hs, 0, nr < 16 ? nr : 16, st);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     float S[4][16];
-    rebuild<K, CH, U, decltype(st), R1>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
+    rebuild<K, CH, U, decltype(st), R1, false, CB>(a, hs, qc, sv.C, nr, what >= 1, st, S, st.gW);
     float *dst = out + (size_t)h * D * D;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
@@ -1083,10 +1088,24 @@ __global__ __launch_bounds__(NT) void k_dequant(StateView sv, int n, int what, f
 
 }  // namespace
 
+template <int CB>
+static void launch_init_bits(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
+                             hipStream_t s)
+{
+    if (sv.C == 4)
+        hipLaunchKernelGGL((k_init<4, false, false, CB>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+    else
+        hipLaunchKernelGGL((k_init<-1, false, false, CB>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
+}
+
 hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoothing, float floor_,
                        hipStream_t s)
 {
-    if (sv.blk) {
+    if (sv.cbits == 6) {
+        launch_init_bits<6>(sv, heads, S0, smoothing, floor_, s);
+    } else if (sv.cbits == 4) {
+        launch_init_bits<4>(sv, heads, S0, smoothing, floor_, s);
+    } else if (sv.blk) {
         if (sv.C == 4)
             hipLaunchKernelGGL((k_init<4, true, true>), dim3(heads), dim3(NT), 0, s, sv, S0, smoothing, floor_);
         else
@@ -1104,18 +1123,32 @@ hipError_t launch_init(const StateView &sv, int heads, const float *S0, int smoo
     return hipGetLastError();
 }
 
-template <typename K, bool CH, typename U = float, bool R1 = false, bool BLK = false>
+template <typename K, bool CH, typename U = float, bool R1 = false, bool BLK = false, int CB = 8>
 static void launch_fold_t(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_fold<K, 4, CH, U, R1, BLK>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, 4, CH, U, R1, BLK, CB>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing,
+                           floor_);
     else
-        hipLaunchKernelGGL((k_fold<K, -1, CH, U, R1, BLK>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing, floor_);
+        hipLaunchKernelGGL((k_fold<K, -1, CH, U, R1, BLK, CB>), dim3(heads), dim3(NT), 0, s, sv, n, smoothing,
+                           floor_);
 }
 
 hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, float floor_, hipStream_t s)
 {
-    if (sv.blk) {
+    if (sv.cbits != 8) {  // 6 or 4 bits: scalar decay, lines, fp32 corrections
+        if (sv.cbits == 6) {
+            if (sv.key_bf16)
+                launch_fold_t<uint16_t, false, float, false, false, 6>(sv, heads, n, smoothing, floor_, s);
+            else
+                launch_fold_t<float, false, float, false, false, 6>(sv, heads, n, smoothing, floor_, s);
+        } else {
+            if (sv.key_bf16)
+                launch_fold_t<uint16_t, false, float, false, false, 4>(sv, heads, n, smoothing, floor_, s);
+            else
+                launch_fold_t<float, false, float, false, false, 4>(sv, heads, n, smoothing, floor_, s);
+        }
+    } else if (sv.blk) {
         if (sv.key_bf16)
             launch_fold_t<uint16_t, false, float, true, true>(sv, heads, n, smoothing, floor_, s);
         else
@@ -1149,17 +1182,17 @@ hipError_t launch_fold(const StateView &sv, int heads, int n, int smoothing, flo
 }
 
 template <typename T, typename K, bool GATED, bool NORM, bool CH = false, typename U = float, bool R1 = false,
-          bool BLK = false>
+          bool BLK = false, int CB = 8>
 static void launch_append_fold_t(const StateView &sv, int heads, int n, const void *q, const void *k, const void *v,
                                  const float *alpha, const float *beta, float *o, int smoothing, float floor_,
                                  const GateArgs &g, hipStream_t s)
 {
     if (sv.C == 4)
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, 4, BLK>), dim3(heads), dim3(NT), 0, s, sv, n,
-                           (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
-    else
-        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, -1, BLK>), dim3(heads), dim3(NT), 0, s, sv,
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, 4, BLK, CB>), dim3(heads), dim3(NT), 0, s, sv,
                            n, (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
+    else
+        hipLaunchKernelGGL((k_append_fold<T, K, GATED, NORM, CH, U, R1, -1, BLK, CB>), dim3(heads), dim3(NT), 0, s,
+                           sv, n, (const T *)q, (const T *)k, (const T *)v, alpha, beta, o, smoothing, floor_, g);
 }
 
 hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, const void *q, const void *k,
@@ -1169,7 +1202,20 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
     // the (inputs, keys, gated, normalize) combinations of launch_append
     const bool kb = sv.key_bf16;
 #define LQ_AF(T, K, G, N) launch_append_fold_t<T, K, G, N>(sv, heads, n, q, k, v, alpha, beta, o, smoothing, floor_, g, s)
-    if (sv.blk) {
+#define LQ_AFB(T, CB)                                                                                               \
+    launch_append_fold_t<T, T, false, false, false, float, false, false, CB>(sv, heads, n, q, k, v, alpha, beta, o, \
+                                                                             smoothing, floor_, g, s)
+    if (sv.cbits == 6) {
+        if (!bf16)
+            LQ_AFB(float, 6);
+        else
+            LQ_AFB(uint16_t, 6);
+    } else if (sv.cbits == 4) {
+        if (!bf16)
+            LQ_AFB(float, 4);
+        else
+            LQ_AFB(uint16_t, 4);
+    } else if (sv.blk) {
         if (!bf16)
             launch_append_fold_t<float, float, false, false, false, float, true, true>(sv, heads, n, q, k, v, alpha,
                                                                                      beta, o, smoothing, floor_, g, s);
@@ -1224,6 +1270,7 @@ hipError_t launch_append_fold(const StateView &sv, int heads, int n, int bf16, c
         LQ_AF(uint16_t, float, true, false);
     }
 #undef LQ_AF
+#undef LQ_AFB
     return hipGetLastError();
 }
 
@@ -1302,7 +1349,19 @@ hipError_t launch_step(const StateView &sv, int heads, int heads_per_req, const 
 hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float *out, hipStream_t s)
 {
 #define LQ_DQ(K, CH, U, R1) hipLaunchKernelGGL((k_dequant<K, CH, U, R1>), dim3(heads), dim3(NT), 0, s, sv, n, what, out)
-    if (sv.r1) {
+#define LQ_DQB(K, CB) \
+    hipLaunchKernelGGL((k_dequant<K, false, float, false, CB>), dim3(heads), dim3(NT), 0, s, sv, n, what, out)
+    if (sv.cbits == 6) {
+        if (sv.key_bf16)
+            LQ_DQB(uint16_t, 6);
+        else
+            LQ_DQB(float, 6);
+    } else if (sv.cbits == 4) {
+        if (sv.key_bf16)
+            LQ_DQB(uint16_t, 4);
+        else
+            LQ_DQB(float, 4);
+    } else if (sv.r1) {
         if (sv.key_bf16)
             LQ_DQ(uint16_t, false, float, true);
         else
@@ -1328,6 +1387,7 @@ hipError_t launch_dequant(const StateView &sv, int heads, int n, int what, float
         LQ_DQ(float, false, float, false);
     }
 #undef LQ_DQ
+#undef LQ_DQB
     return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@ struct StateView {
     int u_rec_bytes;  // bytes of one record's corrections: 512 (fp32), 256 (bf16), 144 (fp8)
     int r1;        // compensator pairs [C][2][128] (a, b) in place of lines
     int blk;       // the pairs are fitted as a block (with r1)
+    int cbits;       // bits per residual code: 8, 6 or 4
+    int code_bytes;  // bytes of one head's codes: 16384, 12288 or 8192
 };
 
 // Gate arithmetic in front of the append (mode 0: alpha and beta are given;

@@ -48,7 +48,8 @@ class leapq_config(ctypes.Structure):
                 ("dv", ctypes.c_int32), ("window", ctypes.c_int32), ("n_comp", ctypes.c_int32),
                 ("smoothing", ctypes.c_int32), ("sigma_floor", ctypes.c_float),
                 ("in_dtype", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("decay", ctypes.c_int32),
-                ("rec_dtype", ctypes.c_int32), ("comp_fit", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("rec_dtype", ctypes.c_int32), ("comp_fit", ctypes.c_int32), ("state_bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class leapq_gate(ctypes.Structure):
@@ -118,7 +119,7 @@ def _check(status, what):
 
 
 def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1e-6, in_dtype="f32",
-                qk_norm=False, decay="scalar", rec_dtype="f32", comp_fit="lines"):
+                qk_norm=False, decay="scalar", rec_dtype="f32", comp_fit="lines", state_bits=8):
     c = leapq_config()
     c.batch, c.heads, c.dk, c.dv = int(batch), int(heads), D, D
     c.window, c.n_comp, c.smoothing = int(window), int(n_comp), int(bool(smoothing))
@@ -130,6 +131,7 @@ def make_config(batch, heads, window=16, n_comp=4, smoothing=True, sigma_floor=1
                    LEAPQ_FP8 if rec_dtype in ("fp8", LEAPQ_FP8) else LEAPQ_F32)
     fits = {"lines": LEAPQ_COMP_LINES, "rank1": LEAPQ_COMP_RANK1, "block": LEAPQ_COMP_BLOCK}
     c.comp_fit = fits.get(comp_fit, comp_fit)
+    c.state_bits = int(state_bits)
     return c
 
 
@@ -235,16 +237,34 @@ class Layer:
         nbytes = count * torch.tensor([], dtype=dtype).element_size()
         return self.state[off:off + nbytes].view(dtype).view(*shape)
 
+    @property
+    def state_bits(self):
+        return self.cfg.state_bits if self.cfg.state_bits in (6, 4) else 8
+
     def codes_physical(self):
-        """int8 [heads, 16384]: each head's codes in stored order."""
-        H = self.heads
-        return self._sec(self.layout.off_codes, H * D * D, torch.int8, (H, D * D))
+        """int8 [heads, bytes]: each head's codes in stored order (16384 bytes; 12288 or 8192 packed
+        bytes with state_bits 6 or 4)."""
+        H, nb = self.heads, D * D * self.state_bits // 8
+        return self._sec(self.layout.off_codes, H * nb, torch.int8, (H, nb))
 
     def codes(self):
-        """int8 [heads, 128(row), 128(column)] in logical order."""
+        """int8 [heads, 128(row), 128(column)] in logical order (the 6- and 4-bit layouts of
+        include/leapq.h unpacked and sign-extended)."""
         r = torch.arange(D, device=self.device).view(D, 1)
         c = torch.arange(D, device=self.device).view(1, D)
-        return self.codes_physical()[:, code_offset(r, c)]
+        phys = self.codes_physical()
+        if self.state_bits == 8:
+            return phys[:, code_offset(r, c)]
+        raw = phys.view(torch.uint8).to(torch.int32)
+        w, p, m = c & 3, r >> 5, c >> 3
+        l = _iperm(r & 31) + 32 * ((c >> 2) & 1)
+        lo_byte = 2048 * w + 1024 * (p >> 1) + 16 * l + 8 * (p & 1) + 4 * (m >> 3) + (m & 3)
+        val = (raw[:, lo_byte] >> (4 * ((m & 7) >> 2))) & 15
+        if self.state_bits == 4:
+            return torch.where(val >= 8, val - 16, val).to(torch.int8)
+        hi_byte = 8192 + 1024 * w + 16 * l + 4 * p + (m & 3)
+        val = val | (((raw[:, hi_byte] >> (2 * (m >> 2))) & 3) << 4)
+        return torch.where(val >= 32, val - 64, val).to(torch.int8)
 
     def rho(self):
         return self._sec(self.layout.off_row_scale, self.heads * D, torch.float32, (self.heads, D))

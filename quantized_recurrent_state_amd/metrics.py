@@ -25,10 +25,11 @@ share of window time is fold / (appends + fold).
 D = 128
 
 
-def boundary_bytes(C=4, rank1=False):
-    """Bytes of one head's boundary state: int8 codes, rho, sigma, and C
-    compensators (an index and a line, or an index and a pair a, b)."""
-    return D * D + 2 * D * 4 + C * (4 + D * 4 * (2 if rank1 else 1))
+def boundary_bytes(C=4, rank1=False, bits=8):
+    """Bytes of one head's boundary state: the codes (int8, or packed 6- or
+    4-bit codes), rho, sigma, and C compensators (an index and a line, or an
+    index and a pair a, b)."""
+    return D * D * bits // 8 + 2 * D * 4 + C * (4 + D * 4 * (2 if rank1 else 1))
 
 
 def record_bytes(in_bytes=2, channel=False, u_bytes=4):
@@ -37,11 +38,11 @@ def record_bytes(in_bytes=2, channel=False, u_bytes=4):
     return 4 * (D if channel else 1) + D * in_bytes + D * u_bytes
 
 
-def append_bytes(n, C=4, in_bytes=2, channel=False, u_bytes=4, rank1=False):
+def append_bytes(n, C=4, in_bytes=2, channel=False, u_bytes=4, rank1=False, bits=8):
     """Algorithmic bytes of one head's append with n records present."""
     gates = 4 * (D if channel else 1) + 4
     rec = record_bytes(in_bytes, channel, u_bytes)
-    read = boundary_bytes(C, rank1) + 3 * D * in_bytes + gates + n * rec
+    read = boundary_bytes(C, rank1, bits) + 3 * D * in_bytes + gates + n * rec
     write = rec + D * 4
     return read + write
 

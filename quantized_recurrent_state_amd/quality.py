@@ -19,7 +19,7 @@ the GPU output and whether a fold followed; the parity tests use it to run
 CPU reference heads beside the GPU path.
 
   python -m quantized_recurrent_state_amd.quality [--workload long] [--layers 3]
-         [--tokens 4095] [--rec-dtype f32|bf16|fp8] [--comp-fit lines|rank1|block]
+         [--tokens 4095] [--rec-dtype f32|bf16|fp8] [--comp-fit lines|rank1|block] [--state-bits 8|6|4]
          [--out result.json]
 """
 import argparse
@@ -45,7 +45,7 @@ def _summ(x):
 
 
 def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, on_token=None, rec_dtype="f32",
-        comp_fit="lines"):
+        comp_fit="lines", state_bits=8):
     wl = workloads.WORKLOADS[workload]
     dev = torch.device(device)
     B, Hh, W, C = wl.batch, wl.heads, wl.window, wl.n_comp
@@ -53,7 +53,7 @@ def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, o
     nlayers = wl.layers if layers is None else layers
     T = wl.tokens if tokens is None else tokens
     cfg = lq.make_config(B, Hh, W, C, wl.smoothing, wl.sigma_floor, wl.in_dtype, decay=wl.decay, rec_dtype=rec_dtype,
-                         comp_fit=comp_fit)
+                         comp_fit=comp_fit, state_bits=state_bits)
     ash = (H, D) if wl.decay == "channel" else (H,)
     rel_q, rel_b, hard = [], [], []
     for layer in range(nlayers):
@@ -99,7 +99,7 @@ def run(workload="long", layers=None, tokens=None, device="cuda:0", log=print, o
     rq, rb, hd = np.concatenate(rel_q), np.concatenate(rel_b), np.concatenate(hard)
     out = {
         "workload": wl.name, "layers": nlayers, "tokens": T, "heads_per_layer": H, "record_corrections": rec_dtype,
-        "compensators": comp_fit,
+        "compensators": comp_fit, "state_bits": state_bits,
         "metric": "per-head ||O - O_fp32||_F / ||O_fp32||_F over all tokens",
         "leapq": {"regular": _summ(rq[~hd]), "hard": _summ(rq[hd])},
         "bf16_per_token": {"regular": _summ(rb[~hd]), "hard": _summ(rb[hd])},
@@ -118,10 +118,12 @@ def main(argv=None):
     p.add_argument("--comp-fit", default="lines", choices=("lines", "rank1", "block"),
                    help="compensator fit: whole rows/columns, rank-one pairs from power sweeps, or pairs "
                         "fitted as a block warm-started from the previous window")
+    p.add_argument("--state-bits", type=int, default=8, choices=(8, 6, 4),
+                   help="bits per residual code (6 and 4: the lower-precision state options)")
     p.add_argument("--out", default=None)
     a = p.parse_args(argv)
     res = run(a.workload, a.layers, a.tokens, log=lambda m: print(m, file=sys.stderr, flush=True),
-              rec_dtype=a.rec_dtype, comp_fit=a.comp_fit)
+              rec_dtype=a.rec_dtype, comp_fit=a.comp_fit, state_bits=a.state_bits)
     s = json.dumps(res, indent=1)
     print(s, flush=True)
     if a.out:

@@ -128,7 +128,7 @@ def _pool():
 
 def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="cuda", check_every_token=True,
               fold_at=None, report=None, log=True, fused=False, gated=None, qk_norm=False, rec_u="f32",
-              fit="lines"):
+              fit="lines", bits=8):
     """Runs `tokens` decode tokens of one layer on the GPU and, for the
     sampled heads, in the oracle; folds whenever the window is full (or at
     the token counts in fold_at).  With fused, the GPU takes each window's
@@ -137,15 +137,16 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     the raw projections of workloads.gated_token_inputs and the GPU runs the
     gated entry points (the oracle applies oracle.gated_inputs first); the
     layer normalizes q and k when qk_norm.  rec_u selects the stored
-    correction's dtype and fit the compensator fit ("lines" or "rank1") on
-    both sides.  Returns (Report, Layer, oracle heads)."""
+    correction's dtype, fit the compensator fit ("lines" or "rank1") and
+    bits the residual code width (8, 6 or 4) on both sides.  Returns
+    (Report, Layer, oracle heads)."""
     rep = report or Report()
     dev = torch.device(device)
     H = wl.batch * wl.heads
     T = wl.tokens if tokens is None else tokens
     sample = list(range(H)) if sample is None else list(sample)
     cfg = lq.make_config(wl.batch, wl.heads, wl.window, wl.n_comp, wl.smoothing, wl.sigma_floor, wl.in_dtype,
-                         qk_norm=qk_norm, decay=wl.decay, rec_dtype=rec_u, comp_fit=fit)
+                         qk_norm=qk_norm, decay=wl.decay, rec_dtype=rec_u, comp_fit=fit, state_bits=bits)
     ash = (H, D) if wl.decay == "channel" else (H,)
     L = lq.Layer(cfg, dev)
     if gated is not None:
@@ -157,7 +158,7 @@ def run_layer(wl, layer=0, tokens=None, sample=None, gen_device="cpu", device="c
     lq.leapq_init_state(L, S0.to(dev))
     S0h = S0[sample].cpu().numpy()
     refs = [oracle.Head(wl.n_comp, wl.window, wl.smoothing, wl.sigma_floor, decay=wl.decay, rec_u=rec_u,
-                        fit=fit) for _ in sample]
+                        fit=fit, bits=bits) for _ in sample]
     with _pool() as pool:
         list(pool.map(lambda a: a[0].init(a[1]), zip(refs, S0h)))
         torch.cuda.synchronize(dev)
@@ -330,15 +331,16 @@ class Twin:
     bf16-valued when in_dtype is bf16).  Every step compares what it
     changed against the oracle into `rep`."""
 
-    def __init__(self, S0, C=4, W=16, smoothing=True, sigma_floor=1e-6, in_dtype="f32", rep=None, device="cuda"):
+    def __init__(self, S0, C=4, W=16, smoothing=True, sigma_floor=1e-6, in_dtype="f32", rep=None, device="cuda",
+                 bits=8):
         self.rep = rep or Report()
         self.dev = torch.device(device)
         S0 = np.ascontiguousarray(S0, np.float32)
         self.H, self.W = S0.shape[0], W
-        self.cfg = lq.make_config(1, self.H, W, C, smoothing, sigma_floor, in_dtype)
+        self.cfg = lq.make_config(1, self.H, W, C, smoothing, sigma_floor, in_dtype, state_bits=bits)
         self.L = lq.Layer(self.cfg, self.dev)
         lq.leapq_init_state(self.L, torch.from_numpy(S0).to(self.dev))
-        self.refs = [oracle.Head(C, W, smoothing, sigma_floor).init(S0[h]) for h in range(self.H)]
+        self.refs = [oracle.Head(C, W, smoothing, sigma_floor, bits=bits).init(S0[h]) for h in range(self.H)]
         self.tdt = torch.bfloat16 if in_dtype == "bf16" else torch.float32
         self.o = torch.empty(self.H, D, dtype=torch.float32, device=self.dev)
         self.compare()

@@ -366,6 +366,22 @@ def test_fp8_corrections_layout_and_checks():
     assert call_gated(fake_layer(cfg(rec_dtype="fp8")), gate_struct()) == lq.LEAPQ_ERR_RANGE
 
 
+def test_low_bit_layout_and_checks():
+    for bits, nb in ((8, 16384), (6, 12288), (4, 8192)):
+        L = layout(batch=2, heads=4, window=16, n_comp=4, state_bits=bits)
+        assert L.boundary_bytes_per_head == nb + 1024 + 4 * 4 + 4 * 512, bits
+        assert L.off_row_scale >= 8 * nb and L.off_row_scale % 256 == 0
+    L0 = layout(batch=2, heads=4, state_bits=0)
+    assert L0.boundary_bytes_per_head == 19472  # 0 means the int8 state
+    out = lq.leapq_layout()
+    for kw in (dict(state_bits=5), dict(state_bits=6, decay="channel"), dict(state_bits=4, comp_fit="rank1"),
+               dict(state_bits=4, rec_dtype="bf16"), dict(state_bits=6, rec_dtype="fp8"),
+               dict(state_bits=4, qk_norm=True)):
+        c = cfg(**kw)
+        assert lq.lib().leapq_query_layout(ctypes.byref(c), ctypes.byref(out)) == lq.LEAPQ_ERR_RANGE, kw
+    assert call_gated(fake_layer(cfg(state_bits=4)), gate_struct()) == lq.LEAPQ_ERR_RANGE
+
+
 # ---------------------------------------------------------------- rank-one compensators
 
 def test_rank1_layout_and_checks():
