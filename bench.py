@@ -56,6 +56,8 @@ def parse():
                    help="skip the measurement of the 6- and 4-bit residual-state options")
     p.add_argument("--no-rank1", action="store_true",
                    help="skip the measurement of the rank-one compensator option")
+    p.add_argument("--no-pattern", action="store_true",
+                   help="skip the probe of the append's memory traffic without its arithmetic")
     p.add_argument("--no-block", action="store_true",
                    help="skip the measurement of the block compensator fit option")
     p.add_argument("--no-staggered", action="store_true",
@@ -89,7 +91,7 @@ def main():
     import torch
 
     from quantized_recurrent_state_amd import leapq as lq
-    from quantized_recurrent_state_amd import metrics, workloads
+    from quantized_recurrent_state_amd import metrics, profiling, workloads
 
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -247,6 +249,22 @@ def main():
     copy_gbps = copy_ceiling(torch, stream)
     log(f"[bench] streaming ceiling (1 GiB elementwise y = -x, 4 B read + 4 B written per element): "
         f"{copy_gbps:.0f} GB/s ({100 * copy_gbps / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
+    # the append's own loads and stores without its arithmetic (measurement
+    # probe, four state copies in turn), and a plain streaming read of the
+    # same bytes: the ceilings of this access pattern on this GPU
+    pattern = None
+    if not args.no_pattern and wl.decay == "scalar":
+        pat = profiling.append_pattern(H, C, W, in_bytes, 4 * D, sched, reps=20)
+        pat_us = float(np.mean([pat[p] for p in sched]))
+        read_gbps = profiling.read_ceiling(int(app_bytes_avg), reps=20)
+        pattern = {"us_mean": pat_us, "gbps": app_bytes_avg / (pat_us * 1e-6) / 1e9,
+                   "us_by_position": [round(pat[p], 2) for p in sched],
+                   "append_frac_of_pattern": pat_us / append_us,
+                   "append_frac_of_pattern_by_position": [round(pat[p] / app_us[p], 3) for p in sched],
+                   "read_ceiling_gbps": read_gbps}
+        log(f"[bench] the append's memory traffic alone: {pat_us:.1f} us ({pattern['gbps']:.0f} GB/s); the "
+            f"append runs at {100 * pattern['append_frac_of_pattern']:.1f}% of that rate; plain streaming read "
+            f"of the same bytes {read_gbps:.0f} GB/s")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -631,7 +649,8 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": append_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
                      "bytes_per_launch_algorithmic": app_bytes_avg,
-                     "copy_ceiling_gbps": copy_gbps, "frac_of_copy_ceiling": append_gbps / copy_gbps},
+                     "copy_ceiling_gbps": copy_gbps, "frac_of_copy_ceiling": append_gbps / copy_gbps,
+                     "pattern_ceiling": pattern},
         "fold_roofline": fold_roofline,
         "gated": gated,
         "kda": kda,

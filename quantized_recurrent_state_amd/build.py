@@ -1,4 +1,6 @@
-"""Build libleapq.so (gfx950) in-tree with hipcc.
+"""Build libleapq.so (gfx950) in-tree with hipcc, and the measurement probes
+(libleapq_probe.so: the append's memory traffic without its arithmetic, a
+plain streaming read) beside it.
 
 Flags that matter for the numbers:
   -ffp-contract=off   no fused multiply-add except the explicit ones
@@ -21,6 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libleapq.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("leapq_append.hip", "leapq_fold.hip", "leapq_dense.hip", "leapq_abi.cpp")]
+PROBE_LIB = os.path.join(PKG, "libleapq_probe.so")
+PROBE_SOURCE = os.path.join(CSRC, "probe_pattern.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -43,17 +47,21 @@ def _run(cmd, verbose):
         raise RuntimeError("hipcc failed building libleapq")
 
 
-def build(out=LIB, extra=(), verbose=False):
+def build(out=LIB, extra=(), verbose=False, probe=True):
     """Compile every HIP source (one hipcc process each, in parallel) and
-    link them into `out`; returns the path."""
-    tmp = out + ".tmp"
+    link them into `out`, and (probe) the probe library; returns `out`."""
+    tmp, ptmp = out + ".tmp", PROBE_LIB + ".tmp"
     with tempfile.TemporaryDirectory(prefix="leapq_build_") as d:
         objs = [os.path.join(d, os.path.basename(src) + ".o") for src in SOURCES]
         cmds = [[HIPCC, *FLAGS, *extra, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        if probe:
+            cmds.append([HIPCC, *FLAGS, "-shared", PROBE_SOURCE, "-o", ptmp])
         with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
+    if probe:
+        os.replace(ptmp, PROBE_LIB)
     return out
 
 

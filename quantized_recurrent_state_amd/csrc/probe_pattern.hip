@@ -1,0 +1,174 @@
+// Measurement probes (libleapq_probe.so; not part of the decode library).
+//
+// lqp_append_pattern: the memory traffic of one append launch with no
+// arithmetic.  Per head it issues the append's loads and stores at the
+// append's addresses in the library's state layout (int8 codes as four
+// 16-byte non-temporal loads per thread, 1 KB contiguous per wave and load;
+// row and column scales, the C compensator lines and indices, the n record
+// decays, keys and corrections, the token's k, q, v, its decay and step size;
+// then the output, the record's key and correction as non-temporal stores and
+// its decay as a plain 4-byte store).  Its time is the practical floor of an
+// append whose arithmetic hides completely under its memory traffic.
+// The probe owns its buffers: four sets, used in turn, so that no launch
+// finds the previous launch's data in the caches (a decode step touches every
+// layer's state before it comes back to this one).
+//
+// lqp_read_ceiling: a plain streaming read (non-temporal 16-byte loads, 21.5
+// KB per workgroup) of `bytes`, in four buffers used in turn.
+//
+// Both return 0, or the HIP error code; times are mean microseconds per
+// launch over `reps` launches after 3 untimed ones, on the null stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+constexpr int D = 128;
+constexpr int NSETS = 4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct Set {
+    int8_t *codes;
+    float *rho, *sigma, *cvec, *rgam, *ru, *alpha, *beta, *o;
+    int32_t *cidx;
+    char *rk, *qkv;
+};
+
+__device__ __forceinline__ uint32_t fold4(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+// one workgroup of 256 threads per head
+__global__ __launch_bounds__(256) void k_pattern(Set s, int C, int W, int in_bytes, int u_bytes, int n)
+{
+    const int h = blockIdx.x, t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int kbytes = D * in_bytes;
+    uint32_t x = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        x ^= fold4(__builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(s.codes + (size_t)h * D * D + 4096 * w + 1024 * p + 16 * l)));
+    // rho and sigma (2 x 512 B), the lines (C x 512 B): 16-byte pieces
+    const int npiece = 64 + 32 * C;
+    for (int i = t; i < npiece; i += 256) {
+        const float *src = i < 32 ? s.rho + (size_t)h * D + 4 * i
+                           : i < 64 ? s.sigma + (size_t)h * D + 4 * (i - 32)
+                                    : s.cvec + (size_t)h * C * D + 4 * (i - 64);
+        x ^= fold4(*reinterpret_cast<const u32x4 *>(src));
+    }
+    if (t < C) x ^= (uint32_t)s.cidx[(size_t)h * C + t];
+    if (t < n) x ^= __float_as_uint(s.rgam[(size_t)h * W + t]);
+    // the n records' keys and corrections, 16-byte pieces
+    const char *rk = s.rk + (size_t)h * W * kbytes;
+    for (int i = t; i < n * kbytes / 16; i += 256) x ^= fold4(reinterpret_cast<const u32x4 *>(rk)[i]);
+    const char *ru = reinterpret_cast<const char *>(s.ru) + (size_t)h * W * u_bytes;
+    for (int i = t; i < n * u_bytes / 16; i += 256) x ^= fold4(reinterpret_cast<const u32x4 *>(ru)[i]);
+    // the token's k, q, v
+    if (t < 3 * kbytes / 16)
+        x ^= fold4(reinterpret_cast<const u32x4 *>(s.qkv + (size_t)h * 3 * kbytes)[t]);
+    x ^= __float_as_uint(s.alpha[h]) ^ __float_as_uint(s.beta[h]);
+    const float val = (float)(x & 0xffu);
+    // the output, the record's key and correction, its decay
+    if (t < D) __builtin_nontemporal_store(val, s.o + (size_t)h * D + t);
+    if (t < kbytes / 4)
+        __builtin_nontemporal_store(val, reinterpret_cast<float *>(s.rk + ((size_t)h * W + n) * kbytes) + t);
+    if (t < u_bytes / 4)
+        __builtin_nontemporal_store(val, reinterpret_cast<float *>(reinterpret_cast<char *>(s.ru) +
+                                                                   ((size_t)h * W + n) * u_bytes) + t);
+    if (t == 0) s.rgam[(size_t)h * W + n] = val;
+}
+
+__global__ __launch_bounds__(256) void k_read(const u32x4 *src, size_t n16, size_t per16, uint32_t *sink)
+{
+    const size_t base = (size_t)blockIdx.x * per16;
+    uint32_t x = 0;
+    for (size_t i = threadIdx.x; i < per16; i += 256)
+        if (base + i < n16) x ^= fold4(__builtin_nontemporal_load(src + base + i));
+    if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads
+}
+
+template <typename F>
+hipError_t time_launches(int reps, float *us, F launch)
+{
+    hipEvent_t e0, e1;
+    hipError_t err = hipEventCreate(&e0);
+    if (err != hipSuccess) return err;
+    err = hipEventCreate(&e1);
+    if (err != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return err;
+    }
+    for (int i = 0; i < 3; ++i) launch(i);
+    err = hipEventRecord(e0, nullptr);
+    for (int i = 0; i < reps; ++i) launch(i);
+    if (err == hipSuccess) err = hipEventRecord(e1, nullptr);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 0.0f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    if (err == hipSuccess) err = hipGetLastError();
+    *us = 1e3f * ms / (float)reps;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return err;
+}
+
+}  // namespace
+
+extern "C" int lqp_append_pattern(int heads, int C, int W, int in_bytes, int u_bytes, int n, int reps, float *us)
+{
+    if (heads <= 0 || C < 0 || C > 8 || W < 1 || W > 64 || (in_bytes != 2 && in_bytes != 4) || u_bytes <= 0 ||
+        u_bytes % 16 != 0 || u_bytes > 512 || n < 0 || n >= W || reps <= 0 || !us)
+        return (int)hipErrorInvalidValue;
+    const size_t H = (size_t)heads, kb = (size_t)D * in_bytes;
+    Set sets[NSETS] = {};
+    hipError_t err = hipSuccess;
+    for (int j = 0; j < NSETS && err == hipSuccess; ++j) {
+        Set &s = sets[j];
+        struct {
+            void **p;
+            size_t bytes;
+        } a[] = {{(void **)&s.codes, H * D * D},          {(void **)&s.rho, H * D * 4},
+                 {(void **)&s.sigma, H * D * 4},          {(void **)&s.cvec, H * (C > 0 ? C : 1) * D * 4},
+                 {(void **)&s.cidx, H * (C > 0 ? C : 1) * 4}, {(void **)&s.rgam, H * W * 4},
+                 {(void **)&s.rk, H * W * kb},            {(void **)&s.ru, H * W * u_bytes},
+                 {(void **)&s.qkv, H * 3 * kb},           {(void **)&s.alpha, H * 4},
+                 {(void **)&s.beta, H * 4},               {(void **)&s.o, H * D * 4}};
+        for (auto &e : a) {
+            if (err != hipSuccess) break;
+            err = hipMalloc(e.p, e.bytes);
+            if (err == hipSuccess) err = hipMemset(*e.p, 0, e.bytes);
+        }
+    }
+    if (err == hipSuccess)
+        err = time_launches(reps, us, [&](int i) {
+            hipLaunchKernelGGL(k_pattern, dim3(heads), dim3(256), 0, nullptr, sets[i % NSETS], C, W, in_bytes,
+                               u_bytes, n);
+        });
+    for (auto &s : sets)
+        for (void *p : {(void *)s.codes, (void *)s.rho, (void *)s.sigma, (void *)s.cvec, (void *)s.cidx,
+                        (void *)s.rgam, (void *)s.rk, (void *)s.ru, (void *)s.qkv, (void *)s.alpha, (void *)s.beta,
+                        (void *)s.o})
+            if (p) (void)hipFree(p);
+    return (int)err;
+}
+
+extern "C" int lqp_read_ceiling(size_t bytes, int reps, float *us)
+{
+    if (bytes < 16 || reps <= 0 || !us) return (int)hipErrorInvalidValue;
+    const size_t n16 = bytes / 16, per16 = 21504 / 16, blocks = (n16 + per16 - 1) / per16;
+    u32x4 *src[NSETS] = {};
+    uint32_t *sink = nullptr;
+    hipError_t err = hipMalloc(&sink, 16);
+    for (int j = 0; j < NSETS && err == hipSuccess; ++j) {
+        err = hipMalloc(&src[j], n16 * 16);
+        if (err == hipSuccess) err = hipMemset(src[j], 1, n16 * 16);
+    }
+    if (err == hipSuccess)
+        err = time_launches(reps, us, [&](int i) {
+            hipLaunchKernelGGL(k_read, dim3((unsigned)blocks), dim3(256), 0, nullptr, src[i % NSETS], n16, per16,
+                               sink);
+        });
+    for (auto p : src)
+        if (p) (void)hipFree(p);
+    if (sink) (void)hipFree(sink);
+    return (int)err;
+}

@@ -9,6 +9,10 @@ Programs (each is what comes after `rocprofv3 ... --`):
       a copy-shaped elementwise kernel (y = -x: 4 bytes read and 4 written
       per element; torch's same-dtype copy_ is a DMA blit, not a kernel) of
       known size, to calibrate FETCH_SIZE and WRITE_SIZE against bytes moved
+  python3 -m quantized_recurrent_state_amd.profiling pattern [--workload b512] [--reps 20]
+      the append's memory traffic alone (libleapq_probe.so: the append's
+      loads and stores in the state layout, no arithmetic) at every window
+      position, and a plain streaming read of the same bytes; one JSON object
 
 Reductions (CPU only, read the CSV files rocprofv3 wrote):
 
@@ -23,6 +27,7 @@ Reductions (CPU only, read the CSV files rocprofv3 wrote):
       SQ_VALU_MFMA_COEXEC_CYCLES, SQ_INSTS_MFMA) counter runs
 """
 import argparse
+import ctypes
 import csv
 import hashlib
 import json
@@ -31,6 +36,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
+D = 128
 
 
 # the sources of the append kernel: its traffic figure holds while they are unchanged
@@ -89,6 +95,69 @@ def run_copy(mib, reps):
         torch.neg(x, out=y)  # an elementwise kernel: one read and one write per element
     torch.cuda.synchronize()
     print(f"[profiling] copy {mib} MiB x {reps} done", flush=True)
+
+
+_PROBE = None
+
+
+def probe_lib():
+    """libleapq_probe.so (built beside libleapq.so).  Raises if it is missing."""
+    global _PROBE
+    if _PROBE is None:
+        from . import build as _build
+
+        if not os.path.exists(_build.PROBE_LIB):
+            raise RuntimeError(f"{_build.PROBE_LIB} not found; run __graft_entry__.build()")
+        L = ctypes.CDLL(_build.PROBE_LIB)
+        i32 = ctypes.c_int
+        L.lqp_append_pattern.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_float)]
+        L.lqp_append_pattern.restype = i32
+        L.lqp_read_ceiling.argtypes = [ctypes.c_size_t, i32, ctypes.POINTER(ctypes.c_float)]
+        L.lqp_read_ceiling.restype = i32
+        _PROBE = L
+    return _PROBE
+
+
+def append_pattern(heads, C, W, in_bytes, u_bytes, positions, reps=20):
+    """Mean microseconds per launch of the append's memory traffic alone, at
+    each record count n in `positions`: {n: us}."""
+    out = {}
+    for n in positions:
+        us = ctypes.c_float()
+        rc = probe_lib().lqp_append_pattern(heads, C, W, in_bytes, u_bytes, n, reps, ctypes.byref(us))
+        if rc != 0:
+            raise RuntimeError(f"lqp_append_pattern(n={n}) failed with HIP error {rc}")
+        out[n] = float(us.value)
+    return out
+
+
+def read_ceiling(nbytes, reps=20):
+    """GB/s of a plain streaming read of `nbytes` (four buffers in turn)."""
+    us = ctypes.c_float()
+    rc = probe_lib().lqp_read_ceiling(int(nbytes), reps, ctypes.byref(us))
+    if rc != 0:
+        raise RuntimeError(f"lqp_read_ceiling failed with HIP error {rc}")
+    return nbytes / (us.value * 1e-6) / 1e9
+
+
+def run_pattern(workload, reps):
+    from . import metrics, workloads
+
+    wl = workloads.WORKLOADS[workload]
+    H, W, C = wl.batch * wl.heads, wl.window, wl.n_comp
+    in_bytes = 2 if wl.in_dtype == "bf16" else 4
+    pos = list(range(W - 1))
+    t = append_pattern(H, C, W, in_bytes, 4 * D, pos, reps)
+    by = {n: metrics.append_bytes(n, C, in_bytes) * H for n in pos}
+    mean_us = sum(t.values()) / len(t)
+    mean_b = sum(by.values()) / len(by)
+    res = {"workload": wl.name, "heads": H, "positions": f"0..{W - 2}",
+           "us_by_position": [round(t[n], 2) for n in pos],
+           "gbps_by_position": [round(by[n] / (t[n] * 1e-6) / 1e9, 1) for n in pos],
+           "us_mean": mean_us, "gbps_mean": mean_b / (mean_us * 1e-6) / 1e9,
+           "read_ceiling_gbps": read_ceiling(int(mean_b), reps)}
+    print(json.dumps(res), flush=True)
+    return res
 
 
 # ---------------------------------------------------------------- reductions
@@ -185,6 +254,9 @@ def main(argv=None):
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=4)
+    pt = sub.add_parser("pattern")
+    pt.add_argument("--workload", default="b512")
+    pt.add_argument("--reps", type=int, default=20)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", default="k_append<", help="substring of the kernel name")
     t.add_argument("--kernel-src", nargs="+", default=list(APPEND_SOURCES))
@@ -208,6 +280,8 @@ def main(argv=None):
         run_layer(a.workload, a.windows, a.fused)
     elif a.cmd == "copy":
         run_copy(a.mib, a.reps)
+    elif a.cmd == "pattern":
+        run_pattern(a.workload, a.reps)
     elif a.cmd == "traffic":
         traffic(a)
     elif a.cmd == "valu":

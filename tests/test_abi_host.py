@@ -32,6 +32,19 @@ def test_header_symbols_exported():
         assert hasattr(L, n), n
 
 
+def test_probe_library_loads():
+    """The measurement probes (libleapq_probe.so) are built beside the
+    library and export their two entry points; a call with invalid
+    arguments returns hipErrorInvalidValue (1) before any HIP call."""
+    from quantized_recurrent_state_amd import profiling
+    P = profiling.probe_lib()
+    us = ctypes.c_float()
+    assert P.lqp_append_pattern(0, 4, 16, 2, 512, 0, 10, ctypes.byref(us)) == 1
+    assert P.lqp_append_pattern(16, 4, 16, 2, 512, 16, 10, ctypes.byref(us)) == 1  # n >= W
+    assert P.lqp_append_pattern(16, 4, 16, 2, 100, 0, 10, ctypes.byref(us)) == 1   # not 16-byte pieces
+    assert P.lqp_read_ceiling(0, 10, ctypes.byref(us)) == 1
+
+
 PAGE_TITLES = ("Recurrent-state quantization for linear attention", "LeapQuant")
 
 
