@@ -1,6 +1,7 @@
 """Build libleapq.so (gfx950) in-tree with hipcc, and the measurement probes
-(libleapq_probe.so: the append's memory traffic without its arithmetic, a
-plain streaming read) beside it.
+beside it (libleapq_probe.so: the append's memory traffic without its
+arithmetic, a plain streaming read, matrix/VALU co-execution; the same
+source built with AGPR accumulators as libleapq_probe_agpr.so).
 
 Flags that matter for the numbers:
   -ffp-contract=off   no fused multiply-add except the explicit ones
@@ -24,6 +25,7 @@ LIB = os.path.join(PKG, "libleapq.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("leapq_append.hip", "leapq_fold.hip", "leapq_dense.hip", "leapq_abi.cpp")]
 PROBE_LIB = os.path.join(PKG, "libleapq_probe.so")
+PROBE_LIB_AGPR = os.path.join(PKG, "libleapq_probe_agpr.so")
 PROBE_SOURCE = os.path.join(CSRC, "probe_pattern.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,18 +52,22 @@ def _run(cmd, verbose):
 def build(out=LIB, extra=(), verbose=False, probe=True):
     """Compile every HIP source (one hipcc process each, in parallel) and
     link them into `out`, and (probe) the probe library; returns `out`."""
-    tmp, ptmp = out + ".tmp", PROBE_LIB + ".tmp"
+    tmp, ptmp, ptmp2 = out + ".tmp", PROBE_LIB + ".tmp", PROBE_LIB_AGPR + ".tmp"
     with tempfile.TemporaryDirectory(prefix="leapq_build_") as d:
         objs = [os.path.join(d, os.path.basename(src) + ".o") for src in SOURCES]
         cmds = [[HIPCC, *FLAGS, *extra, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
         if probe:
             cmds.append([HIPCC, *FLAGS, "-shared", PROBE_SOURCE, "-o", ptmp])
+            # the one -mllvm option of FLAGS is the accumulator form
+            agpr_flags = [f for f in FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+            cmds.append([HIPCC, *agpr_flags, "-shared", PROBE_SOURCE, "-o", ptmp2])
         with cf.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     if probe:
         os.replace(ptmp, PROBE_LIB)
+        os.replace(ptmp2, PROBE_LIB_AGPR)
     return out
 
 

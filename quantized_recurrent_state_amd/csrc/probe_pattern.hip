@@ -16,7 +16,19 @@
 // lqp_read_ceiling: a plain streaming read (non-temporal 16-byte loads, 21.5
 // KB per workgroup) of `bytes`, in four buffers used in turn.
 //
-// Both return 0, or the HIP error code; times are mean microseconds per
+// lqp_coexec: do K = 1 matrix steps (v_mfma_f32_32x32x1_2b_f32, the fold's
+// record steps) of some waves overlap plain VALU work of other waves on the
+// same SIMD?  16,384 workgroups of 256 threads; `lds` bytes of dynamic LDS
+// per workgroup hold the occupancy where the fold's launches have it (40 KB:
+// 4 workgroups per CU).  mode 0: every workgroup runs a chain of 128 matrix
+// steps; mode 1: every workgroup runs 2,048 dependent FMAs per lane (8
+// chains); mode 2: even workgroups the matrix chain, odd ones the FMAs.  If
+// the two kinds overlapped, mode 2 would take about as long as the longer of
+// modes 0 and 1 at half the workgroups each; if they take turns, about the
+// sum of their halves.  The library is built twice: with the accumulators
+// in VGPRs (the decode library's flag) and in AGPRs (libleapq_probe_agpr.so).
+//
+// All return 0, or the HIP error code; times are mean microseconds per
 // launch over `reps` launches after 3 untimed ones, on the null stream.
 #include <hip/hip_runtime.h>
 
@@ -84,6 +96,49 @@ __global__ __launch_bounds__(256) void k_read(const u32x4 *src, size_t n16, size
     for (size_t i = threadIdx.x; i < per16; i += 256)
         if (base + i < n16) x ^= fold4(__builtin_nontemporal_load(src + base + i));
     if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads
+}
+
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_coexec(float *out, float s)
+{
+    extern __shared__ float pad[];
+    const int t = threadIdx.x;
+    const bool do_m = MODE == 0 || (MODE == 2 && (blockIdx.x & 1) == 0);
+    const bool do_v = MODE == 1 || (MODE == 2 && (blockIdx.x & 1) == 1);
+    f32x32 acc0, acc1;
+    for (int e = 0; e < 32; ++e) {
+        acc0[e] = s * e;
+        acc1[e] = s + e;
+    }
+    float x[8];
+    for (int j = 0; j < 8; ++j) x[j] = s * (t + j);
+    const float a = s * t, b0 = s + t, b1 = s - t;
+    if (do_m) {
+        for (int rep = 0; rep < 4; ++rep) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b1, acc1, 0, 0, 0);
+            }
+        }
+    }
+    if (do_v) {
+        for (int rep = 0; rep < 4; ++rep) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(x[j], b0, b1);
+        }
+    }
+    float sum = 0.0f;
+    for (int e = 0; e < 32; ++e) sum += acc0[e] + acc1[e];
+    for (int j = 0; j < 8; ++j) sum += x[j];
+    if (t == 0) pad[0] = sum;
+    out[(size_t)blockIdx.x * 256 + t] = sum;
 }
 
 template <typename F>
@@ -170,5 +225,24 @@ extern "C" int lqp_read_ceiling(size_t bytes, int reps, float *us)
     for (auto p : src)
         if (p) (void)hipFree(p);
     if (sink) (void)hipFree(sink);
+    return (int)err;
+}
+
+extern "C" int lqp_coexec(int mode, int lds, int reps, float *us)
+{
+    constexpr int blocks = 16384;
+    if (mode < 0 || mode > 2 || lds < 0 || lds > 65536 || reps <= 0 || !us) return (int)hipErrorInvalidValue;
+    float *out = nullptr;
+    hipError_t err = hipMalloc(&out, sizeof(float) * blocks * 256);
+    if (err == hipSuccess)
+        err = time_launches(reps, us, [&](int) {
+            if (mode == 0)
+                hipLaunchKernelGGL(k_coexec<0>, dim3(blocks), dim3(256), lds, nullptr, out, 1e-3f);
+            else if (mode == 1)
+                hipLaunchKernelGGL(k_coexec<1>, dim3(blocks), dim3(256), lds, nullptr, out, 1e-3f);
+            else
+                hipLaunchKernelGGL(k_coexec<2>, dim3(blocks), dim3(256), lds, nullptr, out, 1e-3f);
+        });
+    if (out) (void)hipFree(out);
     return (int)err;
 }

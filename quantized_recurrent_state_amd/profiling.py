@@ -9,6 +9,9 @@ Programs (each is what comes after `rocprofv3 ... --`):
       a copy-shaped elementwise kernel (y = -x: 4 bytes read and 4 written
       per element; torch's same-dtype copy_ is a DMA blit, not a kernel) of
       known size, to calibrate FETCH_SIZE and WRITE_SIZE against bytes moved
+  python3 -m quantized_recurrent_state_amd.profiling coexec [--agpr] [--lds 40960] [--reps 10]
+      matrix-step / VALU co-execution probe: all-matrix, all-VALU and half/half
+      launches (libleapq_probe.so, or with --agpr libleapq_probe_agpr.so)
   python3 -m quantized_recurrent_state_amd.profiling pattern [--workload b512] [--reps 20]
       the append's memory traffic alone (libleapq_probe.so: the append's
       loads and stores in the state layout, no arithmetic) at every window
@@ -97,25 +100,50 @@ def run_copy(mib, reps):
     print(f"[profiling] copy {mib} MiB x {reps} done", flush=True)
 
 
-_PROBE = None
+_PROBE = {}
 
 
-def probe_lib():
-    """libleapq_probe.so (built beside libleapq.so).  Raises if it is missing."""
-    global _PROBE
-    if _PROBE is None:
+def probe_lib(agpr=False):
+    """libleapq_probe.so, or with agpr libleapq_probe_agpr.so (built beside
+    libleapq.so).  Raises if it is missing."""
+    if agpr not in _PROBE:
         from . import build as _build
 
-        if not os.path.exists(_build.PROBE_LIB):
-            raise RuntimeError(f"{_build.PROBE_LIB} not found; run __graft_entry__.build()")
-        L = ctypes.CDLL(_build.PROBE_LIB)
+        path = _build.PROBE_LIB_AGPR if agpr else _build.PROBE_LIB
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} not found; run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
         i32 = ctypes.c_int
         L.lqp_append_pattern.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_float)]
         L.lqp_append_pattern.restype = i32
         L.lqp_read_ceiling.argtypes = [ctypes.c_size_t, i32, ctypes.POINTER(ctypes.c_float)]
         L.lqp_read_ceiling.restype = i32
-        _PROBE = L
-    return _PROBE
+        L.lqp_coexec.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_float)]
+        L.lqp_coexec.restype = i32
+        _PROBE[agpr] = L
+    return _PROBE[agpr]
+
+
+def coexec(agpr=False, lds=40960, reps=10):
+    """Microseconds per launch of the co-execution probe: {mode: us} for
+    mode 0 (all matrix steps), 1 (all VALU), 2 (half and half)."""
+    out = {}
+    for mode in (0, 1, 2):
+        us = ctypes.c_float()
+        rc = probe_lib(agpr).lqp_coexec(mode, lds, reps, ctypes.byref(us))
+        if rc != 0:
+            raise RuntimeError(f"lqp_coexec(mode={mode}) failed with HIP error {rc}")
+        out[mode] = float(us.value)
+    return out
+
+
+def run_coexec(agpr, lds, reps):
+    t = coexec(agpr, lds, reps)
+    res = {"accumulators": "AGPR" if agpr else "VGPR", "lds_bytes_per_workgroup": lds, "workgroups": 16384,
+           "us_all_matrix": t[0], "us_all_valu": t[1], "us_half_half": t[2],
+           "us_halves_in_turn": (t[0] + t[1]) / 2, "us_halves_overlapped": max(t[0], t[1]) / 2}
+    print(json.dumps(res), flush=True)
+    return res
 
 
 def append_pattern(heads, C, W, in_bytes, u_bytes, positions, reps=20):
@@ -254,6 +282,10 @@ def main(argv=None):
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=4)
+    cx = sub.add_parser("coexec")
+    cx.add_argument("--agpr", action="store_true")
+    cx.add_argument("--lds", type=int, default=40960)
+    cx.add_argument("--reps", type=int, default=10)
     pt = sub.add_parser("pattern")
     pt.add_argument("--workload", default="b512")
     pt.add_argument("--reps", type=int, default=20)
@@ -280,6 +312,8 @@ def main(argv=None):
         run_layer(a.workload, a.windows, a.fused)
     elif a.cmd == "copy":
         run_copy(a.mib, a.reps)
+    elif a.cmd == "coexec":
+        run_coexec(a.agpr, a.lds, a.reps)
     elif a.cmd == "pattern":
         run_pattern(a.workload, a.reps)
     elif a.cmd == "traffic":

@@ -33,9 +33,10 @@ def test_header_symbols_exported():
 
 
 def test_probe_library_loads():
-    """The measurement probes (libleapq_probe.so) are built beside the
-    library and export their two entry points; a call with invalid
-    arguments returns hipErrorInvalidValue (1) before any HIP call."""
+    """The measurement probes (libleapq_probe.so, and libleapq_probe_agpr.so
+    for the co-execution probe with AGPR accumulators) are built beside the
+    library and export their entry points; a call with invalid arguments
+    returns hipErrorInvalidValue (1) before any HIP call."""
     from quantized_recurrent_state_amd import profiling
     P = profiling.probe_lib()
     us = ctypes.c_float()
@@ -43,6 +44,10 @@ def test_probe_library_loads():
     assert P.lqp_append_pattern(16, 4, 16, 2, 512, 16, 10, ctypes.byref(us)) == 1  # n >= W
     assert P.lqp_append_pattern(16, 4, 16, 2, 100, 0, 10, ctypes.byref(us)) == 1   # not 16-byte pieces
     assert P.lqp_read_ceiling(0, 10, ctypes.byref(us)) == 1
+    for agpr in (False, True):
+        Q = profiling.probe_lib(agpr)
+        assert Q.lqp_coexec(3, 0, 10, ctypes.byref(us)) == 1  # no mode 3
+        assert Q.lqp_coexec(2, 70000, 10, ctypes.byref(us)) == 1  # more LDS than a workgroup gets
 
 
 PAGE_TITLES = ("Recurrent-state quantization for linear attention", "LeapQuant")
