@@ -225,6 +225,18 @@ def test_full_size_b512_layer_sampled():
     _finish(rep)
 
 
+def test_full_size_b512_layer_every_head():
+    """One whole b512 layer (16,384 heads, bf16 inputs) through one window in
+    the benchmark's schedule (15 appends, then the last append and the fold
+    in one launch), every head in the oracle: all 33.5M outputs and, after
+    the fold, all 268M codes with their scales, compensator indices and
+    lines, compared bit for bit."""
+    wl = WL["b512"]
+    rep, _, _ = run_layer(wl, tokens=wl.window, sample=None, gen_device="cuda", check_every_token=False,
+                          fused=True)
+    _finish(rep)
+
+
 def test_full_size_b128_layer_sampled():
     wl = WL["b128"]
     sample = list(range(3, 4096, 64))
