@@ -57,6 +57,16 @@ def test_plain_append_on_fp32_key_layer():
     _finish(rep)
 
 
+def test_gated_full_size_b512_every_head():
+    """A whole gated, normalizing b512 layer, every head in the oracle: one
+    window in the benchmark's schedule, all outputs and, after the fold, the
+    whole boundary state bit for bit."""
+    wl = WL["b512"]
+    rep, _, _ = run_layer(wl, tokens=wl.window, sample=None, gen_device="cuda", check_every_token=False,
+                          fused=True, gated=G, qk_norm=True)
+    _finish(rep)
+
+
 def test_gated_full_size_b512_sampled():
     """The benchmark's launch shape, gated and normalized: 64 sampled heads
     through 2 windows, the fused last token included."""

@@ -92,6 +92,16 @@ def test_kda_dense_baseline():
     assert eo < 1e-5 and es < 1e-5
 
 
+def test_kda_full_size_b512_every_head():
+    """A whole b512 KDA layer, every head in the oracle: one window in the
+    benchmark's schedule, all outputs and, after the fold, the whole
+    boundary state bit for bit."""
+    wl = WL["b512_kda"]
+    rep, _, _ = run_layer(wl, tokens=wl.window, sample=None, gen_device="cuda", check_every_token=False,
+                          fused=True)
+    _finish(rep)
+
+
 def test_kda_full_size_b512_sampled():
     """The KDA benchmark's launch shape (512 x 32 heads, bf16 inputs): 64
     sampled heads through 2 windows, the fused last token included."""
