@@ -145,38 +145,47 @@ __device__ __forceinline__ void rebuild(const MMap &a, const HeadState &hs, cons
         for (int m = 0; m < 16; ++m) TS(S, p, m) = (code_f(cw[p][m >> 2], m & 3) * ap) * sg[m];
     }
     if (!R1 && lines && C > 0) {
-        // line of each of the thread's rows / columns (-1: none).  An entry
-        // on a row line and a column line is +0 in the line extracted second
-        // (it was zeroed by the first), so adding only one of the two gives
-        // the same bits as adding both in order.
-        int rl[4] = {-1, -1, -1, -1}, cl[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) cl[m] = -1;
+        // the line of each of the thread's row blocks and column entries, as
+        // 1 + the line's slot in a nibble (0: none): rows in rpk (nibble p),
+        // columns in cpk[0] (entries m < 8) and cpk[1] (m >= 8, nibble m - 8).
+        // An entry on a row line and a column line is +0 in the line
+        // extracted second (it was zeroed by the first), so adding the row
+        // line and then the column line gives the bits of adding both in
+        // extraction order.
+        uint32_t rpk = 0u, cpk[2] = {0u, 0u};
         for (int jj = 0; jj < C; ++jj) {
             const int id = __builtin_amdgcn_readfirstlane(sm.idx[jj]);
-            const bool isrow = id >= 0 && id < D, iscol = id >= D;
-            const int c = id - D;
-            const bool own_r = isrow && a.i == (id & 31);
-            const bool own_c = iscol && a.w == (c & 3) && a.h == ((c >> 2) & 1);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) rl[p] = (own_r && (id >> 5) == p) ? jj : rl[p];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) cl[m] = (own_c && (c >> 3) == m) ? jj : cl[m];
+            if (id >= 0 && id < D) {
+                const uint32_t bits = (uint32_t)(jj + 1) << (4 * (id >> 5));
+                rpk = a.i == (id & 31) ? rpk | bits : rpk;
+            } else if (id >= D && a.w == ((id - D) & 3)) {
+                const int c = id - D, mm = c >> 3;
+                const uint32_t bits = (uint32_t)(jj + 1) << (4 * (mm & 7));
+                const bool mine = a.h == ((c >> 2) & 1);
+                if (mm < 8)
+                    cpk[0] = mine ? cpk[0] | bits : cpk[0];
+                else
+                    cpk[1] = mine ? cpk[1] | bits : cpk[1];
+            }
         }
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-            if (rl[p] >= 0) {
-                const float *v = sm.lines + rl[p] * D;
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t e = (rpk >> (4 * p)) & 15u;
+            if (e != 0u) {
+                const float *v = sm.lines + (e - 1u) * D;
 #pragma unroll
                 for (int m = 0; m < 16; ++m) TS(S, p, m) = TS(S, p, m) + gr[p] * v[a.col(m)];
             }
+        }
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
-            if (cl[m] >= 0) {
-                const float *v = sm.lines + cl[m] * D;
+        for (int m = 0; m < 16; ++m) {
+            const uint32_t e = (cpk[m >> 3] >> (4 * (m & 7))) & 15u;
+            if (e != 0u) {
+                const float *v = sm.lines + (e - 1u) * D;
 #pragma unroll
                 for (int p = 0; p < 4; ++p) TS(S, p, m) = TS(S, p, m) + gr[p] * v[a.row(p)];
             }
+        }
     }
     // through the accumulators even when n == 0: one definition of S after
     // this point keeps it in one set of registers
